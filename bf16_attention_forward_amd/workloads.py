@@ -1,0 +1,196 @@
+"""Seeded synthetic workloads for bf16 attention forward.
+
+This module only draws inputs; it holds none of the attention arithmetic, so
+both the HIP path and the fp64 oracle can be fed from it.
+
+The shapes stand in for the workloads the pages measure: plain N(0,1)
+attention inputs (HipKittens summary, experiments section), video-diffusion
+self-attention over a latent token grid and cross-attention from video
+tokens to a short text sequence (MoonMath AI MI300X attention article, use
+case section: Wan2.1 text-to-video with BSHD tensors and arbitrary KV
+lengths).  No dataset or trained weights are involved: every tensor is
+drawn from a seeded generator.
+
+Recipe: torch CPU generator seeded per tensor, float32 normal draws, times
+the workload's scale factor (a power of two, so exact), rounded to bf16 by
+torch (round-to-nearest-even), created directly in the workload's layout.
+Seeds: s = 1000 + workload number; q, k, v and the non-finite injection
+sites use streams 4s, 4s+1, 4s+2, 4s+3.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+HEAD_DIM = 128
+DEFAULT_SCALE = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
+
+
+@dataclass(frozen=True)
+class Workload:
+    number: int
+    name: str
+    layout: str          # "bshd" or "bhsd"
+    B: int
+    H: int
+    Sq: int
+    Skv: int
+    q_factor: float = 1.0
+    k_factor: float = 1.0
+    v_factor: float = 1.0
+    modes: tuple = ("rtne", "rtna", "rtz")
+    nonfinite_instance: bool = False
+    note: str = ""
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.number
+
+    @property
+    def flops(self) -> int:
+        return 4 * self.B * self.H * self.Sq * self.Skv * HEAD_DIM
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once and O written once, bf16."""
+        return 2 * HEAD_DIM * self.B * self.H * (2 * self.Sq + 2 * self.Skv)
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "layout": self.layout, "B": self.B, "H": self.H,
+                "Sq": self.Sq, "Skv": self.Skv, "head_dim": HEAD_DIM}
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny_self_attn_bshd_b1_h2_s128", "bshd", 1, 2, 128, 128,
+                note="tiny self-attention"),
+    2: Workload(2, "self_attn_bhsd_b2_h16_s4096_k2x", "bhsd", 2, 16, 4096, 4096, k_factor=2.0,
+                nonfinite_instance=True, note="K scaled x2 to sharpen the softmax"),
+    3: Workload(3, "video_self_attn_bshd_b1_h12_s32760", "bshd", 1, 12, 32760, 32760,
+                q_factor=0.5, k_factor=0.5, v_factor=0.5, modes=("rtne",),
+                note="21x30x52 latent tokens"),
+    4: Workload(4, "video_text_cross_attn_bshd_b1_h12_sq32760_skv512", "bshd", 1, 12, 32760, 512,
+                k_factor=0.5, v_factor=0.5, note="32760 video tokens attend to 512 text tokens"),
+    5: Workload(5, "long_self_attn_bhsd_b1_h32_s16384", "bhsd", 1, 32, 16384, 16384,
+                modes=("rtz", "rtne"), note="long sequence"),
+}
+
+
+def shape(layout: str, B: int, H: int, S: int) -> tuple:
+    if layout == "bshd":
+        return (B, S, H, HEAD_DIM)
+    if layout == "bhsd":
+        return (B, H, S, HEAD_DIM)
+    raise ValueError(layout)
+
+
+def _draw(shape_, seed: int, factor: float) -> torch.Tensor:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    t = torch.randn(shape_, generator=g, dtype=torch.float32)
+    if factor != 1.0:
+        t = t * factor
+    return t.to(torch.bfloat16)
+
+
+def random_qkv(layout: str, B: int, H: int, Sq: int, Skv: int, seed: int,
+               q_factor: float = 1.0, k_factor: float = 1.0, v_factor: float = 1.0):
+    """Return (q, k, v) as bf16 CPU tensors in the given layout."""
+    q = _draw(shape(layout, B, H, Sq), 4 * seed + 0, q_factor)
+    k = _draw(shape(layout, B, H, Skv), 4 * seed + 1, k_factor)
+    v = _draw(shape(layout, B, H, Skv), 4 * seed + 2, v_factor)
+    return q, k, v
+
+
+def make_inputs(w: Workload, *, Sq: int | None = None, Skv: int | None = None,
+                B: int | None = None, H: int | None = None, seed: int | None = None):
+    """Draw the workload's q, k, v (bf16 CPU tensors); sizes may be overridden."""
+    return random_qkv(w.layout, B or w.B, H or w.H, Sq or w.Sq, Skv or w.Skv,
+                      w.seed if seed is None else seed, w.q_factor, w.k_factor, w.v_factor)
+
+
+@dataclass
+class Injection:
+    """Non-finite values planted into q and v (positions as (b, h, s, d))."""
+    q_sites: list = field(default_factory=list)   # (b, h, i, d, value)
+    v_sites: list = field(default_factory=list)   # (b, h, j, d, value)
+
+
+def inject_nonfinite(q: torch.Tensor, v: torch.Tensor, layout: str, seed: int,
+                     n_q=(3, 2, 2), n_v=(2, 2, 2), mixed_inf_column: bool = True) -> Injection:
+    """Plant NaN / +Inf / -Inf into q and v in place at seeded sites.
+
+    n_q, n_v: counts of (NaN, +Inf, -Inf).  With mixed_inf_column, one more
+    column of v (one head, one d) gets both a +Inf and a -Inf.
+    """
+    rng = np.random.default_rng(4 * seed + 3)
+    if layout == "bshd":
+        B, Sq, H, D = q.shape
+        Skv = v.shape[1]
+    else:
+        B, H, Sq, D = q.shape
+        Skv = v.shape[2]
+    inj = Injection()
+
+    def put(t, b, h, s, d, val):
+        if layout == "bshd":
+            t[b, s, h, d] = val
+        else:
+            t[b, h, s, d] = val
+
+    vals = [float("nan"), float("inf"), float("-inf")]
+    for kind, cnt in enumerate(n_q):
+        for _ in range(cnt):
+            b, h, i, d = (int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Sq)), int(rng.integers(D)))
+            put(q, b, h, i, d, vals[kind])
+            inj.q_sites.append((b, h, i, d, vals[kind]))
+    for kind, cnt in enumerate(n_v):
+        for _ in range(cnt):
+            b, h, j, d = (int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Skv)), int(rng.integers(D)))
+            put(v, b, h, j, d, vals[kind])
+            inj.v_sites.append((b, h, j, d, vals[kind]))
+    if mixed_inf_column and Skv >= 2:
+        b, h, d = int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(D))
+        j1, j2 = rng.choice(Skv, size=2, replace=False)
+        put(v, b, h, int(j1), d, float("inf"))
+        put(v, b, h, int(j2), d, float("-inf"))
+        inj.v_sites.append((b, h, int(j1), d, float("inf")))
+        inj.v_sites.append((b, h, int(j2), d, float("-inf")))
+    return inj
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> numpy uint16 bit patterns (a view of the same bytes)."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def row_ids(layout: str, B: int, H: int, Sq: int, b, h, i) -> np.ndarray:
+    """Flat query-row ids r = (b*H + h)*Sq + i (independent of layout)."""
+    return (np.asarray(b) * H + np.asarray(h)) * Sq + np.asarray(i)
+
+
+def gather_rows(o_bits: np.ndarray, layout: str, B: int, H: int, Sq: int, rows) -> np.ndarray:
+    """Pick rows (flat ids) out of an output tensor's bf16 bits -> [n, 128]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    i = rows % Sq
+    bh = rows // Sq
+    h = bh % H
+    b = bh // H
+    if layout == "bshd":
+        return o_bits.reshape(B, Sq, H, HEAD_DIM)[b, i, h]
+    return o_bits.reshape(B, H, Sq, HEAD_DIM)[b, h, i]
+
+
+def sample_rows(B: int, H: int, Sq: int, n_per_head: int, seed: int, tile: int = 128) -> np.ndarray:
+    """Seeded row sample: per head the first and last rows, the first row of
+    the last (ragged) tile, and n_per_head random rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for bh in range(B * H):
+        base = bh * Sq
+        fixed = {0, Sq - 1, (Sq - 1) // tile * tile, min(Sq - 1, tile - 1)}
+        rnd = rng.integers(0, Sq, size=n_per_head)
+        out.extend(base + np.array(sorted(fixed | set(int(x) for x in rnd))))
+    return np.array(out, dtype=np.int64)

@@ -1,0 +1,147 @@
+"""fp64 CPU oracle for bf16 attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library behind
+``attn_fwd_bf16``) never imports it and shares no code with it.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, no fast-math);
+this module only loads the shared library with ctypes and moves numpy
+arrays in and out.  ``gate.py`` holds the accuracy-gate metric.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+LAYOUTS = {"bshd": 0, "bhsd": 1}
+MODES = {"rtne": 0, "rtna": 1, "rtz": 2}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile attn_oracle.c into liboracle.so with gcc (IEEE-exact flags)."""
+    if force or not os.path.exists(_LIB_PATH):
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", "-fno-finite-math-only",
+               _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    _lib = configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def configure(lib):
+    """Attach ctypes signatures to a loaded oracle library."""
+    lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.oracle_round_bf16_array.restype = None
+    lib.oracle_round_bf16_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_bf16_to_double.restype = ctypes.c_double
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_attention.restype = ctypes.c_int
+    lib.oracle_attention.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int]
+    lib.oracle_version.restype = ctypes.c_int
+    return lib
+
+
+def round_bf16(x, mode: str = "rtne") -> np.ndarray:
+    """fp64 -> bf16 bit patterns (uint16), exact, per rounding mode."""
+    lib = _load()
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib.oracle_round_bf16_array(a.ctypes.data, out.ctypes.data, a.size, MODES[mode])
+    return out
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 (pure bit placement)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class OracleResult:
+    """Per-row outputs of the oracle, each shaped [nrows, 128] (float64)."""
+
+    def __init__(self, rows, o_exact, sigma, o_method, sigma_method):
+        self.rows = rows
+        self.o_exact = o_exact
+        self.sigma = sigma
+        self.o_method = o_method
+        self.sigma_method = sigma_method
+
+    def rounded(self, mode: str) -> np.ndarray:
+        return round_bf16(self.o_exact, mode)
+
+
+def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = True,
+              l_from_rounded: bool = False, nthreads: int = 0) -> OracleResult:
+    """Evaluate the oracle.
+
+    q, k, v: uint16 arrays holding bf16 bit patterns, shaped [B,S,H,128]
+    (bshd) or [B,H,S,128] (bhsd).  rows: optional int64 array of flat row ids
+    r = (b*H + h)*Sq + i; None means every row in that order.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    if q.ndim != 4 or q.shape[-1] != 128 or k.shape != v.shape or k.ndim != 4:
+        raise ValueError("q, k, v must be [.., .., .., 128] with k.shape == v.shape")
+    if layout == "bshd":
+        B, Sq, H, _ = q.shape
+        Skv = k.shape[1]
+        if k.shape[0] != B or k.shape[2] != H:
+            raise ValueError("batch/head mismatch")
+    elif layout == "bhsd":
+        B, H, Sq, _ = q.shape
+        Skv = k.shape[2]
+        if k.shape[0] != B or k.shape[1] != H:
+            raise ValueError("batch/head mismatch")
+    else:
+        raise ValueError(layout)
+    if rows is None:
+        nrows = B * H * Sq
+        rows_arr = None
+        rows_ptr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+        if nrows and (rows_arr.min() < 0 or rows_arr.max() >= B * H * Sq):
+            raise ValueError("row id out of range")
+        rows_ptr = rows_arr.ctypes.data
+    o = np.empty((nrows, 128), np.float64)
+    sg = np.empty((nrows, 128), np.float64)
+    om = np.empty((nrows, 128), np.float64) if method else None
+    sm = np.empty((nrows, 128), np.float64) if method else None
+    rc = lib.oracle_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, LAYOUTS[layout],
+                              B, H, Sq, Skv, ctypes.c_float(scale), rows_ptr, nrows,
+                              o.ctypes.data, sg.ctypes.data,
+                              om.ctypes.data if method else None,
+                              sm.ctypes.data if method else None,
+                              1 if l_from_rounded else 0, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention failed ({rc})")
+    rows_out = np.arange(nrows, dtype=np.int64) if rows_arr is None else rows_arr
+    return OracleResult(rows_out, o, sg, om, sm)

@@ -1,0 +1,240 @@
+/*
+ * attn_oracle.c -- plain, slow fp64 CPU reference for non-causal attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path
+ * (the HIP kernels behind attn_fwd_bf16) never calls, links or includes it,
+ * and this file shares no code, header, table or constant with that path.
+ *
+ * What it computes (sources are the web pages the method is described on):
+ *
+ *   - The operation is the fused softmax(Q K^T * scale) V of a transformer
+ *     attention layer, bf16 inputs, head dimension 128, BSHD or BHSD layout,
+ *     any query / key length (MoonMath AI MI300X attention article, opening
+ *     paragraphs describing the kernel and its interface).
+ *   - The output is bf16 and the rounding to bf16 is selectable among
+ *     round-to-nearest-even, round-to-nearest-ties-away and round-toward-zero
+ *     (same article, paragraph on limitations and numerics, and the
+ *     benchmark section that measures each of the three modes).
+ *
+ * The plain definition is evaluated in two passes per query row, in fp64,
+ * with no blocking, no online rescaling and no reordering:
+ *     s_j   = scale * sum_d q_d k_{j,d}            (d ascending)
+ *     m     = max_j s_j
+ *     p_j   = exp(s_j - m)
+ *     l     = sum_j p_j                            (j ascending)
+ *     o_d   = (sum_j p_j v_{j,d}) / l
+ * Alongside it goes sigma_d = sqrt(sum_j p_j^2 v_{j,d}^2) / l, the RMS size
+ * of the terms the p.V contraction adds up; the accuracy gate uses it as the
+ * floor of the ULP scale for outputs that cancel to near zero.
+ *
+ * "Method" companion (an approximation the kernel makes, not the definition):
+ * the probabilities enter the p.V matrix product as bf16 (the article runs
+ * O += P V on the matrix cores; the AITER docs index names the bf16
+ * 16x16x32 MFMA for both attention products on gfx950).  This file writes
+ * that step out directly from the pages' order of operations, with the
+ * reading documented in the design notes: x_j = s_j log2(e), M = ceil(max x),
+ * pt_j = bf16_RTNE(2^(x_j - M)), and
+ *     o_method_d = sum_j pt_j v_{j,d} / L,  L = sum_j 2^(x_j - M)
+ * (or L = sum_j pt_j when l_from_rounded is set).  Because M only rescales by
+ * an exact power of two, pt_j does not depend on how keys are tiled.
+ *
+ * Rounding of the fp64 result to bf16 is done directly (no fp32 step) and
+ * exactly, by locating the value on the bf16 grid; NaN maps to 0x7FC0.
+ *
+ * Build: plain C99, no -ffast-math, -ffp-contract=off (so IEEE NaN/Inf rules
+ * hold and no multiply-add is fused), OpenMP across rows.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_D 128
+
+enum { OR_LAYOUT_BSHD = 0, OR_LAYOUT_BHSD = 1 };
+enum { OR_RTNE = 0, OR_RTNA = 1, OR_RTZ = 2 };
+
+int oracle_version(void) { return 1; }
+
+/* bf16 bit pattern -> exact double. */
+static double bf16_to_double(uint16_t h) {
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double oracle_bf16_to_double(uint16_t h) { return bf16_to_double(h); }
+
+/*
+ * Round an fp64 value to bf16 under the selected mode, exactly.
+ *
+ * bf16: 1 sign bit, 8 exponent bits (bias 127), 7 stored fraction bits.
+ * For |x| in the binade [2^e, 2^(e+1)) the spacing of bf16 values is
+ * 2^(e-7); below 2^-126 the spacing stays 2^-133 (subnormals).  x / spacing
+ * is exact in fp64 (division by a power of two), its integer part n and the
+ * fraction f = x/spacing - n are exact as well, and the mode picks n or n+1.
+ */
+uint16_t oracle_round_bf16(double x, int mode) {
+    if (isnan(x)) return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a)) return sign | 0x7F80;
+    if (a == 0.0) return sign;
+    const double two128 = ldexp(1.0, 128);
+    if (a >= two128) {                      /* beyond the largest binade */
+        return (mode == OR_RTZ) ? (uint16_t)(sign | 0x7F7F) : (uint16_t)(sign | 0x7F80);
+    }
+    int e2;
+    frexp(a, &e2);                          /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                         /* floor(log2 a) */
+    if (e < -126) e = -126;                 /* subnormal spacing */
+    double spacing = ldexp(1.0, e - 7);
+    double n = a / spacing;                 /* exact */
+    double fl = floor(n);
+    double fr = n - fl;                     /* exact */
+    double m = fl;
+    if (mode == OR_RTNE) {
+        if (fr > 0.5) m = fl + 1.0;
+        else if (fr == 0.5) m = (fmod(fl, 2.0) == 1.0) ? fl + 1.0 : fl;
+    } else if (mode == OR_RTNA) {
+        if (fr >= 0.5) m = fl + 1.0;
+    } /* OR_RTZ keeps fl */
+    double v = m * spacing;                 /* exact: m has at most 9 bits */
+    if (v >= two128) return sign | 0x7F80;  /* rounded up past the max finite */
+    if (v == 0.0) return sign;
+    /* encode v */
+    if (v < ldexp(1.0, -126)) {
+        uint16_t frac = (uint16_t)(v / ldexp(1.0, -133));  /* 1..127 */
+        return sign | frac;
+    }
+    frexp(v, &e2);
+    int ev = e2 - 1;
+    double mant = v / ldexp(1.0, ev);       /* in [1, 2), 7 fraction bits */
+    uint16_t frac = (uint16_t)((mant - 1.0) * 128.0);
+    return (uint16_t)(sign | ((uint16_t)(ev + 127) << 7) | frac);
+}
+
+void oracle_round_bf16_array(const double* x, uint16_t* out, int64_t n, int mode) {
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_round_bf16(x[i], mode);
+}
+
+/* Element offset of row (b, h, i) of a [*, 128] tensor in the given layout. */
+static int64_t row_offset(int layout, int64_t b, int64_t h, int64_t i, int64_t H, int64_t S) {
+    if (layout == OR_LAYOUT_BSHD) return ((b * S + i) * H + h) * ORACLE_D;
+    return ((b * H + h) * S + i) * ORACLE_D;
+}
+
+/* Round to bf16 (RTNE) and back, for the method companion's probabilities. */
+static double round_trip_bf16_rtne(double x) { return bf16_to_double(oracle_round_bf16(x, OR_RTNE)); }
+
+/*
+ * Evaluate rows of attention.
+ *   q, k, v   : bf16 bit patterns, contiguous, layout as given.
+ *   rows      : flat query-row ids r = (b*H + h)*Sq + i, or NULL for all
+ *               B*H*Sq rows in that order; nrows is the count.
+ *   o_exact, sigma            : [nrows, 128] doubles (required).
+ *   o_method, sigma_method    : [nrows, 128] doubles, or NULL to skip.
+ *   l_from_rounded            : method companion's normaliser (see header).
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                     float scale, const int64_t* rows, int64_t nrows,
+                     double* o_exact, double* sigma,
+                     double* o_method, double* sigma_method,
+                     int l_from_rounded, int nthreads) {
+    if (!q || !k || !v || !o_exact || !sigma) return -1;
+    if (layout != OR_LAYOUT_BSHD && layout != OR_LAYOUT_BHSD) return -1;
+    if (B < 1 || H < 1 || Sq < 1 || Skv < 1) return -1;
+    if (rows == NULL) nrows = B * H * Sq;
+    if (nrows < 0) return -1;
+    const double sc = (double)scale;
+    const double log2e = 1.4426950408889634073599246810018921;  /* 1/ln 2 */
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)Skv);
+        double* kk = (double*)malloc(sizeof(double) * ORACLE_D);
+        if (!s || !kk) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < nrows; t++) {
+            if (!s || !kk) continue;
+            int64_t r = rows ? rows[t] : t;
+            int64_t i = r % Sq, bh = r / Sq, h = bh % H, b = bh / H;
+            double qq[ORACLE_D];
+            const uint16_t* qp = q + row_offset(layout, b, h, i, H, Sq);
+            for (int d = 0; d < ORACLE_D; d++) qq[d] = bf16_to_double(qp[d]);
+
+            /* pass 1: scores and their maximum (NaN propagates into m) */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < Skv; j++) {
+                const uint16_t* kp = k + row_offset(layout, b, h, j, H, Skv);
+                for (int d = 0; d < ORACLE_D; d++) kk[d] = bf16_to_double(kp[d]);
+                double acc = 0.0;
+                for (int d = 0; d < ORACLE_D; d++) acc += qq[d] * kk[d];
+                s[j] = sc * acc;
+                if (!isnan(m) && (isnan(s[j]) || s[j] > m)) m = s[j];
+            }
+
+            /* pass 2: weights, normaliser, weighted sums */
+            double num[ORACLE_D], sq[ORACLE_D], numm[ORACLE_D], sqm[ORACLE_D];
+            for (int d = 0; d < ORACLE_D; d++) { num[d] = 0.0; sq[d] = 0.0; numm[d] = 0.0; sqm[d] = 0.0; }
+            double l = 0.0, lm = 0.0, lm_rounded = 0.0;
+            double xmax = m * log2e;
+            double M = ceil(xmax);
+            for (int64_t j = 0; j < Skv; j++) {
+                const uint16_t* vp = v + row_offset(layout, b, h, j, H, Skv);
+                double p = exp(s[j] - m);
+                l += p;
+                double pt = 0.0, pm = 0.0;
+                if (o_method) {
+                    pm = exp2(s[j] * log2e - M);
+                    pt = round_trip_bf16_rtne(pm);
+                    lm += pm;
+                    lm_rounded += pt;
+                }
+                for (int d = 0; d < ORACLE_D; d++) {
+                    double vv = bf16_to_double(vp[d]);
+                    num[d] += p * vv;
+                    sq[d] += (p * vv) * (p * vv);
+                    if (o_method) {
+                        numm[d] += pt * vv;
+                        sqm[d] += (pt * vv) * (pt * vv);
+                    }
+                }
+            }
+            double* oe = o_exact + t * ORACLE_D;
+            double* sg = sigma + t * ORACLE_D;
+            for (int d = 0; d < ORACLE_D; d++) {
+                oe[d] = num[d] / l;
+                sg[d] = sqrt(sq[d]) / l;
+            }
+            if (o_method) {
+                double L = l_from_rounded ? lm_rounded : lm;
+                double* om = o_method + t * ORACLE_D;
+                double* sm = sigma_method ? sigma_method + t * ORACLE_D : NULL;
+                for (int d = 0; d < ORACLE_D; d++) {
+                    om[d] = numm[d] / L;
+                    if (sm) sm[d] = sqrt(sqm[d]) / L;
+                }
+            }
+        }
+        free(s);
+        free(kk);
+    }
+    return failed ? -1 : 0;
+}

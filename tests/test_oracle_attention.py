@@ -1,0 +1,250 @@
+"""Pins for the fp64 attention oracle.
+
+The pages print no worked example, so the oracle is pinned against things
+the mathematics fixes (the definition is the fused softmax(Q K^T scale) V of
+the MoonMath AI MI300X attention article's opening paragraphs):
+
+- brute force in 50-digit decimal arithmetic on tiny inputs (exact rational
+  scores, decimal exp), for the output and for sigma;
+- a library routine that reduces to the same definition:
+  torch.nn.functional.scaled_dot_product_attention in float64 on the CPU;
+- closed forms: Skv = 1 returns V's row; constant V returns the constant;
+  equal scores (Q = 0 or scale = 0) return the exact mean of V; a score gap
+  above 800 nats returns the dominant key's V row bit for bit; V = identity
+  returns the softmax weights, which sum to one;
+- invariances: a joint permutation of the key/value rows, BSHD vs BHSD
+  storage of the same data, additivity in V over disjoint supports;
+- the NaN/Inf pattern implied by IEEE arithmetic on the definition,
+  computed in closed form from the injection sites.
+"""
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bf16_attention_forward_amd import workloads as wl
+
+SCALE = wl.DEFAULT_SCALE
+
+
+def bf(x) -> np.ndarray:
+    """float array -> bf16 bit patterns (torch's RTNE cast)."""
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f64(bits):
+    return oracle.bf16_bits_to_f64(bits)
+
+
+def run(q, k, v, layout="bhsd", scale=SCALE, **kw):
+    return oracle.attention(q, k, v, layout=layout, scale=scale, **kw)
+
+
+# ---------------------------------------------------------------- brute force
+def decimal_attention_row(qrow, K, V, scale):
+    """Definition evaluated with exact rationals and 50-digit decimal exp."""
+    getcontext().prec = 50
+    qf = [Fraction(float(x)) for x in qrow]
+    sc = Fraction(float(np.float32(scale)))
+    s = []
+    for j in range(K.shape[0]):
+        s.append(sc * sum(qf[d] * Fraction(float(K[j, d])) for d in range(len(qf))))
+    m = max(s)
+    p = [(Decimal(x.numerator) / Decimal(x.denominator) - Decimal(m.numerator) / Decimal(m.denominator)).exp() for x in s]
+    l = sum(p)
+    o, sg = [], []
+    for d in range(V.shape[1]):
+        num = sum(p[j] * Decimal(float(V[j, d])) for j in range(K.shape[0]))
+        sq = sum((p[j] * Decimal(float(V[j, d]))) ** 2 for j in range(K.shape[0]))
+        o.append(num / l)
+        sg.append(sq.sqrt() / l)
+    return np.array([float(x) for x in o]), np.array([float(x) for x in sg])
+
+
+@pytest.mark.parametrize("skv", [1, 2, 3, 5])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_bruteforce_decimal(skv, seed):
+    q, k, v = wl.random_qkv("bhsd", 1, 1, 2, skv, seed, k_factor=2.0)
+    qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
+    res = run(qb, kb, vb)
+    Q, K, V = f64(qb)[0, 0], f64(kb)[0, 0], f64(vb)[0, 0]
+    for i in range(Q.shape[0]):
+        o_ref, s_ref = decimal_attention_row(Q[i], K, V, SCALE)
+        scale_o = np.maximum(np.abs(o_ref), s_ref) + 1e-300
+        assert np.all(np.abs(res.o_exact[i] - o_ref) <= 1e-13 * scale_o + 1e-15 * np.abs(V).max())
+        assert np.allclose(res.sigma[i], s_ref, rtol=1e-12, atol=0)
+
+
+# ------------------------------------------------------------- library routine
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+def test_matches_torch_sdpa_float64(layout):
+    q, k, v = wl.random_qkv(layout, 2, 3, 37, 211, 11, k_factor=2.0)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout)
+    to_bhsd = (lambda t: t.permute(0, 2, 1, 3)) if layout == "bshd" else (lambda t: t)
+    Q, K, V = (to_bhsd(t).to(torch.float64).contiguous() for t in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=float(SCALE))
+    ref = ref.reshape(-1, 128).numpy()   # rows in (b, h, i) order == oracle's flat row ids
+    assert np.max(np.abs(res.o_exact - ref)) <= 1e-12 * float(V.abs().max())
+
+
+# ----------------------------------------------------------------- closed forms
+def test_single_key_returns_value_row():
+    q, k, v = wl.random_qkv("bshd", 1, 2, 9, 1, 5)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bshd")
+    V = f64(wl.bits(v))            # [1,1,2,128]
+    for h in range(2):
+        assert np.array_equal(res.o_exact[h * 9:(h + 1) * 9], np.broadcast_to(V[0, 0, h], (9, 128)))
+        for mode in ("rtne", "rtna", "rtz"):
+            assert np.array_equal(res.rounded(mode)[h * 9:(h + 1) * 9], np.broadcast_to(wl.bits(v)[0, 0, h], (9, 128)))
+
+
+@pytest.mark.parametrize("c", [1.0, -0.375, 3.140625, 2.0 ** -20])
+def test_constant_value_returns_constant(c):
+    q, k, _ = wl.random_qkv("bhsd", 1, 1, 7, 50, 6, k_factor=2.0)
+    vb = np.full((1, 1, 50, 128), bf([c])[0], dtype=np.uint16)
+    res = run(wl.bits(q), wl.bits(k), vb)
+    assert np.allclose(res.o_exact, c, rtol=4e-16 * 50, atol=0)
+    for mode in ("rtne", "rtna"):
+        assert np.all(res.rounded(mode) == bf([c])[0])
+
+
+@pytest.mark.parametrize("how", ["zero_q", "zero_scale"])
+def test_equal_scores_return_exact_mean(how):
+    skv = 64
+    q, k, v = wl.random_qkv("bhsd", 1, 1, 3, skv, 8)
+    qb = wl.bits(q).copy()
+    scale = SCALE
+    if how == "zero_q":
+        qb[:] = 0
+    else:
+        scale = 0.0
+    vb = wl.bits(v)
+    res = run(qb, wl.bits(k), vb, scale=scale)
+    V = f64(vb)[0, 0]
+    mean = np.array([float(sum(Fraction(x) for x in V[:, d]) / skv) for d in range(128)])
+    assert np.all(np.abs(res.o_exact - mean) <= 1e-15 * np.abs(V).max())
+    # the method companion is exact here too (every weight is 1)
+    assert np.array_equal(res.o_method, res.o_exact)
+
+
+def test_equal_scores_tie_rounding():
+    # V rows alternate 1 and 1 + 2^-7 -> mean 1 + 2^-8, a tie between two bf16 values
+    skv = 8
+    qb = np.zeros((1, 1, 1, 128), np.uint16)
+    kb = bf(np.ones((1, 1, skv, 128)))
+    vals = np.where(np.arange(skv) % 2 == 0, 1.0, 1.0 + 2.0 ** -7)
+    vb = bf(np.broadcast_to(vals[None, None, :, None], (1, 1, skv, 128)))
+    res = run(qb, kb, vb)
+    assert np.all(res.o_exact == 1.0 + 2.0 ** -8)
+    assert np.all(res.rounded("rtne") == 0x3F80)
+    assert np.all(res.rounded("rtna") == 0x3F81)
+    assert np.all(res.rounded("rtz") == 0x3F80)
+
+
+@pytest.mark.parametrize("j0", [0, 17, 40])
+def test_one_hot_dominant_score_selects_row(j0):
+    skv = 41
+    _, _, v = wl.random_qkv("bhsd", 1, 1, 1, skv, 9)
+    qv = np.zeros((1, 1, 1, 128)); qv[..., 0] = 128.0
+    kv = np.zeros((1, 1, skv, 128)); kv[0, 0, j0, 0] = 128.0
+    kv[0, 0, :, 1] = 1.0   # other scores 0; dominant score 128*128*scale ~ 1448
+    res = run(bf(qv), bf(kv), wl.bits(v))
+    vb = wl.bits(v)[0, 0, j0]
+    assert np.array_equal(res.o_exact[0], f64(vb))
+    for mode in ("rtne", "rtna", "rtz"):
+        assert np.array_equal(res.rounded(mode)[0], vb)
+
+
+def test_identity_values_give_softmax_weights():
+    skv = 100
+    q, k, _ = wl.random_qkv("bhsd", 1, 2, 5, skv, 10, k_factor=2.0)
+    vv = np.zeros((1, 2, skv, 128)); vv[0, :, np.arange(skv), np.arange(skv)] = 1.0
+    res = run(wl.bits(q), wl.bits(k), bf(vv))
+    w = res.o_exact[:, :skv]
+    assert np.all(w > 0)
+    assert np.all(res.o_exact[:, skv:] == 0)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=skv * 2.0 ** -52)
+    # ratio of two weights is exp of the score difference (scores from exact products)
+    Q = f64(wl.bits(q))[0, 0, 0]; K = f64(wl.bits(k))[0, 0]
+    s = np.array([float(sum(Fraction(Q[d]) * Fraction(K[j, d]) for d in range(128)) * Fraction(float(SCALE))) for j in (3, 71)])
+    assert np.isclose(w[0, 3] / w[0, 71], np.exp(s[0] - s[1]), rtol=1e-13)
+
+
+# ------------------------------------------------------------------ invariances
+def test_joint_key_value_permutation_invariance():
+    q, k, v = wl.random_qkv("bhsd", 1, 2, 6, 77, 12, k_factor=2.0)
+    perm = np.random.default_rng(0).permutation(77)
+    a = run(wl.bits(q), wl.bits(k), wl.bits(v))
+    b = run(wl.bits(q), wl.bits(k)[:, :, perm], wl.bits(v)[:, :, perm])
+    assert np.allclose(a.o_exact, b.o_exact, rtol=1e-13, atol=1e-15)
+    # a permutation of only K (not V) must change the result
+    c = run(wl.bits(q), wl.bits(k)[:, :, perm], wl.bits(v))
+    assert not np.allclose(a.o_exact, c.o_exact, rtol=1e-6, atol=1e-6)
+
+
+def test_layouts_agree_bitwise():
+    q, k, v = wl.random_qkv("bshd", 2, 3, 19, 23, 13)
+    a = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bshd")
+    perm = lambda t: wl.bits(t.permute(0, 2, 1, 3).contiguous())
+    b = run(perm(q), perm(k), perm(v), layout="bhsd")
+    assert np.array_equal(a.o_exact, b.o_exact)
+    assert np.array_equal(a.sigma, b.sigma)
+
+
+def test_additive_in_values_over_disjoint_supports():
+    q, k, v = wl.random_qkv("bhsd", 1, 1, 4, 30, 14)
+    vb = wl.bits(v)
+    mask = (np.arange(128) % 3 == 0)
+    v1 = np.where(mask, vb, 0).astype(np.uint16)
+    v2 = np.where(~mask, vb, 0).astype(np.uint16)
+    a = run(wl.bits(q), wl.bits(k), vb).o_exact
+    b = run(wl.bits(q), wl.bits(k), v1).o_exact + run(wl.bits(q), wl.bits(k), v2).o_exact
+    assert np.array_equal(a, b)   # each column is computed independently of the others
+
+
+def test_row_subset_matches_full():
+    q, k, v = wl.random_qkv("bshd", 2, 2, 11, 13, 15)
+    full = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bshd")
+    rows = np.array([0, 5, 21, 43, 12])
+    sub = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bshd", rows=rows)
+    assert np.array_equal(sub.o_exact, full.o_exact[rows])
+
+
+# -------------------------------------------------------------------- NaN / Inf
+def closed_form_mask(inj, B, H, Sq):
+    """Expected output class per (b, h, i, d): 0 finite, 1 NaN, 2 +Inf, 3 -Inf."""
+    out = np.zeros((B, H, Sq, 128), np.int8)
+    col = {}
+    for (b, h, j, d, val) in inj.v_sites:
+        st = col.setdefault((b, h, d), set())
+        st.add("nan" if np.isnan(val) else ("+" if val > 0 else "-"))
+    for (b, h, d), st in col.items():
+        cls = 1 if ("nan" in st or {"+", "-"} <= st) else (2 if "+" in st else 3)
+        out[b, h, :, d] = cls
+    for (b, h, i, d, val) in inj.q_sites:
+        out[b, h, i, :] = 1
+    return out
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_nonfinite_positions_closed_form(layout):
+    B, H, Sq, Skv = 2, 3, 21, 33
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 16, k_factor=2.0)
+    inj = wl.inject_nonfinite(q, v, layout, 16)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout)
+    o = res.o_exact.reshape(B, H, Sq, 128)
+    got = np.where(np.isnan(o), 1, np.where(np.isposinf(o), 2, np.where(np.isneginf(o), 3, 0)))
+    assert np.array_equal(got, closed_form_mask(inj, B, H, Sq))
+    assert res.rounded("rtne")[np.isnan(res.o_exact)].tolist() == [0x7FC0] * int(np.isnan(res.o_exact).sum())
+
+
+# ------------------------------------------------------------- method companion
+def test_method_companion_close_to_exact():
+    q, k, v = wl.random_qkv("bhsd", 1, 2, 16, 300, 17, k_factor=2.0)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v))
+    # bf16 weights carry a relative error of at most 2^-9 each
+    assert np.all(np.abs(res.o_method - res.o_exact) <= 2.0 ** -9 * np.sqrt(300) * res.sigma * 1.01 + 1e-300)
+    assert not np.array_equal(res.o_method, res.o_exact)

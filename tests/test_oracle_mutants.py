@@ -1,0 +1,81 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Each mutant is a textual edit of oracle/attn_oracle.c (a dropped term, a
+wrong sign, a wrong index or operand, a layout or tie-rule slip), compiled
+into a temporary library on the CPU and swapped in for the duration of the
+check.  The real oracle source is never modified.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_attention as A
+from tests import test_oracle_round as R
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = {
+    "qk_index_shift": ("acc += qq[d] * kk[d];", "acc += qq[d] * kk[(d + 1) % ORACLE_D];"),
+    "exp_sign": ("double p = exp(s[j] - m);", "double p = exp(m - s[j]);"),
+    "no_normalise": ("oe[d] = num[d] / l;", "oe[d] = num[d];"),
+    "no_scale": ("s[j] = sc * acc;", "s[j] = acc;"),
+    "bshd_offset": ("if (layout == OR_LAYOUT_BSHD) return ((b * S + i) * H + h) * ORACLE_D;",
+                    "if (layout == OR_LAYOUT_BSHD) return ((b * H + h) * S + i) * ORACLE_D;"),
+    "value_from_key": ("const uint16_t* vp = v + row_offset", "const uint16_t* vp = k + row_offset"),
+    "sigma_not_squared": ("sq[d] += (p * vv) * (p * vv);", "sq[d] += (p * vv);"),
+    "rtne_tie_up": ("if (fr > 0.5) m = fl + 1.0;", "if (fr >= 0.5) m = fl + 1.0;"),
+    "rtna_tie_down": ("if (fr >= 0.5) m = fl + 1.0;\n    } /* OR_RTZ", "if (fr > 0.5) m = fl + 1.0;\n    } /* OR_RTZ"),
+    "rtz_overflow_inf": ("return (mode == OR_RTZ) ? (uint16_t)(sign | 0x7F7F)", "return (mode == OR_RTZ) ? (uint16_t)(sign | 0x7F80)"),
+    "subnormal_flush": ("if (e < -126) e = -126;", "if (e < -126) return sign;"),
+    "max_skips_last_key": ("for (int64_t j = 0; j < Skv; j++) {\n                const uint16_t* kp",
+                           "for (int64_t j = 0; j < Skv; j++) {\n                if (j == Skv - 1 && Skv > 1) { s[j] = -INFINITY; continue; }\n                const uint16_t* kp"),
+}
+
+
+def pins():
+    """(name, callable) for every pin; each raises AssertionError on failure."""
+    out = []
+    for mode in ("rtne", "rtna", "rtz"):
+        out.append((f"round_grid_{mode}", lambda m=mode: R.test_round_matches_grid_search(m)))
+    out.append(("round_torch", R.test_rtne_matches_torch_for_float32_inputs))
+    out.append(("round_ties", R.test_tie_cases_distinguish_modes))
+    out.append(("round_overflow", R.test_overflow_and_nonfinite))
+    for skv in (1, 3):
+        out.append((f"brute_{skv}", lambda s=skv: A.test_bruteforce_decimal(s, 1)))
+    for lay in ("bshd", "bhsd"):
+        out.append((f"sdpa_{lay}", lambda l=lay: A.test_matches_torch_sdpa_float64(l)))
+    out.append(("single_key", A.test_single_key_returns_value_row))
+    out.append(("equal_scores", lambda: A.test_equal_scores_return_exact_mean("zero_q")))
+    out.append(("one_hot", lambda: A.test_one_hot_dominant_score_selects_row(40)))
+    out.append(("identity", A.test_identity_values_give_softmax_weights))
+    out.append(("permutation", A.test_joint_key_value_permutation_invariance))
+    out.append(("layouts", A.test_layouts_agree_bitwise))
+    for lay in ("bhsd", "bshd"):
+        out.append((f"nonfinite_{lay}", lambda l=lay: A.test_nonfinite_positions_closed_form(l)))
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                    str(mpath), "-o", str(so), "-lm"], check=True)
+    lib = oracle.configure(ctypes.CDLL(str(so)))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    caught = []
+    for pin_name, fn in pins():
+        try:
+            with np.errstate(all="ignore"):
+                fn()
+        except (AssertionError, RuntimeError, ValueError):
+            caught.append(pin_name)
+    assert caught, f"mutant {name} passed every pin"
