@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark: bf16 attention forward on one MI355X through the C ABI.
+
+One "step" is one call of attn_fwd_bf16 (the whole hot path: key/value
+staging, both MFMA products, the online softmax, the rounding epilogue and,
+when the planner splits keys, the combine kernel) over one batch of seeded
+synthetic input already resident in HBM.
+
+Default workload: self-attention, BHSD, B=2, H=16, Sq=Skv=4096, head dim
+128, K scaled x2, RTNE output.  The other large workloads are timed too and
+reported under "workloads".  Methodology follows the HipKittens summary's
+experiments section: warm-up launches, then timed launches on N(0,1)-style
+inputs.
+
+Prints ONE JSON line:
+  value        = algorithmic TFLOP/s (4*B*H*Sq*Skv*128 / time per step)
+  roofline     = the main kernel's achieved TFLOP/s (HIP events around each
+                 launch on the launch stream) against the dense bf16 MFMA peak
+  cpu_baseline = the fp64 oracle timed on a bounded row sample on the host
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz (dense, published 2.5 PFLOP/s)
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_fwd_kernel.hip", "attn_fwd_internal.h"):
+        with open(os.path.join(ROOT, "bf16_attention_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_main_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("workloads", {}).get(workload_name)
+    if not ent or rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_workload(w, mode, steps, warmup, kv_splits=0):
+    import torch
+    from bf16_attention_forward_amd import attn_fwd_bf16
+    from bf16_attention_forward_amd import workloads as wl
+
+    q, k, v = wl.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, kv_splits=kv_splits)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch HIP events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in evs]   # ms
+    return {"wall_s": wall, "ms": per, "flops": w.flops}
+
+
+def cpu_baseline(w, budget_s: float):
+    import numpy as np
+    import oracle
+    from bf16_attention_forward_amd import workloads as wl
+    q, k, v = wl.make_inputs(w)
+    qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
+    threads = os.cpu_count() or 1
+    total_rows = w.B * w.H * w.Sq
+    rng = np.random.default_rng(w.seed)
+    calib = np.sort(rng.choice(total_rows, size=min(256, total_rows), replace=False))
+    t = time.perf_counter()
+    oracle.attention(qb, kb, vb, layout=w.layout, scale=wl.DEFAULT_SCALE, rows=calib, method=False, nthreads=threads)
+    dt = max(time.perf_counter() - t, 1e-6)
+    n = int(min(total_rows, max(256, len(calib) * budget_s / dt)))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t = time.perf_counter()
+    oracle.attention(qb, kb, vb, layout=w.layout, scale=wl.DEFAULT_SCALE, rows=rows, method=False, nthreads=threads)
+    dt = time.perf_counter() - t
+    flops = 4.0 * n * w.Skv * 128
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total_rows} query rows (seeded uniform sample) of {w.name}, all {w.Skv} keys, "
+                      f"fp64, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--workload", type=int, default=2, help="workload number (1..5)")
+    ap.add_argument("--mode", default="rtne")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work shards over (batch, head, query tile) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bf16_attention_forward_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+
+    w = wl.WORKLOADS[args.workload]
+    r = time_workload(w, args.mode, args.steps, args.warmup)
+    ms_step = r["wall_s"] * 1e3 / args.steps
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+    ev_mean = statistics.fmean(r["ms"])
+    achieved = w.flops / (ev_mean * 1e-3) / 1e12
+    srt = sorted(r["ms"])
+    traffic = measured_traffic(w.name)
+
+    extra = {}
+    if not args.no_extra:
+        for num in (3, 4, 5):
+            ww = wl.WORKLOADS[num]
+            for mode in ww.modes[:1]:
+                rr = time_workload(ww, mode, steps=20, warmup=10)
+                em = statistics.median(rr["ms"])
+                extra[ww.name] = {"mode": mode, "median_ms": round(em, 4),
+                                  "tflops": round(ww.flops / (em * 1e-3) / 1e12, 1),
+                                  "frac_peak": round(ww.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        for mode in w.modes:
+            if mode == args.mode:
+                continue
+            rr = time_workload(w, mode, steps=50, warmup=20)
+            em = statistics.median(rr["ms"])
+            extra[f"{w.name}:{mode}"] = {"mode": mode, "median_ms": round(em, 4),
+                                         "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
+
+    out = {
+        "metric": "attention fwd TFLOPS (4*B*H*Sq*Skv*d) and % of bf16 MFMA peak, d=128",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs, K x2)",
+        "config": {**w.describe(), "round_mode": args.mode, "parallelism": "single GPU"},
+        "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernel_ms": {"mean": round(ev_mean, 5), "median": round(statistics.median(srt), 5),
+                      "min": round(srt[0], 5), "p90": round(srt[int(0.9 * (len(srt) - 1))], 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_main",
+                     "algorithmic_flops_per_launch": w.flops},
+        "cpu_baseline": cpu,
+        "workloads": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+"""ctypes binding of libattn_fwd.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; torch is
+used here only for device memory and the current stream.  If the library is
+missing the binding raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_fwd.so")
+
+ATTN_LAYOUT = {"bshd": 0, "bhsd": 1}
+ATTN_ROUND = {"rtne": 0, "rtna": 1, "rtz": 2}
+ATTN_OK = 0
+ARGUMENT_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -11}
+HEAD_DIM = 128
+
+# names of every entry point the header declares
+EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_status_string", "attn_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn_fwd_bf16 failed ({status}): {message}")
+        self.status = status
+
+
+def load_library(path: str | None = None):
+    """Load and type the C ABI.  Raises if the built library is absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built: run bf16_attention_forward_amd.build.build() "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(p)
+    args = [ctypes.c_void_p] * 4 + [ctypes.c_int] + [ctypes.c_int64] * 4 + \
+           [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_fwd_bf16.argtypes = args
+    lib.attn_fwd_bf16.restype = ctypes.c_int
+    lib.attn_fwd_bf16_ex.argtypes = args + [ctypes.c_int, ctypes.c_int]
+    lib.attn_fwd_bf16_ex.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> int:
+    return int(load_library().attn_version())
+
+
+def _raise(status: int):
+    msg = attn_status_string(status)
+    if status in ARGUMENT_ERRORS:
+        raise ValueError(f"attn_fwd_bf16 argument error ({status}): {msg}")
+    raise AttnError(status, msg)
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor, layout: str):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D")
+    if layout == "bshd":
+        B, Sq, H, D = q.shape
+        Bk, Skv, Hk, Dk = k.shape
+    elif layout == "bhsd":
+        B, H, Sq, D = q.shape
+        Bk, Hk, Skv, Dk = k.shape
+    else:
+        raise ValueError(f"layout must be 'bshd' or 'bhsd', got {layout!r}")
+    if D != HEAD_DIM or Dk != HEAD_DIM:
+        raise ValueError("head dimension must be 128")
+    if (Bk, Hk) != (B, H):
+        raise ValueError("q and k/v must share batch and head counts")
+    return B, H, Sq, Skv
+
+
+def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
+                  layout: str = "bshd", scale: float | None = None, round_mode: str = "rtne",
+                  stream: torch.cuda.Stream | None = None, kv_splits: int = 0,
+                  block_order: int = 0) -> torch.Tensor:
+    """O = softmax(Q K^T * scale) V on the gfx950 library (bf16 in/out).
+
+    q, k, v, o: contiguous bfloat16 CUDA tensors in the given layout.  o is
+    allocated when None.  scale defaults to 1/sqrt(128) (as fp32).  The
+    launch goes to ``stream`` (default: torch's current stream) and is
+    asynchronous.  kv_splits/block_order are the planner overrides of
+    attn_fwd_bf16_ex (0 = automatic).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, H, Sq, Skv = _dims(q, k, layout)
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous bfloat16 device tensor shaped like q")
+    if round_mode not in ATTN_ROUND:
+        raise ValueError(f"round_mode must be one of {sorted(ATTN_ROUND)}")
+    sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_bf16_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, ATTN_ROUND[round_mode],
+                                  st.cuda_stream, int(kv_splits), int(block_order))
+    if rc != ATTN_OK:
+        _raise(rc)
+    return o
+
+
+def attn_fwd_bf16_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, layout: int, B: int, H: int,
+                      Sq: int, Skv: int, scale: float, round_mode: int, stream_ptr: int,
+                      kv_splits: int = 0, block_order: int = 0) -> int:
+    """Call the C entry point with raw integers; returns the status code."""
+    lib = load_library()
+    return int(lib.attn_fwd_bf16_ex(q_ptr, k_ptr, v_ptr, o_ptr, layout, B, H, Sq, Skv, scale,
+                                    round_mode, stream_ptr, kv_splits, block_order))

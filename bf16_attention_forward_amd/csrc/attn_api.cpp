@@ -1,0 +1,215 @@
+// attn_api.cpp -- C ABI of the gfx950 bf16 attention-forward library.
+//
+// Host side only: argument validation, the device check (gfx950 only), the
+// work planner (query tiles, optional key-range split, block order) and the
+// per-(device, stream) split workspace.  Every step of the computation runs
+// in the kernels of attn_fwd_kernel.hip; nothing here touches tensor data.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "attn_fwd_internal.h"
+#include "../../include/attn_fwd.h"
+
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kKeyTile = 64;
+constexpr int kMaxSplits = 64;
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    bool probed = false;
+    bool gfx950 = false;
+    int n_cu = 0;
+};
+
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+struct Workspace {
+    int device;
+    void* stream;
+    void* ptr;
+    size_t bytes;
+};
+std::vector<Workspace> g_ws;
+std::vector<void*> g_retired;   // outgrown buffers, freed at unload (a queued launch may still use them)
+
+struct Cleanup {
+    ~Cleanup() {
+        for (auto& w : g_ws) if (w.ptr) (void)hipFree(w.ptr);
+        for (void* p : g_retired) (void)hipFree(p);
+    }
+} g_cleanup;
+
+int probe_device(int* dev_out, DeviceInfo* info) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+        d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.n_cu = prop.multiProcessorCount;
+        d.probed = true;
+    }
+    *dev_out = dev;
+    *info = d;
+    return d.gfx950 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+// Workspace of at least `bytes` for (device, stream).  Never allocates while
+// the stream is being captured into a graph.
+int get_workspace(int dev, void* stream, size_t bytes, void** out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& w : g_ws) {
+        if (w.device == dev && w.stream == stream) {
+            if (w.bytes >= bytes) { *out = w.ptr; return ATTN_OK; }
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+                return ATTN_ERR_WORKSPACE;
+            void* p = nullptr;
+            if (hipMalloc(&p, bytes) != hipSuccess) return ATTN_ERR_WORKSPACE;
+            g_retired.push_back(w.ptr);
+            w.ptr = p;
+            w.bytes = bytes;
+            *out = p;
+            return ATTN_OK;
+        }
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return ATTN_ERR_WORKSPACE;
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return ATTN_ERR_WORKSPACE;
+    g_ws.push_back(Workspace{dev, stream, p, bytes});
+    *out = p;
+    return ATTN_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" int attn_version(void) { return 10000; }
+
+extern "C" const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_LAYOUT: return "layout must be ATTN_LAYOUT_BSHD or ATTN_LAYOUT_BHSD";
+        case ATTN_ERR_ROUND_MODE: return "round_mode must be ATTN_ROUND_RTNE, _RTNA or _RTZ";
+        case ATTN_ERR_SHAPE: return "B, H, Sq and Skv must be >= 1 and the sizes must fit the kernel's index range";
+        case ATTN_ERR_SCALE: return "scale must be finite";
+        case ATTN_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned";
+        case ATTN_ERR_ALIAS: return "o must not overlap q, k or v";
+        case ATTN_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+        case ATTN_ERR_WORKSPACE: return "split workspace unavailable (allocation failed or stream is being captured)";
+        case ATTN_ERR_LAUNCH: return "kernel launch failed";
+        case ATTN_ERR_OPTION: return "kv_splits or block_order out of range";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
+                                int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                float scale, int round_mode, void* stream,
+                                int kv_splits, int block_order) {
+    if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+    if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
+    if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
+        return ATTN_ERR_ROUND_MODE;
+    if (B < 1 || H < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
+    // index-range limits of the kernels: 32-bit counts and per-head buffer extents
+    const int64_t lim31 = (int64_t)1 << 31;
+    if (B >= lim31 || H >= lim31 || Sq >= lim31 || Skv >= lim31) return ATTN_ERR_SHAPE;
+    if (B * H >= lim31) return ATTN_ERR_SHAPE;
+    const int64_t n_q = B * H * Sq, n_kv = B * H * Skv;
+    if (n_q > ((int64_t)1 << 52) / kHeadDim || n_kv > ((int64_t)1 << 52) / kHeadDim) return ATTN_ERR_SHAPE;
+    const int64_t kv_row = (layout == ATTN_LAYOUT_BSHD) ? H * kHeadDim : kHeadDim;
+    if ((Skv - 1) * kv_row * 2 + kHeadDim * 2 >= lim31) return ATTN_ERR_SHAPE;
+    const int64_t n_qtiles = (Sq + KERNEL_BM - 1) / KERNEL_BM;
+    if (B * H * n_qtiles * kMaxSplits >= lim31) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return ATTN_ERR_ALIGN;
+    const size_t q_bytes = (size_t)n_q * kHeadDim * 2, kv_bytes = (size_t)n_kv * kHeadDim * 2;
+    if (ranges_overlap(o, q_bytes, q, q_bytes) || ranges_overlap(o, q_bytes, k, kv_bytes) ||
+        ranges_overlap(o, q_bytes, v, kv_bytes))
+        return ATTN_ERR_ALIAS;
+    if (kv_splits < 0 || kv_splits > kMaxSplits || block_order < 0 || block_order > 2) return ATTN_ERR_OPTION;
+
+    int dev = -1;
+    DeviceInfo info;
+    const int drc = probe_device(&dev, &info);
+    if (drc != ATTN_OK) return drc;
+
+    attn::AttnParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (uint16_t*)o;
+    if (layout == ATTN_LAYOUT_BSHD) {
+        p.q_row = H * kHeadDim; p.q_head = kHeadDim; p.q_batch = Sq * H * kHeadDim;
+        p.kv_row = H * kHeadDim; p.kv_head = kHeadDim; p.kv_batch = Skv * H * kHeadDim;
+    } else {
+        p.q_row = kHeadDim; p.q_head = Sq * kHeadDim; p.q_batch = H * Sq * kHeadDim;
+        p.kv_row = kHeadDim; p.kv_head = Skv * kHeadDim; p.kv_batch = H * Skv * kHeadDim;
+    }
+    p.B = (int)B; p.H = (int)H; p.Sq = (int)Sq; p.Skv = (int)Skv;
+    p.n_qtiles = (int)n_qtiles;
+    p.n_items = (int)(B * H * n_qtiles);
+    p.round_mode = round_mode;
+    p.c = (float)((double)scale * 1.4426950408889634073599246810018921);
+
+    // ---- plan the key-range split
+    const int n_kv_tiles = (int)((Skv + kKeyTile - 1) / kKeyTile);
+    int splits = kv_splits;
+    if (splits == 0) {
+        // Auto: split only when the query tiles alone leave most work-group slots idle.
+        const int slots = info.n_cu * 2;
+        splits = 1;
+        if (p.n_items * 2 <= slots) {
+            splits = (slots + p.n_items - 1) / p.n_items;
+            splits = std::min(splits, std::max(1, n_kv_tiles / 2));
+            splits = std::min(splits, kMaxSplits);
+        }
+    }
+    if (splits > n_kv_tiles) {
+        if (kv_splits != 0) return ATTN_ERR_OPTION;   // a forced split must leave every range non-empty
+        splits = n_kv_tiles;
+    }
+    p.kv_splits = splits;
+    p.n_kv_tiles = n_kv_tiles;
+    p.n_blocks = p.n_items * splits;
+    p.block_order = (block_order == 1) ? attn::ORDER_NAIVE : attn::ORDER_XCD;
+
+    if (splits > 1) {
+        const size_t per = (size_t)KERNEL_BM * (kHeadDim + 2) * sizeof(float);
+        const size_t need = (size_t)p.n_items * splits * per;
+        void* ws = nullptr;
+        const int wrc = get_workspace(dev, stream, need, &ws);
+        if (wrc != ATTN_OK) return wrc;
+        p.ws_o = (float*)ws;
+        p.ws_ml = (float*)((char*)ws + (size_t)p.n_items * splits * KERNEL_BM * kHeadDim * sizeof(float));
+    }
+
+    if (attn::launch(p, (hipStream_t)stream) != 0) return ATTN_ERR_LAUNCH;
+    return ATTN_OK;
+}
+
+extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
+                             int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                             float scale, int round_mode, void* stream) {
+    return attn_fwd_bf16_ex(q, k, v, o, layout, B, H, Sq, Skv, scale, round_mode, stream, 0, 0);
+}

@@ -1,0 +1,43 @@
+// attn_fwd_internal.h -- parameters shared by the host planner and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Tiling of the compiled kernel: KERNEL_NW waves per work-group, each owning
+// KERNEL_NQB blocks of 16 query rows; KERNEL_BM query rows per work item.
+#ifndef KERNEL_NQB
+#define KERNEL_NQB 2
+#endif
+#ifndef KERNEL_NW
+#define KERNEL_NW 4
+#endif
+#define KERNEL_BM (KERNEL_NW * 16 * KERNEL_NQB)
+
+namespace attn {
+
+enum { ROUND_RTNE = 0, ROUND_RTNA = 1, ROUND_RTZ = 2 };
+enum { ORDER_NAIVE = 1, ORDER_XCD = 2 };
+
+struct AttnParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* ws_o;       // split partial outputs [n_items][kv_splits][BM][128] (fp32)
+    float* ws_ml;      // split partial (M, l) pairs [n_items][kv_splits][BM][2]
+    int64_t q_row, q_head, q_batch;      // element strides of q and o
+    int64_t kv_row, kv_head, kv_batch;   // element strides of k and v
+    int B, H, Sq, Skv;
+    int n_qtiles;      // ceil(Sq / BM)
+    int n_items;       // B * H * n_qtiles
+    int kv_splits;     // key ranges per query tile (1 = no split)
+    int n_kv_tiles;    // ceil(Skv / 64)
+    int n_blocks;      // n_items * kv_splits
+    int block_order;   // ORDER_NAIVE or ORDER_XCD
+    int round_mode;
+    float c;           // fp32(scale * log2(e))
+};
+
+int launch(const AttnParams& p, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,116 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) bf16 attention-forward library.
+ *
+ * One call computes non-causal attention
+ *
+ *     O[b,h,i,:] = sum_j softmax_j(scale * <Q[b,h,i,:], K[b,h,j,:]>) * V[b,h,j,:]
+ *
+ * for head dimension 128, with bf16 inputs and a bf16 output rounded in a
+ * caller-selected mode.  The operation, the fixed head dimension, the two
+ * storage layouts (BSHD and BHSD, used as they are, never transposed), the
+ * freedom of Sq and Skv (cross-attention included) and the three rounding
+ * modes are those of the bf16 forward kernel in "MoonMath AI open-sources a
+ * HIP attention kernel for AMD MI300X that beats AITER" (opening paragraphs
+ * on what the kernel computes, its interface and its numerics).  Causal
+ * masking, grouped-query attention and variable-length batches are not part
+ * of this interface (the same article lists them as limitations).
+ *
+ * Like that kernel, a call launches asynchronously on the caller's stream
+ * (same article, use-case section), so it can overlap with other work.
+ *
+ * No HIP or torch type appears here: pointers are plain device addresses and
+ * the stream is passed as an opaque pointer (a hipStream_t, NULL = the
+ * legacy default stream).
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage layouts of q, k, v and o (all four share one layout). */
+enum {
+    ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128], element (b,s,h,d) at ((b*S + s)*H + h)*128 + d */
+    ATTN_LAYOUT_BHSD = 1  /* [B, H, S, 128], element (b,h,s,d) at ((b*H + h)*S + s)*128 + d */
+};
+
+/* Rounding of the fp32 result to the bf16 output (IEEE 754 meanings). */
+enum {
+    ATTN_ROUND_RTNE = 0, /* to nearest, ties to even                      */
+    ATTN_ROUND_RTNA = 1, /* to nearest, ties away from zero               */
+    ATTN_ROUND_RTZ  = 2  /* toward zero (finite overflow -> max finite)   */
+};
+
+/* Status codes.  Every argument error is detected on the host before any
+ * launch; on error nothing is launched and o is not written. */
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    ATTN_ERR_LAYOUT = -2,      /* layout is not one of ATTN_LAYOUT_*                */
+    ATTN_ERR_ROUND_MODE = -3,  /* round_mode is not one of ATTN_ROUND_*             */
+    ATTN_ERR_SHAPE = -4,       /* B, H, Sq or Skv < 1, or a size overflows          */
+    ATTN_ERR_SCALE = -5,       /* scale is NaN or infinite                          */
+    ATTN_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                  */
+    ATTN_ERR_ALIAS = -7,       /* o overlaps q, k or v                              */
+    ATTN_ERR_DEVICE = -8,      /* current device is not gfx950, or no device        */
+    ATTN_ERR_WORKSPACE = -9,   /* split workspace could not be obtained             */
+    ATTN_ERR_LAUNCH = -10,     /* the HIP runtime rejected a launch                 */
+    ATTN_ERR_OPTION = -11      /* an option of attn_fwd_bf16_ex is out of range     */
+};
+
+/*
+ * attn_fwd_bf16 -- O = softmax(Q K^T * scale) V, bf16 in, bf16 out.
+ *
+ *   q   [B,Sq,H,128] or [B,H,Sq,128] bf16, contiguous, device memory (read)
+ *   k   [B,Skv,H,128] or [B,H,Skv,128] bf16, contiguous, device (read)
+ *   v   same shape as k (read)
+ *   o   same shape as q, bf16, device (written; must not overlap q/k/v)
+ *   layout       ATTN_LAYOUT_BSHD or ATTN_LAYOUT_BHSD, shared by all four
+ *   B, H         batch and heads (>= 1); H is shared by q and k/v
+ *   Sq, Skv      query and key/value lengths (>= 1), independent
+ *   scale        finite fp32 multiplier of the scores (1/sqrt(128) is usual;
+ *                0 gives the uniform average of V)
+ *   round_mode   ATTN_ROUND_* for the final fp32 -> bf16 conversion
+ *   stream       hipStream_t to launch on (NULL = default stream)
+ *
+ * Ownership: the caller owns q, k, v, o and keeps them alive until the
+ * stream's work completes.  The library keeps a per-device workspace for the
+ * split-KV partial results; it grows on demand and lives until unload.
+ *
+ * Returns ATTN_OK or an ATTN_ERR_* code.  The call never synchronizes:
+ * device faults surface at the caller's next synchronization.  NaN and Inf
+ * inputs propagate as IEEE arithmetic on the definition implies; the output
+ * NaN is 0x7FC0.  Results are bitwise deterministic for a given device,
+ * shape, layout and mode.
+ */
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
+                  int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                  float scale, int round_mode, void* stream);
+
+/*
+ * attn_fwd_bf16_ex -- attn_fwd_bf16 with planner overrides, for tests and
+ * ablations.  kv_splits: 0 = planner's choice, n >= 1 forces every query
+ * tile's keys into n contiguous ranges merged by the combine kernel
+ * (n <= 64, and each range must hold at least one key).  block_order:
+ * 0 = planner's choice (XCD-aware), 1 = naive (work item = block id),
+ * 2 = XCD-aware.  Other values return ATTN_ERR_OPTION.
+ */
+int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
+                     int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                     float scale, int round_mode, void* stream,
+                     int kv_splits, int block_order);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* attn_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,70 @@
+"""C ABI checks that need no GPU: every symbol the header declares is
+exported, and argument errors are reported before any device work."""
+import math
+import re
+import os
+
+import numpy as np
+import pytest
+
+import bf16_attention_forward_amd as pkg
+from bf16_attention_forward_amd import attn_fwd_bf16_raw, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s+(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(pkg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    assert pkg.attn_version() >= 10000
+    for code in range(-11, 1):
+        assert pkg.attn_status_string(code)
+    assert pkg.attn_status_string(-999) == "unknown status"
+
+
+FAKE = 1 << 40   # 16-byte aligned, never dereferenced: validation fails first
+
+
+def call(**kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), layout=0, B=1, H=2,
+             Sq=64, Skv=64, scale=0.088, mode=0, stream=0, splits=0, order=0)
+    a.update(kw)
+    return attn_fwd_bf16_raw(a["q"], a["k"], a["v"], a["o"], a["layout"], a["B"], a["H"], a["Sq"], a["Skv"],
+                             a["scale"], a["mode"], a["stream"], a["splits"], a["order"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), -1), (dict(o=0), -1), (dict(layout=2), -2), (dict(layout=-1), -2),
+    (dict(mode=3), -3), (dict(B=0), -4), (dict(H=0), -4), (dict(Sq=0), -4), (dict(Skv=0), -4),
+    (dict(Skv=-5), -4), (dict(Sq=1 << 40), -4), (dict(scale=math.nan), -5), (dict(scale=math.inf), -5),
+    (dict(q=FAKE + 8), -6), (dict(o=FAKE + (3 << 30) + 2), -6), (dict(o=FAKE), -7),
+    (dict(o=FAKE + 64 * 2 * 128 * 2 - 16), -7), (dict(splits=65), -11), (dict(order=3), -11),
+])
+def test_argument_errors_before_device(kw, code):
+    assert call(**kw) == code
+
+
+def test_valid_arguments_reach_device_check():
+    # no GPU here: a valid call stops at the device probe (-8); on a GPU machine this test is skipped
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call() == -8

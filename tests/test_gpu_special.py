@@ -1,0 +1,119 @@
+"""GPU exactness cases, memory-safety checks and device-side error codes."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bf16_attention_forward_amd import workloads as wl
+from bf16_attention_forward_amd import attn_fwd_bf16, attn_fwd_bf16_raw, load_library
+from tests.helpers import check, run_hip, say
+
+pytestmark = pytest.mark.gpu
+MODES = ("rtne", "rtna", "rtz")
+
+
+def bf(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_single_key_returns_value_row_bitwise(mode):
+    q, k, v = wl.random_qkv("bshd", 1, 3, 200, 1, 31)
+    o = run_hip(q, k, v, "bshd", mode).reshape(1, 200, 3, 128)
+    assert np.array_equal(o, np.broadcast_to(wl.bits(v)[:, :1], o.shape))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("how", ["zero_q", "zero_scale"])
+def test_equal_scores_tie_cases_bitwise(mode, how):
+    skv = 64
+    q, k, _ = wl.random_qkv("bhsd", 1, 2, 40, skv, 32)
+    vals = np.where(np.arange(skv) % 2 == 0, 1.0, 1.0 + 2.0 ** -7)
+    v = bf(np.broadcast_to(vals[None, None, :, None], (1, 2, skv, 128)).copy())
+    scale = wl.DEFAULT_SCALE
+    if how == "zero_q":
+        q = torch.zeros_like(q)
+    else:
+        scale = 0.0
+    o = run_hip(q, k, v, "bhsd", mode, scale=scale)
+    expect = {"rtne": 0x3F80, "rtna": 0x3F81, "rtz": 0x3F80}[mode]
+    assert np.all(o == expect)
+    res = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout="bhsd", scale=scale, method=False)
+    assert np.array_equal(o.reshape(-1, 128), res.rounded(mode))
+
+
+@pytest.mark.parametrize("j0", [0, 37, 99])
+def test_one_hot_dominant_score_selects_row_bitwise(j0):
+    skv = 100
+    _, _, v = wl.random_qkv("bshd", 1, 1, 1, skv, 33)
+    qv = np.zeros((1, 4, 1, 128)); qv[..., 0] = 128.0
+    kv = np.zeros((1, skv, 1, 128)); kv[0, j0, 0, 0] = 128.0; kv[0, :, 0, 1] = 1.0
+    for mode in MODES:
+        o = run_hip(bf(qv), bf(kv), v, "bshd", mode)
+        assert np.array_equal(o.reshape(4, 128), np.broadcast_to(wl.bits(v)[0, j0, 0], (4, 128)))
+
+
+@pytest.mark.parametrize("scale", [-0.0883883461356163, 0.5, 1e-3])
+def test_other_scales_match_oracle(scale):
+    q, k, v = wl.random_qkv("bhsd", 1, 2, 150, 270, 34)
+    for mode in MODES:
+        o = run_hip(q, k, v, "bhsd", mode, scale=scale)
+        st, _ = check(o, q, k, v, "bhsd", mode, scale=scale, label=f"scale={scale}")
+        assert st["nonfinite_match"] and st["max_D"] <= 2.0 and st["frac_D_gt1"] <= 1e-3, st
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_poison_tails_are_never_read(layout):
+    """Rows past Sq / Skv hold NaN; a call with the true lengths must ignore them."""
+    Sq, Skv, pad = 131, 97, 64
+    q, k, v = wl.random_qkv(layout, 1, 1, Sq + pad, Skv + pad, 35)
+    sl = (slice(None), slice(None), slice(None), slice(None))
+
+    def cut(t, n):
+        return t[:, :n] if layout == "bshd" else t[:, :, :n]
+    for t, n in ((q, Sq), (k, Skv), (v, Skv)):
+        if layout == "bshd":
+            t[:, n:] = float("nan")
+        else:
+            t[:, :, n:] = float("nan")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    qv, kv_, vv = cut(qd, Sq), cut(kd, Skv), cut(vd, Skv)   # contiguous prefixes (B = H = 1)
+    assert qv.is_contiguous() and kv_.is_contiguous()
+    for splits in (0, 2):
+        o = attn_fwd_bf16(qv, kv_, vv, layout=layout, kv_splits=splits)
+        torch.cuda.synchronize()
+        ob = wl.bits(o.cpu())
+        assert not np.isnan((ob.astype(np.uint32) << 16).view(np.float32)).any()
+        clean = run_hip(cut(q, Sq).contiguous(), cut(k, Skv).contiguous(), cut(v, Skv).contiguous(), layout,
+                        kv_splits=splits)
+        assert np.array_equal(ob, clean)
+
+
+def test_output_canaries_untouched():
+    B, H, Sq, Skv = 1, 3, 77, 120
+    q, k, v = wl.random_qkv("bshd", B, H, Sq, Skv, 36)
+    n = B * Sq * H * 128
+    guard = 2048   # elements (4 KiB) on each side
+    buf = torch.full((n + 2 * guard,), 12345, dtype=torch.int16, device="cuda")
+    o = buf[guard:guard + n].view(torch.bfloat16).view(B, Sq, H, 128)
+    for splits in (0, 2):
+        attn_fwd_bf16(q.cuda(), k.cuda(), v.cuda(), o, layout="bshd", kv_splits=splits)
+        torch.cuda.synchronize()
+        host = buf.cpu().numpy()
+        assert np.all(host[:guard] == 12345) and np.all(host[guard + n:] == 12345)
+        assert np.array_equal(wl.bits(o.cpu()), run_hip(q, k, v, "bshd", kv_splits=splits))
+
+
+def test_device_side_argument_errors():
+    q, k, v = (t.cuda() for t in wl.random_qkv("bshd", 1, 2, 64, 64, 37))
+    o = torch.empty_like(q)
+    st = torch.cuda.current_stream().cuda_stream
+    args = lambda qp, op: (qp, k.data_ptr(), v.data_ptr(), op, 0, 1, 2, 64, 64, 0.088, 0, st)
+    assert attn_fwd_bf16_raw(*args(q.data_ptr() + 2, o.data_ptr())) == -6     # misaligned
+    assert attn_fwd_bf16_raw(*args(q.data_ptr(), q.data_ptr())) == -7         # o aliases q
+    assert attn_fwd_bf16_raw(*args(q.data_ptr(), o.data_ptr())) == 0
+    torch.cuda.synchronize()
+    # forced split larger than the number of key tiles is rejected
+    assert attn_fwd_bf16_raw(*args(q.data_ptr(), o.data_ptr()), kv_splits=2) == -11
