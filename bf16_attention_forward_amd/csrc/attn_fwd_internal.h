@@ -9,7 +9,7 @@
 #define KERNEL_NQB 2
 #endif
 #ifndef KERNEL_NW
-#define KERNEL_NW 4
+#define KERNEL_NW 8
 #endif
 #define KERNEL_BM (KERNEL_NW * 16 * KERNEL_NQB)
 

@@ -55,10 +55,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int D = 128;          // head dimension
 constexpr int BN = 64;          // keys per K/V tile
+constexpr int NW = KERNEL_NW;   // waves per work-group (two groups of 4)
+constexpr int NQB = KERNEL_NQB; // 16-row query blocks per wave
+constexpr int BM = KERNEL_BM;   // query rows per work item
 constexpr int ROW_BYTES = D * 2;
 constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
 
@@ -124,25 +129,41 @@ __device__ __forceinline__ int map_block(int bid, int n, int order) {
 }
 
 // ------------------------------------------------------------ main kernel
-// NQB: 16-row query blocks per wave; NW: waves per work-group.
-template <int NQB, int NW, bool CPOS>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) {
+// Workgroup barrier that keeps outstanding K/V DMA (tracked by vmcnt) in
+// flight across it: a memory fence here would wait for the DMA's LDS writes.
+// Every wave instead waits for its own DMA explicitly before the barrier that
+// publishes a tile, and ds_read/ds_write completion (lgkmcnt) is waited for
+// here; the "memory" clobber keeps the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 8 waves in two groups of 4 (waves w and w+4 share a SIMD).  Each wave owns
+// 32 query rows.  Per key tile t a wave runs an MFMA phase (S_t = K_t Q^T and
+// O += V_{t-1}^T P_{t-1}^T) and a VALU phase (softmax of S_t into P_t).  Group 1
+// starts one barrier late, so at any time one group is on the matrix cores
+// and the other on the vector ALUs, swapping at every barrier (the schedule
+// of the MI300X article's architecture section and of the HipKittens 8-wave
+// ping-pong).  K_{t+1} and V_t are fetched during the interval in which group
+// 0 runs MFMA phase t and must land by the end of the following interval.
+template <bool CPOS>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
-    constexpr int BM = NW * 16 * NQB;
     constexpr int NTHREADS = NW * 64;
     constexpr int DMA_PER_TILE = TILE_BYTES / 16 / NTHREADS;   // 16-byte chunks per lane per tile
     static_assert(TILE_BYTES % (16 * NTHREADS) == 0, "tile must split evenly over lanes");
     // Four distinct LDS objects (K and V, two buffers each): with the buffer
-    // index a compile-time constant the compiler can tell that the prefetch
-    // into one buffer does not alias reads of the other, and does not wait
-    // for it before every LDS read.
+    // choice a compile-time constant the compiler can tell that a DMA into one
+    // buffer does not alias reads of another and does not wait for it.
     __shared__ __attribute__((aligned(1024))) uint8_t sk0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sk1[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sv0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sv1[TILE_BYTES];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
+    const int group = wave >> 2;   // 0 or 1
     const int g = lane >> 4;       // lane group (0..3)
     const int j = lane & 15;       // lane within group
 
@@ -158,7 +179,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     // split s covers key tiles [s*T/ns, (s+1)*T/ns) of the T tiles: never empty for ns <= T
     const int kv_begin = (int)(((int64_t)split * p.n_kv_tiles) / p.kv_splits) * BN;
     const int kv_end = min(p.Skv, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / p.kv_splits) * BN);
-    const int n_tiles = (kv_end - kv_begin + BN - 1) / BN;
+    const int T = (kv_end - kv_begin + BN - 1) / BN;
 
     const uint16_t* qbase = p.q + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
     const char* kbase = (const char*)(p.k + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head);
@@ -179,19 +200,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         dma_off_k[i] = row * kv_row_bytes + ((cp ^ swz_k(row)) << 4);
         dma_off_v[i] = row * kv_row_bytes + ((cp ^ swz_v(row)) << 4);
     }
-    auto issue_tile = [&](int t, uint8_t* skd, uint8_t* svd) {
-        const int row0 = kv_begin + t * BN;
-        const int soff = row0 * kv_row_bytes;
+    auto issue_k = [&](int t, uint8_t* dst) {
+        const int soff = (kv_begin + t * BN) * kv_row_bytes;
 #pragma unroll
-        for (int i = 0; i < DMA_PER_TILE; i++) {
-            LDS_AS void* dk = (LDS_AS void*)(skd + ((i * NW + wave) * 64) * 16);
-            LDS_AS void* dv = (LDS_AS void*)(svd + ((i * NW + wave) * 64) * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dk, 16, dma_off_k[i] + soff, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dv, 16, dma_off_v[i] + soff, 0, 0, 0);
-        }
+        for (int i = 0; i < DMA_PER_TILE; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
+                                                     dma_off_k[i] + soff, 0, 0, 0);
+    };
+    auto issue_v = [&](int t, uint8_t* dst) {
+        const int soff = (kv_begin + t * BN) * kv_row_bytes;
+#pragma unroll
+        for (int i = 0; i < DMA_PER_TILE; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
+                                                     dma_off_v[i] + soff, 0, 0, 0);
     };
 
-    issue_tile(0, sk0, sv0);
+    issue_k(0, sk0);
 
     // ---- Q fragments (operand B of S^T = K Q^T): lane holds query row 16*qb + j,
     // dims 32*ks + 8*g .. +7.  Rows past Sq are clamped (never stored).
@@ -210,21 +234,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     for (int db = 0; db < 8; db++)
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[NQB], l_part[NQB];
+    float m_run[NQB], l_run[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; qb++) { m_run[qb] = -__builtin_inff(); l_part[qb] = 0.f; }
-
+    for (int qb = 0; qb < NQB; qb++) { m_run[qb] = -__builtin_inff(); l_run[qb] = 0.f; }
+    f32x4 s_acc[4][NQB];
+    bf16x8 pf[NQB][2];
     const float c = p.c;
+    const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // One key tile: wait for its DMA, prefetch the next tile into the other
-    // buffer, then S = K Q^T, softmax, O += V^T P^T.
-    auto step = [&](int t, const uint8_t* kt, const uint8_t* vt, uint8_t* nk, uint8_t* nv) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's DMA landed
-        __syncthreads();                      // ...and every other wave's; all reads of the other buffer are done
-        if (t + 1 < n_tiles) issue_tile(t + 1, nk, nv);
-
-        // ---- S^T = K Q^T  (4 key blocks x NQB query blocks, 4 k-steps of 32 dims)
-        f32x4 s_acc[4][NQB];
+    // ---- S^T = K Q^T  (4 key blocks x NQB query blocks, 4 k-steps of 32 dims)
+    auto qk = [&](const uint8_t* kt) {
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
 #pragma unroll
@@ -238,87 +257,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                 for (int qb = 0; qb < NQB; qb++) s_acc[kb][qb] = mfma16x16x32(kf, qf[qb][ks], s_acc[kb][qb]);
             }
         }
+    };
 
-        // ---- mask keys past the range (last tile only) by select, never arithmetic
-        const int valid = kv_end - (kv_begin + t * BN);
-        if (CPOS && valid < BN) {
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int key = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
-#pragma unroll
-                    for (int qb = 0; qb < NQB; qb++)
-                        s_acc[kb][qb][r] = key >= valid ? -__builtin_inff() : s_acc[kb][qb][r];
-                }
-        }
-
-        // ---- online softmax with power-of-two running max
-        bf16x8 pf[NQB][2];
-        bool any_rescale = false;
-        float alpha[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; qb++) {
-            float mx;
-            if (CPOS) {
-                mx = -__builtin_inff();
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++) mx = fmaxf(mx, s_acc[kb][qb][r]);
-                mx = rowmax4(mx) * c;
-            } else {
-                // general scale (c <= 0): x = s*c explicitly, keys past the range -> -inf
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int key = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
-                        s_acc[kb][qb][r] = key >= valid ? -__builtin_inff() : s_acc[kb][qb][r] * c;
-                    }
-                mx = -__builtin_inff();
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++) mx = fmaxf(mx, s_acc[kb][qb][r]);
-                mx = rowmax4(mx);
-            }
-            const float m_new = fmaxf(m_run[qb], ceilf(mx));
-            const float dm = m_run[qb] - m_new;     // <= 0, integer-valued, or -inf / NaN
-            alpha[qb] = ldexpf(1.0f, (int)fmaxf(dm, -200.f));
-            any_rescale |= (dm != 0.f);
-            m_run[qb] = m_new;
-            const float negm = -m_new;
-            f32x4 pv[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float x = CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm);
-                    pv[kb][r] = __builtin_amdgcn_exp2f(x);
-                }
-            }
-            // The row sum adds the bf16-rounded weights, the same values the
-            // P V product uses, so O is normalised by exactly its own weights.
-            float psum = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                const bf16x4 lo = __builtin_convertvector(pv[2 * ks], bf16x4);
-                const bf16x4 hi = __builtin_convertvector(pv[2 * ks + 1], bf16x4);
-                pf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                for (int i = 0; i < 8; i++) psum += (float)pf[qb][ks][i];
-            }
-            l_part[qb] = l_part[qb] * alpha[qb] + psum;
-        }
-        if (__builtin_amdgcn_ballot_w64(any_rescale) != 0) {
-#pragma unroll
-            for (int db = 0; db < 8; db++)
-#pragma unroll
-                for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] *= alpha[qb];
-        }
-
-        // ---- O^T += V^T P^T (8 dim blocks x NQB query blocks, 2 k-steps of 32 keys)
+    // ---- O^T += V^T P^T (8 dim blocks x NQB query blocks, 2 k-steps of 32 keys)
+    auto pv = [&](const uint8_t* vt) {
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
 #pragma unroll
@@ -329,8 +271,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                     const int row = 32 * ks + 8 * g + 4 * hf + (j >> 2);
                     const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v(row);
                     const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(vt + row * ROW_BYTES + (chunk << 4) + ((j & 1) << 3));
-                    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src);
-                    half[hf] = __builtin_bit_cast(bf16x4, raw);
+                    half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
                 }
                 const bf16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
@@ -339,15 +280,121 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         }
     };
 
-    for (int t = 0; t < n_tiles; t += 2) {
-        step(t, sk0, sv0, sk1, sv1);
-        if (t + 1 < n_tiles) step(t + 1, sk1, sv1, sk0, sv0);
-    }
+    // ---- online softmax of S_t with a power-of-two running max; rescales O and l.
+    auto softmax = [&](int t) {
+        const int valid = kv_end - (kv_begin + t * BN);   // keys of this tile inside the range
+        bool any_rescale = false;
+        float alpha[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; qb++) {
+            // keys past the range are masked by select, never by arithmetic
+            if (valid < BN) {
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int key = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
+                        s_acc[kb][qb][r] = key >= valid ? (CPOS ? -__builtin_inff() : __builtin_inff()) : s_acc[kb][qb][r];
+                    }
+            }
+            if (!CPOS) {
+                // general scale (c <= 0): x = s*c explicitly (masked keys: +inf * c -> -inf unless c == 0)
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int key = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
+                        s_acc[kb][qb][r] = key >= valid ? -__builtin_inff() : s_acc[kb][qb][r] * c;
+                    }
+            }
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) mx = fmaxf(mx, s_acc[kb][qb][r]);
+            mx = rowmax4(mx);
+            if (CPOS) mx *= c;
+            const float m_new = fmaxf(m_run[qb], ceilf(mx));
+            const float dm = m_run[qb] - m_new;     // <= 0, integer-valued, or -inf / NaN
+            alpha[qb] = ldexpf(1.0f, (int)fmaxf(dm, -200.f));
+            any_rescale |= (dm != 0.f);
+            m_run[qb] = m_new;
+            const float negm = -m_new;
+            f32x4 pv4[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float x = CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm);
+                    pv4[kb][r] = __builtin_amdgcn_exp2f(x);
+                }
+            // The row sum adds the bf16-rounded weights, the same values the
+            // P V product uses, so O is normalised by exactly its own weights.
+            // (pairs are converted one register at a time and summed with
+            // v_dot2c_f32_bf16 against (1, 1): one instruction per two weights)
+            float psum = l_run[qb] * alpha[qb];
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                bf16x2 pr[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const f32x4& src = pv4[2 * ks + (i >> 1)];
+                    const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
+                    pr[i] = __builtin_convertvector(two, bf16x2);
+                    psum = __builtin_amdgcn_fdot2_f32_bf16(pr[i], ones2, psum, false);
+                }
+                const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
+                const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
+                pf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            l_run[qb] = psum;
+        }
+        if (__builtin_amdgcn_ballot_w64(any_rescale) != 0) {
+#pragma unroll
+            for (int db = 0; db < 8; db++)
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] *= alpha[qb];
+        }
+    };
 
-    // ---- epilogue
+    // ---- the ping-pong loop (see the comment above the kernel)
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): K_0 slice and Q landed
+    lds_barrier();
+    if (group == 1) {
+        if (T > 1) issue_k(1, sk1);
+        issue_v(0, sv0);
+        lds_barrier();                    // the one-phase offset of group 1
+    }
+    // iteration t: K_t in kc, K_{t+1} -> kn, V_t -> vc, V_{t-1} in vp
+    auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp) {
+        // MFMA phase t
+        if (group == 0) {
+            if (t + 1 < T) issue_k(t + 1, kn);
+            if (t < T) issue_v(t, vc);
+        }
+        if (t < T) qk(kc);
+        if (t >= 1) pv(vp);
+        if (group == 1) __builtin_amdgcn_s_waitcnt(0x0f70);
+        lds_barrier();
+        // VALU phase t
+        if (group == 1) {
+            if (t + 2 < T) issue_k(t + 2, kc);
+            if (t + 1 < T) issue_v(t + 1, vp);
+        }
+        if (t < T) softmax(t);
+        if (group == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        lds_barrier();
+    };
+    for (int t = 0; t <= T; t += 2) {
+        iter(t, sk0, sk1, sv0, sv1);
+        if (t + 1 <= T) iter(t + 1, sk1, sk0, sv1, sv0);
+    }
+    if (group == 0) lds_barrier();        // group 0 matches group 1's extra barrier
+
+    // ---- epilogue: the 4 lanes of a row hold partial row sums
     float l_row[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; qb++) l_row[qb] = rowsum4(l_part[qb]);
+    for (int qb = 0; qb < NQB; qb++) l_row[qb] = rowsum4(l_run[qb]);
 
     if (p.kv_splits == 1) {
         uint16_t* obase = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
@@ -434,12 +481,11 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
 
 // ------------------------------------------------------------------ launch
 int launch(const AttnParams& p, hipStream_t stream) {
-    constexpr int NQB = KERNEL_NQB, NW = KERNEL_NW;
     dim3 grid(p.n_blocks), block(NW * 64);
     if (p.c > 0.f)
-        hipLaunchKernelGGL((attn_fwd_main<NQB, NW, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_main<true>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((attn_fwd_main<NQB, NW, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_main<false>), grid, block, 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
     if (p.kv_splits > 1) {
         const int64_t total = (int64_t)p.n_items * KERNEL_BM * (D / 4);
