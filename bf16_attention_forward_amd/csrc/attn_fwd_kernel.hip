@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_fwd_internal.h"
 
 namespace attn {
@@ -106,20 +108,16 @@ __device__ __forceinline__ float div_corrected(float o, float l, float r) {
     return (q1 == q1) ? q1 : q0;
 }
 
-// LDS bank swizzles (16-byte chunk index XOR a function of the row).
-// K is read with ds_read_b128 by 16 lanes at 16 different rows of one chunk;
-// the rows a lane group touches are {0-3, 8-11, 16-19, 24-27} (+4): map them
-// to 16 distinct chunks.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
-// V is read with ds_read_b64_tr_b16: each 16-lane group reads 4 rows x 32 B;
-// the 32-byte pair of chunks moves with the row, keeping pairs intact.
-__device__ __forceinline__ int swz_v(int row) { return ((row & 3) | (((row >> 3) & 1) << 2)) << 1; }
-
-// Key (tile row) held by A-row m of key block kb, chosen so that lane group g
-// of the score fragments holds keys 32*(kb/2) + 8g + 4*(kb%2) + r, r = 0..3.
-__device__ __forceinline__ int k_perm_row(int kb, int m) {
-    return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
-}
+// LDS layout of a K or V tile: 64 rows of 256 bytes (16 chunks of 16 bytes),
+// chunk positions XOR-swizzled per row so the reads below hit distinct banks.
+// K is read with ds_read_b128: the 16 lanes of a lane group read 16
+// consecutive rows at one logical chunk, so chunk c of row r sits at c ^ (r & 15).
+// V is read with ds_read_b64_tr_b16: a read covers 16 consecutive rows, 32
+// bytes (a chunk pair) each, so the pair index moves with r & 7.  Both
+// swizzles depend only on bits of the row that are fixed per lane, which lets
+// every fragment address be a per-lane base plus an immediate offset.
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 7) << 1; }
 
 __device__ __forceinline__ int map_block(int bid, int n, int order) {
     if (order != ORDER_XCD) return bid;
@@ -136,7 +134,9 @@ __device__ __forceinline__ int map_block(int bid, int n, int order) {
 // here; the "memory" clobber keeps the compiler from moving LDS accesses
 // across the barrier.
 __device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);   // no instruction may be scheduled across a phase boundary
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // 8 waves in two groups of 4 (waves w and w+4 share a SIMD).  Each wave owns
@@ -191,35 +191,34 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
 
-    // Per-lane DMA source offsets (relative to the tile's first row).
-    int dma_off_k[DMA_PER_TILE], dma_off_v[DMA_PER_TILE];
-#pragma unroll
-    for (int i = 0; i < DMA_PER_TILE; i++) {
-        const int slot = (i * NW + wave) * 64 + lane;   // 16-byte slot in the LDS tile
-        const int row = slot >> 4, cp = slot & 15;
-        dma_off_k[i] = row * kv_row_bytes + ((cp ^ swz_k(row)) << 4);
-        dma_off_v[i] = row * kv_row_bytes + ((cp ^ swz_v(row)) << 4);
-    }
+    // Per-lane DMA source offsets (relative to the tile's first row).  Slot
+    // (i*NW + wave)*64 + lane of a tile is row (i*NW + wave)*4 + g, chunk j; rows
+    // 32 apart share the swizzle, so one per-lane offset serves every i.
+    static_assert(NW * 4 == 32, "DMA rows per instruction round must be 32");
+    const int dma_row = wave * 4 + g;
+    const int dma_off_k = dma_row * kv_row_bytes + ((j ^ swz_k(dma_row)) << 4);
+    const int dma_off_v = dma_row * kv_row_bytes + ((j ^ swz_v(dma_row)) << 4);
     auto issue_k = [&](int t, uint8_t* dst) {
         const int soff = (kv_begin + t * BN) * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < DMA_PER_TILE; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
-                                                     dma_off_k[i] + soff, 0, 0, 0);
+                                                     dma_off_k, soff + i * 32 * kv_row_bytes, 0, 0);
     };
     auto issue_v = [&](int t, uint8_t* dst) {
         const int soff = (kv_begin + t * BN) * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < DMA_PER_TILE; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
-                                                     dma_off_v[i] + soff, 0, 0, 0);
+                                                     dma_off_v, soff + i * 32 * kv_row_bytes, 0, 0);
     };
 
     issue_k(0, sk0);
 
-    // ---- Q fragments (operand B of S^T = K Q^T): lane holds query row 16*qb + j,
-    // dims 32*ks + 8*g .. +7.  Rows past Sq are clamped (never stored).
-    const int qrow0 = qt * BM + wave * 16 * NQB;
+    // ---- Q fragments (operand B of S^T = K Q^T): lane (g, j) holds query row
+    // 16*qb + j of this wave, dims 32*ks + 8*g .. +7, for the whole key loop.
+    // Rows past Sq are clamped (their results are never stored).
+    const int qrow0 = qt * BM + wave * 16 * NQB;   // first query row of this wave
     bf16x8 qf[NQB][4];
 #pragma unroll
     for (int qb = 0; qb < NQB; qb++) {
@@ -228,7 +227,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) qf[qb][ks] = *(const bf16x8*)(src + 32 * ks);
     }
-
     f32x4 o_acc[8][NQB];
 #pragma unroll
     for (int db = 0; db < 8; db++)
@@ -242,43 +240,89 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     const float c = p.c;
     const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // ---- S^T = K Q^T  (4 key blocks x NQB query blocks, 4 k-steps of 32 dims)
-    auto qk = [&](const uint8_t* kt) {
+    // ---- MFMA phase: steps [S0, S1) of a fixed sequence of 32 fragment steps.
+    // Steps 0..15 compute S^T = K Q^T: step 4*ks + kb reads the K fragment of key
+    // block kb, k-step ks (one ds_read_b128: lane (g, j) gets row 16*kb + j,
+    // dims 32*ks + 8*g .. +7) and feeds NQB MFMAs; k-steps are the outer index
+    // so consecutive MFMAs hit different accumulators.  The score fragment of
+    // lane (g, j) then holds query j and keys 16*kb + 4*g + r, r = 0..3.
+    // Steps 16..31 compute O^T += V^T P^T: step 16 + 8*ks + db reads the V^T
+    // fragment of dim block db for the 32 keys of step ks with two
+    // ds_read_b64_tr_b16 (rows 32*ks + 16*hf + 4*g + r), matching the keys
+    // of P's elements 4*hf + r.  Fragment reads run PF steps ahead of their
+    // MFMAs so LDS latency hides behind the matrix core.
+    int k_addr[4], v_addr[8];   // per-lane byte offsets within a tile
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
+    for (int ks = 0; ks < 4; ks++) k_addr[ks] = j * ROW_BYTES + ((((4 * ks + g) ^ swz_k(j))) << 4);
 #pragma unroll
-            for (int qb = 0; qb < NQB; qb++) s_acc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int row = k_perm_row(kb, j);
-            const int rsw = swz_k(row);
+    for (int db = 0; db < 8; db++) {
+        const int row = 4 * g + (j >> 2);                    // + 32*ks + 16*hf (multiples of 8)
+        const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v(row);
+        v_addr[db] = row * ROW_BYTES + (chunk << 4) + ((j & 1) << 3);
+    }
+    auto read_frag = [&](int st, const uint8_t* kt, const uint8_t* vt) -> bf16x8 {
+        if (st < 16) {
+            const int kb = st & 3, ks = st >> 2;
+            return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(kt + k_addr[ks] + kb * 16 * ROW_BYTES);
+        }
+        const int db = (st - 16) & 7, ks = (st - 16) >> 3;
+        bf16x4 half[2];
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const bf16x8 kf = *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(kt + row * ROW_BYTES + (((4 * ks + g) ^ rsw) << 4));
+        for (int hf = 0; hf < 2; hf++) {
+            const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(vt + v_addr[db] + (32 * ks + 16 * hf) * ROW_BYTES);
+            half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
+        }
+        return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto use_frag = [&](int st, const bf16x8 f) {
+        if (st < 16) {
+            const int kb = st & 3, ks = st >> 2;
 #pragma unroll
-                for (int qb = 0; qb < NQB; qb++) s_acc[kb][qb] = mfma16x16x32(kf, qf[qb][ks], s_acc[kb][qb]);
-            }
+            for (int qb = 0; qb < NQB; qb++)
+                s_acc[kb][qb] = mfma16x16x32(f, qf[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s_acc[kb][qb]);
+        } else {
+            const int db = (st - 16) & 7, ks = (st - 16) >> 3;
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = mfma16x16x32(f, pf[qb][ks], o_acc[db][qb]);
         }
     };
-
-    // ---- O^T += V^T P^T (8 dim blocks x NQB query blocks, 2 k-steps of 32 keys)
-    auto pv = [&](const uint8_t* vt) {
+    constexpr int PF = 4;   // fragment prefetch distance (steps)
+    auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c) {
+        constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
+        // Opaque per-lane offsets: stops the compiler from hoisting every
+        // buffer x fragment address combination out of the loop (and spilling
+        // them); each phase adds its buffer base to 12 offsets instead.
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
+        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(k_addr[i]));
 #pragma unroll
-            for (int db = 0; db < 8; db++) {
-                bf16x4 half[2];
+        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(v_addr[i]));
+        bf16x8 fr[PF];
 #pragma unroll
-                for (int hf = 0; hf < 2; hf++) {
-                    const int row = 32 * ks + 8 * g + 4 * hf + (j >> 2);
-                    const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v(row);
-                    const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(vt + row * ROW_BYTES + (chunk << 4) + ((j & 1) << 3));
-                    half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
-                }
-                const bf16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int st = S0; st < S0 + PF && st < S1; st++) fr[(st - S0) % PF] = read_frag(st, kt, vt);
 #pragma unroll
-                for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = mfma16x16x32(vf, pf[qb][ks], o_acc[db][qb]);
+        for (int st = S0; st < S1; st++) {
+            const bf16x8 cur = fr[(st - S0) % PF];
+            if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
+            use_frag(st, cur);
+        }
+        // keep the interleave: the reads of step st+PF, then the MFMAs of step st
+#pragma unroll
+        for (int st = S0; st < S0 + PF && st < S1; st++) {
+            if (st < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int st = S0; st < S1; st++) {
+            if (st + PF < S1) {
+                if (st + PF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, NQB, 0);
         }
     };
+    using C0 = std::integral_constant<int, 0>;
+    using C16 = std::integral_constant<int, 16>;
+    using C32 = std::integral_constant<int, 32>;
 
     // ---- online softmax of S_t with a power-of-two running max; rescales O and l.
     auto softmax = [&](int t) {
@@ -288,24 +332,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
             // keys past the range are masked by select, never by arithmetic
-            if (valid < BN) {
+            // key 16*kb + 4*g + r is inside the range iff 16*kb + r < lim
+            const int lim = valid - 4 * g;
+            if (CPOS && valid < BN) {
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int key = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
-                        s_acc[kb][qb][r] = key >= valid ? (CPOS ? -__builtin_inff() : __builtin_inff()) : s_acc[kb][qb][r];
-                    }
+                    for (int r = 0; r < 4; r++)
+                        s_acc[kb][qb][r] = (16 * kb + r < lim) ? s_acc[kb][qb][r] : -__builtin_inff();
             }
             if (!CPOS) {
-                // general scale (c <= 0): x = s*c explicitly (masked keys: +inf * c -> -inf unless c == 0)
+                // general scale (c <= 0): x = s*c explicitly, keys past the range -> -inf
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int key = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
-                        s_acc[kb][qb][r] = key >= valid ? -__builtin_inff() : s_acc[kb][qb][r] * c;
-                    }
+                    for (int r = 0; r < 4; r++)
+                        s_acc[kb][qb][r] = (16 * kb + r < lim) ? s_acc[kb][qb][r] * c : -__builtin_inff();
             }
             float mx = -__builtin_inff();
 #pragma unroll
@@ -358,22 +400,25 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     };
 
     // ---- the ping-pong loop (see the comment above the kernel)
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): K_0 slice and Q landed
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's K_0 slice and its Q landed
     lds_barrier();
     if (group == 1) {
         if (T > 1) issue_k(1, sk1);
         issue_v(0, sv0);
         lds_barrier();                    // the one-phase offset of group 1
     }
-    // iteration t: K_t in kc, K_{t+1} -> kn, V_t -> vc, V_{t-1} in vp
-    auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp) {
+    // Iteration t: MFMA phase (S_t = K_t Q^T, O += V_{t-1}^T P_{t-1}^T), then VALU
+    // phase (softmax of S_t).  K_t and V_t live in buffer t % 2.  The first
+    // iteration has no P.V step and iteration T (past the last tile) only the
+    // P.V step; the steady-state loop in between is branch-free in vector
+    // state, which keeps the accumulators in place across iterations.
+    auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c) {
         // MFMA phase t
         if (group == 0) {
             if (t + 1 < T) issue_k(t + 1, kn);
             if (t < T) issue_v(t, vc);
         }
-        if (t < T) qk(kc);
-        if (t >= 1) pv(vp);
+        mfma_phase(kc, vp, s0c, s1c);
         if (group == 1) __builtin_amdgcn_s_waitcnt(0x0f70);
         lds_barrier();
         // VALU phase t
@@ -381,14 +426,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
             if (t + 2 < T) issue_k(t + 2, kc);
             if (t + 1 < T) issue_v(t + 1, vp);
         }
-        if (t < T) softmax(t);
+        if (decltype(s0c)::value == 0) softmax(t);
         if (group == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
         lds_barrier();
     };
-    for (int t = 0; t <= T; t += 2) {
-        iter(t, sk0, sk1, sv0, sv1);
-        if (t + 1 <= T) iter(t + 1, sk1, sk0, sv1, sv0);
+    iter(0, sk0, sk1, sv0, sv1, C0{}, C16{});
+    int t = 1;
+    for (; t + 1 < T; t += 2) {
+        iter(t, sk1, sk0, sv1, sv0, C0{}, C32{});
+        iter(t + 1, sk0, sk1, sv0, sv1, C0{}, C32{});
     }
+    if (t < T) {   // one more full iteration (t odd)
+        iter(t, sk1, sk0, sv1, sv0, C0{}, C32{});
+        t++;
+    }
+    // iteration T: the P.V step of the last tile, whose V sits in buffer (T-1) % 2
+    if (T & 1) iter(T, sk1, sk0, sv1, sv0, C16{}, C32{});
+    else iter(T, sk0, sk1, sv0, sv1, C16{}, C32{});
     if (group == 0) lds_barrier();        // group 0 matches group 1's extra barrier
 
     // ---- epilogue: the 4 lanes of a row hold partial row sums
