@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -173,35 +174,45 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
     p.c = (float)((double)scale * 1.4426950408889634073599246810018921);
 
     // ---- plan the key-range split
+    // One work-group fills a CU (two waves per SIMD), so a launch runs in
+    // rounds of n_cu items.  When the last round is ragged, the items of that
+    // round have their key range split so that the round fills the chip (the
+    // tail split); when there is less than one round of items, every item is
+    // split.  A forced kv_splits = n splits every item n ways.
     const int n_kv_tiles = (int)((Skv + kKeyTile - 1) / kKeyTile);
-    int splits = kv_splits;
-    if (splits == 0) {
-        // Auto: split only when the query tiles alone leave most work-group slots idle.
-        const int slots = info.n_cu * 2;
-        splits = 1;
-        if (p.n_items * 2 <= slots) {
-            splits = (slots + p.n_items - 1) / p.n_items;
-            splits = std::min(splits, std::max(1, n_kv_tiles / 2));
-            splits = std::min(splits, kMaxSplits);
+    const int slots = info.n_cu;
+    int n_full = p.n_items, splits = 1;
+    if (kv_splits > 0) {
+        if (kv_splits > n_kv_tiles) return ATTN_ERR_OPTION;   // every range must hold a key
+        splits = kv_splits;
+        n_full = (splits == 1) ? p.n_items : 0;
+    } else {
+        const int rem = p.n_items % slots;
+        const int tail = (p.n_items < slots) ? p.n_items : rem;
+        if (tail > 0 && tail <= slots / 2) {
+            int s_auto = slots / tail;                           // blocks per tail item
+            s_auto = std::min(s_auto, n_kv_tiles / 2);           // keep >= 2 key tiles per range
+            s_auto = std::min(s_auto, kMaxSplits);
+            if (s_auto >= 2) {
+                splits = s_auto;
+                n_full = p.n_items - tail;
+            }
         }
     }
-    if (splits > n_kv_tiles) {
-        if (kv_splits != 0) return ATTN_ERR_OPTION;   // a forced split must leave every range non-empty
-        splits = n_kv_tiles;
-    }
+    p.n_full = n_full;
     p.kv_splits = splits;
     p.n_kv_tiles = n_kv_tiles;
-    p.n_blocks = p.n_items * splits;
+    p.n_blocks = n_full + (p.n_items - n_full) * splits;
     p.block_order = (block_order == 1) ? attn::ORDER_NAIVE : attn::ORDER_XCD;
 
-    if (splits > 1) {
-        const size_t per = (size_t)KERNEL_BM * (kHeadDim + 2) * sizeof(float);
-        const size_t need = (size_t)p.n_items * splits * per;
+    if (n_full < p.n_items) {
+        const size_t n_part = (size_t)(p.n_items - n_full) * splits;
+        const size_t need = n_part * KERNEL_BM * (kHeadDim + 2) * sizeof(float);
         void* ws = nullptr;
         const int wrc = get_workspace(dev, stream, need, &ws);
         if (wrc != ATTN_OK) return wrc;
         p.ws_o = (float*)ws;
-        p.ws_ml = (float*)((char*)ws + (size_t)p.n_items * splits * KERNEL_BM * kHeadDim * sizeof(float));
+        p.ws_ml = (float*)((char*)ws + n_part * KERNEL_BM * kHeadDim * sizeof(float));
     }
 
     if (attn::launch(p, (hipStream_t)stream) != 0) return ATTN_ERR_LAUNCH;

@@ -23,16 +23,17 @@ struct AttnParams {
     const uint16_t* k;
     const uint16_t* v;
     uint16_t* o;
-    float* ws_o;       // split partial outputs [n_items][kv_splits][BM][128] (fp32)
-    float* ws_ml;      // split partial (M, l) pairs [n_items][kv_splits][BM][2]
+    float* ws_o;       // split partial outputs [n_items - n_full][kv_splits][BM][128] (fp32)
+    float* ws_ml;      // split partial (M, l) pairs [n_items - n_full][kv_splits][BM][2]
     int64_t q_row, q_head, q_batch;      // element strides of q and o
     int64_t kv_row, kv_head, kv_batch;   // element strides of k and v
     int B, H, Sq, Skv;
     int n_qtiles;      // ceil(Sq / BM)
     int n_items;       // B * H * n_qtiles
-    int kv_splits;     // key ranges per query tile (1 = no split)
+    int n_full;        // work items [0, n_full) run unsplit (one block each)
+    int kv_splits;     // key ranges of each item in [n_full, n_items) (1 = no split)
     int n_kv_tiles;    // ceil(Skv / 64)
-    int n_blocks;      // n_items * kv_splits
+    int n_blocks;      // n_full + (n_items - n_full) * kv_splits
     int block_order;   // ORDER_NAIVE or ORDER_XCD
     int round_mode;
     float c;           // fp32(scale * log2(e))

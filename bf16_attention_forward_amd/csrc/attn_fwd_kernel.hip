@@ -168,17 +168,27 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     const int j = lane & 15;       // lane within group
 
     // ---- work item
-    const int w = map_block(blockIdx.x, p.n_blocks, p.block_order);
-    const int split = w % p.kv_splits;
-    const int item = w / p.kv_splits;
+    // Blocks [0, n_full) take the unsplit items (in XCD-aware order); the
+    // remaining blocks take the key ranges of the split items.
+    int item, split, nsplit;
+    if ((int)blockIdx.x < p.n_full) {
+        item = map_block(blockIdx.x, p.n_full, p.block_order);
+        split = 0;
+        nsplit = 1;
+    } else {
+        const int tb = blockIdx.x - p.n_full;
+        item = p.n_full + tb / p.kv_splits;
+        split = tb % p.kv_splits;
+        nsplit = p.kv_splits;
+    }
     const int qt = item % p.n_qtiles;
     const int bh = item / p.n_qtiles;
     const int h = bh % p.H;
     const int b = bh / p.H;
 
     // split s covers key tiles [s*T/ns, (s+1)*T/ns) of the T tiles: never empty for ns <= T
-    const int kv_begin = (int)(((int64_t)split * p.n_kv_tiles) / p.kv_splits) * BN;
-    const int kv_end = min(p.Skv, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / p.kv_splits) * BN);
+    const int kv_begin = (int)(((int64_t)split * p.n_kv_tiles) / nsplit) * BN;
+    const int kv_end = min(p.Skv, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / nsplit) * BN);
     const int T = (kv_end - kv_begin + BN - 1) / BN;
 
     const uint16_t* qbase = p.q + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
@@ -450,7 +460,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 #pragma unroll
     for (int qb = 0; qb < NQB; qb++) l_row[qb] = rowsum4(l_run[qb]);
 
-    if (p.kv_splits == 1) {
+    if (nsplit == 1) {
         uint16_t* obase = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
@@ -474,7 +484,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         }
     } else {
         // partial results: O (unnormalised, fp32) [item][split][BM][128], M and l [item][split][BM]
-        const int64_t part = (int64_t)item * p.kv_splits + split;
+        // (items counted from n_full)
+        const int64_t part = (int64_t)(item - p.n_full) * nsplit + split;
         float* ow = p.ws_o + part * (int64_t)BM * D;
         float* mw = p.ws_ml + part * (int64_t)BM * 2;
 #pragma unroll
@@ -497,12 +508,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 template <int BM>
 __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)p.n_items * BM * (D / 4);
+    const int64_t total = (int64_t)(p.n_items - p.n_full) * BM * (D / 4);
     if (gid >= total) return;
     const int d4 = (int)(gid % (D / 4));
     const int64_t r = gid / (D / 4);
     const int lrow = (int)(r % BM);
-    const int item = (int)(r / BM);
+    const int sidx = (int)(r / BM);          // index among the split items
+    const int item = p.n_full + sidx;
     const int qt = item % p.n_qtiles;
     const int bh = item / p.n_qtiles;
     const int h = bh % p.H, b = bh / p.H;
@@ -510,7 +522,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
     if (row >= p.Sq) return;
 
     const int ns = p.kv_splits;
-    const float* mw = p.ws_ml + (int64_t)item * ns * BM * 2;
+    const float* mw = p.ws_ml + (int64_t)sidx * ns * BM * 2;
     float M = -__builtin_inff();
     for (int s = 0; s < ns; s++) M = fmaxf(M, mw[(int64_t)s * BM * 2 + 2 * lrow]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -519,7 +531,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
         const float ms = mw[(int64_t)s * BM * 2 + 2 * lrow];
         const float ls = mw[(int64_t)s * BM * 2 + 2 * lrow + 1];
         const float wgt = ldexpf(1.0f, (int)fmaxf(ms - M, -200.f));
-        const f32x4 os = *(const f32x4*)(p.ws_o + ((int64_t)item * ns + s) * BM * D + (int64_t)lrow * D + 4 * d4);
+        const f32x4 os = *(const f32x4*)(p.ws_o + ((int64_t)sidx * ns + s) * BM * D + (int64_t)lrow * D + 4 * d4);
         acc += os * wgt;
         l += ls * wgt;
     }
@@ -541,8 +553,8 @@ int launch(const AttnParams& p, hipStream_t stream) {
     else
         hipLaunchKernelGGL((attn_fwd_main<false>), grid, block, 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
-    if (p.kv_splits > 1) {
-        const int64_t total = (int64_t)p.n_items * KERNEL_BM * (D / 4);
+    if (p.n_full < p.n_items) {
+        const int64_t total = (int64_t)(p.n_items - p.n_full) * KERNEL_BM * (D / 4);
         dim3 cgrid((unsigned)((total + 255) / 256));
         hipLaunchKernelGGL((attn_fwd_combine<KERNEL_BM>), cgrid, dim3(256), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return -1;

@@ -92,11 +92,20 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 
 /*
  * attn_fwd_bf16_ex -- attn_fwd_bf16 with planner overrides, for tests and
- * ablations.  kv_splits: 0 = planner's choice, n >= 1 forces every query
- * tile's keys into n contiguous ranges merged by the combine kernel
- * (n <= 64, and each range must hold at least one key).  block_order:
- * 0 = planner's choice (XCD-aware), 1 = naive (work item = block id),
- * 2 = XCD-aware.  Other values return ATTN_ERR_OPTION.
+ * ablations.
+ *
+ * The planner (kv_splits = 0) runs one work-group per CU per round; when the
+ * last round of query tiles is ragged (or there is less than one round), the
+ * query tiles of that round have their key range split so the round fills
+ * the GPU, and a combine kernel merges the partial results in a fixed order
+ * (the flash-decoding style tail split of "MoonMath AI open-sources a HIP
+ * attention kernel for AMD MI300X", section on the two later improvements).
+ *
+ * kv_splits: 0 = planner's choice; 1 = never split; n >= 2 splits every
+ * query tile's keys into n contiguous ranges of whole 64-key tiles (n must
+ * not exceed the number of 64-key tiles, n <= 64).  block_order: 0 =
+ * planner's choice (XCD-aware), 1 = naive (work item = block id), 2 =
+ * XCD-aware.  Other values return ATTN_ERR_OPTION.
  */
 int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
                      int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,

@@ -111,3 +111,27 @@ def test_layouts_give_identical_bits():
     perm = lambda t: t.permute(0, 2, 1, 3).contiguous()
     b = run_hip(perm(q), perm(k), perm(v), "bhsd")
     assert np.array_equal(a.reshape(2, 190, 3, 128).transpose(0, 2, 1, 3), b.reshape(2, 3, 190, 128))
+
+
+def test_planner_tail_split_ragged_round():
+    """270 query tiles of 256 rows on 256 CUs: the planner splits the keys of
+    the 14 tiles of the ragged last round; both the split and the unsplit
+    tiles must pass the gate."""
+    layout, B, H, Sq, Skv = "bhsd", 1, 3, 256 * 90, 1024
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 91, 1.0, 2.0, 1.0)
+    rng = np.random.default_rng(5)
+    tail_rows = 2 * Sq + 76 * 256 + rng.integers(0, 14 * 256, size=96)     # items 256..269
+    head_rows = rng.integers(0, 2 * Sq, size=64)
+    rows = np.unique(np.concatenate([tail_rows, head_rows, [B * H * Sq - 1]]))
+    res = None
+    for splits in (0, 1):
+        o = run_hip(q, k, v, layout, "rtne", kv_splits=splits)
+        st, res = check(o, q, k, v, layout, "rtne", rows=rows, label=f"tail planner splits={splits}", oracle_res=res)
+        assert_gate(st)
+
+
+def test_xcd_and_naive_block_order_agree_bitwise():
+    q, k, v = wl.random_qkv("bshd", 1, 4, 1000, 700, 92)
+    a = run_hip(q, k, v, "bshd", block_order=1)
+    b = run_hip(q, k, v, "bshd", block_order=2)
+    assert np.array_equal(a, b)
