@@ -21,7 +21,6 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -35,14 +34,6 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz (de
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    for f in ("attn_fwd_kernel.hip", "attn_fwd_internal.h"):
-        with open(os.path.join(ROOT, "bf16_attention_forward_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -51,8 +42,9 @@ def measured_traffic(workload_name: str):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from bf16_attention_forward_amd.profiling import kernel_source_sha
     ent = rec.get("workloads", {}).get(workload_name)
-    if not ent or rec.get("kernel_source_sha") != kernel_source_sha():
+    if not ent or rec.get("kernel_source_sha") != kernel_source_sha(ROOT):
         return None
     return ent.get("hbm_bytes_per_launch")
 

@@ -9,6 +9,12 @@
 
   python -m bf16_attention_forward_amd.profiling counters --dir D --out F --command C
       Per-kernel average of every collected counter (from --pmc CSV output).
+
+  python -m bf16_attention_forward_amd.profiling traffic --fetch D1 --write D2 \
+        --copy-fetch D3 --copy-write D4 --copy-mib 1024 --workload NAME --out JSON
+      HBM bytes per launch of attn_fwd_main: FETCH_SIZE and WRITE_SIZE (KiB per
+      dispatch) each divided by what the same counter reads per byte of the
+      calibration copy, recorded with the kernel source hash it was taken on.
 """
 from __future__ import annotations
 
@@ -38,15 +44,19 @@ def short_name(name: str) -> str:
     return name[:80]
 
 
-def kernel_stats(d: str) -> dict:
-    """{kernel: {calls, avg_ns, min_ns, max_ns, total_ns}} from the kernel trace CSV."""
+def kernel_stats(d: str, last: int = 0) -> dict:
+    """{kernel: {calls, avg_ns, min_ns, max_ns, total_ns}} from the kernel trace CSV
+    (dispatch order; with last > 0 only each kernel's last `last` dispatches)."""
     rows = []
     for f in _find(d, "kernel_trace.csv"):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     per = defaultdict(list)
     for r in rows:
         per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if last > 0:
+        per = {k: v[-last:] for k, v in per.items()}
     return {k: {"calls": len(v), "avg_ns": statistics.fmean(v), "median_ns": statistics.median(v),
                 "min_ns": min(v), "max_ns": max(v), "total_ns": sum(v)} for k, v in per.items()}
 
@@ -61,6 +71,46 @@ def counter_means(d: str) -> dict:
     # several rows per dispatch when a counter is reported per dimension: sum within dispatch is
     # already done by rocprofv3 for derived counters; average over dispatches here
     return {k: {c: statistics.fmean(v) for c, v in cs.items()} for k, cs in per.items()}
+
+
+def kernel_source_sha(root: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn_fwd_kernel.hip", "attn_fwd_internal.h"):
+        with open(os.path.join(root, "bf16_attention_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, workload, out, command):
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    f = counter_means(fetch_dir)["attn_fwd_main"]["FETCH_SIZE"]
+    w = counter_means(write_dir)["attn_fwd_main"]["WRITE_SIZE"]
+    cf = [v["FETCH_SIZE"] for k, v in counter_means(cfetch_dir).items() if k.startswith("copy:")][0]
+    cw = [v["WRITE_SIZE"] for k, v in counter_means(cwrite_dir).items() if k.startswith("copy:")][0]
+    copy_bytes = copy_mib * 1024 * 1024
+    f_scale = cf * 1024.0 / copy_bytes      # counter bytes per true byte read
+    w_scale = cw * 1024.0 / copy_bytes
+    rec = {}
+    if os.path.exists(out):
+        with open(out) as fh:
+            rec = json.load(fh)
+    sha = kernel_source_sha(root)
+    if rec.get("kernel_source_sha") != sha:
+        rec = {"kernel_source_sha": sha, "workloads": {}}
+    rec["workloads"][workload] = {
+        "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w,
+        "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_read_bytes_per_launch": f * 1024.0 / f_scale,
+        "hbm_write_bytes_per_launch": w * 1024.0 / w_scale,
+        "hbm_bytes_per_launch": f * 1024.0 / f_scale + w * 1024.0 / w_scale,
+        "command": command,
+    }
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec["workloads"][workload], indent=1))
 
 
 def do_copy(mib: int, iters: int):
@@ -86,17 +136,30 @@ def main():
         s.add_argument("--out", required=True)
         s.add_argument("--command", required=True)
         s.add_argument("--title", default="")
+        s.add_argument("--last", type=int, default=0, help="also summarise each kernel's last N dispatches")
+    t = sub.add_parser("traffic")
+    for n in ("fetch", "write", "copy-fetch", "copy-write", "workload", "out", "command"):
+        t.add_argument("--" + n, required=True)
+    t.add_argument("--copy-mib", type=int, default=1024)
     a = ap.parse_args()
+    if a.cmd == "traffic":
+        traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.workload, a.out, a.command)
+        return
     if a.cmd == "copy":
         do_copy(a.mib, a.iters)
         return
     lines = [f"# {a.title}".rstrip(), "", f"command: {a.command}", ""]
     if a.cmd == "stats":
-        st = kernel_stats(a.dir)
-        lines.append(f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} {'max_us':>10s}")
-        for k, v in sorted(st.items(), key=lambda kv: -kv[1]["total_ns"]):
-            lines.append(f"{k:40s} {v['calls']:6d} {v['avg_ns'] / 1e3:10.2f} {v['median_ns'] / 1e3:10.2f} "
-                         f"{v['min_ns'] / 1e3:10.2f} {v['max_ns'] / 1e3:10.2f}")
+        for label, last in (("all dispatches", 0), (f"last {a.last} dispatches (the timed steps)", a.last)):
+            if label.startswith("last") and last <= 0:
+                continue
+            st = kernel_stats(a.dir, last)
+            lines.append(f"## {label}")
+            lines.append(f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+            for k, v in sorted(st.items(), key=lambda kv: -kv[1]["total_ns"]):
+                lines.append(f"{k:40s} {v['calls']:6d} {v['avg_ns'] / 1e3:10.2f} {v['median_ns'] / 1e3:10.2f} "
+                             f"{v['min_ns'] / 1e3:10.2f} {v['max_ns'] / 1e3:10.2f}")
+            lines.append("")
     else:
         cm = counter_means(a.dir)
         for k, cs in sorted(cm.items()):
