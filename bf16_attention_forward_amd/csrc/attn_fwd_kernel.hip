@@ -3,39 +3,48 @@
 // Computes O = softmax(Q K^T * scale) V for head dimension 128 (the fused
 // operation of "MoonMath AI open-sources a HIP attention kernel for AMD
 // MI300X that beats AITER", opening paragraphs), streaming K/V tiles with an
-// online softmax.  Design, per work-group:
+// online softmax.  Design, per work-group (8 waves, 256 query rows of one
+// (batch, head), one work-group per CU):
 //
-//  * Work item = (batch, head, tile of BM query rows, key range).  Each of the
-//    NW waves owns 16*NQB query rows; its Q fragments stay in VGPRs for the
+//  * Each wave owns 32 query rows; its Q fragments stay in VGPRs for the
 //    whole key loop and O accumulates in registers (the MI300X article's data
 //    placement section keeps Q and the accumulators in registers too).
 //  * K and V tiles of 64 keys go HBM -> LDS with buffer_load ... lds (16 B per
 //    lane, lane-contiguous in LDS), double-buffered and shared by all waves.
 //    The bank swizzle is applied to the source address of each lane, not to
 //    the LDS address (HipKittens summary, method section on global async
-//    loads).  Rows past Skv read as zero through the buffer range check.
+//    loads).  Rows past the key range read as zero through the buffer range
+//    check.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, K as operand A and Q as
-//    operand B.  With that order each lane ends up holding scores of ONE
-//    query for a set of keys, which is exactly the B-operand layout of the
-//    next product O^T = V^T P^T, so P never leaves registers (the FlyDSL
-//    procedure article, optimisation section, states the operand-order trick
-//    for gfx942; here it is re-derived for the 16x16x32 shape: K rows are
-//    read in a permuted order so that every lane group holds 8 consecutive
-//    keys of each 32-key step).  The AITER docs index names the same bf16
-//    16x16x32 MFMA for both attention products on gfx950.
+//    operand B.  With that order each lane holds scores of ONE query for a
+//    set of keys, which is the B-operand layout of the next product
+//    O^T = V^T P^T, so P never leaves registers (the FlyDSL procedure article,
+//    optimisation section, states the operand-order trick for gfx942; here it
+//    is re-derived for the 16x16x32 shape).  The AITER docs index names the
+//    same bf16 16x16x32 MFMA for both attention products on gfx950.
 //  * V^T fragments come from the row-major V tile through ds_read_b64_tr_b16,
 //    the gfx950 transposing LDS read (FlyDSL article: gfx950 adds
-//    LDS-to-register transpose loads), so V needs no shuffle.
+//    LDS-to-register transpose loads); its 4+4 source rows are chosen to match
+//    the keys of P's elements, so V needs no shuffle.
 //  * Online softmax with a power-of-two running maximum: M = ceil(max x) with
 //    x = s * scale * log2(e), p = 2^(x - M).  A change of M rescales O and the
 //    row sum by an exact power of two, and is skipped when no row's M moved.
 //    Row maxima and sums are reduced across the 4 lanes of a row with the
 //    gfx950 v_permlane16/32_swap instructions.
 //  * P enters the second product as bf16 rounded to nearest-even
-//    (v_cvt_pk_bf16_f32); the row sum adds those same bf16 weights, and the
-//    output is divided by it and
+//    (v_cvt_pk_bf16_f32); the row sum adds those same bf16 weights
+//    (v_dot2c_f32_bf16 against (1, 1)), and the output is divided by it and
 //    rounded to bf16 in the requested mode with integer bit arithmetic after
 //    a NaN guard.
+//  * One barrier per key tile.  Right after it every wave issues its slice of
+//    the DMA for K_{t+1} and V_t, then runs S_t = K_t Q^T interleaved with the
+//    fragment reads of O += V_{t-1}^T P_{t-1}^T, then the softmax of S_t, and
+//    waits for its own DMA before the next barrier.  The two waves sharing a
+//    SIMD drift freely, so one's MFMAs overlap the other's softmax.  (A
+//    two-group ping-pong with a barrier between the matrix and the softmax
+//    phase, the schedule of the MI300X article's architecture section and of
+//    the HipKittens 8-wave ping-pong, was built and measured ~3% slower on
+//    gfx950 for long sequences.)
 //  * Optional split of the key range (the flash-decoding style tail split of
 //    the MI300X article, section on the two later improvements): each split
 //    writes its unnormalised fp32 O, M and row sum; a combine kernel merges the
@@ -63,7 +72,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;          // head dimension
 constexpr int BN = 64;          // keys per K/V tile
-constexpr int NW = KERNEL_NW;   // waves per work-group (two groups of 4)
+constexpr int NW = KERNEL_NW;   // waves per work-group
 constexpr int NQB = KERNEL_NQB; // 16-row query blocks per wave
 constexpr int BM = KERNEL_BM;   // query rows per work item
 constexpr int ROW_BYTES = D * 2;
@@ -127,26 +136,18 @@ __device__ __forceinline__ int map_block(int bid, int n, int order) {
 }
 
 // ------------------------------------------------------------ main kernel
-// Workgroup barrier that keeps outstanding K/V DMA (tracked by vmcnt) in
-// flight across it: a memory fence here would wait for the DMA's LDS writes.
-// Every wave instead waits for its own DMA explicitly before the barrier that
-// publishes a tile, and ds_read/ds_write completion (lgkmcnt) is waited for
-// here; the "memory" clobber keeps the compiler from moving LDS accesses
-// across the barrier.
+// Workgroup barrier between key tiles.  Every wave waits for its own K/V DMA
+// (vmcnt) explicitly before it, so the barrier itself only needs the LDS
+// reads done (lgkmcnt); the "memory" clobber and the scheduling barriers
+// keep the compiler from moving any instruction across it.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);   // no instruction may be scheduled across a phase boundary
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// 8 waves in two groups of 4 (waves w and w+4 share a SIMD).  Each wave owns
-// 32 query rows.  Per key tile t a wave runs an MFMA phase (S_t = K_t Q^T and
-// O += V_{t-1}^T P_{t-1}^T) and a VALU phase (softmax of S_t into P_t).  Group 1
-// starts one barrier late, so at any time one group is on the matrix cores
-// and the other on the vector ALUs, swapping at every barrier (the schedule
-// of the MI300X article's architecture section and of the HipKittens 8-wave
-// ping-pong).  K_{t+1} and V_t are fetched during the interval in which group
-// 0 runs MFMA phase t and must land by the end of the following interval.
+// 8 waves, each owning 32 query rows of the work item; see the file header
+// for the per-tile schedule.
 template <bool CPOS>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
@@ -163,7 +164,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
-    const int group = wave >> 2;   // 0 or 1
     const int g = lane >> 4;       // lane group (0..3)
     const int j = lane & 15;       // lane within group
 
@@ -409,35 +409,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         }
     };
 
-    // ---- the ping-pong loop (see the comment above the kernel)
+    // ---- key loop: one barrier per tile.  Iteration t issues the DMA of K_{t+1}
+    // (into the buffer K_{t-1} used) and V_t (into V_{t-2}'s), computes
+    // S_t = K_t Q^T and O += V_{t-1}^T P_{t-1}^T, then the softmax of S_t, and
+    // waits for its DMA before the barrier.  Iteration 0 has no P.V step and
+    // iteration T (past the last tile) only the P.V step; the steady-state
+    // loop in between is branch-free in vector state, which keeps the
+    // accumulators in place.
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's K_0 slice and its Q landed
     lds_barrier();
-    if (group == 1) {
-        if (T > 1) issue_k(1, sk1);
-        issue_v(0, sv0);
-        lds_barrier();                    // the one-phase offset of group 1
-    }
-    // Iteration t: MFMA phase (S_t = K_t Q^T, O += V_{t-1}^T P_{t-1}^T), then VALU
-    // phase (softmax of S_t).  K_t and V_t live in buffer t % 2.  The first
-    // iteration has no P.V step and iteration T (past the last tile) only the
-    // P.V step; the steady-state loop in between is branch-free in vector
-    // state, which keeps the accumulators in place across iterations.
     auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c) {
-        // MFMA phase t
-        if (group == 0) {
-            if (t + 1 < T) issue_k(t + 1, kn);
-            if (t < T) issue_v(t, vc);
-        }
+        if (t + 1 < T) issue_k(t + 1, kn);
+        if (t < T) issue_v(t, vc);
         mfma_phase(kc, vp, s0c, s1c);
-        if (group == 1) __builtin_amdgcn_s_waitcnt(0x0f70);
-        lds_barrier();
-        // VALU phase t
-        if (group == 1) {
-            if (t + 2 < T) issue_k(t + 2, kc);
-            if (t + 1 < T) issue_v(t + 1, vp);
-        }
         if (decltype(s0c)::value == 0) softmax(t);
-        if (group == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        __builtin_amdgcn_s_waitcnt(0x0f70);
         lds_barrier();
     };
     iter(0, sk0, sk1, sv0, sv1, C0{}, C16{});
@@ -446,14 +432,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         iter(t, sk1, sk0, sv1, sv0, C0{}, C32{});
         iter(t + 1, sk0, sk1, sv0, sv1, C0{}, C32{});
     }
-    if (t < T) {   // one more full iteration (t odd)
+    if (t < T) {
         iter(t, sk1, sk0, sv1, sv0, C0{}, C32{});
         t++;
     }
-    // iteration T: the P.V step of the last tile, whose V sits in buffer (T-1) % 2
     if (T & 1) iter(T, sk1, sk0, sv1, sv0, C16{}, C32{});
     else iter(T, sk0, sk1, sv0, sv1, C16{}, C32{});
-    if (group == 0) lds_barrier();        // group 0 matches group 1's extra barrier
 
     // ---- epilogue: the 4 lanes of a row hold partial row sums
     float l_row[NQB];
