@@ -83,12 +83,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// max over lanes {l, l^16, l^32, l^48}
+// max over lanes {l, l^16, l^32, l^48} (NaN-propagating)
 __device__ __forceinline__ float rowmax4(float x) {
     auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    x = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
     auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
 
 // sum over lanes {l, l^16, l^32, l^48}, in a fixed pairing order
@@ -339,34 +339,42 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         const int valid = kv_end - (kv_begin + t * BN);   // keys of this tile inside the range
         bool any_rescale = false;
         float alpha[NQB];
+        // Keys past the range are masked by select, never by arithmetic: key
+        // 16*kb + 4*g + r is inside the range iff 16*kb + r < valid - 4*g.
+        // With c > 0 only a ragged last tile needs it, and one branch covers
+        // both query blocks so the compares stay inside it.
+        const int lim = valid - 4 * g;
+        if (CPOS && valid < BN) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; qb++) {
-            // keys past the range are masked by select, never by arithmetic
-            // key 16*kb + 4*g + r is inside the range iff 16*kb + r < lim
-            const int lim = valid - 4 * g;
-            if (CPOS && valid < BN) {
+            for (int qb = 0; qb < NQB; qb++)
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
                         s_acc[kb][qb][r] = (16 * kb + r < lim) ? s_acc[kb][qb][r] : -__builtin_inff();
-            }
-            if (!CPOS) {
-                // general scale (c <= 0): x = s*c explicitly, keys past the range -> -inf
+        }
+        if (!CPOS) {
+            // general scale (c <= 0): x = s*c explicitly, keys past the range -> -inf
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++)
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
                         s_acc[kb][qb][r] = (16 * kb + r < lim) ? s_acc[kb][qb][r] * c : -__builtin_inff();
-            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; qb++) {
+            // NaN-propagating maximum (v_maximum3_f32): a NaN score makes the
+            // row's max NaN, as its weights and output are NaN anyway.
             float mx = -__builtin_inff();
 #pragma unroll
             for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) mx = fmaxf(mx, s_acc[kb][qb][r]);
+                for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
             mx = rowmax4(mx);
             if (CPOS) mx *= c;
-            const float m_new = fmaxf(m_run[qb], ceilf(mx));
+            const float m_new = __builtin_elementwise_maximum(m_run[qb], ceilf(mx));
             const float dm = m_run[qb] - m_new;     // <= 0, integer-valued, or -inf / NaN
             alpha[qb] = ldexpf(1.0f, (int)fmaxf(dm, -200.f));
             any_rescale |= (dm != 0.f);
