@@ -77,6 +77,7 @@ constexpr int NQB = KERNEL_NQB; // 16-row query blocks per wave
 constexpr int BM = KERNEL_BM;   // query rows per work item
 constexpr int ROW_BYTES = D * 2;
 constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
+constexpr float MAX_LAG = 8.0f;             // log2 headroom of the softmax weights
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -374,7 +375,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
                 for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
             mx = rowmax4(mx);
             if (CPOS) mx *= c;
-            const float m_new = __builtin_elementwise_maximum(m_run[qb], ceilf(mx));
+            // Lazy rescale: the running offset M only moves when the tile's
+            // max exceeds it by more than MAX_LAG (then to ceil(max)), so
+            // weights stay <= 2^MAX_LAG and the O / l rescale is rare.  A
+            // NaN max leaves M as is; the NaN weights make the row NaN.
+            const float tmax = ceilf(mx);
+            const float m_new = (tmax > m_run[qb] + MAX_LAG) ? tmax : m_run[qb];
             const float dm = m_run[qb] - m_new;     // <= 0, integer-valued, or -inf / NaN
             alpha[qb] = ldexpf(1.0f, (int)fmaxf(dm, -200.f));
             any_rescale |= (dm != 0.f);

@@ -73,6 +73,47 @@ def counter_means(d: str) -> dict:
     return {k: {c: statistics.fmean(v) for c, v in cs.items()} for k, cs in per.items()}
 
 
+# MI355X: 8 XCDs (GRBM_GUI_ACTIVE is summed over them), 256 CUs, 4 SIMDs each
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def derived_lines(cs: dict) -> list:
+    """Utilisation figures from the per-dispatch means of attn_fwd_main."""
+    out = []
+    gui = cs.get("GRBM_GUI_ACTIVE")
+    if not gui:
+        return out
+    cyc = gui / N_XCD
+    out.append(f"  GPU cycles per dispatch (GRBM_GUI_ACTIVE / {N_XCD} XCDs) = {cyc:,.0f}")
+    mb = cs.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    if mb:
+        out.append(f"  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {N_SIMD} SIMDs) = {mb / (cyc * N_SIMD):.3f}")
+        if cs.get("SQ_INSTS_MFMA"):
+            out.append(f"     ({mb / cs['SQ_INSTS_MFMA']:.1f} busy cycles charged per MFMA instruction)")
+    co = cs.get("SQ_VALU_MFMA_COEXEC_CYCLES")
+    if co is not None:
+        out.append(f"  VALU issued while MFMA busy = SQ_VALU_MFMA_COEXEC_CYCLES / (cycles x {N_SIMD}) = {co / (cyc * N_SIMD):.3f}")
+    waves = cs.get("SQ_WAVES")
+    if waves:
+        per = [f"{n} per wave = {cs[c] / waves:,.0f}" for n, c in
+               (("MFMA", "SQ_INSTS_MFMA"), ("VALU incl. MFMA", "SQ_INSTS_VALU"), ("LDS", "SQ_INSTS_LDS")) if c in cs]
+        if per:
+            out.append("  instructions: " + "; ".join(per))
+    lds = cs.get("SQ_LDS_IDX_ACTIVE")
+    if lds:
+        out.append(f"  LDS busy = SQ_LDS_IDX_ACTIVE / (cycles x {N_CU} CUs) = {lds / (cyc * N_CU):.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in cs:
+        out.append(f"  LDS bank-conflict cycles per dispatch = {cs['SQ_LDS_BANK_CONFLICT']:,.0f}")
+    av = cs.get("SQ_ACTIVE_INST_VALU")
+    if av:
+        out.append(f"  VALU active (quad-cycles x 4) / (cycles x {N_SIMD}) = {4 * av / (cyc * N_SIMD):.3f}")
+    wl = cs.get("SQ_WAIT_INST_LDS")
+    if wl is not None:
+        out.append(f"  wave-cycles waiting for LDS issue (x 4) / (cycles x waves resident) = "
+                   f"{4 * wl / (cyc * 2 * N_SIMD):.3f}")
+    return out
+
+
 def kernel_source_sha(root: str) -> str:
     import hashlib
     h = hashlib.sha256()
@@ -132,7 +173,7 @@ def main():
     c.add_argument("--iters", type=int, default=5)
     for name in ("stats", "counters"):
         s = sub.add_parser(name)
-        s.add_argument("--dir", required=True)
+        s.add_argument("--dir", required=True, nargs="+")
         s.add_argument("--out", required=True)
         s.add_argument("--command", required=True)
         s.add_argument("--title", default="")
@@ -153,7 +194,7 @@ def main():
         for label, last in (("all dispatches", 0), (f"last {a.last} dispatches (the timed steps)", a.last)):
             if label.startswith("last") and last <= 0:
                 continue
-            st = kernel_stats(a.dir, last)
+            st = kernel_stats(a.dir[0], last)
             lines.append(f"## {label}")
             lines.append(f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} {'max_us':>10s}")
             for k, v in sorted(st.items(), key=lambda kv: -kv[1]["total_ns"]):
@@ -161,11 +202,17 @@ def main():
                              f"{v['min_ns'] / 1e3:10.2f} {v['max_ns'] / 1e3:10.2f}")
             lines.append("")
     else:
-        cm = counter_means(a.dir)
+        cm = defaultdict(dict)
+        for d in a.dir:
+            for k, cs in counter_means(d).items():
+                cm[k].update(cs)
         for k, cs in sorted(cm.items()):
-            lines.append(f"[{k}]")
+            lines.append(f"[{k}] per-dispatch means")
             for cn, val in sorted(cs.items()):
                 lines.append(f"  {cn:40s} {val:20.3f}")
+            if k == "attn_fwd_main":
+                lines += ["", "Derived:"] + derived_lines(cs)
+            lines.append("")
     text = "\n".join(lines) + "\n"
     with open(a.out, "w") as f:
         f.write(text)
