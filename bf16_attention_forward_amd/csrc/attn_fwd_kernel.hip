@@ -26,11 +26,13 @@
 //    the gfx950 transposing LDS read (FlyDSL article: gfx950 adds
 //    LDS-to-register transpose loads); its 4+4 source rows are chosen to match
 //    the keys of P's elements, so V needs no shuffle.
-//  * Online softmax with a power-of-two running maximum: M = ceil(max x) with
-//    x = s * scale * log2(e), p = 2^(x - M).  A change of M rescales O and the
-//    row sum by an exact power of two, and is skipped when no row's M moved.
-//    Row maxima and sums are reduced across the 4 lanes of a row with the
-//    gfx950 v_permlane16/32_swap instructions.
+//  * Online softmax with a power-of-two running offset: x = s * scale *
+//    log2(e), p = 2^(x - M), M an integer that is set to ceil(max x) on the
+//    first tile and moves only when a tile's max exceeds it by more than 8
+//    (so p <= 2^8).  A move rescales O and the row sum by an exact power of
+//    two, and is skipped when no row of the wave moved -- after the first
+//    tiles it almost never happens.  Row maxima and sums are reduced across
+//    the 4 lanes of a row with the gfx950 v_permlane16/32_swap instructions.
 //  * P enters the second product as bf16 rounded to nearest-even
 //    (v_cvt_pk_bf16_f32); the row sum adds those same bf16 weights
 //    (v_dot2c_f32_bf16 against (1, 1)), and the output is divided by it and
@@ -40,7 +42,9 @@
 //    the DMA for K_{t+1} and V_t, then runs S_t = K_t Q^T interleaved with the
 //    fragment reads of O += V_{t-1}^T P_{t-1}^T, then the softmax of S_t, and
 //    waits for its own DMA before the next barrier.  The two waves sharing a
-//    SIMD drift freely, so one's MFMAs overlap the other's softmax.  (A
+//    SIMD drift freely; a wave in its MFMA phase runs at raised issue
+//    priority (s_setprio) so the matrix core stays fed while the other
+//    wave's softmax fills the gaps.  (A
 //    two-group ping-pong with a barrier between the matrix and the softmax
 //    phase, the schedule of the MI300X article's architecture section and of
 //    the HipKittens 8-wave ping-pong, was built and measured ~3% slower on
@@ -435,7 +439,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c) {
         if (t + 1 < T) issue_k(t + 1, kn);
         if (t < T) issue_v(t, vc);
+        // A wave in its MFMA phase takes issue priority over one in its
+        // softmax, so the matrix core of a SIMD stays fed; the softmax VALU
+        // work fills the MFMA phase's gaps.
+        __builtin_amdgcn_s_setprio(1);
         mfma_phase(kc, vp, s0c, s1c);
+        __builtin_amdgcn_s_setprio(0);
         if (decltype(s0c)::value == 0) softmax(t);
         __builtin_amdgcn_s_waitcnt(0x0f70);
         lds_barrier();

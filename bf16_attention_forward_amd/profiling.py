@@ -115,11 +115,17 @@ def derived_lines(cs: dict) -> list:
 
 
 def kernel_source_sha(root: str) -> str:
+    """Hash of the kernel sources with comments and blank space removed, so a
+    record stays valid across comment edits and goes stale on code changes."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("attn_fwd_kernel.hip", "attn_fwd_internal.h"):
-        with open(os.path.join(root, "bf16_attention_forward_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root, "bf16_attention_forward_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
