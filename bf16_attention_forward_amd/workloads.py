@@ -44,23 +44,48 @@ class Workload:
     modes: tuple = ("rtne", "rtna", "rtz")
     nonfinite_instance: bool = False
     note: str = ""
+    Hkv: int = 0          # key/value heads (grouped-query attention); 0 = H
+    causal: bool = False  # bottom-right aligned causal mask
 
     @property
     def seed(self) -> int:
         return 1000 + self.number
 
     @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def pairs(self) -> int:
+        """Attended (query, key) pairs per (batch, query head)."""
+        return attended_pairs(self.Sq, self.Skv, self.causal)
+
+    @property
     def flops(self) -> int:
-        return 4 * self.B * self.H * self.Sq * self.Skv * HEAD_DIM
+        return 4 * self.B * self.H * self.pairs * HEAD_DIM
 
     @property
     def algorithmic_bytes(self) -> int:
         """Q, K, V read once and O written once, bf16."""
-        return 2 * HEAD_DIM * self.B * self.H * (2 * self.Sq + 2 * self.Skv)
+        return 2 * HEAD_DIM * self.B * (2 * self.H * self.Sq + 2 * self.kv_heads * self.Skv)
 
     def describe(self) -> dict:
-        return {"workload": self.name, "layout": self.layout, "B": self.B, "H": self.H,
-                "Sq": self.Sq, "Skv": self.Skv, "head_dim": HEAD_DIM}
+        d = {"workload": self.name, "layout": self.layout, "B": self.B, "H": self.H,
+             "Sq": self.Sq, "Skv": self.Skv, "head_dim": HEAD_DIM}
+        if self.Hkv:
+            d["Hkv"] = self.Hkv
+        if self.causal:
+            d["causal"] = True
+        return d
+
+
+def attended_pairs(Sq: int, Skv: int, causal: bool) -> int:
+    """Number of (query, key) pairs per head: all of them, or under the
+    bottom-right causal mask (query i sees keys j <= i + Skv - Sq)."""
+    if not causal:
+        return Sq * Skv
+    i = np.arange(Sq, dtype=np.int64)
+    return int(np.clip(i + (Skv - Sq) + 1, 0, Skv).sum())
 
 
 WORKLOADS = {
@@ -75,6 +100,11 @@ WORKLOADS = {
                 k_factor=0.5, v_factor=0.5, note="32760 video tokens attend to 512 text tokens"),
     5: Workload(5, "long_self_attn_bhsd_b1_h32_s16384", "bhsd", 1, 32, 16384, 16384,
                 modes=("rtz", "rtne"), note="long sequence"),
+    6: Workload(6, "causal_gqa_bhsd_b1_hq32_hkv8_s16384", "bhsd", 1, 32, 16384, 16384,
+                Hkv=8, causal=True, modes=("rtne",),
+                note="causal grouped-query attention, 4 query heads per key/value head"),
+    7: Workload(7, "causal_self_attn_bshd_b2_h16_s4096", "bshd", 2, 16, 4096, 4096,
+                causal=True, modes=("rtne", "rtz"), note="causal self-attention"),
 }
 
 
@@ -96,11 +126,13 @@ def _draw(shape_, seed: int, factor: float) -> torch.Tensor:
 
 
 def random_qkv(layout: str, B: int, H: int, Sq: int, Skv: int, seed: int,
-               q_factor: float = 1.0, k_factor: float = 1.0, v_factor: float = 1.0):
-    """Return (q, k, v) as bf16 CPU tensors in the given layout."""
+               q_factor: float = 1.0, k_factor: float = 1.0, v_factor: float = 1.0,
+               Hkv: int | None = None):
+    """Return (q, k, v) as bf16 CPU tensors in the given layout; k and v have
+    Hkv heads (default H)."""
     q = _draw(shape(layout, B, H, Sq), 4 * seed + 0, q_factor)
-    k = _draw(shape(layout, B, H, Skv), 4 * seed + 1, k_factor)
-    v = _draw(shape(layout, B, H, Skv), 4 * seed + 2, v_factor)
+    k = _draw(shape(layout, B, Hkv or H, Skv), 4 * seed + 1, k_factor)
+    v = _draw(shape(layout, B, Hkv or H, Skv), 4 * seed + 2, v_factor)
     return q, k, v
 
 
@@ -108,7 +140,8 @@ def make_inputs(w: Workload, *, Sq: int | None = None, Skv: int | None = None,
                 B: int | None = None, H: int | None = None, seed: int | None = None):
     """Draw the workload's q, k, v (bf16 CPU tensors); sizes may be overridden."""
     return random_qkv(w.layout, B or w.B, H or w.H, Sq or w.Sq, Skv or w.Skv,
-                      w.seed if seed is None else seed, w.q_factor, w.k_factor, w.v_factor)
+                      w.seed if seed is None else seed, w.q_factor, w.k_factor, w.v_factor,
+                      Hkv=w.Hkv or None)
 
 
 @dataclass

@@ -62,6 +62,13 @@ def configure(lib):
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int]
+    lib.oracle_attention_gqa.restype = ctypes.c_int
+    lib.oracle_attention_gqa.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int]
     lib.oracle_version.restype = ctypes.c_int
     return lib
 
@@ -96,12 +103,16 @@ class OracleResult:
 
 
 def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = True,
-              l_from_rounded: bool = False, nthreads: int = 0) -> OracleResult:
+              l_from_rounded: bool = False, nthreads: int = 0, causal: bool = False) -> OracleResult:
     """Evaluate the oracle.
 
     q, k, v: uint16 arrays holding bf16 bit patterns, shaped [B,S,H,128]
-    (bshd) or [B,H,S,128] (bhsd).  rows: optional int64 array of flat row ids
-    r = (b*H + h)*Sq + i; None means every row in that order.
+    (bshd) or [B,H,S,128] (bhsd); k and v may have fewer heads than q
+    (grouped-query attention, query head h reads key/value head
+    h // (Hq // Hkv)).  causal: bottom-right aligned causal mask (query i sees
+    keys j <= i + Skv - Sq; rows seeing no key are zero).  rows: optional
+    int64 array of flat row ids r = (b*Hq + h)*Sq + i; None means every row in
+    that order.
     """
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.uint16)
@@ -111,16 +122,14 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
         raise ValueError("q, k, v must be [.., .., .., 128] with k.shape == v.shape")
     if layout == "bshd":
         B, Sq, H, _ = q.shape
-        Skv = k.shape[1]
-        if k.shape[0] != B or k.shape[2] != H:
-            raise ValueError("batch/head mismatch")
+        Skv, Hkv = k.shape[1], k.shape[2]
     elif layout == "bhsd":
         B, H, Sq, _ = q.shape
-        Skv = k.shape[2]
-        if k.shape[0] != B or k.shape[1] != H:
-            raise ValueError("batch/head mismatch")
+        Hkv, Skv = k.shape[1], k.shape[2]
     else:
         raise ValueError(layout)
+    if k.shape[0] != B or Hkv < 1 or H % Hkv != 0:
+        raise ValueError("batch mismatch, or query heads not a multiple of key/value heads")
     if rows is None:
         nrows = B * H * Sq
         rows_arr = None
@@ -135,12 +144,12 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
     sg = np.empty((nrows, 128), np.float64)
     om = np.empty((nrows, 128), np.float64) if method else None
     sm = np.empty((nrows, 128), np.float64) if method else None
-    rc = lib.oracle_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, LAYOUTS[layout],
-                              B, H, Sq, Skv, ctypes.c_float(scale), rows_ptr, nrows,
-                              o.ctypes.data, sg.ctypes.data,
-                              om.ctypes.data if method else None,
-                              sm.ctypes.data if method else None,
-                              1 if l_from_rounded else 0, int(nthreads))
+    rc = lib.oracle_attention_gqa(q.ctypes.data, k.ctypes.data, v.ctypes.data, LAYOUTS[layout],
+                                  B, H, Hkv, Sq, Skv, ctypes.c_float(scale), 1 if causal else 0,
+                                  rows_ptr, nrows, o.ctypes.data, sg.ctypes.data,
+                                  om.ctypes.data if method else None,
+                                  sm.ctypes.data if method else None,
+                                  1 if l_from_rounded else 0, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed ({rc})")
     rows_out = np.arange(nrows, dtype=np.int64) if rows_arr is None else rows_arr

@@ -1,5 +1,5 @@
 /*
- * attn_oracle.c -- plain, slow fp64 CPU reference for non-causal attention.
+ * attn_oracle.c -- plain, slow fp64 CPU reference for attention forward.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The product path
@@ -38,6 +38,17 @@
  *     o_method_d = sum_j pt_j v_{j,d} / L,  L = sum_j 2^(x_j - M)
  * (or L = sum_j pt_j when l_from_rounded is set).  Because M only rescales by
  * an exact power of two, pt_j does not depend on how keys are tiled.
+ *
+ * Two extensions the pages list as limitations of the kernel they describe
+ * (MoonMath article, limitations paragraph: no causal masking, no grouped-
+ * query attention), kept separate from the plain entry point:
+ *   - grouped-query attention: Hq query heads share Hkv key/value heads, query
+ *     head h reading key/value head h / (Hq / Hkv);
+ *   - a causal mask aligned at the bottom-right: query i (of Sq) may attend
+ *     key j (of Skv) iff j <= i + (Skv - Sq), i.e. the queries are the last Sq
+ *     positions of the key sequence.  A row with no admissible key (possible
+ *     only when Sq > Skv) is defined as all zeros, with sigma zero.
+ * Masked keys are left out of the sums; nothing else changes.
  *
  * Rounding of the fp64 result to bf16 is done directly (no fp32 step) and
  * exactly, by locating the value on the bf16 grid; NaN maps to 0x7FC0.
@@ -134,23 +145,27 @@ static double round_trip_bf16_rtne(double x) { return bf16_to_double(oracle_roun
 
 /*
  * Evaluate rows of attention.
- *   q, k, v   : bf16 bit patterns, contiguous, layout as given.
- *   rows      : flat query-row ids r = (b*H + h)*Sq + i, or NULL for all
- *               B*H*Sq rows in that order; nrows is the count.
+ *   q         : bf16 bit patterns [B,Sq,Hq,128] or [B,Hq,Sq,128];
+ *   k, v      : [B,Skv,Hkv,128] or [B,Hkv,Skv,128]; Hq a multiple of Hkv.
+ *   causal    : 0 = every key, 1 = bottom-right aligned causal mask.
+ *   rows      : flat query-row ids r = (b*Hq + h)*Sq + i, or NULL for all
+ *               B*Hq*Sq rows in that order; nrows is the count.
  *   o_exact, sigma            : [nrows, 128] doubles (required).
  *   o_method, sigma_method    : [nrows, 128] doubles, or NULL to skip.
  *   l_from_rounded            : method companion's normaliser (see header).
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                     int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
-                     float scale, const int64_t* rows, int64_t nrows,
-                     double* o_exact, double* sigma,
-                     double* o_method, double* sigma_method,
-                     int l_from_rounded, int nthreads) {
+int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                         float scale, int causal, const int64_t* rows, int64_t nrows,
+                         double* o_exact, double* sigma,
+                         double* o_method, double* sigma_method,
+                         int l_from_rounded, int nthreads) {
     if (!q || !k || !v || !o_exact || !sigma) return -1;
     if (layout != OR_LAYOUT_BSHD && layout != OR_LAYOUT_BHSD) return -1;
-    if (B < 1 || H < 1 || Sq < 1 || Skv < 1) return -1;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return -1;
+    if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return -1;
+    const int64_t H = Hq, group = Hq / Hkv;
     if (rows == NULL) nrows = B * H * Sq;
     if (nrows < 0) return -1;
     const double sc = (double)scale;
@@ -175,14 +190,32 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
             if (!s || !kk) continue;
             int64_t r = rows ? rows[t] : t;
             int64_t i = r % Sq, bh = r / Sq, h = bh % H, b = bh / H;
+            int64_t hk = h / group;                       /* key/value head of query head h */
+            /* admissible keys: j < n_keys (all of them unless causal) */
+            int64_t n_keys = Skv;
+            if (causal) {
+                n_keys = i + (Skv - Sq) + 1;
+                if (n_keys > Skv) n_keys = Skv;
+            }
+            double* oe = o_exact + t * ORACLE_D;
+            double* sg = sigma + t * ORACLE_D;
+            if (n_keys <= 0) {                            /* no admissible key: zeros */
+                for (int d = 0; d < ORACLE_D; d++) {
+                    oe[d] = 0.0;
+                    sg[d] = 0.0;
+                    if (o_method) o_method[t * ORACLE_D + d] = 0.0;
+                    if (o_method && sigma_method) sigma_method[t * ORACLE_D + d] = 0.0;
+                }
+                continue;
+            }
             double qq[ORACLE_D];
             const uint16_t* qp = q + row_offset(layout, b, h, i, H, Sq);
             for (int d = 0; d < ORACLE_D; d++) qq[d] = bf16_to_double(qp[d]);
 
             /* pass 1: scores and their maximum (NaN propagates into m) */
             double m = -INFINITY;
-            for (int64_t j = 0; j < Skv; j++) {
-                const uint16_t* kp = k + row_offset(layout, b, h, j, H, Skv);
+            for (int64_t j = 0; j < n_keys; j++) {
+                const uint16_t* kp = k + row_offset(layout, b, hk, j, Hkv, Skv);
                 for (int d = 0; d < ORACLE_D; d++) kk[d] = bf16_to_double(kp[d]);
                 double acc = 0.0;
                 for (int d = 0; d < ORACLE_D; d++) acc += qq[d] * kk[d];
@@ -196,8 +229,8 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
             double l = 0.0, lm = 0.0, lm_rounded = 0.0;
             double xmax = m * log2e;
             double M = ceil(xmax);
-            for (int64_t j = 0; j < Skv; j++) {
-                const uint16_t* vp = v + row_offset(layout, b, h, j, H, Skv);
+            for (int64_t j = 0; j < n_keys; j++) {
+                const uint16_t* vp = v + row_offset(layout, b, hk, j, Hkv, Skv);
                 double p = exp(s[j] - m);
                 l += p;
                 double pt = 0.0, pm = 0.0;
@@ -217,8 +250,6 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     }
                 }
             }
-            double* oe = o_exact + t * ORACLE_D;
-            double* sg = sigma + t * ORACLE_D;
             for (int d = 0; d < ORACLE_D; d++) {
                 oe[d] = num[d] / l;
                 sg[d] = sqrt(sq[d]) / l;
@@ -237,4 +268,15 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         free(kk);
     }
     return failed ? -1 : 0;
+}
+
+/* The plain operation: every query head has its own key/value head, no mask. */
+int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                     float scale, const int64_t* rows, int64_t nrows,
+                     double* o_exact, double* sigma,
+                     double* o_method, double* sigma_method,
+                     int l_from_rounded, int nthreads) {
+    return oracle_attention_gqa(q, k, v, layout, B, H, H, Sq, Skv, scale, 0, rows, nrows,
+                                o_exact, sigma, o_method, sigma_method, l_from_rounded, nthreads);
 }

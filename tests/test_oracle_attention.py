@@ -248,3 +248,85 @@ def test_method_companion_close_to_exact():
     # bf16 weights carry a relative error of at most 2^-9 each
     assert np.all(np.abs(res.o_method - res.o_exact) <= 2.0 ** -9 * np.sqrt(300) * res.sigma * 1.01 + 1e-300)
     assert not np.array_equal(res.o_method, res.o_exact)
+
+
+# ------------------------------------------- grouped-query heads, causal mask
+# The pages list causal masking and grouped-query attention as limitations of
+# the kernel they describe (MoonMath article, limitations paragraph); the
+# oracle's extension is pinned like the plain operation: a library routine
+# (SDPA in float64 with an explicit boolean mask), decimal brute force on the
+# admissible keys, closed forms, and the identity GQA = MHA on repeated heads.
+def repeat_kv_heads(t: np.ndarray, layout: str, group: int) -> np.ndarray:
+    """Key/value head h -> query heads h*group .. h*group+group-1."""
+    return np.repeat(t, group, axis=2 if layout == "bshd" else 1)
+
+
+def causal_mask(Sq: int, Skv: int) -> torch.Tensor:
+    """Bottom-right aligned: query i sees keys j <= i + Skv - Sq."""
+    return torch.ones(Sq, Skv, dtype=torch.bool).tril(diagonal=Skv - Sq)
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (6, 3), (4, 1)])
+def test_gqa_equals_mha_on_repeated_heads(layout, hq, hkv):
+    q, k, v = wl.random_qkv(layout, 2, hq, 19, 45, 21, k_factor=2.0, Hkv=hkv)
+    qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
+    res = run(qb, kb, vb, layout=layout)
+    ref = run(qb, repeat_kv_heads(kb, layout, hq // hkv), repeat_kv_heads(vb, layout, hq // hkv), layout=layout)
+    assert np.array_equal(res.o_exact, ref.o_exact)
+    assert np.array_equal(res.sigma, ref.sigma)
+
+
+@pytest.mark.parametrize("sq,skv", [(37, 37), (20, 53), (53, 20), (1, 9)])
+def test_causal_matches_torch_sdpa_float64(sq, skv):
+    layout, B, H, hkv = "bhsd", 1, 4, 2
+    q, k, v = wl.random_qkv(layout, B, H, sq, skv, 31, k_factor=2.0, Hkv=hkv)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, causal=True)
+    Q = q.to(torch.float64)
+    K = torch.repeat_interleave(k.to(torch.float64), H // hkv, dim=1).contiguous()
+    V = torch.repeat_interleave(v.to(torch.float64), H // hkv, dim=1).contiguous()
+    mask = causal_mask(sq, skv)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=float(SCALE))
+    ref = ref.reshape(-1, 128).numpy()
+    has_key = np.tile(mask.any(dim=1).numpy(), B * H)
+    assert np.max(np.abs(res.o_exact[has_key] - ref[has_key])) <= 1e-12 * float(V.abs().max())
+    assert np.all(res.o_exact[~has_key] == 0.0) and np.all(res.sigma[~has_key] == 0.0)
+
+
+@pytest.mark.parametrize("sq,skv", [(3, 4), (4, 3), (2, 2)])
+def test_causal_bruteforce_decimal(sq, skv):
+    q, k, v = wl.random_qkv("bhsd", 1, 1, sq, skv, 41, k_factor=2.0)
+    qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
+    res = run(qb, kb, vb, causal=True)
+    Q, K, V = f64(qb)[0, 0], f64(kb)[0, 0], f64(vb)[0, 0]
+    for i in range(sq):
+        n = min(skv, i + skv - sq + 1)
+        if n <= 0:
+            assert np.all(res.o_exact[i] == 0.0)
+            continue
+        o_ref, s_ref = decimal_attention_row(Q[i], K[:n], V[:n], SCALE)
+        scale_o = np.maximum(np.abs(o_ref), s_ref) + 1e-300
+        assert np.all(np.abs(res.o_exact[i] - o_ref) <= 1e-13 * scale_o + 1e-15 * np.abs(V).max())
+        assert np.allclose(res.sigma[i], s_ref, rtol=1e-12, atol=0)
+
+
+def test_causal_first_query_sees_only_first_key():
+    """Sq == Skv: query 0 has one admissible key, so its output is V's row 0
+    exactly, in every rounding mode."""
+    q, k, v = wl.random_qkv("bshd", 1, 2, 40, 40, 43, Hkv=1)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bshd", causal=True)
+    V = f64(wl.bits(v))                       # [1, 40, 1, 128]
+    for h in range(2):
+        assert np.array_equal(res.o_exact[h * 40], V[0, 0, 0])
+        for mode in ("rtne", "rtna", "rtz"):
+            assert np.array_equal(res.rounded(mode)[h * 40], wl.bits(v)[0, 0, 0])
+
+
+def test_causal_last_query_sees_every_key():
+    """The last query row is unmasked: it equals the plain operation's row."""
+    q, k, v = wl.random_qkv("bhsd", 1, 2, 30, 70, 44, k_factor=2.0)
+    qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
+    rows = np.array([29, 59])
+    a = run(qb, kb, vb, causal=True, rows=rows)
+    b = run(qb, kb, vb, causal=False, rows=rows)
+    assert np.array_equal(a.o_exact, b.o_exact)

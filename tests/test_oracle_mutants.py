@@ -31,8 +31,12 @@ MUTANTS = {
     "rtna_tie_down": ("if (fr >= 0.5) m = fl + 1.0;\n    } /* OR_RTZ", "if (fr > 0.5) m = fl + 1.0;\n    } /* OR_RTZ"),
     "rtz_overflow_inf": ("return (mode == OR_RTZ) ? (uint16_t)(sign | 0x7F7F)", "return (mode == OR_RTZ) ? (uint16_t)(sign | 0x7F80)"),
     "subnormal_flush": ("if (e < -126) e = -126;", "if (e < -126) return sign;"),
-    "max_skips_last_key": ("for (int64_t j = 0; j < Skv; j++) {\n                const uint16_t* kp",
-                           "for (int64_t j = 0; j < Skv; j++) {\n                if (j == Skv - 1 && Skv > 1) { s[j] = -INFINITY; continue; }\n                const uint16_t* kp"),
+    "max_skips_last_key": ("for (int64_t j = 0; j < n_keys; j++) {\n                const uint16_t* kp",
+                           "for (int64_t j = 0; j < n_keys; j++) {\n                if (j == n_keys - 1 && n_keys > 1) { s[j] = -INFINITY; continue; }\n                const uint16_t* kp"),
+    "gqa_head_modulo": ("int64_t hk = h / group;", "int64_t hk = h % Hkv;"),
+    "causal_off_by_one": ("n_keys = i + (Skv - Sq) + 1;", "n_keys = i + (Skv - Sq);"),
+    "causal_top_left": ("n_keys = i + (Skv - Sq) + 1;", "n_keys = i + 1;"),
+    "empty_rows_not_zero": ("if (n_keys <= 0) {", "if (n_keys < 0) {"),
 }
 
 
@@ -56,6 +60,11 @@ def pins():
     out.append(("layouts", A.test_layouts_agree_bitwise))
     for lay in ("bhsd", "bshd"):
         out.append((f"nonfinite_{lay}", lambda l=lay: A.test_nonfinite_positions_closed_form(l)))
+    out.append(("gqa_repeat", lambda: A.test_gqa_equals_mha_on_repeated_heads("bshd", 6, 2)))
+    for sq, skv in ((37, 37), (20, 53), (53, 20)):
+        out.append((f"causal_sdpa_{sq}x{skv}", lambda a=sq, b=skv: A.test_causal_matches_torch_sdpa_float64(a, b)))
+    out.append(("causal_brute", lambda: A.test_causal_bruteforce_decimal(4, 3)))
+    out.append(("causal_first_row", A.test_causal_first_query_sees_only_first_key))
     return out
 
 
