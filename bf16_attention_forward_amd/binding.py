@@ -22,7 +22,7 @@ ARGUMENT_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -11}
 HEAD_DIM = 128
 
 # names of every entry point the header declares
-EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -49,6 +49,9 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16.restype = ctypes.c_int
     lib.attn_fwd_bf16_ex.argtypes = args + [ctypes.c_int, ctypes.c_int]
     lib.attn_fwd_bf16_ex.restype = ctypes.c_int
+    lib.attn_fwd_bf16_gqa.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_fwd_bf16_gqa.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -73,7 +76,8 @@ def _raise(status: int):
     raise AttnError(status, msg)
 
 
-def _dims(q: torch.Tensor, k: torch.Tensor, layout: str):
+def _dims(q: torch.Tensor, k: torch.Tensor, layout: str, grouped: bool = False):
+    """(B, Hq, Hkv, Sq, Skv) from the tensor shapes."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be 4-D")
     if layout == "bshd":
@@ -86,9 +90,31 @@ def _dims(q: torch.Tensor, k: torch.Tensor, layout: str):
         raise ValueError(f"layout must be 'bshd' or 'bhsd', got {layout!r}")
     if D != HEAD_DIM or Dk != HEAD_DIM:
         raise ValueError("head dimension must be 128")
-    if (Bk, Hk) != (B, H):
-        raise ValueError("q and k/v must share batch and head counts")
-    return B, H, Sq, Skv
+    if Bk != B:
+        raise ValueError("q and k/v must share the batch count")
+    if grouped:
+        if Hk < 1 or H % Hk != 0:
+            raise ValueError("query heads must be a multiple of key/value heads")
+    elif Hk != H:
+        raise ValueError("q and k/v must share the head count (use attn_fwd_bf16_gqa for grouped heads)")
+    return B, H, Hk, Sq, Skv
+
+
+def _check_tensors(q, k, v, o):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if o is None:
+        return torch.empty_like(q)
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous bfloat16 device tensor shaped like q")
+    return o
 
 
 def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
@@ -104,20 +130,8 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     attn_fwd_bf16_ex (0 = automatic).
     """
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape")
-    B, H, Sq, Skv = _dims(q, k, layout)
-    if o is None:
-        o = torch.empty_like(q)
-    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or not o.is_cuda:
-        raise ValueError("o must be a contiguous bfloat16 device tensor shaped like q")
+    o = _check_tensors(q, k, v, o)
+    B, H, _, Sq, Skv = _dims(q, k, layout)
     if round_mode not in ATTN_ROUND:
         raise ValueError(f"round_mode must be one of {sorted(ATTN_ROUND)}")
     sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
@@ -126,6 +140,31 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
         rc = lib.attn_fwd_bf16_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, ATTN_ROUND[round_mode],
                                   st.cuda_stream, int(kv_splits), int(block_order))
+    if rc != ATTN_OK:
+        _raise(rc)
+    return o
+
+
+def attn_fwd_bf16_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
+                      layout: str = "bshd", scale: float | None = None, causal: bool = False,
+                      round_mode: str = "rtne", stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Grouped-query attention with an optional causal mask (attn_fwd_bf16_gqa).
+
+    k and v may have fewer heads than q (query head h reads key/value head
+    h // (Hq // Hkv)).  causal: query i sees keys j <= i + Skv - Sq; rows that
+    see no key come out as zeros.  Other arguments as attn_fwd_bf16.
+    """
+    lib = load_library()
+    o = _check_tensors(q, k, v, o)
+    B, Hq, Hkv, Sq, Skv = _dims(q, k, layout, grouped=True)
+    if round_mode not in ATTN_ROUND:
+        raise ValueError(f"round_mode must be one of {sorted(ATTN_ROUND)}")
+    sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, sc, 1 if causal else 0,
+                                   ATTN_ROUND[round_mode], st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
     return o

@@ -102,7 +102,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-extern "C" int attn_version(void) { return 10000; }
+extern "C" int attn_version(void) { return 10100; }
 
 extern "C" const char* attn_status_string(int status) {
     switch (status) {
@@ -110,34 +110,38 @@ extern "C" const char* attn_status_string(int status) {
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_LAYOUT: return "layout must be ATTN_LAYOUT_BSHD or ATTN_LAYOUT_BHSD";
         case ATTN_ERR_ROUND_MODE: return "round_mode must be ATTN_ROUND_RTNE, _RTNA or _RTZ";
-        case ATTN_ERR_SHAPE: return "B, H, Sq and Skv must be >= 1 and the sizes must fit the kernel's index range";
+        case ATTN_ERR_SHAPE: return "B, H (Hq, Hkv), Sq and Skv must be >= 1, Hq a multiple of Hkv, and the sizes must fit the kernel's index range";
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned";
         case ATTN_ERR_ALIAS: return "o must not overlap q, k or v";
         case ATTN_ERR_DEVICE: return "the current device is not a gfx950 GPU";
         case ATTN_ERR_WORKSPACE: return "split workspace unavailable (allocation failed or stream is being captured)";
         case ATTN_ERR_LAUNCH: return "kernel launch failed";
-        case ATTN_ERR_OPTION: return "kv_splits or block_order out of range";
+        case ATTN_ERR_OPTION: return "kv_splits, block_order or causal out of range";
         default: return "unknown status";
     }
 }
 
-extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
-                                int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
-                                float scale, int round_mode, void* stream,
-                                int kv_splits, int block_order) {
+namespace {
+
+// Shared by every entry point: H = query heads, Hkv = key/value heads.
+int run_attention(const void* q, const void* k, const void* v, void* o,
+                  int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv,
+                  float scale, int causal, int round_mode, void* stream,
+                  int kv_splits, int block_order) {
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
     if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
         return ATTN_ERR_ROUND_MODE;
-    if (B < 1 || H < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
+    if (B < 1 || H < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
+    if (H % Hkv != 0) return ATTN_ERR_SHAPE;
     // index-range limits of the kernels: 32-bit counts and per-head buffer extents
     const int64_t lim31 = (int64_t)1 << 31;
     if (B >= lim31 || H >= lim31 || Sq >= lim31 || Skv >= lim31) return ATTN_ERR_SHAPE;
     if (B * H >= lim31) return ATTN_ERR_SHAPE;
-    const int64_t n_q = B * H * Sq, n_kv = B * H * Skv;
+    const int64_t n_q = B * H * Sq, n_kv = B * Hkv * Skv;
     if (n_q > ((int64_t)1 << 52) / kHeadDim || n_kv > ((int64_t)1 << 52) / kHeadDim) return ATTN_ERR_SHAPE;
-    const int64_t kv_row = (layout == ATTN_LAYOUT_BSHD) ? H * kHeadDim : kHeadDim;
+    const int64_t kv_row = (layout == ATTN_LAYOUT_BSHD) ? Hkv * kHeadDim : kHeadDim;
     if ((Skv - 1) * kv_row * 2 + kHeadDim * 2 >= lim31) return ATTN_ERR_SHAPE;
     const int64_t n_qtiles = (Sq + KERNEL_BM - 1) / KERNEL_BM;
     if (B * H * n_qtiles * kMaxSplits >= lim31) return ATTN_ERR_SHAPE;
@@ -148,6 +152,8 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
         ranges_overlap(o, q_bytes, v, kv_bytes))
         return ATTN_ERR_ALIAS;
     if (kv_splits < 0 || kv_splits > kMaxSplits || block_order < 0 || block_order > 2) return ATTN_ERR_OPTION;
+    if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
+    if (causal && (kv_splits > 1 || block_order == 2)) return ATTN_ERR_OPTION;
 
     int dev = -1;
     DeviceInfo info;
@@ -162,12 +168,15 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
     p.o = (uint16_t*)o;
     if (layout == ATTN_LAYOUT_BSHD) {
         p.q_row = H * kHeadDim; p.q_head = kHeadDim; p.q_batch = Sq * H * kHeadDim;
-        p.kv_row = H * kHeadDim; p.kv_head = kHeadDim; p.kv_batch = Skv * H * kHeadDim;
+        p.kv_row = Hkv * kHeadDim; p.kv_head = kHeadDim; p.kv_batch = Skv * Hkv * kHeadDim;
     } else {
         p.q_row = kHeadDim; p.q_head = Sq * kHeadDim; p.q_batch = H * Sq * kHeadDim;
-        p.kv_row = kHeadDim; p.kv_head = Skv * kHeadDim; p.kv_batch = H * Skv * kHeadDim;
+        p.kv_row = kHeadDim; p.kv_head = Skv * kHeadDim; p.kv_batch = Hkv * Skv * kHeadDim;
     }
     p.B = (int)B; p.H = (int)H; p.Sq = (int)Sq; p.Skv = (int)Skv;
+    p.group = (int)(H / Hkv);
+    p.causal = causal;
+    p.causal_off = (int)(Skv - Sq);
     p.n_qtiles = (int)n_qtiles;
     p.n_items = (int)(B * H * n_qtiles);
     p.round_mode = round_mode;
@@ -182,7 +191,10 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
     const int n_kv_tiles = (int)((Skv + kKeyTile - 1) / kKeyTile);
     const int slots = info.n_cu;
     int n_full = p.n_items, splits = 1;
-    if (kv_splits > 0) {
+    if (causal) {
+        // Causal items differ in length (the diagonal): they run unsplit,
+        // longest first, in naive block order (the kernel numbers them so).
+    } else if (kv_splits > 0) {
         if (kv_splits > n_kv_tiles) return ATTN_ERR_OPTION;   // every range must hold a key
         splits = kv_splits;
         n_full = (splits == 1) ? p.n_items : 0;
@@ -203,7 +215,7 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
     p.kv_splits = splits;
     p.n_kv_tiles = n_kv_tiles;
     p.n_blocks = n_full + (p.n_items - n_full) * splits;
-    p.block_order = (block_order == 1) ? attn::ORDER_NAIVE : attn::ORDER_XCD;
+    p.block_order = (block_order == 1 || causal) ? attn::ORDER_NAIVE : attn::ORDER_XCD;
 
     if (n_full < p.n_items) {
         const size_t n_part = (size_t)(p.n_items - n_full) * splits;
@@ -217,6 +229,22 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
 
     if (attn::launch(p, (hipStream_t)stream) != 0) return ATTN_ERR_LAUNCH;
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
+                                int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                float scale, int round_mode, void* stream,
+                                int kv_splits, int block_order) {
+    return run_attention(q, k, v, o, layout, B, H, H, Sq, Skv, scale, 0, round_mode, stream,
+                         kv_splits, block_order);
+}
+
+extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o,
+                                 int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                 float scale, int causal, int round_mode, void* stream) {
+    return run_attention(q, k, v, o, layout, B, Hq, Hkv, Sq, Skv, scale, causal, round_mode, stream, 0, 0);
 }
 
 extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,

@@ -27,7 +27,10 @@ struct AttnParams {
     float* ws_ml;      // split partial (M, l) pairs [n_items - n_full][kv_splits][BM][2]
     int64_t q_row, q_head, q_batch;      // element strides of q and o
     int64_t kv_row, kv_head, kv_batch;   // element strides of k and v
-    int B, H, Sq, Skv;
+    int B, H, Sq, Skv;  // H = query heads
+    int group;         // query heads per key/value head (query head h reads key/value head h / group)
+    int causal;        // 1: query i sees keys j <= i + causal_off (items never split, longest first)
+    int causal_off;    // Skv - Sq
     int n_qtiles;      // ceil(Sq / BM)
     int n_items;       // B * H * n_qtiles
     int n_full;        // work items [0, n_full) run unsplit (one block each)

@@ -153,7 +153,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // 8 waves, each owning 32 query rows of the work item; see the file header
 // for the per-tile schedule.
-template <bool CPOS>
+template <bool CPOS, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     constexpr int NTHREADS = NW * 64;
@@ -186,20 +186,54 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         split = tb % p.kv_splits;
         nsplit = p.kv_splits;
     }
-    const int qt = item % p.n_qtiles;
-    const int bh = item / p.n_qtiles;
+    int qt, bh;
+    if (CAUSAL) {
+        // Causal items run longest first: items [0, BH) are the last query
+        // tile of every head, then the second last, ...; the block order is
+        // naive, so the XCD of item i is i mod 8 and each XCD gets an equal
+        // share of every tile length.  Within a tile length, XCD x takes
+        // heads [x*BH/8, (x+1)*BH/8), which share key/value heads under GQA.
+        const int BH = p.B * p.H;
+        const int slot = item % BH;
+        qt = p.n_qtiles - 1 - item / BH;
+        bh = (BH % 8 == 0) ? (slot % 8) * (BH / 8) + slot / 8 : slot;
+    } else {
+        qt = item % p.n_qtiles;
+        bh = item / p.n_qtiles;
+    }
     const int h = bh % p.H;
     const int b = bh / p.H;
+    const int hk = h / p.group;                      // key/value head of query head h
 
     // split s covers key tiles [s*T/ns, (s+1)*T/ns) of the T tiles: never empty for ns <= T
     const int kv_begin = (int)(((int64_t)split * p.n_kv_tiles) / nsplit) * BN;
-    const int kv_end = min(p.Skv, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / nsplit) * BN);
+    int kv_end = min(p.Skv, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / nsplit) * BN);
+    if (CAUSAL) {
+        // keys up to the diagonal of the tile's last row (never split)
+        const int last_row = min(p.Sq, (qt + 1) * BM) - 1;
+        kv_end = min(kv_end, last_row + p.causal_off + 1);
+    }
     const int T = (kv_end - kv_begin + BN - 1) / BN;
 
     const uint16_t* qbase = p.q + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
-    const char* kbase = (const char*)(p.k + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head);
-    const char* vbase = (const char*)(p.v + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head);
+    const char* kbase = (const char*)(p.k + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head);
+    const char* vbase = (const char*)(p.v + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head);
     const int kv_row_bytes = (int)(p.kv_row * 2);
+
+    if (CAUSAL && kv_end <= kv_begin) {
+        // Causal tile entirely above the diagonal (Sq > Skv): no query row of
+        // it sees a key; its rows are zeros.  Uniform across the work-group,
+        // before any barrier or DMA.
+        uint16_t* obase = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
+#pragma unroll
+        for (int qb = 0; qb < NQB; qb++) {
+            const int row = qt * BM + wave * 16 * NQB + qb * 16 + j;
+            if (row >= p.Sq) continue;
+#pragma unroll
+            for (int db = 0; db < 8; db++) *(uint2*)(obase + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
+        }
+        return;
+    }
 
     // ---- K/V buffer resources: reads at or beyond kv_end return zero.
     const uint32_t nrec = (uint32_t)((int64_t)(kv_end - 1) * kv_row_bytes + ROW_BYTES);
@@ -344,29 +378,38 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         const int valid = kv_end - (kv_begin + t * BN);   // keys of this tile inside the range
         bool any_rescale = false;
         float alpha[NQB];
-        // Keys past the range are masked by select, never by arithmetic: key
-        // 16*kb + 4*g + r is inside the range iff 16*kb + r < valid - 4*g.
-        // With c > 0 only a ragged last tile needs it, and one branch covers
-        // both query blocks so the compares stay inside it.
-        const int lim = valid - 4 * g;
-        if (CPOS && valid < BN) {
+        // Keys outside the range are masked by select, never by arithmetic:
+        // key 16*kb + 4*g + r of the tile is inside iff 16*kb + r < lim[qb],
+        // lim = valid - 4*g, and under the causal mask also key <= row + off.
+        // With c > 0 only a ragged last tile or a tile crossing this wave's
+        // diagonal needs it, and one branch covers both query blocks so the
+        // compares stay inside it.
+        const int ts = kv_begin + t * BN;              // first key of the tile
+        const bool diag = CAUSAL && ts + BN - 1 > qrow0 + p.causal_off;
+        int lim[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; qb++) {
+            lim[qb] = valid - 4 * g;
+            if (CAUSAL) lim[qb] = min(lim[qb], qrow0 + qb * 16 + j + p.causal_off - ts + 1 - 4 * g);
+        }
+        if (CPOS && (valid < BN || diag)) {
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++)
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        s_acc[kb][qb][r] = (16 * kb + r < lim) ? s_acc[kb][qb][r] : -__builtin_inff();
+                        s_acc[kb][qb][r] = (16 * kb + r < lim[qb]) ? s_acc[kb][qb][r] : -__builtin_inff();
         }
         if (!CPOS) {
-            // general scale (c <= 0): x = s*c explicitly, keys past the range -> -inf
+            // general scale (c <= 0): x = s*c explicitly, masked keys -> -inf
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++)
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        s_acc[kb][qb][r] = (16 * kb + r < lim) ? s_acc[kb][qb][r] * c : -__builtin_inff();
+                        s_acc[kb][qb][r] = (16 * kb + r < lim[qb]) ? s_acc[kb][qb][r] * c : -__builtin_inff();
         }
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
@@ -475,12 +518,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
             if (row >= p.Sq) continue;
             const float lr = l_row[qb];
             const float inv = 1.0f / lr;
+            // a causal row that sees no key at all (Sq > Skv) is zeros
+            const bool no_key = CAUSAL && row + p.causal_off < 0;
             uint16_t* dst = obase + (int64_t)row * p.q_row + 4 * g;
 #pragma unroll
             for (int db = 0; db < 8; db++) {
                 f32x4 ov;
 #pragma unroll
-                for (int r = 0; r < 4; r++) ov[r] = div_corrected(o_acc[db][qb][r], lr, inv);
+                for (int r = 0; r < 4; r++) ov[r] = no_key ? 0.f : div_corrected(o_acc[db][qb][r], lr, inv);
                 const uint32_t b0 = to_bf16_bits(ov[0], p.round_mode), b1 = to_bf16_bits(ov[1], p.round_mode);
                 const uint32_t b2 = to_bf16_bits(ov[2], p.round_mode), b3 = to_bf16_bits(ov[3], p.round_mode);
                 uint2 packed;
@@ -555,10 +600,19 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
 // ------------------------------------------------------------------ launch
 int launch(const AttnParams& p, hipStream_t stream) {
     dim3 grid(p.n_blocks), block(NW * 64);
-    if (p.c > 0.f)
-        hipLaunchKernelGGL((attn_fwd_main<true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((attn_fwd_main<false>), grid, block, 0, stream, p);
+    // c > 0 (the usual positive scale) and the causal mask are compile-time
+    // variants, so the plain path carries no code for either alternative.
+    if (p.causal) {
+        if (p.c > 0.f)
+            hipLaunchKernelGGL((attn_fwd_main<true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_main<false, true>), grid, block, 0, stream, p);
+    } else {
+        if (p.c > 0.f)
+            hipLaunchKernelGGL((attn_fwd_main<true, false>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_main<false, false>), grid, block, 0, stream, p);
+    }
     if (hipGetLastError() != hipSuccess) return -1;
     if (p.n_full < p.n_items) {
         const int64_t total = (int64_t)(p.n_items - p.n_full) * KERNEL_BM * (D / 4);

@@ -51,14 +51,14 @@ enum {
     ATTN_ERR_NULL = -1,        /* a required pointer is NULL                        */
     ATTN_ERR_LAYOUT = -2,      /* layout is not one of ATTN_LAYOUT_*                */
     ATTN_ERR_ROUND_MODE = -3,  /* round_mode is not one of ATTN_ROUND_*             */
-    ATTN_ERR_SHAPE = -4,       /* B, H, Sq or Skv < 1, or a size overflows          */
+    ATTN_ERR_SHAPE = -4,       /* a size < 1, Hq not a multiple of Hkv, or overflow */
     ATTN_ERR_SCALE = -5,       /* scale is NaN or infinite                          */
     ATTN_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                  */
     ATTN_ERR_ALIAS = -7,       /* o overlaps q, k or v                              */
     ATTN_ERR_DEVICE = -8,      /* current device is not gfx950, or no device        */
     ATTN_ERR_WORKSPACE = -9,   /* split workspace could not be obtained             */
     ATTN_ERR_LAUNCH = -10,     /* the HIP runtime rejected a launch                 */
-    ATTN_ERR_OPTION = -11      /* an option of attn_fwd_bf16_ex is out of range     */
+    ATTN_ERR_OPTION = -11      /* kv_splits, block_order or causal out of range     */
 };
 
 /*
@@ -111,6 +111,31 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
                      int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                      float scale, int round_mode, void* stream,
                      int kv_splits, int block_order);
+
+/*
+ * attn_fwd_bf16_gqa -- attn_fwd_bf16 with grouped-query heads and an optional
+ * causal mask, the two limitations the MoonMath article lists first
+ * (limitations paragraph); the mask alignment is this library's choice.
+ *
+ *   q, o   [B,Sq,Hq,128] or [B,Hq,Sq,128] bf16 (as attn_fwd_bf16)
+ *   k, v   [B,Skv,Hkv,128] or [B,Hkv,Skv,128] bf16
+ *   Hq, Hkv  query and key/value heads (>= 1), Hq a multiple of Hkv; query
+ *            head h reads key/value head h / (Hq / Hkv).  Hq == Hkv is
+ *            plain multi-head attention.
+ *   causal   0: every key; 1: query i sees keys j <= i + (Skv - Sq), i.e.
+ *            the queries are the last Sq positions of the key sequence
+ *            (for Sq == Skv the usual lower-triangular mask).  A query row
+ *            that sees no key (only when Sq > Skv) is written as zeros.
+ *
+ * All other arguments, ownership, asynchrony and error behaviour are those of
+ * attn_fwd_bf16; Hq not a multiple of Hkv gives ATTN_ERR_SHAPE and a causal
+ * value other than 0 or 1 gives ATTN_ERR_OPTION.  Causal calls never split
+ * the key range (no workspace): their work items, of unequal length, run
+ * longest first instead.
+ */
+int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o,
+                      int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                      float scale, int causal, int round_mode, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* attn_status_string(int status);

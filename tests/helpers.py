@@ -30,7 +30,17 @@ def run_hip(q, k, v, layout, mode="rtne", scale=None, **kw) -> np.ndarray:
     return wl.bits(o.cpu())
 
 
-def check(o_bits, q, k, v, layout, mode, *, rows=None, scale=None, label="", oracle_res=None):
+def run_hip_gqa(q, k, v, layout, mode="rtne", causal=False, scale=None) -> np.ndarray:
+    """attn_fwd_bf16_gqa on CPU bf16 tensors (k, v may have fewer heads); output bits."""
+    from bf16_attention_forward_amd import attn_fwd_bf16_gqa
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = attn_fwd_bf16_gqa(qd, kd, vd, layout=layout, round_mode=mode, causal=causal,
+                          scale=wl.DEFAULT_SCALE if scale is None else scale)
+    torch.cuda.synchronize()
+    return wl.bits(o.cpu())
+
+
+def check(o_bits, q, k, v, layout, mode, *, rows=None, scale=None, label="", oracle_res=None, causal=False):
     """Gate the HIP output against the oracle on all rows (rows=None) or a sample."""
     if layout == "bshd":
         B, Sq, H, _ = q.shape
@@ -38,7 +48,7 @@ def check(o_bits, q, k, v, layout, mode, *, rows=None, scale=None, label="", ora
         B, H, Sq, _ = q.shape
     sc = wl.DEFAULT_SCALE if scale is None else scale
     res = oracle_res if oracle_res is not None else oracle.attention(
-        wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=sc, rows=rows, method=False)
+        wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=sc, rows=rows, method=False, causal=causal)
     if rows is None:
         g = wl.gather_rows(o_bits, layout, B, H, Sq, np.arange(B * H * Sq))
     else:
