@@ -27,12 +27,13 @@
 //    LDS-to-register transpose loads); its 4+4 source rows are chosen to match
 //    the keys of P's elements, so V needs no shuffle.
 //  * Online softmax with a power-of-two running offset: x = s * scale *
-//    log2(e), p = 2^(x - M), M an integer that is set to ceil(max x) on the
-//    first tile and moves only when a tile's max exceeds it by more than 8
-//    (so p <= 2^8).  A move rescales O and the row sum by an exact power of
-//    two, and is skipped when no row of the wave moved -- after the first
-//    tiles it almost never happens.  Row maxima and sums are reduced across
-//    the 4 lanes of a row with the gfx950 v_permlane16/32_swap instructions.
+//    log2(e), p = 2^(x - M), M an integer set to ceil(max x) on the first
+//    tile.  Later tiles compute no maximum at all: a weight can exceed 2^16
+//    only if its lane's sum of the tile's weights does, and only then (the
+//    row max moved far past M) is the tile redone with M = ceil(max x) and O
+//    and the row sum rescaled by the exact power of two.  Row maxima and sums
+//    are reduced across the 4 lanes of a row with the gfx950
+//    v_permlane16/32_swap instructions.
 //  * P enters the second product as bf16 rounded to nearest-even
 //    (v_cvt_pk_bf16_f32); the row sum adds those same bf16 weights
 //    (v_dot2c_f32_bf16 against (1, 1)), and the output is divided by it and
@@ -81,7 +82,7 @@ constexpr int NQB = KERNEL_NQB; // 16-row query blocks per wave
 constexpr int BM = KERNEL_BM;   // query rows per work item
 constexpr int ROW_BYTES = D * 2;
 constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
-constexpr float MAX_LAG = 8.0f;             // log2 headroom of the softmax weights
+constexpr float WEIGHT_LIMIT = 65536.0f;    // a lane's tile sum of weights above this triggers a new offset
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -281,9 +282,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     for (int db = 0; db < 8; db++)
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[NQB], l_run[NQB];
+    float moff[NQB], l_run[NQB];    // power-of-two offset of the weights (integer-valued), row-sum partials
 #pragma unroll
-    for (int qb = 0; qb < NQB; qb++) { m_run[qb] = -__builtin_inff(); l_run[qb] = 0.f; }
+    for (int qb = 0; qb < NQB; qb++) { moff[qb] = 0.f; l_run[qb] = 0.f; }
     f32x4 s_acc[4][NQB];
     bf16x8 pf[NQB][2];
     const float c = p.c;
@@ -373,11 +374,55 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     using C16 = std::integral_constant<int, 16>;
     using C32 = std::integral_constant<int, 32>;
 
-    // ---- online softmax of S_t with a power-of-two running max; rescales O and l.
-    auto softmax = [&](int t) {
+    // Weights of query block qb against offset m: p = 2^(x - m) (v_exp_f32),
+    // rounded to bf16 pairs for the P.V product (pf), and this lane's sum of
+    // those bf16 weights -- the row sum adds the same values the product uses,
+    // so O is normalised by exactly its own weights (v_dot2c_f32_bf16 against
+    // (1, 1): one instruction per two weights).
+    auto weights = [&](int qb, float m) -> float {
+        const float negm = -m;
+        f32x4 pv4[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float x = CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm);
+                pv4[kb][r] = __builtin_amdgcn_exp2f(x);
+            }
+        float tsum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            bf16x2 pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const f32x4& src = pv4[2 * ks + (i >> 1)];
+                const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
+                pr[i] = __builtin_convertvector(two, bf16x2);
+                tsum = __builtin_amdgcn_fdot2_f32_bf16(pr[i], ones2, tsum, false);
+            }
+            const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
+            const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
+            pf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        return tsum;
+    };
+    // ceil of the tile's largest x for query block qb (NaN-propagating
+    // v_maximum3_f32 in the lane, then across the 4 lanes of a row)
+    auto tile_max_ceil = [&](int qb) -> float {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
+        mx = rowmax4(mx);
+        if (CPOS) mx *= c;
+        return ceilf(mx);
+    };
+
+    // ---- online softmax of S_t with a power-of-two running offset.
+    auto softmax = [&](int t, auto firstc) {
+        constexpr bool FIRST = decltype(firstc)::value;
         const int valid = kv_end - (kv_begin + t * BN);   // keys of this tile inside the range
-        bool any_rescale = false;
-        float alpha[NQB];
         // Keys outside the range are masked by select, never by arithmetic:
         // key 16*kb + 4*g + r of the tile is inside iff 16*kb + r < lim[qb],
         // lim = valid - 4*g, and under the causal mask also key <= row + off.
@@ -411,63 +456,45 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
                     for (int r = 0; r < 4; r++)
                         s_acc[kb][qb][r] = (16 * kb + r < lim[qb]) ? s_acc[kb][qb][r] * c : -__builtin_inff();
         }
+        if (FIRST) {
+            // first tile: the offset starts at ceil(max x) (0 for a row whose
+            // scores are all -inf or NaN; its weights are then 0 or NaN)
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) {
+                const float m = tile_max_ceil(qb);
+                moff[qb] = __builtin_isfinite(m) ? m : 0.f;
+                l_run[qb] = weights(qb, moff[qb]);
+            }
+            return;
+        }
+        // Later tiles: weights against the running offset, with no max.  A
+        // weight can exceed 2^16 only if its lane's tile sum does; then (rare:
+        // the row max moved far past the offset) the tile is redone with the
+        // offset at ceil(max) and O and l rescaled by the exact power of two.
+        float tsum[NQB];
+        bool big = false;
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
-            // NaN-propagating maximum (v_maximum3_f32): a NaN score makes the
-            // row's max NaN, as its weights and output are NaN anyway.
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
-            mx = rowmax4(mx);
-            if (CPOS) mx *= c;
-            // Lazy rescale: the running offset M only moves when the tile's
-            // max exceeds it by more than MAX_LAG (then to ceil(max)), so
-            // weights stay <= 2^MAX_LAG and the O / l rescale is rare.  A
-            // NaN max leaves M as is; the NaN weights make the row NaN.
-            const float tmax = ceilf(mx);
-            const float m_new = (tmax > m_run[qb] + MAX_LAG) ? tmax : m_run[qb];
-            const float dm = m_run[qb] - m_new;     // <= 0, integer-valued, or -inf / NaN
-            alpha[qb] = ldexpf(1.0f, (int)fmaxf(dm, -200.f));
-            any_rescale |= (dm != 0.f);
-            m_run[qb] = m_new;
-            const float negm = -m_new;
-            f32x4 pv4[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float x = CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm);
-                    pv4[kb][r] = __builtin_amdgcn_exp2f(x);
-                }
-            // The row sum adds the bf16-rounded weights, the same values the
-            // P V product uses, so O is normalised by exactly its own weights.
-            // (pairs are converted one register at a time and summed with
-            // v_dot2c_f32_bf16 against (1, 1): one instruction per two weights)
-            float psum = l_run[qb] * alpha[qb];
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                bf16x2 pr[4];
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const f32x4& src = pv4[2 * ks + (i >> 1)];
-                    const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
-                    pr[i] = __builtin_convertvector(two, bf16x2);
-                    psum = __builtin_amdgcn_fdot2_f32_bf16(pr[i], ones2, psum, false);
-                }
-                const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
-                const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
-                pf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-            l_run[qb] = psum;
+            tsum[qb] = weights(qb, moff[qb]);
+            big |= tsum[qb] > WEIGHT_LIMIT;
         }
-        if (__builtin_amdgcn_ballot_w64(any_rescale) != 0) {
+        if (__builtin_amdgcn_ballot_w64(big) != 0) {
+            float alpha[NQB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) {
+                const float m_new = fmaxf(moff[qb], tile_max_ceil(qb));   // a NaN max keeps the offset
+                alpha[qb] = ldexpf(1.0f, (int)fmaxf(moff[qb] - m_new, -200.f));
+                moff[qb] = m_new;
+                tsum[qb] = weights(qb, m_new);
+                l_run[qb] *= alpha[qb];
+            }
 #pragma unroll
             for (int db = 0; db < 8; db++)
 #pragma unroll
                 for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] *= alpha[qb];
         }
+#pragma unroll
+        for (int qb = 0; qb < NQB; qb++) l_run[qb] += tsum[qb];
     };
 
     // ---- key loop: one barrier per tile.  Iteration t issues the DMA of K_{t+1}
@@ -488,7 +515,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         __builtin_amdgcn_s_setprio(1);
         mfma_phase(kc, vp, s0c, s1c);
         __builtin_amdgcn_s_setprio(0);
-        if (decltype(s0c)::value == 0) softmax(t);
+        if (decltype(s0c)::value == 0)
+            softmax(t, std::integral_constant<bool, decltype(s1c)::value == 16>{});
         __builtin_amdgcn_s_waitcnt(0x0f70);
         lds_barrier();
     };
@@ -546,7 +574,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 #pragma unroll
             for (int db = 0; db < 8; db++) *(f32x4*)(ow + (int64_t)lrow * D + 16 * db + 4 * g) = o_acc[db][qb];
             if (g == 0) {
-                mw[2 * lrow] = m_run[qb];
+                mw[2 * lrow] = moff[qb];
                 mw[2 * lrow + 1] = l_row[qb];
             }
         }

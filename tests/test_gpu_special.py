@@ -117,3 +117,38 @@ def test_device_side_argument_errors():
     torch.cuda.synchronize()
     # forced split larger than the number of key tiles is rejected
     assert attn_fwd_bf16_raw(*args(q.data_ptr(), o.data_ptr()), kv_splits=2) == -11
+
+
+def ramp_inputs(layout, B, H, Sq, Skv, seed, t_max=470.0):
+    """Scores that grow along the keys (for queries with a positive component
+    along a shared direction, shrink for the others): later key tiles keep
+    outgrowing the softmax offset, which exercises the offset moves."""
+    q, _, v = wl.random_qkv(layout, B, H, Sq, Skv, seed)
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(128, generator=g)
+    u = u / u.norm()
+    t = torch.linspace(0.0, t_max, Skv)
+    noise = torch.randn(B, Skv, H, 128, generator=g)
+    k = t[None, :, None, None] * u + noise
+    if layout == "bhsd":
+        k = k.permute(0, 2, 1, 3)
+    return q, k.contiguous().to(torch.bfloat16), v
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_growing_scores_move_the_offset(layout, splits):
+    q, k, v = ramp_inputs(layout, 1, 2, 300, 1000, 71)
+    say(f"[case] growing scores {layout} splits={splits}")
+    for mode in MODES:
+        o = run_hip(q, k, v, layout, mode, kv_splits=splits)
+        st, _ = check(o, q, k, v, layout, mode, label=f"ramp {layout} {splits}")
+        assert st["nonfinite_match"] and st["max_D"] <= 2.0 and st["frac_D_gt1"] <= 1e-3, st
+
+
+def test_growing_scores_causal():
+    from tests.helpers import run_hip_gqa
+    q, k, v = ramp_inputs("bhsd", 1, 2, 700, 700, 72)
+    o = run_hip_gqa(q, k, v, "bhsd", "rtne", causal=True)
+    st, _ = check(o, q, k, v, "bhsd", "rtne", label="ramp causal", causal=True)
+    assert st["nonfinite_match"] and st["max_D"] <= 2.0 and st["frac_D_gt1"] <= 1e-3, st
