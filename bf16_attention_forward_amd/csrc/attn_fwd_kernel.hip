@@ -31,9 +31,11 @@
 //    tile.  Later tiles compute no maximum at all: a weight can exceed 2^16
 //    only if its lane's sum of the tile's weights does, and only then (the
 //    row max moved far past M) is the tile redone with M = ceil(max x) and O
-//    and the row sum rescaled by the exact power of two.  Row maxima and sums
-//    are reduced across the 4 lanes of a row with the gfx950
-//    v_permlane16/32_swap instructions.
+//    and the row sum rescaled by the exact power of two.  With a positive
+//    scale the score MFMAs start from -M/c instead of zero, so the exponent
+//    x - M is one multiply by c (which co-issues) rather than a multiply-add.
+//    Row maxima and sums are reduced across the 4 lanes of a row with the
+//    gfx950 v_permlane16/32_swap instructions.
 //  * P enters the second product as bf16 rounded to nearest-even
 //    (v_cvt_pk_bf16_f32); the row sum adds those same bf16 weights
 //    (v_dot2c_f32_bf16 against (1, 1)), and the output is divided by it and
@@ -283,8 +285,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float moff[NQB], l_run[NQB];    // power-of-two offset of the weights (integer-valued), row-sum partials
+    f32x4 bias4[NQB];               // c > 0: S^T accumulates from -moff/c, so c * S^T = x - moff
 #pragma unroll
-    for (int qb = 0; qb < NQB; qb++) { moff[qb] = 0.f; l_run[qb] = 0.f; }
+    for (int qb = 0; qb < NQB; qb++) { moff[qb] = 0.f; l_run[qb] = 0.f; bias4[qb] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    const float rc = 1.0f / p.c;
     f32x4 s_acc[4][NQB];
     bf16x8 pf[NQB][2];
     const float c = p.c;
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
             const int kb = st & 3, ks = st >> 2;
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++)
-                s_acc[kb][qb] = mfma16x16x32(f, qf[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s_acc[kb][qb]);
+                s_acc[kb][qb] = mfma16x16x32(f, qf[qb][ks], ks == 0 ? (CPOS ? bias4[qb] : f32x4{0.f, 0.f, 0.f, 0.f}) : s_acc[kb][qb]);
         } else {
             const int db = (st - 16) & 7, ks = (st - 16) >> 3;
 #pragma unroll
@@ -379,14 +383,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     // those bf16 weights -- the row sum adds the same values the product uses,
     // so O is normalised by exactly its own weights (v_dot2c_f32_bf16 against
     // (1, 1): one instruction per two weights).
-    auto weights = [&](int qb, float m) -> float {
+    auto weights = [&](int qb, float m, auto biasc) -> float {
+        constexpr bool BIASED = decltype(biasc)::value;   // S^T already holds s - moff/c: exponent = c * S^T
         const float negm = -m;
         f32x4 pv4[4];
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float x = CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm);
+                const float x = BIASED ? s_acc[kb][qb][r] * c
+                                       : (CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm));
                 pv4[kb][r] = __builtin_amdgcn_exp2f(x);
             }
         float tsum = 0.f;
@@ -417,6 +423,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         mx = rowmax4(mx);
         if (CPOS) mx *= c;
         return ceilf(mx);
+    };
+    auto set_bias = [&](int qb) {
+        if (CPOS) {
+            const float bb = -moff[qb] * rc;
+            bias4[qb] = f32x4{bb, bb, bb, bb};
+        }
     };
 
     // ---- online softmax of S_t with a power-of-two running offset.
@@ -463,7 +475,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
             for (int qb = 0; qb < NQB; qb++) {
                 const float m = tile_max_ceil(qb);
                 moff[qb] = __builtin_isfinite(m) ? m : 0.f;
-                l_run[qb] = weights(qb, moff[qb]);
+                l_run[qb] = weights(qb, moff[qb], std::false_type{});
+                set_bias(qb);
             }
             return;
         }
@@ -475,17 +488,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
         bool big = false;
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
-            tsum[qb] = weights(qb, moff[qb]);
+            tsum[qb] = weights(qb, moff[qb], std::integral_constant<bool, CPOS>{});
             big |= tsum[qb] > WEIGHT_LIMIT;
         }
         if (__builtin_amdgcn_ballot_w64(big) != 0) {
             float alpha[NQB];
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) {
-                const float m_new = fmaxf(moff[qb], tile_max_ceil(qb));   // a NaN max keeps the offset
+                // with c > 0 the scores hold s - moff/c: x = c * S^T + moff
+                const float m_new = fmaxf(moff[qb], tile_max_ceil(qb) + (CPOS ? moff[qb] : 0.f));
                 alpha[qb] = ldexpf(1.0f, (int)fmaxf(moff[qb] - m_new, -200.f));
+                tsum[qb] = weights(qb, CPOS ? m_new - moff[qb] : m_new, std::false_type{});
                 moff[qb] = m_new;
-                tsum[qb] = weights(qb, m_new);
+                set_bias(qb);
                 l_run[qb] *= alpha[qb];
             }
 #pragma unroll
