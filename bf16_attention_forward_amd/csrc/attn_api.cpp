@@ -189,7 +189,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o,
     // tail split); when there is less than one round of items, every item is
     // split.  A forced kv_splits = n splits every item n ways.
     const int n_kv_tiles = (int)((Skv + kKeyTile - 1) / kKeyTile);
-    const int slots = info.n_cu;
+    const int slots = info.n_cu * KERNEL_WG_PER_CU;
     int n_full = p.n_items, splits = 1;
     if (causal) {
         // Causal items differ in length (the diagonal): they run unsplit,

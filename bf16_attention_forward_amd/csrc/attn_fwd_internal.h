@@ -12,6 +12,9 @@
 #define KERNEL_NW 8
 #endif
 #define KERNEL_BM (KERNEL_NW * 16 * KERNEL_NQB)
+// work-groups resident per CU: two waves per SIMD in total (the register
+// budget of a wave is then 256 VGPRs)
+#define KERNEL_WG_PER_CU (8 / KERNEL_NW)
 
 namespace attn {
 

@@ -157,7 +157,7 @@ __device__ __forceinline__ void lds_barrier() {
 // 8 waves, each owning 32 query rows of the work item; see the file header
 // for the per-tile schedule.
 template <bool CPOS, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     constexpr int NTHREADS = NW * 64;
     constexpr int DMA_PER_TILE = TILE_BYTES / 16 / NTHREADS;   // 16-byte chunks per lane per tile
@@ -246,7 +246,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
     // Per-lane DMA source offsets (relative to the tile's first row).  Slot
     // (i*NW + wave)*64 + lane of a tile is row (i*NW + wave)*4 + g, chunk j; rows
     // 32 apart share the swizzle, so one per-lane offset serves every i.
-    static_assert(NW * 4 == 32, "DMA rows per instruction round must be 32");
+    constexpr int RPR = NW * 4;   // rows per DMA instruction round (64 lanes x 16 B = 4 rows per wave)
+    static_assert(RPR % 16 == 0, "rows of one DMA round must repeat the 16-row swizzle period");
     const int dma_row = wave * 4 + g;
     const int dma_off_k = dma_row * kv_row_bytes + ((j ^ swz_k(dma_row)) << 4);
     const int dma_off_v = dma_row * kv_row_bytes + ((j ^ swz_v(dma_row)) << 4);
@@ -255,14 +256,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_main(const AttnParams p) 
 #pragma unroll
         for (int i = 0; i < DMA_PER_TILE; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
-                                                     dma_off_k, soff + i * 32 * kv_row_bytes, 0, 0);
+                                                     dma_off_k, soff + i * RPR * kv_row_bytes, 0, 0);
     };
     auto issue_v = [&](int t, uint8_t* dst) {
         const int soff = (kv_begin + t * BN) * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < DMA_PER_TILE; i++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
-                                                     dma_off_v, soff + i * 32 * kv_row_bytes, 0, 0);
+                                                     dma_off_v, soff + i * RPR * kv_row_bytes, 0, 0);
     };
 
     issue_k(0, sk0);
