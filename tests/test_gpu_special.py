@@ -152,3 +152,32 @@ def test_growing_scores_causal():
     o = run_hip_gqa(q, k, v, "bhsd", "rtne", causal=True)
     st, _ = check(o, q, k, v, "bhsd", "rtne", label="ramp causal", causal=True)
     assert st["nonfinite_match"] and st["max_D"] <= 2.0 and st["frac_D_gt1"] <= 1e-3, st
+
+
+def test_graph_capture_replays_match_eager():
+    """A launch captured into a HIP graph (torch.cuda.graph) replays to the
+    eager result, replay after replay, with eager work in between; the split
+    path's workspace is allocated before capture by the eager warm-up call."""
+    q, k, v = wl.random_qkv("bhsd", 1, 4, 700, 900, 81)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for splits in (0, 3):
+        eager = attn_fwd_bf16(qd, kd, vd, layout="bhsd", kv_splits=splits)
+        torch.cuda.synchronize()
+        ref = eager.clone()
+        out = torch.empty_like(qd)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            attn_fwd_bf16(qd, kd, vd, out, layout="bhsd", kv_splits=splits, stream=s)   # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            attn_fwd_bf16(qd, kd, vd, out, layout="bhsd", kv_splits=splits, stream=s)
+        for rep in range(4):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"splits={splits} replay {rep}"
+            attn_fwd_bf16(qd, kd, vd, layout="bhsd")   # eager work between replays
+            torch.cuda.synchronize()
