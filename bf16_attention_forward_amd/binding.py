@@ -49,7 +49,7 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16.restype = ctypes.c_int
     lib.attn_fwd_bf16_ex.argtypes = args + [ctypes.c_int, ctypes.c_int]
     lib.attn_fwd_bf16_ex.restype = ctypes.c_int
-    lib.attn_fwd_bf16_gqa.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
+    lib.attn_fwd_bf16_gqa.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_bf16_gqa.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -147,27 +147,36 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
 
 def attn_fwd_bf16_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
                       layout: str = "bshd", scale: float | None = None, causal: bool = False,
-                      round_mode: str = "rtne", stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+                      round_mode: str = "rtne", stream: torch.cuda.Stream | None = None,
+                      lse: torch.Tensor | None = None, return_lse: bool = False):
     """Grouped-query attention with an optional causal mask (attn_fwd_bf16_gqa).
 
     k and v may have fewer heads than q (query head h reads key/value head
     h // (Hq // Hkv)).  causal: query i sees keys j <= i + Skv - Sq; rows that
-    see no key come out as zeros.  Other arguments as attn_fwd_bf16.
+    see no key come out as zeros.  lse (float32 [B, Hq, Sq], or allocated when
+    return_lse) receives each row's log-sum-exp of its scaled scores; then
+    (o, lse) is returned.  Other arguments as attn_fwd_bf16.
     """
     lib = load_library()
     o = _check_tensors(q, k, v, o)
     B, Hq, Hkv, Sq, Skv = _dims(q, k, layout, grouped=True)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq)
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 device tensor shaped [B, Hq, Sq]")
     if round_mode not in ATTN_ROUND:
         raise ValueError(f"round_mode must be one of {sorted(ATTN_ROUND)}")
     sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
         rc = lib.attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None,
                                    ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, sc, 1 if causal else 0,
                                    ATTN_ROUND[round_mode], st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
-    return o
+    return (o, lse) if lse is not None else o
 
 
 def attn_fwd_bf16_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, layout: int, B: int, H: int,

@@ -125,7 +125,7 @@ extern "C" const char* attn_status_string(int status) {
 namespace {
 
 // Shared by every entry point: H = query heads, Hkv = key/value heads.
-int run_attention(const void* q, const void* k, const void* v, void* o,
+int run_attention(const void* q, const void* k, const void* v, void* o, float* lse,
                   int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv,
                   float scale, int causal, int round_mode, void* stream,
                   int kv_splits, int block_order) {
@@ -151,6 +151,13 @@ int run_attention(const void* q, const void* k, const void* v, void* o,
     if (ranges_overlap(o, q_bytes, q, q_bytes) || ranges_overlap(o, q_bytes, k, kv_bytes) ||
         ranges_overlap(o, q_bytes, v, kv_bytes))
         return ATTN_ERR_ALIAS;
+    if (lse) {
+        if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+        const size_t lse_bytes = (size_t)n_q * sizeof(float);
+        if (ranges_overlap(lse, lse_bytes, q, q_bytes) || ranges_overlap(lse, lse_bytes, k, kv_bytes) ||
+            ranges_overlap(lse, lse_bytes, v, kv_bytes) || ranges_overlap(lse, lse_bytes, o, q_bytes))
+            return ATTN_ERR_ALIAS;
+    }
     if (kv_splits < 0 || kv_splits > kMaxSplits || block_order < 0 || block_order > 2) return ATTN_ERR_OPTION;
     if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
     if (causal && (kv_splits > 1 || block_order == 2)) return ATTN_ERR_OPTION;
@@ -166,6 +173,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o,
     p.k = (const uint16_t*)k;
     p.v = (const uint16_t*)v;
     p.o = (uint16_t*)o;
+    p.lse = lse;
     if (layout == ATTN_LAYOUT_BSHD) {
         p.q_row = H * kHeadDim; p.q_head = kHeadDim; p.q_batch = Sq * H * kHeadDim;
         p.kv_row = Hkv * kHeadDim; p.kv_head = kHeadDim; p.kv_batch = Skv * Hkv * kHeadDim;
@@ -237,14 +245,14 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
                                 int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                                 float scale, int round_mode, void* stream,
                                 int kv_splits, int block_order) {
-    return run_attention(q, k, v, o, layout, B, H, H, Sq, Skv, scale, 0, round_mode, stream,
+    return run_attention(q, k, v, o, nullptr, layout, B, H, H, Sq, Skv, scale, 0, round_mode, stream,
                          kv_splits, block_order);
 }
 
-extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o,
+extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                  float scale, int causal, int round_mode, void* stream) {
-    return run_attention(q, k, v, o, layout, B, Hq, Hkv, Sq, Skv, scale, causal, round_mode, stream, 0, 0);
+    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, scale, causal, round_mode, stream, 0, 0);
 }
 
 extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,

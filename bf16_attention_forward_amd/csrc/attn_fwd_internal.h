@@ -26,6 +26,7 @@ struct AttnParams {
     const uint16_t* k;
     const uint16_t* v;
     uint16_t* o;
+    float* lse;        // optional [B][H][Sq] natural-log log-sum-exp per query row (NULL: not written)
     float* ws_o;       // split partial outputs [n_items - n_full][kv_splits][BM][128] (fp32)
     float* ws_ml;      // split partial (M, l) pairs [n_items - n_full][kv_splits][BM][2]
     int64_t q_row, q_head, q_batch;      // element strides of q and o

@@ -84,6 +84,7 @@ constexpr int NQB = KERNEL_NQB; // 16-row query blocks per wave
 constexpr int BM = KERNEL_BM;   // query rows per work item
 constexpr int ROW_BYTES = D * 2;
 constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
+constexpr float LN2 = 0.693147180559945309f;
 constexpr float WEIGHT_LIMIT = 65536.0f;    // a lane's tile sum of weights above this triggers a new offset
 
 // ---------------------------------------------------------------- helpers
@@ -555,6 +556,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     for (int qb = 0; qb < NQB; qb++) l_row[qb] = rowsum4(l_run[qb]);
 
     if (nsplit == 1) {
+        if (p.lse && g == 0) {
+            // log-sum-exp of the row's scaled scores: sum_j 2^x_j = l * 2^moff
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) {
+                const int row = qrow0 + qb * 16 + j;
+                if (row >= p.Sq) continue;
+                float v = (moff[qb] + __builtin_amdgcn_logf(l_row[qb])) * LN2;
+                if (CAUSAL && row + p.causal_off < 0) v = -__builtin_inff();   // sees no key
+                p.lse[((int64_t)b * p.H + h) * p.Sq + row] = v;
+            }
+        }
         uint16_t* obase = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
@@ -631,6 +643,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
         acc += os * wgt;
         l += ls * wgt;
     }
+    if (p.lse && d4 == 0) p.lse[((int64_t)b * p.H + h) * p.Sq + row] = (M + __builtin_amdgcn_logf(l)) * LN2;
     const float inv = 1.0f / l;
     f32x4 ov;
     for (int r = 0; r < 4; r++) ov[r] = div_corrected(acc[r], l, inv);

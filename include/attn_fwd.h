@@ -126,14 +126,24 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
  *            the queries are the last Sq positions of the key sequence
  *            (for Sq == Skv the usual lower-triangular mask).  A query row
  *            that sees no key (only when Sq > Skv) is written as zeros.
+ *   lse      NULL, or fp32 [B, Hq, Sq] (this order in both layouts), device
+ *            memory, 4-byte aligned, not overlapping q/k/v/o: receives each
+ *            row's natural-log log-sum-exp of its scaled scores,
+ *            log(sum_j exp(scale * <q_i, k_j>)) over the keys it sees
+ *            (-inf for a row that sees none) -- the softmax statistic a
+ *            backward pass needs, and the intermediate the FlyDSL procedure
+ *            article (debugging advice) compares against a reference.  It is
+ *            computed from the bf16-rounded weights the product uses, so it
+ *            differs from the exact value by about their rounding (< 2^-8).
  *
  * All other arguments, ownership, asynchrony and error behaviour are those of
- * attn_fwd_bf16; Hq not a multiple of Hkv gives ATTN_ERR_SHAPE and a causal
- * value other than 0 or 1 gives ATTN_ERR_OPTION.  Causal calls never split
+ * attn_fwd_bf16; Hq not a multiple of Hkv gives ATTN_ERR_SHAPE, a causal
+ * value other than 0 or 1 gives ATTN_ERR_OPTION, a misaligned lse
+ * ATTN_ERR_ALIGN and an lse overlapping q, k, v or o ATTN_ERR_ALIAS.  Causal calls never split
  * the key range (no workspace): their work items, of unequal length, run
  * longest first instead.
  */
-int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o,
+int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                       int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                       float scale, int causal, int round_mode, void* stream);
 

@@ -67,7 +67,7 @@ def configure(lib):
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int]
     lib.oracle_version.restype = ctypes.c_int
     return lib
@@ -91,12 +91,13 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
 class OracleResult:
     """Per-row outputs of the oracle, each shaped [nrows, 128] (float64)."""
 
-    def __init__(self, rows, o_exact, sigma, o_method, sigma_method):
+    def __init__(self, rows, o_exact, sigma, o_method, sigma_method, lse=None):
         self.rows = rows
         self.o_exact = o_exact
         self.sigma = sigma
         self.o_method = o_method
         self.sigma_method = sigma_method
+        self.lse = lse          # [nrows] natural-log log-sum-exp of the scaled scores
 
     def rounded(self, mode: str) -> np.ndarray:
         return round_bf16(self.o_exact, mode)
@@ -144,13 +145,14 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
     sg = np.empty((nrows, 128), np.float64)
     om = np.empty((nrows, 128), np.float64) if method else None
     sm = np.empty((nrows, 128), np.float64) if method else None
+    ls = np.empty(nrows, np.float64)
     rc = lib.oracle_attention_gqa(q.ctypes.data, k.ctypes.data, v.ctypes.data, LAYOUTS[layout],
                                   B, H, Hkv, Sq, Skv, ctypes.c_float(scale), 1 if causal else 0,
                                   rows_ptr, nrows, o.ctypes.data, sg.ctypes.data,
                                   om.ctypes.data if method else None,
-                                  sm.ctypes.data if method else None,
+                                  sm.ctypes.data if method else None, ls.ctypes.data,
                                   1 if l_from_rounded else 0, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed ({rc})")
     rows_out = np.arange(nrows, dtype=np.int64) if rows_arr is None else rows_arr
-    return OracleResult(rows_out, o, sg, om, sm)
+    return OracleResult(rows_out, o, sg, om, sm, ls)

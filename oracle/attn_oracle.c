@@ -50,6 +50,12 @@
  *     only when Sq > Skv) is defined as all zeros, with sigma zero.
  * Masked keys are left out of the sums; nothing else changes.
  *
+ * Optionally the row's log-sum-exp of the scaled scores is returned as well,
+ * lse = m + log(sum_j exp(s_j - m)) over the admissible keys (natural log;
+ * -inf for a row with no admissible key): the intermediate the FlyDSL
+ * procedure article (debugging advice) suggests comparing against a
+ * reference, and the side output a backward pass consumes.
+ *
  * Rounding of the fp64 result to bf16 is done directly (no fp32 step) and
  * exactly, by locating the value on the bf16 grid; NaN maps to 0x7FC0.
  *
@@ -152,6 +158,7 @@ static double round_trip_bf16_rtne(double x) { return bf16_to_double(oracle_roun
  *               B*Hq*Sq rows in that order; nrows is the count.
  *   o_exact, sigma            : [nrows, 128] doubles (required).
  *   o_method, sigma_method    : [nrows, 128] doubles, or NULL to skip.
+ *   lse                       : [nrows] doubles, or NULL to skip.
  *   l_from_rounded            : method companion's normaliser (see header).
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
@@ -159,7 +166,7 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                          float scale, int causal, const int64_t* rows, int64_t nrows,
                          double* o_exact, double* sigma,
-                         double* o_method, double* sigma_method,
+                         double* o_method, double* sigma_method, double* lse,
                          int l_from_rounded, int nthreads) {
     if (!q || !k || !v || !o_exact || !sigma) return -1;
     if (layout != OR_LAYOUT_BSHD && layout != OR_LAYOUT_BHSD) return -1;
@@ -200,6 +207,7 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
             double* oe = o_exact + t * ORACLE_D;
             double* sg = sigma + t * ORACLE_D;
             if (n_keys <= 0) {                            /* no admissible key: zeros */
+                if (lse) lse[t] = -INFINITY;
                 for (int d = 0; d < ORACLE_D; d++) {
                     oe[d] = 0.0;
                     sg[d] = 0.0;
@@ -254,6 +262,7 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
                 oe[d] = num[d] / l;
                 sg[d] = sqrt(sq[d]) / l;
             }
+            if (lse) lse[t] = m + log(l);
             if (o_method) {
                 double L = l_from_rounded ? lm_rounded : lm;
                 double* om = o_method + t * ORACLE_D;
@@ -278,5 +287,5 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      double* o_method, double* sigma_method,
                      int l_from_rounded, int nthreads) {
     return oracle_attention_gqa(q, k, v, layout, B, H, H, Sq, Skv, scale, 0, rows, nrows,
-                                o_exact, sigma, o_method, sigma_method, l_from_rounded, nthreads);
+                                o_exact, sigma, o_method, sigma_method, NULL, l_from_rounded, nthreads);
 }

@@ -71,17 +71,18 @@ def test_valid_arguments_reach_device_check():
 
 
 def call_gqa(**kw):
-    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), layout=1, B=1, Hq=8, Hkv=2,
-             Sq=64, Skv=64, scale=0.088, causal=1, mode=0, stream=0)
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), lse=None, layout=1, B=1, Hq=8,
+             Hkv=2, Sq=64, Skv=64, scale=0.088, causal=1, mode=0, stream=0)
     a.update(kw)
-    return load_library().attn_fwd_bf16_gqa(a["q"], a["k"], a["v"], a["o"], a["layout"], a["B"], a["Hq"], a["Hkv"],
-                                            a["Sq"], a["Skv"], a["scale"], a["causal"], a["mode"], a["stream"])
+    return load_library().attn_fwd_bf16_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["layout"], a["B"], a["Hq"],
+                                            a["Hkv"], a["Sq"], a["Skv"], a["scale"], a["causal"], a["mode"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(k=0), -1), (dict(layout=5), -2), (dict(mode=-1), -3), (dict(Hkv=0), -4), (dict(Hkv=3), -4),
     (dict(Hq=2, Hkv=4), -4), (dict(scale=-math.inf), -5), (dict(v=FAKE + (2 << 30) + 4), -6),
     (dict(o=FAKE + (2 << 30) + 64 * 2 * 128 * 2 - 16), -7), (dict(causal=2), -11), (dict(causal=-1), -11),
+    (dict(lse=FAKE + (4 << 30) + 2), -6), (dict(lse=FAKE + (3 << 30) + 64), -7), (dict(lse=FAKE + 4), -7),
 ])
 def test_gqa_argument_errors_before_device(kw, code):
     assert call_gqa(**kw) == code
@@ -93,3 +94,4 @@ def test_gqa_valid_arguments_reach_device_check():
         pytest.skip("a GPU is present")
     assert call_gqa() == -8
     assert call_gqa(causal=0, Hkv=8) == -8
+    assert call_gqa(lse=FAKE + (4 << 30)) == -8

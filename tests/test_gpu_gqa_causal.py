@@ -92,3 +92,39 @@ def test_full_size_causal_workloads_sampled(number):
         o = run_hip_gqa(q, k, v, w.layout, mode, causal=w.causal)
         st, res = check(o, q, k, v, w.layout, mode, rows=rows, label=w.name, oracle_res=res, causal=w.causal)
         assert_gate(st)
+
+
+LSE_CASES = [
+    # layout, B, Hq, Hkv, Sq, Skv, causal
+    ("bhsd", 1, 4, 2, 300, 300, True),
+    ("bshd", 1, 2, 1, 333, 130, True),     # leading rows see no key: -inf
+    ("bhsd", 1, 2, 2, 300, 1000, False),   # few work items: the planner splits the keys
+    ("bshd", 2, 8, 2, 257, 513, False),
+]
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=lambda c: f"{c[0]}_Hq{c[2]}Hkv{c[3]}_{c[4]}x{c[5]}_{'causal' if c[6] else 'full'}")
+def test_lse_matches_oracle(case):
+    """The log-sum-exp side output against the oracle's fp64 value.  The
+    kernel forms it from the bf16-rounded weights (relative error of the
+    row sum below 2^-8), so the bound is 2^-8 absolute plus fp32 rounding
+    of the result."""
+    import torch
+    from bf16_attention_forward_amd import attn_fwd_bf16_gqa
+    import oracle
+    layout, B, Hq, Hkv, Sq, Skv, causal = case
+    q, k, v = wl.random_qkv(layout, B, Hq, Sq, Skv, 300 + Sq, 1.0, 2.0, 1.0, Hkv=Hkv)
+    o, lse = attn_fwd_bf16_gqa(q.cuda(), k.cuda(), v.cuda(), layout=layout, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    got = lse.cpu().numpy().reshape(-1).astype(np.float64)
+    res = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=wl.DEFAULT_SCALE,
+                           method=False, causal=causal)
+    ref = res.lse
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    err = np.abs(got[fin] - ref[fin])
+    say(f"[lse] {case} max err {err.max():.3e}")
+    assert np.all(err <= 2.0 ** -8 + 2.0 ** -20 * np.abs(ref[fin]))
+    # the output is unchanged by asking for the statistic
+    st, _ = check(wl.bits(o.cpu()), q, k, v, layout, "rtne", label=f"lse {case}", causal=causal)
+    assert_gate(st)

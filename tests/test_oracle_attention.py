@@ -330,3 +330,34 @@ def test_causal_last_query_sees_every_key():
     a = run(qb, kb, vb, causal=True, rows=rows)
     b = run(qb, kb, vb, causal=False, rows=rows)
     assert np.array_equal(a.o_exact, b.o_exact)
+
+
+# -------------------------------------------------------------- log-sum-exp
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_matches_torch_logsumexp(causal):
+    layout, B, H, hkv, sq, skv = "bshd", 2, 4, 2, 23, 41
+    q, k, v = wl.random_qkv(layout, B, H, sq, skv, 51, k_factor=2.0, Hkv=hkv)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, causal=causal)
+    Q = q.to(torch.float64).permute(0, 2, 1, 3)
+    K = torch.repeat_interleave(k.to(torch.float64).permute(0, 2, 1, 3), H // hkv, dim=1)
+    S = float(SCALE) * (Q @ K.transpose(-1, -2))
+    if causal:
+        S = S.masked_fill(~causal_mask(sq, skv), float("-inf"))
+    ref = torch.logsumexp(S, dim=-1).reshape(-1).numpy()
+    assert np.allclose(res.lse, ref, rtol=1e-14, atol=1e-13)
+
+
+def test_lse_closed_forms():
+    # one key: lse is that key's scaled score; equal scores: log(Skv) + score
+    q, k, v = wl.random_qkv("bhsd", 1, 1, 5, 1, 52)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v))
+    s0 = float(SCALE) * (f64(wl.bits(q))[0, 0] @ f64(wl.bits(k))[0, 0, 0])
+    assert np.allclose(res.lse, s0, rtol=1e-15, atol=0)
+    q0 = np.zeros((1, 1, 3, 128), np.uint16)
+    _, k2, v2 = wl.random_qkv("bhsd", 1, 1, 3, 37, 53)
+    res = run(q0, wl.bits(k2), wl.bits(v2))
+    assert np.allclose(res.lse, np.log(37.0), rtol=1e-15, atol=0)
+    # causal rows that see no key
+    q3, k3, v3 = wl.random_qkv("bhsd", 1, 1, 9, 4, 54)
+    res = run(wl.bits(q3), wl.bits(k3), wl.bits(v3), causal=True)
+    assert np.all(np.isneginf(res.lse[:5])) and np.all(np.isfinite(res.lse[5:]))

@@ -37,6 +37,7 @@ MUTANTS = {
     "causal_off_by_one": ("n_keys = i + (Skv - Sq) + 1;", "n_keys = i + (Skv - Sq);"),
     "causal_top_left": ("n_keys = i + (Skv - Sq) + 1;", "n_keys = i + 1;"),
     "empty_rows_not_zero": ("if (n_keys <= 0) {", "if (n_keys < 0) {"),
+    "lse_drops_max": ("if (lse) lse[t] = m + log(l);", "if (lse) lse[t] = log(l);"),
 }
 
 
@@ -65,6 +66,8 @@ def pins():
         out.append((f"causal_sdpa_{sq}x{skv}", lambda a=sq, b=skv: A.test_causal_matches_torch_sdpa_float64(a, b)))
     out.append(("causal_brute", lambda: A.test_causal_bruteforce_decimal(4, 3)))
     out.append(("causal_first_row", A.test_causal_first_query_sees_only_first_key))
+    out.append(("lse_torch", lambda: A.test_lse_matches_torch_logsumexp(True)))
+    out.append(("lse_closed", A.test_lse_closed_forms))
     return out
 
 
