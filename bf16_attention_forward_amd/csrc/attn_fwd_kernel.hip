@@ -14,7 +14,9 @@
 //    The bank swizzle is applied to the source address of each lane, not to
 //    the LDS address (HipKittens summary, method section on global async
 //    loads).  Rows past the key range read as zero through the buffer range
-//    check.
+//    check.  The first four waves issue all of it, one instruction every few
+//    MFMA steps: issued at once, the 32 KiB of a tile queue behind the CU's
+//    address unit and stall the issuing waves for ~500 cycles.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16, K as operand A and Q as
 //    operand B.  With that order each lane holds scores of ONE query for a
 //    set of keys, which is the B-operand layout of the next product
@@ -37,21 +39,20 @@
 //    Row maxima and sums are reduced across the 4 lanes of a row with the
 //    gfx950 v_permlane16/32_swap instructions.
 //  * P enters the second product as bf16 rounded to nearest-even
-//    (v_cvt_pk_bf16_f32); the row sum adds those same bf16 weights
-//    (v_dot2c_f32_bf16 against (1, 1)), and the output is divided by it and
-//    rounded to bf16 in the requested mode with integer bit arithmetic after
-//    a NaN guard.
-//  * One barrier per key tile.  Right after it every wave issues its slice of
-//    the DMA for K_{t+1} and V_t, then runs S_t = K_t Q^T interleaved with the
-//    fragment reads of O += V_{t-1}^T P_{t-1}^T, then the softmax of S_t, and
-//    waits for its own DMA before the next barrier.  The two waves sharing a
-//    SIMD drift freely; a wave in its MFMA phase runs at raised issue
-//    priority (s_setprio) so the matrix core stays fed while the other
-//    wave's softmax fills the gaps.  (A
-//    two-group ping-pong with a barrier between the matrix and the softmax
-//    phase, the schedule of the MI300X article's architecture section and of
-//    the HipKittens 8-wave ping-pong, was built and measured ~3% slower on
-//    gfx950 for long sequences.)
+//    (v_cvt_pk_bf16_f32); the row sum adds those same bf16 weights (as fp32,
+//    by bit placement: v_dot2c_f32_bf16 would wait for the matrix core that
+//    the other wave of the SIMD keeps busy), and the output is divided by it
+//    and rounded to bf16 in the requested mode with integer bit arithmetic
+//    after a NaN guard.
+//  * One barrier per key tile, at a different place for the two waves of a
+//    SIMD (the two-group schedule of the MI300X article's architecture
+//    section and of the HipKittens 8-wave ping-pong).  Waves 0-3 run, between
+//    barriers t and t+1, S_t = K_t Q^T interleaved with the fragment reads of
+//    O += V_{t-1}^T P_{t-1}^T and then the softmax of S_t; waves 4-7 run the
+//    softmax of S_{t-1} and then the same MFMA phase.  One wave of each SIMD
+//    is thus in its softmax while the other feeds the matrix core (at raised
+//    issue priority, s_setprio).  Both groups read K_t and V_{t-1} between
+//    the same two barriers, so one double-buffered protocol serves both.
 //  * Optional split of the key range (the flash-decoding style tail split of
 //    the MI300X article, section on the two later improvements): each split
 //    writes its unnormalised fp32 O, M and row sum; a combine kernel merges the
@@ -75,6 +76,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int D = 128;          // head dimension
@@ -161,8 +163,6 @@ template <bool CPOS, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     constexpr int NTHREADS = NW * 64;
-    constexpr int DMA_PER_TILE = TILE_BYTES / 16 / NTHREADS;   // 16-byte chunks per lane per tile
-    static_assert(TILE_BYTES % (16 * NTHREADS) == 0, "tile must split evenly over lanes");
     // Four distinct LDS objects (K and V, two buffers each): with the buffer
     // choice a compile-time constant the compiler can tell that a DMA into one
     // buffer does not alias reads of another and does not wait for it.
@@ -244,30 +244,39 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
 
-    // Per-lane DMA source offsets (relative to the tile's first row).  Slot
-    // (i*NW + wave)*64 + lane of a tile is row (i*NW + wave)*4 + g, chunk j; rows
-    // 32 apart share the swizzle, so one per-lane offset serves every i.
-    constexpr int RPR = NW * 4;   // rows per DMA instruction round (64 lanes x 16 B = 4 rows per wave)
-    static_assert(RPR % 16 == 0, "rows of one DMA round must repeat the 16-row swizzle period");
-    const int dma_row = wave * 4 + g;
+    // The first four waves issue all K/V DMA: tile rows 16*r + 4*w + g (w = wave,
+    // r = round 0..3), chunk j, land at LDS slot (4*r + w)*64 + lane, i.e. row
+    // by row in order; rows 16 apart share the swizzle, so one per-lane source
+    // offset serves all four rounds.  The DMA is issued with inline assembly:
+    // the compiler then does not track it and inserts no vmcnt wait before
+    // LDS reads of other buffers (its alias tracking is lost at loop heads);
+    // the issuing waves wait for their DMA explicitly (vmcnt(0)) before the
+    // barrier that publishes a tile.
+    const bool late = NW == 8 && wave >= 4;   // second wave of each SIMD (see the key loop)
+    constexpr int DMA_ROUNDS = TILE_BYTES / 16 / (4 * 64);
+    static_assert(DMA_ROUNDS == 4, "four waves move a tile in four rounds of 16 rows");
+    const int dma_row = (wave & 3) * 4 + g;
     const int dma_off_k = dma_row * kv_row_bytes + ((j ^ swz_k(dma_row)) << 4);
     const int dma_off_v = dma_row * kv_row_bytes + ((j ^ swz_v(dma_row)) << 4);
-    auto issue_k = [&](int t, uint8_t* dst) {
-        const int soff = (kv_begin + t * BN) * kv_row_bytes;
-#pragma unroll
-        for (int i = 0; i < DMA_PER_TILE; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
-                                                     dma_off_k, soff + i * RPR * kv_row_bytes, 0, 0);
+    const uint64_t ka = (uint64_t)(uintptr_t)kbase, va = (uint64_t)(uintptr_t)vbase;
+    const i32x4 krs4 = {(int)(uint32_t)ka, (int)((ka >> 32) & 0xffffu), (int)nrec, 0x00020000};
+    const i32x4 vrs4 = {(int)(uint32_t)va, (int)((va >> 32) & 0xffffu), (int)nrec, 0x00020000};
+    auto dma16 = [&](const i32x4 rs, uint8_t* dst, int voff, int soff) {
+        const uint32_t lds = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst;
+        __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                         :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
     };
-    auto issue_v = [&](int t, uint8_t* dst) {
-        const int soff = (kv_begin + t * BN) * kv_row_bytes;
-#pragma unroll
-        for (int i = 0; i < DMA_PER_TILE; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
-                                                     dma_off_v, soff + i * RPR * kv_row_bytes, 0, 0);
+    // round r of the K (or V) tile that starts at key k0
+    auto dma_k = [&](int r, int k0, uint8_t* dst) {
+        dma16(krs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 + 16 * r) * kv_row_bytes);
     };
-
-    issue_k(0, sk0);
+    auto dma_v = [&](int r, int k0, uint8_t* dst) {
+        dma16(vrs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 + 16 * r) * kv_row_bytes);
+    };
+    if (!late) {
+#pragma unroll
+        for (int r = 0; r < DMA_ROUNDS; r++) dma_k(r, kv_begin, sk0);
+    }
 
     // ---- Q fragments (operand B of S^T = K Q^T): lane (g, j) holds query row
     // 16*qb + j of this wave, dims 32*ks + 8*g .. +7, for the whole key loop.
@@ -294,7 +303,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     f32x4 s_acc[4][NQB];
     bf16x8 pf[NQB][2];
     const float c = p.c;
-    const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
     // ---- MFMA phase: steps [S0, S1) of a fixed sequence of 32 fragment steps.
     // Steps 0..15 compute S^T = K Q^T: step 4*ks + kb reads the K fragment of key
@@ -343,8 +351,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         }
     };
     constexpr int PF = 4;   // fragment prefetch distance (steps)
-    auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c) {
+    // The DMA of iteration t (K_{t+1} into kn, V_t into vc) is spread over the
+    // issuing waves' MFMA phase, one instruction every (S1 - S0)/8 steps, so
+    // the CU's address unit drains it while the matrix core runs instead of
+    // stalling a wave that issues all of it at once.
+    auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c, int t, uint8_t* kn, uint8_t* vc) {
         constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
+        constexpr int STRIDE = (S1 - S0) / 8;
         // Opaque per-lane offsets: stops the compiler from hoisting every
         // buffer x fragment address combination out of the loop (and spilling
         // them); each phase adds its buffer base to 12 offsets instead.
@@ -359,6 +372,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         for (int st = S0; st < S1; st++) {
             const bf16x8 cur = fr[(st - S0) % PF];
             if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
+            if (S0 == 0 && (st - S0) % STRIDE == 0 && !late) {
+                const int k = (st - S0) / STRIDE;     // K and V rounds alternate
+                if (k & 1) dma_v(k >> 1, kv_begin + t * BN, vc);
+                else if (t + 1 < T) dma_k(k >> 1, kv_begin + (t + 1) * BN, kn);
+            }
             use_frag(st, cur);
         }
         // keep the interleave: the reads of step st+PF, then the MFMAs of step st
@@ -383,8 +401,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     // Weights of query block qb against offset m: p = 2^(x - m) (v_exp_f32),
     // rounded to bf16 pairs for the P.V product (pf), and this lane's sum of
     // those bf16 weights -- the row sum adds the same values the product uses,
-    // so O is normalised by exactly its own weights (v_dot2c_f32_bf16 against
-    // (1, 1): one instruction per two weights).
+    // so O is normalised by exactly its own weights.
     auto weights = [&](int qb, float m, auto biasc) -> float {
         constexpr bool BIASED = decltype(biasc)::value;   // S^T already holds s - moff/c: exponent = c * S^T
         const float negm = -m;
@@ -397,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                                        : (CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm));
                 pv4[kb][r] = __builtin_amdgcn_exp2f(x);
             }
-        float tsum = 0.f;
+        float tlo = 0.f, thi = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
             bf16x2 pr[4];
@@ -406,13 +423,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                 const f32x4& src = pv4[2 * ks + (i >> 1)];
                 const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
                 pr[i] = __builtin_convertvector(two, bf16x2);
-                tsum = __builtin_amdgcn_fdot2_f32_bf16(pr[i], ones2, tsum, false);
+                // the two bf16 weights as fp32 (bit placement), summed with plain
+                // adds: v_dot2c would wait for the matrix core a co-resident
+                // wave keeps busy
+                const uint32_t u = __builtin_bit_cast(uint32_t, pr[i]);
+                tlo += __uint_as_float(u << 16);
+                thi += __uint_as_float(u & 0xffff0000u);
             }
             const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
             const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
             pf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        return tsum;
+        return tlo + thi;
     };
     // ceil of the tile's largest x for query block qb (NaN-propagating
     // v_maximum3_f32 in the lane, then across the 4 lanes of a row)
@@ -514,28 +536,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         for (int qb = 0; qb < NQB; qb++) l_run[qb] += tsum[qb];
     };
 
-    // ---- key loop: one barrier per tile.  Iteration t issues the DMA of K_{t+1}
-    // (into the buffer K_{t-1} used) and V_t (into V_{t-2}'s), computes
-    // S_t = K_t Q^T and O += V_{t-1}^T P_{t-1}^T, then the softmax of S_t, and
-    // waits for its DMA before the barrier.  Iteration 0 has no P.V step and
-    // iteration T (past the last tile) only the P.V step; the steady-state
-    // loop in between is branch-free in vector state, which keeps the
-    // accumulators in place.
+    // ---- key loop: one barrier per tile.  Iteration t computes S_t = K_t Q^T
+    // and O += V_{t-1}^T P_{t-1}^T (with the DMA of K_{t+1} into the buffer
+    // K_{t-1} used and of V_t into V_{t-2}'s), then the softmax of S_t; the
+    // issuing waves wait for their DMA before the barrier.  Iteration 0 has
+    // no P.V step and iteration T (past the last tile) only the P.V step; the
+    // steady-state loop in between is branch-free in vector state, which
+    // keeps the accumulators in place.
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's K_0 slice and its Q landed
     lds_barrier();
+    // Waves w and w + 4 share a SIMD.  The second group takes the barrier
+    // between its MFMA phase and its softmax instead of after the softmax, so
+    // between two barriers it runs the softmax of S_{t-1} and then the MFMA
+    // phase of tile t while the first group runs the MFMA phase of tile t and
+    // then the softmax of S_t: the two waves of a SIMD are in opposite phases
+    // and one's softmax fills the gaps of the other's MFMAs.  Both groups
+    // read K_t and V_{t-1} between the same two barriers, so the buffer
+    // protocol is the same for both.
+    auto sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        lds_barrier();
+    };
     auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c) {
-        if (t + 1 < T) issue_k(t + 1, kn);
-        if (t < T) issue_v(t, vc);
         // A wave in its MFMA phase takes issue priority over one in its
         // softmax, so the matrix core of a SIMD stays fed; the softmax VALU
         // work fills the MFMA phase's gaps.
         __builtin_amdgcn_s_setprio(1);
-        mfma_phase(kc, vp, s0c, s1c);
+        mfma_phase(kc, vp, s0c, s1c, t, kn, vc);
         __builtin_amdgcn_s_setprio(0);
+        if (late) sync();
         if (decltype(s0c)::value == 0)
             softmax(t, std::integral_constant<bool, decltype(s1c)::value == 16>{});
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-        lds_barrier();
+        if (!late) sync();
     };
     iter(0, sk0, sk1, sv0, sv1, C0{}, C16{});
     int t = 1;
