@@ -68,7 +68,7 @@ def configure(lib):
         ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_int, ctypes.c_int]
+        ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.oracle_version.restype = ctypes.c_int
     return lib
 
@@ -104,7 +104,8 @@ class OracleResult:
 
 
 def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = True,
-              l_from_rounded: bool = False, nthreads: int = 0, causal: bool = False) -> OracleResult:
+              l_from_rounded: bool = False, nthreads: int = 0, causal: bool = False,
+              p_round: str = "rtne") -> OracleResult:
     """Evaluate the oracle.
 
     q, k, v: uint16 arrays holding bf16 bit patterns, shaped [B,S,H,128]
@@ -113,7 +114,8 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
     h // (Hq // Hkv)).  causal: bottom-right aligned causal mask (query i sees
     keys j <= i + Skv - Sq; rows seeing no key are zero).  rows: optional
     int64 array of flat row ids r = (b*Hq + h)*Sq + i; None means every row in
-    that order.
+    that order.  p_round: rounding mode of the method companion's bf16
+    probabilities (the plain definition does not depend on it).
     """
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.uint16)
@@ -151,7 +153,7 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
                                   rows_ptr, nrows, o.ctypes.data, sg.ctypes.data,
                                   om.ctypes.data if method else None,
                                   sm.ctypes.data if method else None, ls.ctypes.data,
-                                  1 if l_from_rounded else 0, int(nthreads))
+                                  1 if l_from_rounded else 0, MODES[p_round], int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed ({rc})")
     rows_out = np.arange(nrows, dtype=np.int64) if rows_arr is None else rows_arr

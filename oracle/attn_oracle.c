@@ -34,10 +34,14 @@
  * 16x16x32 MFMA for both attention products on gfx950).  This file writes
  * that step out directly from the pages' order of operations, with the
  * reading documented in the design notes: x_j = s_j log2(e), M = ceil(max x),
- * pt_j = bf16_RTNE(2^(x_j - M)), and
+ * pt_j = bf16(2^(x_j - M)), and
  *     o_method_d = sum_j pt_j v_{j,d} / L,  L = sum_j 2^(x_j - M)
  * (or L = sum_j pt_j when l_from_rounded is set).  Because M only rescales by
- * an exact power of two, pt_j does not depend on how keys are tiled.
+ * an exact power of two, pt_j does not depend on how keys are tiled.  The
+ * bf16 rounding of pt_j is to nearest-even unless p_round names another mode:
+ * the article measures each output rounding mode at a different speed, which
+ * reads as the weights being rounded in the loop with the selected mode too,
+ * so that reading is selectable.
  *
  * Two extensions the pages list as limitations of the kernel they describe
  * (MoonMath article, limitations paragraph: no causal masking, no grouped-
@@ -146,8 +150,8 @@ static int64_t row_offset(int layout, int64_t b, int64_t h, int64_t i, int64_t H
     return ((b * H + h) * S + i) * ORACLE_D;
 }
 
-/* Round to bf16 (RTNE) and back, for the method companion's probabilities. */
-static double round_trip_bf16_rtne(double x) { return bf16_to_double(oracle_round_bf16(x, OR_RTNE)); }
+/* Round to bf16 in the given mode and back, for the method companion's probabilities. */
+static double round_trip_bf16(double x, int mode) { return bf16_to_double(oracle_round_bf16(x, mode)); }
 
 /*
  * Evaluate rows of attention.
@@ -160,6 +164,8 @@ static double round_trip_bf16_rtne(double x) { return bf16_to_double(oracle_roun
  *   o_method, sigma_method    : [nrows, 128] doubles, or NULL to skip.
  *   lse                       : [nrows] doubles, or NULL to skip.
  *   l_from_rounded            : method companion's normaliser (see header).
+ *   p_round                   : OR_RTNE / OR_RTNA / OR_RTZ for the method
+ *                               companion's bf16 probabilities.
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
 int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -167,8 +173,9 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          float scale, int causal, const int64_t* rows, int64_t nrows,
                          double* o_exact, double* sigma,
                          double* o_method, double* sigma_method, double* lse,
-                         int l_from_rounded, int nthreads) {
+                         int l_from_rounded, int p_round, int nthreads) {
     if (!q || !k || !v || !o_exact || !sigma) return -1;
+    if (p_round != OR_RTNE && p_round != OR_RTNA && p_round != OR_RTZ) return -1;
     if (layout != OR_LAYOUT_BSHD && layout != OR_LAYOUT_BHSD) return -1;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return -1;
     if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return -1;
@@ -244,7 +251,7 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
                 double pt = 0.0, pm = 0.0;
                 if (o_method) {
                     pm = exp2(s[j] * log2e - M);
-                    pt = round_trip_bf16_rtne(pm);
+                    pt = round_trip_bf16(pm, p_round);
                     lm += pm;
                     lm_rounded += pt;
                 }
@@ -287,5 +294,5 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      double* o_method, double* sigma_method,
                      int l_from_rounded, int nthreads) {
     return oracle_attention_gqa(q, k, v, layout, B, H, H, Sq, Skv, scale, 0, rows, nrows,
-                                o_exact, sigma, o_method, sigma_method, NULL, l_from_rounded, nthreads);
+                                o_exact, sigma, o_method, sigma_method, NULL, l_from_rounded, OR_RTNE, nthreads);
 }

@@ -250,6 +250,35 @@ def test_method_companion_close_to_exact():
     assert not np.array_equal(res.o_method, res.o_exact)
 
 
+@pytest.mark.parametrize("mode", ["rtne", "rtna", "rtz"])
+def test_method_weights_rounded_in_mode(mode):
+    """Method companion with the weights rounded in a given mode (the reading in
+    which the MoonMath article's per-mode speeds come from rounding the weights
+    in the loop): with V the identity over the keys and L the sum of the
+    rounded weights, o_method is pt_j / sum pt with pt_j = mode(2^(x_j - M)),
+    rebuilt here from exact (rational) scores and the grid-search rounding."""
+    from tests.test_oracle_round import reference_round
+    skv, sq = 100, 3
+    q, k, _ = wl.random_qkv("bhsd", 1, 1, sq, skv, 61, k_factor=2.0)
+    vv = np.zeros((1, 1, skv, 128)); vv[0, 0, np.arange(skv), np.arange(skv)] = 1.0
+    res = run(wl.bits(q), wl.bits(k), bf(vv), method=True, l_from_rounded=True, p_round=mode)
+    Q = f64(wl.bits(q))[0, 0]; K = f64(wl.bits(k))[0, 0]
+    log2e = 1.4426950408889634
+    differs_from_rtne = 0
+    for i in range(sq):
+        s = np.array([float(sum(Fraction(Q[i, d]) * Fraction(K[j, d]) for d in range(128)) * Fraction(float(SCALE)))
+                      for j in range(skv)])
+        x = s * log2e
+        p = np.exp2(x - np.ceil(x.max()))
+        pt = oracle.bf16_bits_to_f64(reference_round(p, mode))
+        assert np.allclose(res.o_method[i, :skv], pt / pt.sum(), rtol=1e-14, atol=0)
+        assert np.all(res.o_method[i, skv:] == 0)
+        differs_from_rtne += int(np.sum(pt != oracle.bf16_bits_to_f64(reference_round(p, "rtne"))))
+    # truncation changes most weights; the two nearest modes differ only on
+    # exact ties, which fp64 powers of two of these scores never hit
+    assert (differs_from_rtne > 0) == (mode == "rtz")
+
+
 # ------------------------------------------- grouped-query heads, causal mask
 # The pages list causal masking and grouped-query attention as limitations of
 # the kernel they describe (MoonMath article, limitations paragraph); the

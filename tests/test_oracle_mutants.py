@@ -38,6 +38,7 @@ MUTANTS = {
     "causal_top_left": ("n_keys = i + (Skv - Sq) + 1;", "n_keys = i + 1;"),
     "empty_rows_not_zero": ("if (n_keys <= 0) {", "if (n_keys < 0) {"),
     "lse_drops_max": ("if (lse) lse[t] = m + log(l);", "if (lse) lse[t] = log(l);"),
+    "weights_mode_ignored": ("pt = round_trip_bf16(pm, p_round);", "pt = round_trip_bf16(pm, OR_RTNE);"),
 }
 
 
@@ -68,6 +69,8 @@ def pins():
     out.append(("causal_first_row", A.test_causal_first_query_sees_only_first_key))
     out.append(("lse_torch", lambda: A.test_lse_matches_torch_logsumexp(True)))
     out.append(("lse_closed", A.test_lse_closed_forms))
+    for mode in ("rtna", "rtz"):
+        out.append((f"weights_{mode}", lambda m=mode: A.test_method_weights_rounded_in_mode(m)))
     return out
 
 
