@@ -49,7 +49,7 @@ def measured_traffic(workload_name: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def time_workload(w, mode, steps, warmup, kv_splits=0):
+def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
     import torch
     from bf16_attention_forward_amd import attn_fwd_bf16, attn_fwd_bf16_gqa
     from bf16_attention_forward_amd import workloads as wl
@@ -62,9 +62,11 @@ def time_workload(w, mode, steps, warmup, kv_splits=0):
 
     def step():
         if w.causal or w.Hkv:
-            attn_fwd_bf16_gqa(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, causal=w.causal)
+            attn_fwd_bf16_gqa(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, causal=w.causal,
+                              round_weights=round_weights)
         else:
-            attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, kv_splits=kv_splits)
+            attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, kv_splits=kv_splits,
+                          round_weights=round_weights)
 
     for _ in range(warmup):
         step()
@@ -157,6 +159,12 @@ def main():
             em = statistics.median(rr["ms"])
             extra[f"{w.name}:{mode}"] = {"mode": mode, "median_ms": round(em, 4),
                                          "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
+        # the option that rounds the in-loop weights with the output's mode
+        for mode in w.modes:
+            rr = time_workload(w, mode, steps=50, warmup=20, round_weights=True)
+            em = statistics.median(rr["ms"])
+            extra[f"{w.name}:{mode}+weights"] = {"mode": mode, "round_weights": True, "median_ms": round(em, 4),
+                                                 "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
 

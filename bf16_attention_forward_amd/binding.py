@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libattn_fwd.so")
 
 ATTN_LAYOUT = {"bshd": 0, "bhsd": 1}
 ATTN_ROUND = {"rtne": 0, "rtna": 1, "rtz": 2}
+ATTN_ROUND_WEIGHTS = 0x100   # round_mode flag: the in-loop softmax weights use the output's mode too
 ATTN_OK = 0
 ARGUMENT_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -11}
 HEAD_DIM = 128
@@ -100,6 +101,12 @@ def _dims(q: torch.Tensor, k: torch.Tensor, layout: str, grouped: bool = False):
     return B, H, Hk, Sq, Skv
 
 
+def _mode(round_mode: str, round_weights: bool) -> int:
+    if round_mode not in ATTN_ROUND:
+        raise ValueError(f"round_mode must be one of {sorted(ATTN_ROUND)}")
+    return ATTN_ROUND[round_mode] | (ATTN_ROUND_WEIGHTS if round_weights else 0)
+
+
 def _check_tensors(q, k, v, o):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16:
@@ -120,25 +127,25 @@ def _check_tensors(q, k, v, o):
 def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
                   layout: str = "bshd", scale: float | None = None, round_mode: str = "rtne",
                   stream: torch.cuda.Stream | None = None, kv_splits: int = 0,
-                  block_order: int = 0) -> torch.Tensor:
+                  block_order: int = 0, round_weights: bool = False) -> torch.Tensor:
     """O = softmax(Q K^T * scale) V on the gfx950 library (bf16 in/out).
 
     q, k, v, o: contiguous bfloat16 CUDA tensors in the given layout.  o is
     allocated when None.  scale defaults to 1/sqrt(128) (as fp32).  The
     launch goes to ``stream`` (default: torch's current stream) and is
     asynchronous.  kv_splits/block_order are the planner overrides of
-    attn_fwd_bf16_ex (0 = automatic).
+    attn_fwd_bf16_ex (0 = automatic).  round_weights: round the in-loop
+    softmax weights with ``round_mode`` too (ATTN_ROUND_WEIGHTS; default:
+    nearest-even).
     """
     lib = load_library()
     o = _check_tensors(q, k, v, o)
     B, H, _, Sq, Skv = _dims(q, k, layout)
-    if round_mode not in ATTN_ROUND:
-        raise ValueError(f"round_mode must be one of {sorted(ATTN_ROUND)}")
     sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
         rc = lib.attn_fwd_bf16_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                  ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, ATTN_ROUND[round_mode],
+                                  ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, _mode(round_mode, round_weights),
                                   st.cuda_stream, int(kv_splits), int(block_order))
     if rc != ATTN_OK:
         _raise(rc)
@@ -148,7 +155,8 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
 def attn_fwd_bf16_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
                       layout: str = "bshd", scale: float | None = None, causal: bool = False,
                       round_mode: str = "rtne", stream: torch.cuda.Stream | None = None,
-                      lse: torch.Tensor | None = None, return_lse: bool = False):
+                      lse: torch.Tensor | None = None, return_lse: bool = False,
+                      round_weights: bool = False):
     """Grouped-query attention with an optional causal mask (attn_fwd_bf16_gqa).
 
     k and v may have fewer heads than q (query head h reads key/value head
@@ -165,15 +173,13 @@ def attn_fwd_bf16_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq)
                             or not lse.is_contiguous() or not lse.is_cuda):
         raise ValueError("lse must be a contiguous float32 device tensor shaped [B, Hq, Sq]")
-    if round_mode not in ATTN_ROUND:
-        raise ValueError(f"round_mode must be one of {sorted(ATTN_ROUND)}")
     sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
         rc = lib.attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    lse.data_ptr() if lse is not None else None,
                                    ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, sc, 1 if causal else 0,
-                                   ATTN_ROUND[round_mode], st.cuda_stream)
+                                   _mode(round_mode, round_weights), st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (o, lse) if lse is not None else o

@@ -102,14 +102,14 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-extern "C" int attn_version(void) { return 10100; }
+extern "C" int attn_version(void) { return 10200; }
 
 extern "C" const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_LAYOUT: return "layout must be ATTN_LAYOUT_BSHD or ATTN_LAYOUT_BHSD";
-        case ATTN_ERR_ROUND_MODE: return "round_mode must be ATTN_ROUND_RTNE, _RTNA or _RTZ";
+        case ATTN_ERR_ROUND_MODE: return "round_mode must be ATTN_ROUND_RTNE, _RTNA or _RTZ, optionally | ATTN_ROUND_WEIGHTS";
         case ATTN_ERR_SHAPE: return "B, H (Hq, Hkv), Sq and Skv must be >= 1, Hq a multiple of Hkv, and the sizes must fit the kernel's index range";
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned";
@@ -131,7 +131,8 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
                   int kv_splits, int block_order) {
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
-    if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
+    const int out_mode = round_mode & ~ATTN_ROUND_WEIGHTS;
+    if (out_mode != ATTN_ROUND_RTNE && out_mode != ATTN_ROUND_RTNA && out_mode != ATTN_ROUND_RTZ)
         return ATTN_ERR_ROUND_MODE;
     if (B < 1 || H < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
     if (H % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -187,7 +188,8 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.causal_off = (int)(Skv - Sq);
     p.n_qtiles = (int)n_qtiles;
     p.n_items = (int)(B * H * n_qtiles);
-    p.round_mode = round_mode;
+    p.round_mode = out_mode;
+    p.p_mode = (round_mode & ATTN_ROUND_WEIGHTS) ? out_mode : ATTN_ROUND_RTNE;
     p.c = (float)((double)scale * 1.4426950408889634073599246810018921);
 
     // ---- plan the key-range split

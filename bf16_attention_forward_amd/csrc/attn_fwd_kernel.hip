@@ -159,7 +159,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // 8 waves, each owning 32 query rows of the work item; see the file header
 // for the per-tile schedule.
-template <bool CPOS, bool CAUSAL>
+template <bool CPOS, bool CAUSAL, int PMODE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     constexpr int NTHREADS = NW * 64;
@@ -398,6 +398,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     using C16 = std::integral_constant<int, 16>;
     using C32 = std::integral_constant<int, 32>;
 
+    // Two weights (>= 0, or NaN) to packed bf16 in the weights' rounding mode.
+    // Nearest-even: the hardware conversion.  Ties away: the same conversion
+    // after setting the lowest fp32 bit, which turns an exact tie into a value
+    // just above it and changes no other decision (an infinite weight would
+    // become NaN, but it only arises in rows whose output is NaN anyway).
+    // Toward zero: the high half of the bit pattern, after clamping every NaN
+    // to the canonical one so truncation cannot make it an infinity.
+    auto weight_pair = [&](const f32x2 two) -> bf16x2 {
+        if (PMODE == ROUND_RTNE) return __builtin_convertvector(two, bf16x2);
+        if (PMODE == ROUND_RTNA) {
+            const f32x2 up = {__uint_as_float(__float_as_uint(two[0]) | 1u), __uint_as_float(__float_as_uint(two[1]) | 1u)};
+            return __builtin_convertvector(up, bf16x2);
+        }
+        const uint32_t u0 = min(__float_as_uint(two[0]), 0x7fc00000u);
+        const uint32_t u1 = min(__float_as_uint(two[1]), 0x7fc00000u);
+        return __builtin_bit_cast(bf16x2, (u1 & 0xffff0000u) | (u0 >> 16));
+    };
     // Weights of query block qb against offset m: p = 2^(x - m) (v_exp_f32),
     // rounded to bf16 pairs for the P.V product (pf), and this lane's sum of
     // those bf16 weights -- the row sum adds the same values the product uses,
@@ -422,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
             for (int i = 0; i < 4; i++) {
                 const f32x4& src = pv4[2 * ks + (i >> 1)];
                 const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
-                pr[i] = __builtin_convertvector(two, bf16x2);
+                pr[i] = weight_pair(two);
                 // the two bf16 weights as fp32 (bit placement), summed with plain
                 // adds: v_dot2c would wait for the matrix core a co-resident
                 // wave keeps busy
@@ -689,18 +706,24 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
 // ------------------------------------------------------------------ launch
 int launch(const AttnParams& p, hipStream_t stream) {
     dim3 grid(p.n_blocks), block(NW * 64);
-    // c > 0 (the usual positive scale) and the causal mask are compile-time
-    // variants, so the plain path carries no code for either alternative.
+    // c > 0 (the usual positive scale), the causal mask and the weights'
+    // rounding mode are compile-time variants, so the plain path carries no
+    // code for any alternative.
+    auto go = [&](auto cpos, auto causal) {
+        constexpr bool CP = decltype(cpos)::value, CA = decltype(causal)::value;
+        if (p.p_mode == ROUND_RTNA)
+            hipLaunchKernelGGL((attn_fwd_main<CP, CA, ROUND_RTNA>), grid, block, 0, stream, p);
+        else if (p.p_mode == ROUND_RTZ)
+            hipLaunchKernelGGL((attn_fwd_main<CP, CA, ROUND_RTZ>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_main<CP, CA, ROUND_RTNE>), grid, block, 0, stream, p);
+    };
     if (p.causal) {
-        if (p.c > 0.f)
-            hipLaunchKernelGGL((attn_fwd_main<true, true>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_fwd_main<false, true>), grid, block, 0, stream, p);
+        if (p.c > 0.f) go(std::true_type{}, std::true_type{});
+        else go(std::false_type{}, std::true_type{});
     } else {
-        if (p.c > 0.f)
-            hipLaunchKernelGGL((attn_fwd_main<true, false>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_fwd_main<false, false>), grid, block, 0, stream, p);
+        if (p.c > 0.f) go(std::true_type{}, std::false_type{});
+        else go(std::false_type{}, std::false_type{});
     }
     if (hipGetLastError() != hipSuccess) return -1;
     if (p.n_full < p.n_items) {

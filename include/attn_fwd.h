@@ -44,13 +44,21 @@ enum {
     ATTN_ROUND_RTZ  = 2  /* toward zero (finite overflow -> max finite)   */
 };
 
+/* Flag OR'ed into round_mode: the softmax weights that enter the bf16 P.V
+ * product are rounded with the same mode as the output (without it they are
+ * rounded to nearest-even).  The MoonMath article measures each output mode
+ * at a different speed (benchmark section), which reads as the weights being
+ * rounded in the loop with the selected mode too; this flag selects that
+ * reading.  RTNA and RTNE weights differ only on exact ties. */
+enum { ATTN_ROUND_WEIGHTS = 0x100 };
+
 /* Status codes.  Every argument error is detected on the host before any
  * launch; on error nothing is launched and o is not written. */
 enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = -1,        /* a required pointer is NULL                        */
     ATTN_ERR_LAYOUT = -2,      /* layout is not one of ATTN_LAYOUT_*                */
-    ATTN_ERR_ROUND_MODE = -3,  /* round_mode is not one of ATTN_ROUND_*             */
+    ATTN_ERR_ROUND_MODE = -3,  /* round_mode is not ATTN_ROUND_* [| ATTN_ROUND_WEIGHTS] */
     ATTN_ERR_SHAPE = -4,       /* a size < 1, Hq not a multiple of Hkv, or overflow */
     ATTN_ERR_SCALE = -5,       /* scale is NaN or infinite                          */
     ATTN_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                  */
@@ -73,7 +81,8 @@ enum {
  *   Sq, Skv      query and key/value lengths (>= 1), independent
  *   scale        finite fp32 multiplier of the scores (1/sqrt(128) is usual;
  *                0 gives the uniform average of V)
- *   round_mode   ATTN_ROUND_* for the final fp32 -> bf16 conversion
+ *   round_mode   ATTN_ROUND_* for the final fp32 -> bf16 conversion, optionally
+ *                | ATTN_ROUND_WEIGHTS to round the in-loop weights the same way
  *   stream       hipStream_t to launch on (NULL = default stream)
  *
  * Ownership: the caller owns q, k, v, o and keeps them alive until the

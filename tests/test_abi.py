@@ -53,7 +53,8 @@ def call(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), -1), (dict(o=0), -1), (dict(layout=2), -2), (dict(layout=-1), -2),
-    (dict(mode=3), -3), (dict(B=0), -4), (dict(H=0), -4), (dict(Sq=0), -4), (dict(Skv=0), -4),
+    (dict(mode=3), -3), (dict(mode=0x100 | 3), -3), (dict(mode=0x200), -3), (dict(mode=0x101 | 0x10000), -3),
+    (dict(B=0), -4), (dict(H=0), -4), (dict(Sq=0), -4), (dict(Skv=0), -4),
     (dict(Skv=-5), -4), (dict(Sq=1 << 40), -4), (dict(scale=math.nan), -5), (dict(scale=math.inf), -5),
     (dict(q=FAKE + 8), -6), (dict(o=FAKE + (3 << 30) + 2), -6), (dict(o=FAKE), -7),
     (dict(o=FAKE + 64 * 2 * 128 * 2 - 16), -7), (dict(splits=65), -11), (dict(order=3), -11),
@@ -68,6 +69,8 @@ def test_valid_arguments_reach_device_check():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert call() == -8
+    for m in (0x100, 0x101, 0x102):   # ATTN_ROUND_WEIGHTS with each output mode is valid
+        assert call(mode=m) == -8
 
 
 def call_gqa(**kw):
@@ -95,3 +98,4 @@ def test_gqa_valid_arguments_reach_device_check():
     assert call_gqa() == -8
     assert call_gqa(causal=0, Hkv=8) == -8
     assert call_gqa(lse=FAKE + (4 << 30)) == -8
+    assert call_gqa(mode=0x102) == -8
