@@ -46,6 +46,12 @@ class Workload:
     note: str = ""
     Hkv: int = 0          # key/value heads (grouped-query attention); 0 = H
     causal: bool = False  # bottom-right aligned causal mask
+    D: int = HEAD_DIM     # head dimension (128, or 64)
+
+    @property
+    def scale(self) -> float:
+        """fp32(1/sqrt(D)), the usual softmax scale."""
+        return float(np.float32(1.0 / math.sqrt(self.D)))
 
     @property
     def seed(self) -> int:
@@ -62,16 +68,16 @@ class Workload:
 
     @property
     def flops(self) -> int:
-        return 4 * self.B * self.H * self.pairs * HEAD_DIM
+        return 4 * self.B * self.H * self.pairs * self.D
 
     @property
     def algorithmic_bytes(self) -> int:
         """Q, K, V read once and O written once, bf16."""
-        return 2 * HEAD_DIM * self.B * (2 * self.H * self.Sq + 2 * self.kv_heads * self.Skv)
+        return 2 * self.D * self.B * (2 * self.H * self.Sq + 2 * self.kv_heads * self.Skv)
 
     def describe(self) -> dict:
         d = {"workload": self.name, "layout": self.layout, "B": self.B, "H": self.H,
-             "Sq": self.Sq, "Skv": self.Skv, "head_dim": HEAD_DIM}
+             "Sq": self.Sq, "Skv": self.Skv, "head_dim": self.D}
         if self.Hkv:
             d["Hkv"] = self.Hkv
         if self.causal:
@@ -105,14 +111,19 @@ WORKLOADS = {
                 note="causal grouped-query attention, 4 query heads per key/value head"),
     7: Workload(7, "causal_self_attn_bshd_b2_h16_s4096", "bshd", 2, 16, 4096, 4096,
                 causal=True, modes=("rtne", "rtz"), note="causal self-attention"),
+    8: Workload(8, "self_attn_bhsd_b4_h16_s4096_d64", "bhsd", 4, 16, 4096, 4096, D=64,
+                modes=("rtne",), note="head dimension 64, same FLOPs as the 4096^2 d=128 workload"),
+    9: Workload(9, "video_self_attn_bshd_b1_h24_s32760_d64", "bshd", 1, 24, 32760, 32760, D=64,
+                q_factor=0.5, k_factor=0.5, v_factor=0.5, modes=("rtne",),
+                note="the video self-attention split into twice the heads of dimension 64"),
 }
 
 
-def shape(layout: str, B: int, H: int, S: int) -> tuple:
+def shape(layout: str, B: int, H: int, S: int, D: int = HEAD_DIM) -> tuple:
     if layout == "bshd":
-        return (B, S, H, HEAD_DIM)
+        return (B, S, H, D)
     if layout == "bhsd":
-        return (B, H, S, HEAD_DIM)
+        return (B, H, S, D)
     raise ValueError(layout)
 
 
@@ -127,12 +138,12 @@ def _draw(shape_, seed: int, factor: float) -> torch.Tensor:
 
 def random_qkv(layout: str, B: int, H: int, Sq: int, Skv: int, seed: int,
                q_factor: float = 1.0, k_factor: float = 1.0, v_factor: float = 1.0,
-               Hkv: int | None = None):
+               Hkv: int | None = None, D: int = HEAD_DIM):
     """Return (q, k, v) as bf16 CPU tensors in the given layout; k and v have
-    Hkv heads (default H)."""
-    q = _draw(shape(layout, B, H, Sq), 4 * seed + 0, q_factor)
-    k = _draw(shape(layout, B, Hkv or H, Skv), 4 * seed + 1, k_factor)
-    v = _draw(shape(layout, B, Hkv or H, Skv), 4 * seed + 2, v_factor)
+    Hkv heads (default H); D is the head dimension."""
+    q = _draw(shape(layout, B, H, Sq, D), 4 * seed + 0, q_factor)
+    k = _draw(shape(layout, B, Hkv or H, Skv, D), 4 * seed + 1, k_factor)
+    v = _draw(shape(layout, B, Hkv or H, Skv, D), 4 * seed + 2, v_factor)
     return q, k, v
 
 
@@ -141,7 +152,7 @@ def make_inputs(w: Workload, *, Sq: int | None = None, Skv: int | None = None,
     """Draw the workload's q, k, v (bf16 CPU tensors); sizes may be overridden."""
     return random_qkv(w.layout, B or w.B, H or w.H, Sq or w.Sq, Skv or w.Skv,
                       w.seed if seed is None else seed, w.q_factor, w.k_factor, w.v_factor,
-                      Hkv=w.Hkv or None)
+                      Hkv=w.Hkv or None, D=w.D)
 
 
 @dataclass
@@ -205,15 +216,15 @@ def row_ids(layout: str, B: int, H: int, Sq: int, b, h, i) -> np.ndarray:
 
 
 def gather_rows(o_bits: np.ndarray, layout: str, B: int, H: int, Sq: int, rows) -> np.ndarray:
-    """Pick rows (flat ids) out of an output tensor's bf16 bits -> [n, 128]."""
+    """Pick rows (flat ids) out of an output tensor's bf16 bits -> [n, D]."""
     rows = np.asarray(rows, dtype=np.int64)
     i = rows % Sq
     bh = rows // Sq
     h = bh % H
     b = bh // H
     if layout == "bshd":
-        return o_bits.reshape(B, Sq, H, HEAD_DIM)[b, i, h]
-    return o_bits.reshape(B, H, Sq, HEAD_DIM)[b, h, i]
+        return o_bits.reshape(B, Sq, H, -1)[b, i, h]
+    return o_bits.reshape(B, H, Sq, -1)[b, h, i]
 
 
 def sample_rows(B: int, H: int, Sq: int, n_per_head: int, seed: int, tile: int = 128) -> np.ndarray:

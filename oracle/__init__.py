@@ -65,7 +65,7 @@ def configure(lib):
     lib.oracle_attention_gqa.restype = ctypes.c_int
     lib.oracle_attention_gqa.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int]
@@ -89,7 +89,7 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
 
 
 class OracleResult:
-    """Per-row outputs of the oracle, each shaped [nrows, 128] (float64)."""
+    """Per-row outputs of the oracle, each shaped [nrows, D] (float64)."""
 
     def __init__(self, rows, o_exact, sigma, o_method, sigma_method, lse=None):
         self.rows = rows
@@ -108,8 +108,9 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
               p_round: str = "rtne") -> OracleResult:
     """Evaluate the oracle.
 
-    q, k, v: uint16 arrays holding bf16 bit patterns, shaped [B,S,H,128]
-    (bshd) or [B,H,S,128] (bhsd); k and v may have fewer heads than q
+    q, k, v: uint16 arrays holding bf16 bit patterns, shaped [B,S,H,D]
+    (bshd) or [B,H,S,D] (bhsd), D the head dimension (1 .. 256, usually 128
+    or 64); k and v may have fewer heads than q
     (grouped-query attention, query head h reads key/value head
     h // (Hq // Hkv)).  causal: bottom-right aligned causal mask (query i sees
     keys j <= i + Skv - Sq; rows seeing no key are zero).  rows: optional
@@ -121,8 +122,9 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
     q = np.ascontiguousarray(q, dtype=np.uint16)
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
-    if q.ndim != 4 or q.shape[-1] != 128 or k.shape != v.shape or k.ndim != 4:
-        raise ValueError("q, k, v must be [.., .., .., 128] with k.shape == v.shape")
+    D = q.shape[-1] if q.ndim == 4 else 0
+    if q.ndim != 4 or not 1 <= D <= 256 or k.shape != v.shape or k.ndim != 4 or k.shape[-1] != D:
+        raise ValueError("q, k, v must be [.., .., .., D] (1 <= D <= 256) with k.shape == v.shape")
     if layout == "bshd":
         B, Sq, H, _ = q.shape
         Skv, Hkv = k.shape[1], k.shape[2]
@@ -143,13 +145,13 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
         if nrows and (rows_arr.min() < 0 or rows_arr.max() >= B * H * Sq):
             raise ValueError("row id out of range")
         rows_ptr = rows_arr.ctypes.data
-    o = np.empty((nrows, 128), np.float64)
-    sg = np.empty((nrows, 128), np.float64)
-    om = np.empty((nrows, 128), np.float64) if method else None
-    sm = np.empty((nrows, 128), np.float64) if method else None
+    o = np.empty((nrows, D), np.float64)
+    sg = np.empty((nrows, D), np.float64)
+    om = np.empty((nrows, D), np.float64) if method else None
+    sm = np.empty((nrows, D), np.float64) if method else None
     ls = np.empty(nrows, np.float64)
     rc = lib.oracle_attention_gqa(q.ctypes.data, k.ctypes.data, v.ctypes.data, LAYOUTS[layout],
-                                  B, H, Hkv, Sq, Skv, ctypes.c_float(scale), 1 if causal else 0,
+                                  B, H, Hkv, Sq, Skv, D, ctypes.c_float(scale), 1 if causal else 0,
                                   rows_ptr, nrows, o.ctypes.data, sg.ctypes.data,
                                   om.ctypes.data if method else None,
                                   sm.ctypes.data if method else None, ls.ctypes.data,

@@ -11,7 +11,9 @@
  *   - The operation is the fused softmax(Q K^T * scale) V of a transformer
  *     attention layer, bf16 inputs, head dimension 128, BSHD or BHSD layout,
  *     any query / key length (MoonMath AI MI300X attention article, opening
- *     paragraphs describing the kernel and its interface).
+ *     paragraphs describing the kernel and its interface).  Head dimension
+ *     64, the other size the HipKittens summary's kernel suite covers, is a
+ *     parameter here (any D from 1 to 256).
  *   - The output is bf16 and the rounding to bf16 is selectable among
  *     round-to-nearest-even, round-to-nearest-ties-away and round-toward-zero
  *     (same article, paragraph on limitations and numerics, and the
@@ -74,7 +76,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_D 128
+#define ORACLE_DMAX 256   /* largest head dimension */
 
 enum { OR_LAYOUT_BSHD = 0, OR_LAYOUT_BHSD = 1 };
 enum { OR_RTNE = 0, OR_RTNA = 1, OR_RTZ = 2 };
@@ -144,10 +146,10 @@ void oracle_round_bf16_array(const double* x, uint16_t* out, int64_t n, int mode
     for (int64_t i = 0; i < n; i++) out[i] = oracle_round_bf16(x[i], mode);
 }
 
-/* Element offset of row (b, h, i) of a [*, 128] tensor in the given layout. */
-static int64_t row_offset(int layout, int64_t b, int64_t h, int64_t i, int64_t H, int64_t S) {
-    if (layout == OR_LAYOUT_BSHD) return ((b * S + i) * H + h) * ORACLE_D;
-    return ((b * H + h) * S + i) * ORACLE_D;
+/* Element offset of row (b, h, i) of a [*, D] tensor in the given layout. */
+static int64_t row_offset(int layout, int64_t b, int64_t h, int64_t i, int64_t H, int64_t S, int64_t D) {
+    if (layout == OR_LAYOUT_BSHD) return ((b * S + i) * H + h) * D;
+    return ((b * H + h) * S + i) * D;
 }
 
 /* Round to bf16 in the given mode and back, for the method companion's probabilities. */
@@ -155,13 +157,14 @@ static double round_trip_bf16(double x, int mode) { return bf16_to_double(oracle
 
 /*
  * Evaluate rows of attention.
- *   q         : bf16 bit patterns [B,Sq,Hq,128] or [B,Hq,Sq,128];
- *   k, v      : [B,Skv,Hkv,128] or [B,Hkv,Skv,128]; Hq a multiple of Hkv.
+ *   q         : bf16 bit patterns [B,Sq,Hq,D] or [B,Hq,Sq,D];
+ *   k, v      : [B,Skv,Hkv,D] or [B,Hkv,Skv,D]; Hq a multiple of Hkv;
+ *               D the head dimension (1 .. 256).
  *   causal    : 0 = every key, 1 = bottom-right aligned causal mask.
  *   rows      : flat query-row ids r = (b*Hq + h)*Sq + i, or NULL for all
  *               B*Hq*Sq rows in that order; nrows is the count.
- *   o_exact, sigma            : [nrows, 128] doubles (required).
- *   o_method, sigma_method    : [nrows, 128] doubles, or NULL to skip.
+ *   o_exact, sigma            : [nrows, D] doubles (required).
+ *   o_method, sigma_method    : [nrows, D] doubles, or NULL to skip.
  *   lse                       : [nrows] doubles, or NULL to skip.
  *   l_from_rounded            : method companion's normaliser (see header).
  *   p_round                   : OR_RTNE / OR_RTNA / OR_RTZ for the method
@@ -169,7 +172,7 @@ static double round_trip_bf16(double x, int mode) { return bf16_to_double(oracle
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
 int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                         int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
                          float scale, int causal, const int64_t* rows, int64_t nrows,
                          double* o_exact, double* sigma,
                          double* o_method, double* sigma_method, double* lse,
@@ -177,7 +180,7 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
     if (!q || !k || !v || !o_exact || !sigma) return -1;
     if (p_round != OR_RTNE && p_round != OR_RTNA && p_round != OR_RTZ) return -1;
     if (layout != OR_LAYOUT_BSHD && layout != OR_LAYOUT_BHSD) return -1;
-    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return -1;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1 || D > ORACLE_DMAX) return -1;
     if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return -1;
     const int64_t H = Hq, group = Hq / Hkv;
     if (rows == NULL) nrows = B * H * Sq;
@@ -194,7 +197,7 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
 #pragma omp parallel
     {
         double* s = (double*)malloc(sizeof(double) * (size_t)Skv);
-        double* kk = (double*)malloc(sizeof(double) * ORACLE_D);
+        double* kk = (double*)malloc(sizeof(double) * D);
         if (!s || !kk) {
 #pragma omp atomic write
             failed = 1;
@@ -211,41 +214,41 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
                 n_keys = i + (Skv - Sq) + 1;
                 if (n_keys > Skv) n_keys = Skv;
             }
-            double* oe = o_exact + t * ORACLE_D;
-            double* sg = sigma + t * ORACLE_D;
+            double* oe = o_exact + t * D;
+            double* sg = sigma + t * D;
             if (n_keys <= 0) {                            /* no admissible key: zeros */
                 if (lse) lse[t] = -INFINITY;
-                for (int d = 0; d < ORACLE_D; d++) {
+                for (int d = 0; d < D; d++) {
                     oe[d] = 0.0;
                     sg[d] = 0.0;
-                    if (o_method) o_method[t * ORACLE_D + d] = 0.0;
-                    if (o_method && sigma_method) sigma_method[t * ORACLE_D + d] = 0.0;
+                    if (o_method) o_method[t * D + d] = 0.0;
+                    if (o_method && sigma_method) sigma_method[t * D + d] = 0.0;
                 }
                 continue;
             }
-            double qq[ORACLE_D];
-            const uint16_t* qp = q + row_offset(layout, b, h, i, H, Sq);
-            for (int d = 0; d < ORACLE_D; d++) qq[d] = bf16_to_double(qp[d]);
+            double qq[ORACLE_DMAX];
+            const uint16_t* qp = q + row_offset(layout, b, h, i, H, Sq, D);
+            for (int d = 0; d < D; d++) qq[d] = bf16_to_double(qp[d]);
 
             /* pass 1: scores and their maximum (NaN propagates into m) */
             double m = -INFINITY;
             for (int64_t j = 0; j < n_keys; j++) {
-                const uint16_t* kp = k + row_offset(layout, b, hk, j, Hkv, Skv);
-                for (int d = 0; d < ORACLE_D; d++) kk[d] = bf16_to_double(kp[d]);
+                const uint16_t* kp = k + row_offset(layout, b, hk, j, Hkv, Skv, D);
+                for (int d = 0; d < D; d++) kk[d] = bf16_to_double(kp[d]);
                 double acc = 0.0;
-                for (int d = 0; d < ORACLE_D; d++) acc += qq[d] * kk[d];
+                for (int d = 0; d < D; d++) acc += qq[d] * kk[d];
                 s[j] = sc * acc;
                 if (!isnan(m) && (isnan(s[j]) || s[j] > m)) m = s[j];
             }
 
             /* pass 2: weights, normaliser, weighted sums */
-            double num[ORACLE_D], sq[ORACLE_D], numm[ORACLE_D], sqm[ORACLE_D];
-            for (int d = 0; d < ORACLE_D; d++) { num[d] = 0.0; sq[d] = 0.0; numm[d] = 0.0; sqm[d] = 0.0; }
+            double num[ORACLE_DMAX], sq[ORACLE_DMAX], numm[ORACLE_DMAX], sqm[ORACLE_DMAX];
+            for (int d = 0; d < D; d++) { num[d] = 0.0; sq[d] = 0.0; numm[d] = 0.0; sqm[d] = 0.0; }
             double l = 0.0, lm = 0.0, lm_rounded = 0.0;
             double xmax = m * log2e;
             double M = ceil(xmax);
             for (int64_t j = 0; j < n_keys; j++) {
-                const uint16_t* vp = v + row_offset(layout, b, hk, j, Hkv, Skv);
+                const uint16_t* vp = v + row_offset(layout, b, hk, j, Hkv, Skv, D);
                 double p = exp(s[j] - m);
                 l += p;
                 double pt = 0.0, pm = 0.0;
@@ -255,7 +258,7 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
                     lm += pm;
                     lm_rounded += pt;
                 }
-                for (int d = 0; d < ORACLE_D; d++) {
+                for (int d = 0; d < D; d++) {
                     double vv = bf16_to_double(vp[d]);
                     num[d] += p * vv;
                     sq[d] += (p * vv) * (p * vv);
@@ -265,16 +268,16 @@ int oracle_attention_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v
                     }
                 }
             }
-            for (int d = 0; d < ORACLE_D; d++) {
+            for (int d = 0; d < D; d++) {
                 oe[d] = num[d] / l;
                 sg[d] = sqrt(sq[d]) / l;
             }
             if (lse) lse[t] = m + log(l);
             if (o_method) {
                 double L = l_from_rounded ? lm_rounded : lm;
-                double* om = o_method + t * ORACLE_D;
-                double* sm = sigma_method ? sigma_method + t * ORACLE_D : NULL;
-                for (int d = 0; d < ORACLE_D; d++) {
+                double* om = o_method + t * D;
+                double* sm = sigma_method ? sigma_method + t * D : NULL;
+                for (int d = 0; d < D; d++) {
                     om[d] = numm[d] / L;
                     if (sm) sm[d] = sqrt(sqm[d]) / L;
                 }
@@ -293,6 +296,6 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      double* o_exact, double* sigma,
                      double* o_method, double* sigma_method,
                      int l_from_rounded, int nthreads) {
-    return oracle_attention_gqa(q, k, v, layout, B, H, H, Sq, Skv, scale, 0, rows, nrows,
+    return oracle_attention_gqa(q, k, v, layout, B, H, H, Sq, Skv, 128, scale, 0, rows, nrows,
                                 o_exact, sigma, o_method, sigma_method, NULL, l_from_rounded, OR_RTNE, nthreads);
 }

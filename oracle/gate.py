@@ -39,8 +39,8 @@ def ordinal(bits) -> np.ndarray:
 def compare(gpu_bits, o_exact, sigma, mode: str, floor_factor: float = 2.0) -> dict:
     """Gate statistics for one output tensor.
 
-    gpu_bits: uint16 [n, 128] bf16 patterns from the device.
-    o_exact, sigma: float64 [n, 128] from the oracle (same rows).
+    gpu_bits: uint16 [n, D] bf16 patterns from the device.
+    o_exact, sigma: float64 [n, D] from the oracle (same rows).
     """
     g_bits = np.asarray(gpu_bits, dtype=np.uint16)
     g = bf16_bits_to_f64(g_bits)

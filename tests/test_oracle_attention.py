@@ -390,3 +390,49 @@ def test_lse_closed_forms():
     q3, k3, v3 = wl.random_qkv("bhsd", 1, 1, 9, 4, 54)
     res = run(wl.bits(q3), wl.bits(k3), wl.bits(v3), causal=True)
     assert np.all(np.isneginf(res.lse[:5])) and np.all(np.isfinite(res.lse[5:]))
+
+
+# ------------------------------------------------------- head dimension 64
+# The HipKittens summary's kernel suite lists attention forward for head
+# dimensions 64 and 128; the oracle takes D as a parameter and is pinned at
+# D = 64 like at 128: the library routine in float64, brute force in decimal,
+# and the identity that zero-padding Q, K, V to 128 dimensions changes no score.
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("causal,hkv", [(False, 3), (True, 1)])
+def test_d64_matches_torch_sdpa_float64(layout, causal, hkv):
+    B, H, sq, skv = 2, 3, 37, 53
+    q, k, v = wl.random_qkv(layout, B, H, sq, skv, 81, k_factor=2.0, Hkv=hkv, D=64)
+    scale = float(np.float32(0.125))
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=scale, causal=causal)
+    assert res.o_exact.shape == (B * H * sq, 64)
+    perm = (0, 2, 1, 3) if layout == "bshd" else (0, 1, 2, 3)
+    Q = q.to(torch.float64).permute(*perm)
+    K = torch.repeat_interleave(k.to(torch.float64).permute(*perm), H // hkv, dim=1)
+    V = torch.repeat_interleave(v.to(torch.float64).permute(*perm), H // hkv, dim=1)
+    mask = causal_mask(sq, skv) if causal else None
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)
+    assert np.allclose(res.o_exact, ref.reshape(-1, 64).numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("skv", [1, 3])
+def test_d64_bruteforce_decimal(skv):
+    q, k, v = wl.random_qkv("bhsd", 1, 1, 2, skv, 82, D=64)
+    scale = float(np.float32(0.125))
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bhsd", scale=scale)
+    Q = f64(wl.bits(q))[0, 0]; K = f64(wl.bits(k))[0, 0]; V = f64(wl.bits(v))[0, 0]
+    for i in range(2):
+        o_ref, s_ref = decimal_attention_row(Q[i], K, V, scale)
+        scale_o = np.maximum(np.abs(o_ref), s_ref) + 1e-300
+        assert np.all(np.abs(res.o_exact[i] - o_ref) <= 1e-13 * scale_o + 1e-15 * np.abs(V).max())
+        assert np.allclose(res.sigma[i], s_ref, rtol=1e-12, atol=0)
+
+
+def test_d64_equals_d128_zero_padded():
+    q, k, v = wl.random_qkv("bshd", 1, 2, 40, 70, 83, k_factor=2.0, D=64)
+    pad = lambda t: torch.nn.functional.pad(t, (0, 64))
+    scale = float(np.float32(0.125))
+    r64 = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bshd", scale=scale, method=True)
+    r128 = run(wl.bits(pad(q)), wl.bits(pad(k)), wl.bits(pad(v)), layout="bshd", scale=scale, method=True)
+    assert np.array_equal(r128.o_exact[:, :64], r64.o_exact) and np.all(r128.o_exact[:, 64:] == 0)
+    assert np.array_equal(r128.sigma[:, :64], r64.sigma)
+    assert np.array_equal(r128.o_method[:, :64], r64.o_method)

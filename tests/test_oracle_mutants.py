@@ -19,12 +19,13 @@ from tests import test_oracle_round as R
 SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
 MUTANTS = {
-    "qk_index_shift": ("acc += qq[d] * kk[d];", "acc += qq[d] * kk[(d + 1) % ORACLE_D];"),
+    "qk_index_shift": ("acc += qq[d] * kk[d];", "acc += qq[d] * kk[(d + 1) % D];"),
     "exp_sign": ("double p = exp(s[j] - m);", "double p = exp(m - s[j]);"),
     "no_normalise": ("oe[d] = num[d] / l;", "oe[d] = num[d];"),
     "no_scale": ("s[j] = sc * acc;", "s[j] = acc;"),
-    "bshd_offset": ("if (layout == OR_LAYOUT_BSHD) return ((b * S + i) * H + h) * ORACLE_D;",
-                    "if (layout == OR_LAYOUT_BSHD) return ((b * H + h) * S + i) * ORACLE_D;"),
+    "bshd_offset": ("if (layout == OR_LAYOUT_BSHD) return ((b * S + i) * H + h) * D;",
+                    "if (layout == OR_LAYOUT_BSHD) return ((b * H + h) * S + i) * D;"),
+    "row_stride_128": ("    return ((b * H + h) * S + i) * D;", "    return ((b * H + h) * S + i) * 128;"),
     "value_from_key": ("const uint16_t* vp = v + row_offset", "const uint16_t* vp = k + row_offset"),
     "sigma_not_squared": ("sq[d] += (p * vv) * (p * vv);", "sq[d] += (p * vv);"),
     "rtne_tie_up": ("if (fr > 0.5) m = fl + 1.0;", "if (fr >= 0.5) m = fl + 1.0;"),
@@ -71,6 +72,9 @@ def pins():
     out.append(("lse_closed", A.test_lse_closed_forms))
     for mode in ("rtna", "rtz"):
         out.append((f"weights_{mode}", lambda m=mode: A.test_method_weights_rounded_in_mode(m)))
+    out.append(("d64_sdpa", lambda: A.test_d64_matches_torch_sdpa_float64("bhsd", False, 3)))
+    out.append(("d64_brute", lambda: A.test_d64_bruteforce_decimal(3)))
+    out.append(("d64_pad", A.test_d64_equals_d128_zero_padded))
     return out
 
 
