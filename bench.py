@@ -51,7 +51,7 @@ def measured_traffic(workload_name: str):
 
 def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
     import torch
-    from bf16_attention_forward_amd import attn_fwd_bf16, attn_fwd_bf16_gqa
+    from bf16_attention_forward_amd import attn_fwd_bf16, attn_fwd_bf16_gqa, attn_fwd_bf16_hd
     from bf16_attention_forward_amd import workloads as wl
 
     q, k, v = wl.make_inputs(w)
@@ -61,7 +61,10 @@ def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        if w.causal or w.Hkv:
+        if w.D != 128:
+            attn_fwd_bf16_hd(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, causal=w.causal,
+                             scale=w.scale, round_weights=round_weights)
+        elif w.causal or w.Hkv:
             attn_fwd_bf16_gqa(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, causal=w.causal,
                               round_weights=round_weights)
         else:
@@ -144,7 +147,7 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for num in (3, 4, 5, 6, 7):
+        for num in (3, 4, 5, 6, 7, 8, 9):
             ww = wl.WORKLOADS[num]
             for mode in ww.modes[:1]:
                 rr = time_workload(ww, mode, steps=20, warmup=10)

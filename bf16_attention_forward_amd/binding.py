@@ -23,7 +23,9 @@ ARGUMENT_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -11}
 HEAD_DIM = 128
 
 # names of every entry point the header declares
-EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_status_string",
+           "attn_version")
+HEAD_DIMS = (128, 64)
 
 _lib = None
 
@@ -53,6 +55,9 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16_gqa.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_bf16_gqa.restype = ctypes.c_int
+    lib.attn_fwd_bf16_hd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_fwd_bf16_hd.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -77,7 +82,7 @@ def _raise(status: int):
     raise AttnError(status, msg)
 
 
-def _dims(q: torch.Tensor, k: torch.Tensor, layout: str, grouped: bool = False):
+def _dims(q: torch.Tensor, k: torch.Tensor, layout: str, grouped: bool = False, head_dims=(HEAD_DIM,)):
     """(B, Hq, Hkv, Sq, Skv) from the tensor shapes."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be 4-D")
@@ -89,8 +94,8 @@ def _dims(q: torch.Tensor, k: torch.Tensor, layout: str, grouped: bool = False):
         Bk, Hk, Skv, Dk = k.shape
     else:
         raise ValueError(f"layout must be 'bshd' or 'bhsd', got {layout!r}")
-    if D != HEAD_DIM or Dk != HEAD_DIM:
-        raise ValueError("head dimension must be 128")
+    if D not in head_dims or Dk != D:
+        raise ValueError(f"head dimension must be one of {head_dims} (the same for q and k)")
     if Bk != B:
         raise ValueError("q and k/v must share the batch count")
     if grouped:
@@ -180,6 +185,34 @@ def attn_fwd_bf16_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
                                    lse.data_ptr() if lse is not None else None,
                                    ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, sc, 1 if causal else 0,
                                    _mode(round_mode, round_weights), st.cuda_stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return (o, lse) if lse is not None else o
+
+
+def attn_fwd_bf16_hd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
+                     layout: str = "bshd", scale: float | None = None, causal: bool = False,
+                     round_mode: str = "rtne", stream: torch.cuda.Stream | None = None,
+                     lse: torch.Tensor | None = None, return_lse: bool = False,
+                     round_weights: bool = False):
+    """attn_fwd_bf16_gqa for head dimension 128 or 64 (attn_fwd_bf16_hd), taken
+    from the tensors' last axis; scale defaults to 1/sqrt(head_dim)."""
+    lib = load_library()
+    o = _check_tensors(q, k, v, o)
+    B, Hq, Hkv, Sq, Skv = _dims(q, k, layout, grouped=True, head_dims=HEAD_DIMS)
+    hd = int(q.shape[-1])
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq)
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 device tensor shaped [B, Hq, Sq]")
+    sc = float(1.0 / math.sqrt(hd)) if scale is None else float(scale)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_bf16_hd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None,
+                                  ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, hd, sc, 1 if causal else 0,
+                                  _mode(round_mode, round_weights), st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (o, lse) if lse is not None else o

@@ -19,7 +19,6 @@
 
 namespace {
 
-constexpr int kHeadDim = 128;
 constexpr int kKeyTile = 64;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxDevices = 64;
@@ -102,7 +101,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-extern "C" int attn_version(void) { return 10200; }
+extern "C" int attn_version(void) { return 10300; }
 
 extern "C" const char* attn_status_string(int status) {
     switch (status) {
@@ -110,7 +109,7 @@ extern "C" const char* attn_status_string(int status) {
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_LAYOUT: return "layout must be ATTN_LAYOUT_BSHD or ATTN_LAYOUT_BHSD";
         case ATTN_ERR_ROUND_MODE: return "round_mode must be ATTN_ROUND_RTNE, _RTNA or _RTZ, optionally | ATTN_ROUND_WEIGHTS";
-        case ATTN_ERR_SHAPE: return "B, H (Hq, Hkv), Sq and Skv must be >= 1, Hq a multiple of Hkv, and the sizes must fit the kernel's index range";
+        case ATTN_ERR_SHAPE: return "B, H (Hq, Hkv), Sq and Skv must be >= 1, Hq a multiple of Hkv, head_dim 128 or 64, and the sizes must fit the kernel's index range";
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned";
         case ATTN_ERR_ALIAS: return "o must not overlap q, k or v";
@@ -126,7 +125,7 @@ namespace {
 
 // Shared by every entry point: H = query heads, Hkv = key/value heads.
 int run_attention(const void* q, const void* k, const void* v, void* o, float* lse,
-                  int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv,
+                  int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t head_dim,
                   float scale, int causal, int round_mode, void* stream,
                   int kv_splits, int block_order) {
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
@@ -135,6 +134,8 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     if (out_mode != ATTN_ROUND_RTNE && out_mode != ATTN_ROUND_RTNA && out_mode != ATTN_ROUND_RTZ)
         return ATTN_ERR_ROUND_MODE;
     if (B < 1 || H < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
+    if (head_dim != 128 && head_dim != 64) return ATTN_ERR_SHAPE;
+    const int64_t kHeadDim = head_dim;
     if (H % Hkv != 0) return ATTN_ERR_SHAPE;
     // index-range limits of the kernels: 32-bit counts and per-head buffer extents
     const int64_t lim31 = (int64_t)1 << 31;
@@ -190,6 +191,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.n_items = (int)(B * H * n_qtiles);
     p.round_mode = out_mode;
     p.p_mode = (round_mode & ATTN_ROUND_WEIGHTS) ? out_mode : ATTN_ROUND_RTNE;
+    p.head_dim = (int)head_dim;
     p.c = (float)((double)scale * 1.4426950408889634073599246810018921);
 
     // ---- plan the key-range split
@@ -247,14 +249,21 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
                                 int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                                 float scale, int round_mode, void* stream,
                                 int kv_splits, int block_order) {
-    return run_attention(q, k, v, o, nullptr, layout, B, H, H, Sq, Skv, scale, 0, round_mode, stream,
+    return run_attention(q, k, v, o, nullptr, layout, B, H, H, Sq, Skv, 128, scale, 0, round_mode, stream,
                          kv_splits, block_order);
 }
 
 extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                  float scale, int causal, int round_mode, void* stream) {
-    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, scale, causal, round_mode, stream, 0, 0);
+    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, 128, scale, causal, round_mode, stream, 0, 0);
+}
+
+extern "C" int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                int64_t head_dim, float scale, int causal, int round_mode, void* stream) {
+    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, head_dim, scale, causal, round_mode,
+                         stream, 0, 0);
 }
 
 extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,

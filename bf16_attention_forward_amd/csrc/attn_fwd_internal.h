@@ -43,6 +43,7 @@ struct AttnParams {
     int n_blocks;      // n_full + (n_items - n_full) * kv_splits
     int block_order;   // ORDER_NAIVE or ORDER_XCD
     int round_mode;
+    int head_dim;      // 128 or 64
     int p_mode;        // rounding of the in-loop bf16 weights (ROUND_RTNE unless asked otherwise)
     float c;           // fp32(scale * log2(e))
 };

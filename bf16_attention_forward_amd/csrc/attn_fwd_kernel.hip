@@ -79,13 +79,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int D = 128;          // head dimension
 constexpr int BN = 64;          // keys per K/V tile
 constexpr int NW = KERNEL_NW;   // waves per work-group
 constexpr int NQB = KERNEL_NQB; // 16-row query blocks per wave
 constexpr int BM = KERNEL_BM;   // query rows per work item
-constexpr int ROW_BYTES = D * 2;
-constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float WEIGHT_LIMIT = 65536.0f;    // a lane's tile sum of weights above this triggers a new offset
 
@@ -128,16 +125,21 @@ __device__ __forceinline__ float div_corrected(float o, float l, float r) {
     return (q1 == q1) ? q1 : q0;
 }
 
-// LDS layout of a K or V tile: 64 rows of 256 bytes (16 chunks of 16 bytes),
-// chunk positions XOR-swizzled per row so the reads below hit distinct banks.
+// LDS layout of a K or V tile: 64 rows of HD*2 bytes (16-byte chunks), chunk
+// positions XOR-swizzled per row so the reads below hit distinct banks (the
+// LDS serves 256 bytes, 16 chunk positions, per pass).
 // K is read with ds_read_b128: the 16 lanes of a lane group read 16
-// consecutive rows at one logical chunk, so chunk c of row r sits at c ^ (r & 15).
-// V is read with ds_read_b64_tr_b16: a read covers 16 consecutive rows, 32
-// bytes (a chunk pair) each, so the pair index moves with r & 7.  Both
-// swizzles depend only on bits of the row that are fixed per lane, which lets
-// every fragment address be a per-lane base plus an immediate offset.
-__device__ __forceinline__ int swz_k(int row) { return row & 15; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 7) << 1; }
+// consecutive rows at one logical chunk.  With 256-byte rows (HD = 128)
+// chunk c of row r sits at c ^ (r & 15); with 128-byte rows (HD = 64) two
+// rows share a pass, so c ^ ((r >> 1) & 7).
+// V is read with ds_read_b64_tr_b16: per 16 lanes, 4 consecutive rows, 32
+// bytes (a chunk pair) each.  With 256-byte rows the pair index moves with
+// r & 7; with 128-byte rows (8 rows per 32 lanes, two per pass position)
+// with (r >> 1) & 3.  Every swizzle depends only on bits of the row that are
+// fixed per lane, which lets each fragment address be a per-lane base plus
+// an immediate offset.
+template <int HD> __device__ __forceinline__ int swz_k(int row) { return HD == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int HD> __device__ __forceinline__ int swz_v(int row) { return HD == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1); }
 
 __device__ __forceinline__ int map_block(int bid, int n, int order) {
     if (order != ORDER_XCD) return bid;
@@ -159,10 +161,16 @@ __device__ __forceinline__ void lds_barrier() {
 
 // 8 waves, each owning 32 query rows of the work item; see the file header
 // for the per-tile schedule.
-template <bool CPOS, bool CAUSAL, int PMODE>
+template <int HD, bool CPOS, bool CAUSAL, int PMODE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
-    constexpr int NTHREADS = NW * 64;
+    static_assert(HD == 128 || HD == 64, "head dimension 128 or 64");
+    constexpr int ROW_BYTES = HD * 2;
+    constexpr int TILE_BYTES = BN * ROW_BYTES;   // 16 KiB (HD = 128) or 8 KiB
+    constexpr int NKS = HD / 32;                 // k-steps of S^T = K Q^T
+    constexpr int NDB = HD / 16;                 // 16-dim blocks of O
+    constexpr int SS = 4 * NKS;                  // fragment steps of S^T (4 key blocks x NKS)
+    constexpr int ST = SS + 2 * NDB;             // all steps of a tile (+ NDB x 2 k-steps of O^T)
     // Four distinct LDS objects (K and V, two buffers each): with the buffer
     // choice a compile-time constant the compiler can tell that a DMA into one
     // buffer does not alias reads of another and does not wait for it.
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
             const int row = qt * BM + wave * 16 * NQB + qb * 16 + j;
             if (row >= p.Sq) continue;
 #pragma unroll
-            for (int db = 0; db < 8; db++) *(uint2*)(obase + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
+            for (int db = 0; db < NDB; db++) *(uint2*)(obase + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
         }
         return;
     }
@@ -244,20 +252,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
 
-    // The first four waves issue all K/V DMA: tile rows 16*r + 4*w + g (w = wave,
-    // r = round 0..3), chunk j, land at LDS slot (4*r + w)*64 + lane, i.e. row
-    // by row in order; rows 16 apart share the swizzle, so one per-lane source
-    // offset serves all four rounds.  The DMA is issued with inline assembly:
+    // The first four waves issue all K/V DMA: lane l of wave w in round r
+    // lands at LDS slot (4*r + w)*64 + l, i.e. row by row in order: row
+    // RPR*r + RPW*w + l / CPR, chunk l % CPR (CPR chunks per row, RPW rows per
+    // wave, RPR rows per round: 16, 4, 16 for HD = 128 and 8, 8, 32 for 64);
+    // rows RPR apart share the swizzle, so one per-lane source offset serves
+    // every round.  The DMA is issued with inline assembly:
     // the compiler then does not track it and inserts no vmcnt wait before
     // LDS reads of other buffers (its alias tracking is lost at loop heads);
     // the issuing waves wait for their DMA explicitly (vmcnt(0)) before the
     // barrier that publishes a tile.
     const bool late = NW == 8 && wave >= 4;   // second wave of each SIMD (see the key loop)
-    constexpr int DMA_ROUNDS = TILE_BYTES / 16 / (4 * 64);
-    static_assert(DMA_ROUNDS == 4, "four waves move a tile in four rounds of 16 rows");
-    const int dma_row = (wave & 3) * 4 + g;
-    const int dma_off_k = dma_row * kv_row_bytes + ((j ^ swz_k(dma_row)) << 4);
-    const int dma_off_v = dma_row * kv_row_bytes + ((j ^ swz_v(dma_row)) << 4);
+    constexpr int CPR = ROW_BYTES / 16, RPW = 64 / CPR, RPR = 4 * RPW;
+    constexpr int DMA_ROUNDS = BN / RPR;
+    static_assert(DMA_ROUNDS * RPR == BN && RPR % 16 == 0, "rounds of whole swizzle periods");
+    const int dma_row = (wave & 3) * RPW + lane / CPR, dma_chunk = lane % CPR;
+    const int dma_off_k = dma_row * kv_row_bytes + ((dma_chunk ^ swz_k<HD>(dma_row)) << 4);
+    const int dma_off_v = dma_row * kv_row_bytes + ((dma_chunk ^ swz_v<HD>(dma_row)) << 4);
     const uint64_t ka = (uint64_t)(uintptr_t)kbase, va = (uint64_t)(uintptr_t)vbase;
     const i32x4 krs4 = {(int)(uint32_t)ka, (int)((ka >> 32) & 0xffffu), (int)nrec, 0x00020000};
     const i32x4 vrs4 = {(int)(uint32_t)va, (int)((va >> 32) & 0xffffu), (int)nrec, 0x00020000};
@@ -268,10 +279,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     };
     // round r of the K (or V) tile that starts at key k0
     auto dma_k = [&](int r, int k0, uint8_t* dst) {
-        dma16(krs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 + 16 * r) * kv_row_bytes);
+        dma16(krs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 + RPR * r) * kv_row_bytes);
     };
     auto dma_v = [&](int r, int k0, uint8_t* dst) {
-        dma16(vrs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 + 16 * r) * kv_row_bytes);
+        dma16(vrs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 + RPR * r) * kv_row_bytes);
     };
     if (!late) {
 #pragma unroll
@@ -282,17 +293,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     // 16*qb + j of this wave, dims 32*ks + 8*g .. +7, for the whole key loop.
     // Rows past Sq are clamped (their results are never stored).
     const int qrow0 = qt * BM + wave * 16 * NQB;   // first query row of this wave
-    bf16x8 qf[NQB][4];
+    bf16x8 qf[NQB][NKS];
 #pragma unroll
     for (int qb = 0; qb < NQB; qb++) {
         const int row = min(qrow0 + qb * 16 + j, p.Sq - 1);
         const uint16_t* src = qbase + (int64_t)row * p.q_row + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) qf[qb][ks] = *(const bf16x8*)(src + 32 * ks);
+        for (int ks = 0; ks < NKS; ks++) qf[qb][ks] = *(const bf16x8*)(src + 32 * ks);
     }
-    f32x4 o_acc[8][NQB];
+    f32x4 o_acc[NDB][NQB];
 #pragma unroll
-    for (int db = 0; db < 8; db++)
+    for (int db = 0; db < NDB; db++)
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float moff[NQB], l_run[NQB];    // power-of-two offset of the weights (integer-valued), row-sum partials
@@ -304,32 +315,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     bf16x8 pf[NQB][2];
     const float c = p.c;
 
-    // ---- MFMA phase: steps [S0, S1) of a fixed sequence of 32 fragment steps.
-    // Steps 0..15 compute S^T = K Q^T: step 4*ks + kb reads the K fragment of key
-    // block kb, k-step ks (one ds_read_b128: lane (g, j) gets row 16*kb + j,
+    // ---- MFMA phase: steps [S0, S1) of a fixed sequence of ST fragment steps.
+    // Steps 0..SS-1 compute S^T = K Q^T: step 4*ks + kb reads the K fragment of
+    // key block kb, k-step ks (one ds_read_b128: lane (g, j) gets row 16*kb + j,
     // dims 32*ks + 8*g .. +7) and feeds NQB MFMAs; k-steps are the outer index
     // so consecutive MFMAs hit different accumulators.  The score fragment of
     // lane (g, j) then holds query j and keys 16*kb + 4*g + r, r = 0..3.
-    // Steps 16..31 compute O^T += V^T P^T: step 16 + 8*ks + db reads the V^T
-    // fragment of dim block db for the 32 keys of step ks with two
+    // Steps SS..ST-1 compute O^T += V^T P^T: step SS + NDB*ks + db reads the
+    // V^T fragment of dim block db for the 32 keys of step ks with two
     // ds_read_b64_tr_b16 (rows 32*ks + 16*hf + 4*g + r), matching the keys
     // of P's elements 4*hf + r.  Fragment reads run PF steps ahead of their
     // MFMAs so LDS latency hides behind the matrix core.
-    int k_addr[4], v_addr[8];   // per-lane byte offsets within a tile
+    int k_addr[NKS], v_addr[NDB];   // per-lane byte offsets within a tile
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) k_addr[ks] = j * ROW_BYTES + ((((4 * ks + g) ^ swz_k(j))) << 4);
+    for (int ks = 0; ks < NKS; ks++) k_addr[ks] = j * ROW_BYTES + ((((4 * ks + g) ^ swz_k<HD>(j))) << 4);
 #pragma unroll
-    for (int db = 0; db < 8; db++) {
+    for (int db = 0; db < NDB; db++) {
         const int row = 4 * g + (j >> 2);                    // + 32*ks + 16*hf (multiples of 8)
-        const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v(row);
+        const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v<HD>(row);
         v_addr[db] = row * ROW_BYTES + (chunk << 4) + ((j & 1) << 3);
     }
     auto read_frag = [&](int st, const uint8_t* kt, const uint8_t* vt) -> bf16x8 {
-        if (st < 16) {
+        if (st < SS) {
             const int kb = st & 3, ks = st >> 2;
             return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(kt + k_addr[ks] + kb * 16 * ROW_BYTES);
         }
-        const int db = (st - 16) & 7, ks = (st - 16) >> 3;
+        const int db = (st - SS) % NDB, ks = (st - SS) / NDB;
         bf16x4 half[2];
 #pragma unroll
         for (int hf = 0; hf < 2; hf++) {
@@ -339,32 +350,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto use_frag = [&](int st, const bf16x8 f) {
-        if (st < 16) {
+        if (st < SS) {
             const int kb = st & 3, ks = st >> 2;
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++)
                 s_acc[kb][qb] = mfma16x16x32(f, qf[qb][ks], ks == 0 ? (CPOS ? bias4[qb] : f32x4{0.f, 0.f, 0.f, 0.f}) : s_acc[kb][qb]);
         } else {
-            const int db = (st - 16) & 7, ks = (st - 16) >> 3;
+            const int db = (st - SS) % NDB, ks = (st - SS) / NDB;
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = mfma16x16x32(f, pf[qb][ks], o_acc[db][qb]);
         }
     };
     constexpr int PF = 4;   // fragment prefetch distance (steps)
     // The DMA of iteration t (K_{t+1} into kn, V_t into vc) is spread over the
-    // issuing waves' MFMA phase, one instruction every (S1 - S0)/8 steps, so
-    // the CU's address unit drains it while the matrix core runs instead of
+    // issuing waves' MFMA phase, one instruction every STRIDE steps, so the
+    // CU's address unit drains it while the matrix core runs instead of
     // stalling a wave that issues all of it at once.
+    constexpr int NDMA = 2 * DMA_ROUNDS;   // instructions per wave and tile
     auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c, int t, uint8_t* kn, uint8_t* vc) {
         constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
-        constexpr int STRIDE = (S1 - S0) / 8;
+        constexpr int STRIDE = (S1 - S0) / NDMA;
+        static_assert(S0 != 0 || STRIDE * NDMA <= S1 - S0, "the DMA fits the phase");
         // Opaque per-lane offsets: stops the compiler from hoisting every
         // buffer x fragment address combination out of the loop (and spilling
-        // them); each phase adds its buffer base to 12 offsets instead.
+        // them); each phase adds its buffer base to these offsets instead.
 #pragma unroll
-        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(k_addr[i]));
+        for (int i = 0; i < NKS; i++) __asm__ volatile("" : "+v"(k_addr[i]));
 #pragma unroll
-        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(v_addr[i]));
+        for (int i = 0; i < NDB; i++) __asm__ volatile("" : "+v"(v_addr[i]));
         bf16x8 fr[PF];
 #pragma unroll
         for (int st = S0; st < S0 + PF && st < S1; st++) fr[(st - S0) % PF] = read_frag(st, kt, vt);
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         for (int st = S0; st < S1; st++) {
             const bf16x8 cur = fr[(st - S0) % PF];
             if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
-            if (S0 == 0 && (st - S0) % STRIDE == 0 && !late) {
+            if (S0 == 0 && (st - S0) % STRIDE == 0 && (st - S0) / STRIDE < NDMA && !late) {
                 const int k = (st - S0) / STRIDE;     // K and V rounds alternate
                 if (k & 1) dma_v(k >> 1, kv_begin + t * BN, vc);
                 else if (t + 1 < T) dma_k(k >> 1, kv_begin + (t + 1) * BN, kn);
@@ -382,21 +395,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         // keep the interleave: the reads of step st+PF, then the MFMAs of step st
 #pragma unroll
         for (int st = S0; st < S0 + PF && st < S1; st++) {
-            if (st < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (st < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
 #pragma unroll
         for (int st = S0; st < S1; st++) {
             if (st + PF < S1) {
-                if (st + PF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (st + PF < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, NQB, 0);
         }
     };
     using C0 = std::integral_constant<int, 0>;
-    using C16 = std::integral_constant<int, 16>;
-    using C32 = std::integral_constant<int, 32>;
+    using CS = std::integral_constant<int, SS>;
+    using CT = std::integral_constant<int, ST>;
 
     // Two weights (>= 0, or NaN) to packed bf16 in the weights' rounding mode.
     // Nearest-even: the hardware conversion.  Ties away: the same conversion
@@ -545,7 +558,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                 l_run[qb] *= alpha[qb];
             }
 #pragma unroll
-            for (int db = 0; db < 8; db++)
+            for (int db = 0; db < NDB; db++)
 #pragma unroll
                 for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] *= alpha[qb];
         }
@@ -583,21 +596,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
         __builtin_amdgcn_s_setprio(0);
         if (late) sync();
         if (decltype(s0c)::value == 0)
-            softmax(t, std::integral_constant<bool, decltype(s1c)::value == 16>{});
+            softmax(t, std::integral_constant<bool, decltype(s1c)::value == SS>{});
         if (!late) sync();
     };
-    iter(0, sk0, sk1, sv0, sv1, C0{}, C16{});
+    iter(0, sk0, sk1, sv0, sv1, C0{}, CS{});
     int t = 1;
     for (; t + 1 < T; t += 2) {
-        iter(t, sk1, sk0, sv1, sv0, C0{}, C32{});
-        iter(t + 1, sk0, sk1, sv0, sv1, C0{}, C32{});
+        iter(t, sk1, sk0, sv1, sv0, C0{}, CT{});
+        iter(t + 1, sk0, sk1, sv0, sv1, C0{}, CT{});
     }
     if (t < T) {
-        iter(t, sk1, sk0, sv1, sv0, C0{}, C32{});
+        iter(t, sk1, sk0, sv1, sv0, C0{}, CT{});
         t++;
     }
-    if (T & 1) iter(T, sk1, sk0, sv1, sv0, C16{}, C32{});
-    else iter(T, sk0, sk1, sv0, sv1, C16{}, C32{});
+    if (T & 1) iter(T, sk1, sk0, sv1, sv0, CS{}, CT{});
+    else iter(T, sk0, sk1, sv0, sv1, CS{}, CT{});
 
     // ---- epilogue: the 4 lanes of a row hold partial row sums
     float l_row[NQB];
@@ -627,7 +640,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
             const bool no_key = CAUSAL && row + p.causal_off < 0;
             uint16_t* dst = obase + (int64_t)row * p.q_row + 4 * g;
 #pragma unroll
-            for (int db = 0; db < 8; db++) {
+            for (int db = 0; db < NDB; db++) {
                 f32x4 ov;
 #pragma unroll
                 for (int r = 0; r < 4; r++) ov[r] = no_key ? 0.f : div_corrected(o_acc[db][qb][r], lr, inv);
@@ -640,16 +653,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
             }
         }
     } else {
-        // partial results: O (unnormalised, fp32) [item][split][BM][128], M and l [item][split][BM]
+        // partial results: O (unnormalised, fp32) [item][split][BM][HD], M and l [item][split][BM]
         // (items counted from n_full)
         const int64_t part = (int64_t)(item - p.n_full) * nsplit + split;
-        float* ow = p.ws_o + part * (int64_t)BM * D;
+        float* ow = p.ws_o + part * (int64_t)BM * HD;
         float* mw = p.ws_ml + part * (int64_t)BM * 2;
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
             const int lrow = wave * 16 * NQB + qb * 16 + j;   // row within the tile
 #pragma unroll
-            for (int db = 0; db < 8; db++) *(f32x4*)(ow + (int64_t)lrow * D + 16 * db + 4 * g) = o_acc[db][qb];
+            for (int db = 0; db < NDB; db++) *(f32x4*)(ow + (int64_t)lrow * HD + 16 * db + 4 * g) = o_acc[db][qb];
             if (g == 0) {
                 mw[2 * lrow] = moff[qb];
                 mw[2 * lrow + 1] = l_row[qb];
@@ -662,13 +675,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
 // ---------------------------------------------------------- combine kernel
 // One thread per (row, 4 dims): merges the splits of a query tile in split
 // order: M = max_s M_s, O = sum_s 2^(M_s - M) O_s / sum_s 2^(M_s - M) l_s.
-template <int BM>
+template <int BM, int HD>
 __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)(p.n_items - p.n_full) * BM * (D / 4);
+    const int64_t total = (int64_t)(p.n_items - p.n_full) * BM * (HD / 4);
     if (gid >= total) return;
-    const int d4 = (int)(gid % (D / 4));
-    const int64_t r = gid / (D / 4);
+    const int d4 = (int)(gid % (HD / 4));
+    const int64_t r = gid / (HD / 4);
     const int lrow = (int)(r % BM);
     const int sidx = (int)(r / BM);          // index among the split items
     const int item = p.n_full + sidx;
@@ -688,7 +701,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
         const float ms = mw[(int64_t)s * BM * 2 + 2 * lrow];
         const float ls = mw[(int64_t)s * BM * 2 + 2 * lrow + 1];
         const float wgt = ldexpf(1.0f, (int)fmaxf(ms - M, -200.f));
-        const f32x4 os = *(const f32x4*)(p.ws_o + ((int64_t)sidx * ns + s) * BM * D + (int64_t)lrow * D + 4 * d4);
+        const f32x4 os = *(const f32x4*)(p.ws_o + ((int64_t)sidx * ns + s) * BM * HD + (int64_t)lrow * HD + 4 * d4);
         acc += os * wgt;
         l += ls * wgt;
     }
@@ -706,30 +719,38 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
 // ------------------------------------------------------------------ launch
 int launch(const AttnParams& p, hipStream_t stream) {
     dim3 grid(p.n_blocks), block(NW * 64);
-    // c > 0 (the usual positive scale), the causal mask and the weights'
-    // rounding mode are compile-time variants, so the plain path carries no
-    // code for any alternative.
-    auto go = [&](auto cpos, auto causal) {
+    // The head dimension, c > 0 (the usual positive scale), the causal mask
+    // and the weights' rounding mode are compile-time variants, so the plain
+    // path carries no code for any alternative.
+    auto go = [&](auto hd, auto cpos, auto causal) {
+        constexpr int H_ = decltype(hd)::value;
         constexpr bool CP = decltype(cpos)::value, CA = decltype(causal)::value;
         if (p.p_mode == ROUND_RTNA)
-            hipLaunchKernelGGL((attn_fwd_main<CP, CA, ROUND_RTNA>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNA>), grid, block, 0, stream, p);
         else if (p.p_mode == ROUND_RTZ)
-            hipLaunchKernelGGL((attn_fwd_main<CP, CA, ROUND_RTZ>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTZ>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((attn_fwd_main<CP, CA, ROUND_RTNE>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNE>), grid, block, 0, stream, p);
     };
-    if (p.causal) {
-        if (p.c > 0.f) go(std::true_type{}, std::true_type{});
-        else go(std::false_type{}, std::true_type{});
-    } else {
-        if (p.c > 0.f) go(std::true_type{}, std::false_type{});
-        else go(std::false_type{}, std::false_type{});
-    }
+    auto go_hd = [&](auto hd) {
+        if (p.causal) {
+            if (p.c > 0.f) go(hd, std::true_type{}, std::true_type{});
+            else go(hd, std::false_type{}, std::true_type{});
+        } else {
+            if (p.c > 0.f) go(hd, std::true_type{}, std::false_type{});
+            else go(hd, std::false_type{}, std::false_type{});
+        }
+    };
+    if (p.head_dim == 64) go_hd(std::integral_constant<int, 64>{});
+    else go_hd(std::integral_constant<int, 128>{});
     if (hipGetLastError() != hipSuccess) return -1;
     if (p.n_full < p.n_items) {
-        const int64_t total = (int64_t)(p.n_items - p.n_full) * KERNEL_BM * (D / 4);
+        const int64_t total = (int64_t)(p.n_items - p.n_full) * KERNEL_BM * (p.head_dim / 4);
         dim3 cgrid((unsigned)((total + 255) / 256));
-        hipLaunchKernelGGL((attn_fwd_combine<KERNEL_BM>), cgrid, dim3(256), 0, stream, p);
+        if (p.head_dim == 64)
+            hipLaunchKernelGGL((attn_fwd_combine<KERNEL_BM, 64>), cgrid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_combine<KERNEL_BM, 128>), cgrid, dim3(256), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;

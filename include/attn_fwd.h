@@ -59,7 +59,8 @@ enum {
     ATTN_ERR_NULL = -1,        /* a required pointer is NULL                        */
     ATTN_ERR_LAYOUT = -2,      /* layout is not one of ATTN_LAYOUT_*                */
     ATTN_ERR_ROUND_MODE = -3,  /* round_mode is not ATTN_ROUND_* [| ATTN_ROUND_WEIGHTS] */
-    ATTN_ERR_SHAPE = -4,       /* a size < 1, Hq not a multiple of Hkv, or overflow */
+    ATTN_ERR_SHAPE = -4,       /* a size < 1, Hq not a multiple of Hkv, head_dim not
+                                  64 or 128, or overflow                            */
     ATTN_ERR_SCALE = -5,       /* scale is NaN or infinite                          */
     ATTN_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                  */
     ATTN_ERR_ALIAS = -7,       /* o overlaps q, k or v                              */
@@ -155,6 +156,24 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
 int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                       int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                       float scale, int causal, int round_mode, void* stream);
+
+/*
+ * attn_fwd_bf16_hd -- attn_fwd_bf16_gqa for head dimension 128 or 64 (the two
+ * sizes of the attention forward kernels in the HipKittens summary's kernel
+ * suite).
+ *
+ *   q, o   [B,Sq,Hq,head_dim] or [B,Hq,Sq,head_dim] bf16
+ *   k, v   [B,Skv,Hkv,head_dim] or [B,Hkv,Skv,head_dim] bf16
+ *   head_dim 128 or 64; other values give ATTN_ERR_SHAPE.  The usual scale
+ *            is 1/sqrt(head_dim).
+ *
+ * Every other argument, the lse output, ownership, asynchrony and error
+ * behaviour are those of attn_fwd_bf16_gqa; with head_dim 128 the two calls
+ * are the same.
+ */
+int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                     int64_t head_dim, float scale, int causal, int round_mode, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* attn_status_string(int status);

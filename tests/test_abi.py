@@ -91,6 +91,34 @@ def test_gqa_argument_errors_before_device(kw, code):
     assert call_gqa(**kw) == code
 
 
+def call_hd(**kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), lse=None, layout=0, B=1, Hq=4,
+             Hkv=2, Sq=64, Skv=64, hd=64, scale=0.125, causal=0, mode=0, stream=0)
+    a.update(kw)
+    return load_library().attn_fwd_bf16_hd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["layout"], a["B"], a["Hq"],
+                                           a["Hkv"], a["Sq"], a["Skv"], a["hd"], a["scale"], a["causal"], a["mode"],
+                                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hd=96), -4), (dict(hd=0), -4), (dict(hd=256), -4), (dict(hd=-64), -4), (dict(q=0), -1),
+    (dict(Hkv=3), -4), (dict(mode=5), -3), (dict(causal=3), -11), (dict(v=FAKE + (2 << 30) + 8), -6),
+    # with head_dim 64, o overlaps q only if it starts inside q's 64*4*64*2 bytes
+    (dict(o=FAKE + 64 * 4 * 64 * 2 - 16), -7),
+])
+def test_hd_argument_errors_before_device(kw, code):
+    assert call_hd(**kw) == code
+
+
+def test_hd_valid_arguments_reach_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_hd() == -8
+    assert call_hd(hd=128) == -8
+    assert call_hd(o=FAKE + 64 * 4 * 64 * 2) == -8    # just past q (64-dim rows): no overlap
+
+
 def test_gqa_valid_arguments_reach_device_check():
     import torch
     if torch.cuda.is_available():

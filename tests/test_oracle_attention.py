@@ -214,9 +214,9 @@ def test_row_subset_matches_full():
 
 
 # -------------------------------------------------------------------- NaN / Inf
-def closed_form_mask(inj, B, H, Sq):
+def closed_form_mask(inj, B, H, Sq, D=128):
     """Expected output class per (b, h, i, d): 0 finite, 1 NaN, 2 +Inf, 3 -Inf."""
-    out = np.zeros((B, H, Sq, 128), np.int8)
+    out = np.zeros((B, H, Sq, D), np.int8)
     col = {}
     for (b, h, j, d, val) in inj.v_sites:
         st = col.setdefault((b, h, d), set())
