@@ -171,6 +171,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     constexpr int NDB = HD / 16;                 // 16-dim blocks of O
     constexpr int SS = 4 * NKS;                  // fragment steps of S^T (4 key blocks x NKS)
     constexpr int ST = SS + 2 * NDB;             // all steps of a tile (+ NDB x 2 k-steps of O^T)
+    // Row sums of the weights: with HD = 64 the softmax VALU work outweighs
+    // the MFMAs, so the sums go to the matrix core (ones^T P^T, 2 MFMAs per
+    // query block and tile); with HD = 128 the MFMAs dominate and the VALU
+    // adds the weights.
+    constexpr bool MFMA_SUM = HD == 64;
     // Four distinct LDS objects (K and V, two buffers each): with the buffer
     // choice a compile-time constant the compiler can tell that a DMA into one
     // buffer does not alias reads of another and does not wait for it.
@@ -307,9 +312,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float moff[NQB], l_run[NQB];    // power-of-two offset of the weights (integer-valued), row-sum partials
+    f32x4 l_acc[NQB];               // MFMA_SUM: row sums, every element the lane's query
     f32x4 bias4[NQB];               // c > 0: S^T accumulates from -moff/c, so c * S^T = x - moff
 #pragma unroll
-    for (int qb = 0; qb < NQB; qb++) { moff[qb] = 0.f; l_run[qb] = 0.f; bias4[qb] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    for (int qb = 0; qb < NQB; qb++) {
+        moff[qb] = 0.f; l_run[qb] = 0.f;
+        bias4[qb] = f32x4{0.f, 0.f, 0.f, 0.f}; l_acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                          (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     const float rc = 1.0f / p.c;
     f32x4 s_acc[4][NQB];
     bf16x8 pf[NQB][2];
@@ -359,6 +370,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
             const int db = (st - SS) % NDB, ks = (st - SS) / NDB;
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = mfma16x16x32(f, pf[qb][ks], o_acc[db][qb]);
+            if (MFMA_SUM && db == NDB - 1) {
+                // ones^T P^T: every lane gets the sum of the step's 32 bf16
+                // weights of its query (exact products, fp32 sums)
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++) l_acc[qb] = mfma16x16x32(ones8, pf[qb][ks], l_acc[qb]);
+            }
         }
     };
     constexpr int PF = 4;   // fragment prefetch distance (steps)
@@ -404,7 +421,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                 if (st + PF < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, NQB, 0);
+            if (MFMA_SUM && st >= SS && (st - SS) % NDB == NDB - 1) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x008, NQB, 0);
         }
     };
     using C0 = std::integral_constant<int, 0>;
@@ -453,12 +471,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                 const f32x4& src = pv4[2 * ks + (i >> 1)];
                 const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
                 pr[i] = weight_pair(two);
-                // the two bf16 weights as fp32 (bit placement), summed with plain
-                // adds: v_dot2c would wait for the matrix core a co-resident
-                // wave keeps busy
-                const uint32_t u = __builtin_bit_cast(uint32_t, pr[i]);
-                tlo += __uint_as_float(u << 16);
-                thi += __uint_as_float(u & 0xffff0000u);
+                if (!MFMA_SUM) {
+                    // the two bf16 weights as fp32 (bit placement), summed with
+                    // plain adds: v_dot2c would wait for the matrix core a
+                    // co-resident wave keeps busy
+                    const uint32_t u = __builtin_bit_cast(uint32_t, pr[i]);
+                    tlo += __uint_as_float(u << 16);
+                    thi += __uint_as_float(u & 0xffff0000u);
+                }
             }
             const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
             const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
@@ -535,15 +555,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
             return;
         }
         // Later tiles: weights against the running offset, with no max.  A
-        // weight can exceed 2^16 only if its lane's tile sum does; then (rare:
-        // the row max moved far past the offset) the tile is redone with the
-        // offset at ceil(max) and O and l rescaled by the exact power of two.
+        // weight can exceed 2^16 only if its lane's tile sum does (with the
+        // MFMA row sums: only if the lane's largest exponent exceeds 16); then
+        // (rare: the row max moved far past the offset) the tile is redone with
+        // the offset at ceil(max) and O and l rescaled by the exact power of two.
         float tsum[NQB];
         bool big = false;
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
+            if (MFMA_SUM) {
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
+                big |= (CPOS ? mx * c : mx - moff[qb]) > 16.0f;
+            }
             tsum[qb] = weights(qb, moff[qb], std::integral_constant<bool, CPOS>{});
-            big |= tsum[qb] > WEIGHT_LIMIT;
+            if (!MFMA_SUM) big |= tsum[qb] > WEIGHT_LIMIT;
         }
         if (__builtin_amdgcn_ballot_w64(big) != 0) {
             float alpha[NQB];
@@ -556,6 +585,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
                 moff[qb] = m_new;
                 set_bias(qb);
                 l_run[qb] *= alpha[qb];
+                l_acc[qb] *= alpha[qb];
             }
 #pragma unroll
             for (int db = 0; db < NDB; db++)
@@ -615,7 +645,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) 
     // ---- epilogue: the 4 lanes of a row hold partial row sums
     float l_row[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; qb++) l_row[qb] = rowsum4(l_run[qb]);
+    for (int qb = 0; qb < NQB; qb++) l_row[qb] = MFMA_SUM ? l_acc[qb][0] : rowsum4(l_run[qb]);
 
     if (nsplit == 1) {
         if (p.lse && g == 0) {

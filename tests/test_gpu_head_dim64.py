@@ -1,9 +1,11 @@
 """GPU parity of head dimension 64 (attn_fwd_bf16_hd), through the C ABI,
 against the fp64 oracle at D = 64: every finite element within 2 bf16 ULP, at
 least 99.9% within 1, NaN/Inf positions identical; plus the identity that the
-64-dimension kernel gives, bit for bit, the first 64 dimensions of the
-128-dimension kernel on inputs zero-padded to 128 (the scores and weights are
-the same numbers)."""
+64-dimension kernel gives the first 64 dimensions of the 128-dimension kernel
+on inputs zero-padded to 128: the scores, weights and weighted sums are the
+same numbers, only the row sums add the same weights in another order (on the
+matrix core at 64, on the vector ALU at 128), so an output may move by one
+bf16 step where it lies within fp32 rounding of a bf16 boundary."""
 import numpy as np
 import pytest
 import torch
@@ -74,15 +76,16 @@ def test_d64_lse():
 
 @pytest.mark.parametrize("case", [("bshd", 2, 3, 257, 130, False), ("bhsd", 1, 4, 300, 1000, False),
                                   ("bhsd", 1, 2, 300, 300, True)])
-def test_d64_equals_d128_zero_padded_bitwise(case):
+def test_d64_equals_d128_zero_padded(case):
     layout, B, H, Sq, Skv, causal = case
     q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 95, 1.0, 2.0, 1.0, D=64)
     pad = lambda t: torch.nn.functional.pad(t, (0, 64))
     o64 = run64(q, k, v, layout, causal=causal)
     o128 = run64(pad(q), pad(k), pad(v), layout, causal=causal)
-    o128 = o128.reshape(o128.shape[:-1] + (128,)) if o128.ndim == 4 else o128
-    assert np.array_equal(o128[..., :64], o64)
     assert np.all(o128[..., 64:] == 0)
+    steps = np.abs(gate.ordinal(o128[..., :64]).astype(np.int64) - gate.ordinal(o64).astype(np.int64))
+    say(f"[pad] {case}: differing elements {np.mean(steps > 0):.2e}, max steps {steps.max()}")
+    assert steps.max() <= 1 and np.mean(steps > 0) <= 1e-3
 
 
 def test_d64_nonfinite_positions():
