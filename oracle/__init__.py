@@ -69,6 +69,9 @@ def configure(lib):
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
+    lib.oracle_attention_bwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
+        [ctypes.c_float, ctypes.c_int] + [ctypes.c_void_p] * 6 + [ctypes.c_int]
     lib.oracle_version.restype = ctypes.c_int
     return lib
 
@@ -160,3 +163,46 @@ def attention(q, k, v, *, layout: str, scale: float, rows=None, method: bool = T
         raise RuntimeError(f"oracle_attention failed ({rc})")
     rows_out = np.arange(nrows, dtype=np.int64) if rows_arr is None else rows_arr
     return OracleResult(rows_out, o, sg, om, sm, ls)
+
+
+class OracleGrads:
+    """Gradients [rows, D] (float64): dq rows (b*H + h)*Sq + i, dk/dv rows
+    (b*H + h)*Skv + j, each with the RMS size of the terms its sum adds."""
+
+    def __init__(self, dq, sdq, dk, sdk, dv, sdv):
+        self.dq, self.sdq, self.dk, self.sdk, self.dv, self.sdv = dq, sdq, dk, sdk, dv, sdv
+
+
+def attention_bwd(q, k, v, do, *, layout: str, scale: float, o=None, causal: bool = False,
+                  nthreads: int = 0) -> OracleGrads:
+    """Gradients of the plain operation for the output gradient ``do`` (bf16
+    bit patterns like q).  ``o``: the forward output the backward starts from
+    (bf16 bits; its row dot product with do enters the softmax gradient), or
+    None for the exact output.  Heads of q and k/v are equal."""
+    lib = _load()
+    q, k, v, do = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v, do))
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or do.shape != q.shape:
+        raise ValueError("q, do [.., .., .., D]; k, v of one shape")
+    D = q.shape[-1]
+    if layout == "bshd":
+        B, Sq, H, _ = q.shape
+        Skv, Hk = k.shape[1], k.shape[2]
+    elif layout == "bhsd":
+        B, H, Sq, _ = q.shape
+        Hk, Skv = k.shape[1], k.shape[2]
+    else:
+        raise ValueError(layout)
+    if Hk != H or k.shape[0] != B or k.shape[-1] != D:
+        raise ValueError("q and k/v must share batch, heads and head dimension")
+    if o is not None:
+        o = np.ascontiguousarray(o, dtype=np.uint16)
+        if o.shape != q.shape:
+            raise ValueError("o must be shaped like q")
+    out = [np.empty((B * H * n, D), np.float64) for n in (Sq, Sq, Skv, Skv, Skv, Skv)]
+    rc = lib.oracle_attention_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                  o.ctypes.data if o is not None else None, do.ctypes.data,
+                                  LAYOUTS[layout], B, H, Sq, Skv, D, ctypes.c_float(scale), 1 if causal else 0,
+                                  *[a.ctypes.data for a in out], int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
+    return OracleGrads(*out)

@@ -299,3 +299,138 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     return oracle_attention_gqa(q, k, v, layout, B, H, H, Sq, Skv, 128, scale, 0, rows, nrows,
                                 o_exact, sigma, o_method, sigma_method, NULL, l_from_rounded, OR_RTNE, nthreads);
 }
+
+/*
+ * Backward pass of the same operation (NEXT to the forward: the gradients a
+ * training step needs; the HipKittens summary's kernel suite pairs attention
+ * forward with its backward).  With a loss L and dO = dL/dO given, the chain
+ * rule on the plain definition gives, per (batch, head), with p the softmax
+ * weights and causal-masked pairs left out:
+ *     dv_j = sum_i p_ij do_i
+ *     dp_ij = <do_i, v_j>
+ *     ds_ij = p_ij (dp_ij - delta_i),    delta_i = sum_j p_ij dp_ij = <do_i, o_i>
+ *     dq_i = scale sum_j ds_ij k_j,     dk_j = scale sum_i ds_ij q_i
+ * delta_i is evaluated as <do_i, o_i> with the o the caller passes (the
+ * forward's stored bf16 output, as a backward pass that starts from the saved
+ * output does), or with the exact o when o is NULL; the two agree up to o's
+ * rounding.  Everything in fp64, rows in ascending order, no blocking.
+ *
+ *   q, o, dO : [B,Sq,H,D] or [B,H,Sq,D] bf16 bits (o may be NULL);
+ *   k, v     : [B,Skv,H,D] or [B,H,Skv,D]
+ *   dq, sdq  : [B*H*Sq, D] doubles, rows (b*H + h)*Sq + i: the gradient and
+ *              the RMS size of the terms its sum adds (scale |ds_ij k_jd|)
+ *   dk, sdk, dv, sdv : [B*H*Skv, D] doubles, rows (b*H + h)*Skv + j
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                         const uint16_t* dO, int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                         int64_t D, float scale, int causal,
+                         double* dq, double* sdq, double* dk, double* sdk, double* dv, double* sdv,
+                         int nthreads) {
+    if (!q || !k || !v || !dO || !dq || !sdq || !dk || !sdk || !dv || !sdv) return -1;
+    if (layout != OR_LAYOUT_BSHD && layout != OR_LAYOUT_BHSD) return -1;
+    if (B < 1 || H < 1 || Sq < 1 || Skv < 1 || D < 1 || D > ORACLE_DMAX) return -1;
+    if (causal != 0 && causal != 1) return -1;
+    const double sc = (double)scale;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    double* P = (double*)malloc(sizeof(double) * (size_t)(Sq * Skv));
+    double* dS = (double*)malloc(sizeof(double) * (size_t)(Sq * Skv));
+    if (!P || !dS) { free(P); free(dS); return -1; }
+    for (int64_t b = 0; b < B; b++) {
+        for (int64_t h = 0; h < H; h++) {
+            /* weights p_ij (masked pairs 0), per row */
+#pragma omp parallel for schedule(dynamic, 8)
+            for (int64_t i = 0; i < Sq; i++) {
+                int64_t n_keys = Skv;
+                if (causal) {
+                    n_keys = i + (Skv - Sq) + 1;
+                    if (n_keys > Skv) n_keys = Skv;
+                    if (n_keys < 0) n_keys = 0;
+                }
+                const uint16_t* qp = q + row_offset(layout, b, h, i, H, Sq, D);
+                double m = -INFINITY;
+                double* pr = P + i * Skv;
+                for (int64_t j = 0; j < Skv; j++) {
+                    if (j >= n_keys) { pr[j] = 0.0; continue; }
+                    const uint16_t* kp = k + row_offset(layout, b, h, j, H, Skv, D);
+                    double acc = 0.0;
+                    for (int d = 0; d < D; d++) acc += bf16_to_double(qp[d]) * bf16_to_double(kp[d]);
+                    pr[j] = sc * acc;
+                    if (!isnan(m) && (isnan(pr[j]) || pr[j] > m)) m = pr[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < n_keys; j++) { pr[j] = exp(pr[j] - m); l += pr[j]; }
+                for (int64_t j = 0; j < n_keys; j++) pr[j] /= l;
+                /* delta_i = <do_i, o_i> (given o, or the exact o = sum_j p_ij v_j) */
+                const uint16_t* gp = dO + row_offset(layout, b, h, i, H, Sq, D);
+                double delta = 0.0;
+                for (int d = 0; d < D; d++) {
+                    double od;
+                    if (o) {
+                        od = bf16_to_double(o[row_offset(layout, b, h, i, H, Sq, D) + d]);
+                    } else {
+                        od = 0.0;
+                        for (int64_t j = 0; j < n_keys; j++)
+                            od += pr[j] * bf16_to_double(v[row_offset(layout, b, h, j, H, Skv, D) + d]);
+                    }
+                    delta += bf16_to_double(gp[d]) * od;
+                }
+                /* ds_ij = p_ij (<do_i, v_j> - delta_i) */
+                double* dr = dS + i * Skv;
+                for (int64_t j = 0; j < Skv; j++) {
+                    if (j >= n_keys) { dr[j] = 0.0; continue; }
+                    const uint16_t* vp = v + row_offset(layout, b, h, j, H, Skv, D);
+                    double dp = 0.0;
+                    for (int d = 0; d < D; d++) dp += bf16_to_double(gp[d]) * bf16_to_double(vp[d]);
+                    dr[j] = pr[j] * (dp - delta);
+                }
+            }
+            /* dq_i = scale sum_j ds_ij k_j */
+#pragma omp parallel for schedule(dynamic, 8)
+            for (int64_t i = 0; i < Sq; i++) {
+                double* g = dq + ((b * H + h) * Sq + i) * D;
+                double* sg = sdq + ((b * H + h) * Sq + i) * D;
+                for (int d = 0; d < D; d++) { g[d] = 0.0; sg[d] = 0.0; }
+                for (int64_t j = 0; j < Skv; j++) {
+                    const double w = dS[i * Skv + j];
+                    if (w == 0.0) continue;
+                    const uint16_t* kp = k + row_offset(layout, b, h, j, H, Skv, D);
+                    for (int d = 0; d < D; d++) {
+                        const double t = sc * w * bf16_to_double(kp[d]);
+                        g[d] += t;
+                        sg[d] += t * t;
+                    }
+                }
+                for (int d = 0; d < D; d++) sg[d] = sqrt(sg[d]);
+            }
+            /* dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij do_i */
+#pragma omp parallel for schedule(dynamic, 8)
+            for (int64_t j = 0; j < Skv; j++) {
+                double* gk = dk + ((b * H + h) * Skv + j) * D;
+                double* sk = sdk + ((b * H + h) * Skv + j) * D;
+                double* gv = dv + ((b * H + h) * Skv + j) * D;
+                double* sv = sdv + ((b * H + h) * Skv + j) * D;
+                for (int d = 0; d < D; d++) { gk[d] = 0.0; sk[d] = 0.0; gv[d] = 0.0; sv[d] = 0.0; }
+                for (int64_t i = 0; i < Sq; i++) {
+                    const double w = dS[i * Skv + j], pw = P[i * Skv + j];
+                    const uint16_t* qp = q + row_offset(layout, b, h, i, H, Sq, D);
+                    const uint16_t* gp = dO + row_offset(layout, b, h, i, H, Sq, D);
+                    for (int d = 0; d < D; d++) {
+                        const double tk = sc * w * bf16_to_double(qp[d]);
+                        const double tv = pw * bf16_to_double(gp[d]);
+                        gk[d] += tk; sk[d] += tk * tk;
+                        gv[d] += tv; sv[d] += tv * tv;
+                    }
+                }
+                for (int d = 0; d < D; d++) { sk[d] = sqrt(sk[d]); sv[d] = sqrt(sv[d]); }
+            }
+        }
+    }
+    free(P);
+    free(dS);
+    return 0;
+}

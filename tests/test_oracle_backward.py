@@ -1,0 +1,100 @@
+"""Pins of the oracle's backward pass (gradients of the plain operation).
+
+The backward is pinned against a library routine (torch autograd through
+softmax(Q K^T * scale) V in float64), a closed form (a single key: the softmax
+is constant, so dQ = dK = 0 and dV is the sum of dO over the queries), and
+the exact effect of starting from a given (rounded) forward output o: only the
+row term delta_i = <dO_i, o_i> changes, by a known amount."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bf16_attention_forward_amd import workloads as wl
+
+SCALE = float(np.float32(1.0 / np.sqrt(128)))
+
+
+def f64(t):
+    return t.to(torch.float64)
+
+
+def heads_first(t, layout):
+    return t.permute(0, 2, 1, 3) if layout == "bshd" else t
+
+
+def autograd_grads(q, k, v, do, layout, scale, causal):
+    Q, K, V, G = (heads_first(f64(t), layout).clone().requires_grad_(i < 3) for i, t in enumerate((q, k, v, do)))
+    S = scale * (Q @ K.transpose(-1, -2))
+    keep = torch.ones(S.shape[-2:], dtype=torch.bool)
+    if causal:
+        sq, skv = Q.shape[2], K.shape[2]
+        i = torch.arange(sq)[:, None]; j = torch.arange(skv)[None, :]
+        keep = j <= i + (skv - sq)
+    # rows that see no key get weights 0 (a finite stand-in score, then masked
+    # by multiplication, so no NaN enters the graph)
+    has_key = keep.any(dim=-1, keepdim=True)
+    S = torch.where(keep | ~has_key, S, torch.full_like(S, float("-inf")))
+    P = torch.softmax(S, dim=-1) * has_key
+    O = P @ V
+    (O * G).sum().backward()
+    D = q.shape[-1]
+    return (Q.grad.reshape(-1, D).numpy(), K.grad.reshape(-1, D).numpy(), V.grad.reshape(-1, D).numpy(),
+            O.detach())
+
+
+def inputs(layout, B, H, sq, skv, seed, D=128):
+    q, k, v = wl.random_qkv(layout, B, H, sq, skv, seed, k_factor=2.0, D=D)
+    do = wl.random_qkv(layout, B, H, sq, 1, seed + 1000, D=D)[0]
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("causal,sq,skv", [(False, 23, 41), (True, 37, 37), (True, 20, 53), (True, 41, 17)])
+def test_matches_torch_autograd_float64(layout, causal, sq, skv):
+    q, k, v, do = inputs(layout, 2, 3, sq, skv, 5)
+    g = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                             causal=causal)
+    dq, dk, dv, _ = autograd_grads(q, k, v, do, layout, SCALE, causal)
+    for got, ref in ((g.dq, dq), (g.dk, dk), (g.dv, dv)):
+        assert np.allclose(got, ref, rtol=1e-11, atol=1e-12), np.abs(got - ref).max()
+
+
+def test_head_dim_64_matches_autograd():
+    q, k, v, do = inputs("bhsd", 1, 2, 30, 45, 7, D=64)
+    s = float(np.float32(0.125))
+    g = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout="bhsd", scale=s)
+    dq, dk, dv, _ = autograd_grads(q, k, v, do, "bhsd", s, False)
+    for got, ref in ((g.dq, dq), (g.dk, dk), (g.dv, dv)):
+        assert np.allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_single_key_closed_form():
+    q, k, v, do = inputs("bhsd", 1, 2, 9, 1, 11)
+    g = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout="bhsd", scale=SCALE)
+    assert np.all(np.abs(g.dq) < 1e-15) and np.all(np.abs(g.dk) < 1e-15)
+    assert np.allclose(g.dv, f64(do).sum(dim=2).reshape(-1, 128).numpy(), rtol=1e-15, atol=1e-15)
+
+
+def test_given_output_changes_only_delta():
+    """With o given (the exact output rounded to bf16), dv is unchanged and
+    dq, dk move by exactly the delta correction: with e_i = <dO_i, o_i - O_i>,
+    dq_i -= scale e_i sum_j p_ij k_j and dk_j -= scale sum_i e_i p_ij q_i."""
+    layout, B, H, sq, skv = "bshd", 1, 2, 19, 33
+    q, k, v, do = inputs(layout, B, H, sq, skv, 13)
+    exact = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE)
+    fwd = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=SCALE, method=False)
+    o_bits = fwd.rounded("rtne").reshape(B, H, sq, 128).transpose(0, 2, 1, 3).copy()   # [B,S,H,D] bits
+    given = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                                 o=o_bits)
+    assert np.array_equal(given.dv, exact.dv)
+    Q, K, G = (heads_first(f64(t), layout) for t in (q, k, do))
+    P = torch.softmax(SCALE * (Q @ K.transpose(-1, -2)), dim=-1)
+    O = P @ heads_first(f64(v), layout)
+    Og = heads_first(f64(torch.from_numpy(oracle.bf16_bits_to_f64(o_bits))), layout)
+    e = ((Og - O) * G).sum(-1, keepdim=True)                     # [B,H,Sq,1]
+    ddq = -SCALE * e * (P @ K)
+    ddk = -SCALE * (P * e).transpose(-1, -2) @ Q
+    assert np.allclose(given.dq - exact.dq, ddq.reshape(-1, 128).numpy(), rtol=1e-9, atol=1e-14)
+    assert np.allclose(given.dk - exact.dk, ddk.reshape(-1, 128).numpy(), rtol=1e-9, atol=1e-14)
+    assert np.abs(given.dq - exact.dq).max() > 0

@@ -25,8 +25,11 @@ MUTANTS = {
     "no_scale": ("s[j] = sc * acc;", "s[j] = acc;"),
     "bshd_offset": ("if (layout == OR_LAYOUT_BSHD) return ((b * S + i) * H + h) * D;",
                     "if (layout == OR_LAYOUT_BSHD) return ((b * H + h) * S + i) * D;"),
+    "bwd_no_delta": ("dr[j] = pr[j] * (dp - delta);", "dr[j] = pr[j] * dp;"),
+    "bwd_dv_from_ds": ("const double tv = pw * bf16_to_double(gp[d]);", "const double tv = w * bf16_to_double(gp[d]);"),
     "row_stride_128": ("    return ((b * H + h) * S + i) * D;", "    return ((b * H + h) * S + i) * 128;"),
-    "value_from_key": ("const uint16_t* vp = v + row_offset", "const uint16_t* vp = k + row_offset"),
+    "value_from_key": ("const uint16_t* vp = v + row_offset(layout, b, hk, j, Hkv, Skv, D);",
+                       "const uint16_t* vp = k + row_offset(layout, b, hk, j, Hkv, Skv, D);"),
     "sigma_not_squared": ("sq[d] += (p * vv) * (p * vv);", "sq[d] += (p * vv);"),
     "rtne_tie_up": ("if (fr > 0.5) m = fl + 1.0;", "if (fr >= 0.5) m = fl + 1.0;"),
     "rtna_tie_down": ("if (fr >= 0.5) m = fl + 1.0;\n    } /* OR_RTZ", "if (fr > 0.5) m = fl + 1.0;\n    } /* OR_RTZ"),
@@ -35,8 +38,9 @@ MUTANTS = {
     "max_skips_last_key": ("for (int64_t j = 0; j < n_keys; j++) {\n                const uint16_t* kp",
                            "for (int64_t j = 0; j < n_keys; j++) {\n                if (j == n_keys - 1 && n_keys > 1) { s[j] = -INFINITY; continue; }\n                const uint16_t* kp"),
     "gqa_head_modulo": ("int64_t hk = h / group;", "int64_t hk = h % Hkv;"),
-    "causal_off_by_one": ("n_keys = i + (Skv - Sq) + 1;", "n_keys = i + (Skv - Sq);"),
-    "causal_top_left": ("n_keys = i + (Skv - Sq) + 1;", "n_keys = i + 1;"),
+    "causal_off_by_one": ("\n                n_keys = i + (Skv - Sq) + 1;", "\n                n_keys = i + (Skv - Sq);"),
+    "causal_top_left": ("\n                n_keys = i + (Skv - Sq) + 1;", "\n                n_keys = i + 1;"),
+    "bwd_causal_off_by_one": ("\n                    n_keys = i + (Skv - Sq) + 1;", "\n                    n_keys = i + (Skv - Sq);"),
     "empty_rows_not_zero": ("if (n_keys <= 0) {", "if (n_keys < 0) {"),
     "lse_drops_max": ("if (lse) lse[t] = m + log(l);", "if (lse) lse[t] = log(l);"),
     "weights_mode_ignored": ("pt = round_trip_bf16(pm, p_round);", "pt = round_trip_bf16(pm, OR_RTNE);"),
@@ -75,6 +79,10 @@ def pins():
     out.append(("d64_sdpa", lambda: A.test_d64_matches_torch_sdpa_float64("bhsd", False, 3)))
     out.append(("d64_brute", lambda: A.test_d64_bruteforce_decimal(3)))
     out.append(("d64_pad", A.test_d64_equals_d128_zero_padded))
+    from tests import test_oracle_backward as BW
+    out.append(("bwd_autograd", lambda: BW.test_matches_torch_autograd_float64("bhsd", False, 23, 41)))
+    out.append(("bwd_single_key", BW.test_single_key_closed_form))
+    out.append(("bwd_causal", lambda: BW.test_matches_torch_autograd_float64("bshd", True, 37, 37)))
     return out
 
 
