@@ -88,6 +88,30 @@ def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
     return {"wall_s": wall, "ms": per, "flops": w.flops}
 
 
+def time_backward(w, steps, warmup):
+    """Median ms of attn_bwd_bf16 on workload w (O and lse from the forward)."""
+    import torch
+    from bf16_attention_forward_amd import attn_bwd_bf16, attn_fwd_bf16_gqa
+    from bf16_attention_forward_amd import workloads as wl
+
+    q, k, v = wl.make_inputs(w)
+    do = wl.random_qkv(w.layout, w.B, w.H, w.Sq, 1, w.seed + 5000)[0]
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = attn_fwd_bf16_gqa(qd, kd, vd, layout=w.layout, return_lse=True)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    for _ in range(warmup):
+        attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=w.layout, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=w.layout, dq=dq, dk=dk, dv=dv)
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) for a, b in evs])
+
+
 def cpu_baseline(w, budget_s: float):
     import numpy as np
     import oracle
@@ -168,6 +192,14 @@ def main():
             em = statistics.median(rr["ms"])
             extra[f"{w.name}:{mode}+weights"] = {"mode": mode, "round_weights": True, "median_ms": round(em, 4),
                                                  "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
+
+        # backward pass of the default workload (algorithmic FLOPs 2.5x the forward's:
+        # five products of the forward's size, dV, dP, dQ, dK and the recomputed S)
+        if w.D == 128 and not w.causal and not w.Hkv:
+            em = time_backward(w, steps=20, warmup=5)
+            extra[f"{w.name}:backward"] = {"median_ms": round(em, 4),
+                                           "tflops": round(2.5 * w.flops / (em * 1e-3) / 1e12, 1),
+                                           "frac_peak": round(2.5 * w.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
 

@@ -6,8 +6,8 @@ holds the thin ctypes binding with the same entry-point names and the
 seeded workload generators.  Importing it does not load the library; the
 first call does, and raises if it is not built.
 """
-from .binding import (AttnError, attn_fwd_bf16, attn_fwd_bf16_gqa, attn_fwd_bf16_hd,  # noqa: F401
+from .binding import (AttnError, attn_bwd_bf16, attn_fwd_bf16, attn_fwd_bf16_gqa, attn_fwd_bf16_hd,  # noqa: F401
                       attn_fwd_bf16_raw, attn_status_string, attn_version, load_library, LIB_PATH, EXPORTS)
 
-__all__ = ["attn_fwd_bf16", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_fwd_bf16_raw", "attn_status_string",
+__all__ = ["attn_fwd_bf16", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_bwd_bf16", "attn_fwd_bf16_raw", "attn_status_string",
            "attn_version", "load_library", "AttnError", "LIB_PATH", "EXPORTS"]

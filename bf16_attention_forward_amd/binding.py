@@ -23,8 +23,8 @@ ARGUMENT_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -11}
 HEAD_DIM = 128
 
 # names of every entry point the header declares
-EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_status_string",
-           "attn_version")
+EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_bwd_bf16",
+           "attn_status_string", "attn_version")
 HEAD_DIMS = (128, 64)
 
 _lib = None
@@ -58,6 +58,9 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16_hd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_bf16_hd.restype = ctypes.c_int
+    lib.attn_bwd_bf16.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] + [ctypes.c_int64] * 4 + \
+        [ctypes.c_float, ctypes.c_void_p]
+    lib.attn_bwd_bf16.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -216,6 +219,38 @@ def attn_fwd_bf16_hd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
     if rc != ATTN_OK:
         _raise(rc)
     return (o, lse) if lse is not None else o
+
+
+def attn_bwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
+                  lse: torch.Tensor, *, layout: str = "bshd", scale: float | None = None,
+                  stream: torch.cuda.Stream | None = None, dq: torch.Tensor | None = None,
+                  dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """Backward pass (attn_bwd_bf16): returns (dq, dk, dv) for the output
+    gradient ``do``, from the forward's output ``o`` and log-sum-exp ``lse``
+    (float32 [B, H, Sq]).  Head dimension 128, q and k/v with the same heads."""
+    lib = load_library()
+    _check_tensors(q, k, v, o)
+    B, H, _, Sq, Skv = _dims(q, k, layout)
+    for name, t in (("do", do),):
+        if t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 device tensor shaped [B, H, Sq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != torch.bfloat16 or t.shape != ref.shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor shaped like its input")
+    sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ATTN_LAYOUT[layout],
+                               B, H, Sq, Skv, sc, st.cuda_stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return dq, dk, dv
 
 
 def attn_fwd_bf16_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, layout: int, B: int, H: int,

@@ -14,6 +14,7 @@
 #include <mutex>
 #include <vector>
 
+#include "attn_bwd_internal.h"
 #include "attn_fwd_internal.h"
 #include "../../include/attn_fwd.h"
 
@@ -101,7 +102,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-extern "C" int attn_version(void) { return 10300; }
+extern "C" int attn_version(void) { return 10400; }
 
 extern "C" const char* attn_status_string(int status) {
     switch (status) {
@@ -257,6 +258,66 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
                                  int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                  float scale, int causal, int round_mode, void* stream) {
     return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, 128, scale, causal, round_mode, stream, 0, 0);
+}
+
+extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                             const float* lse, void* dq, void* dk, void* dv, int layout, int64_t B, int64_t H,
+                             int64_t Sq, int64_t Skv, float scale, void* stream) {
+    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
+    if (B < 1 || H < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
+    const int64_t lim31 = (int64_t)1 << 31, hd = 128;
+    if (B >= lim31 || H >= lim31 || Sq >= lim31 || Skv >= lim31 || B * H >= lim31) return ATTN_ERR_SHAPE;
+    const int64_t n_q = B * H * Sq, n_kv = B * H * Skv;
+    if (n_q > ((int64_t)1 << 52) / hd || n_kv > ((int64_t)1 << 52) / hd) return ATTN_ERR_SHAPE;
+    const int64_t q_rowe = (layout == ATTN_LAYOUT_BSHD) ? H * hd : hd;
+    if ((Sq - 1) * q_rowe * 2 + hd * 2 >= lim31 || (Skv - 1) * q_rowe * 2 + hd * 2 >= lim31) return ATTN_ERR_SHAPE;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO | (uintptr_t)dq |
+         (uintptr_t)dk | (uintptr_t)dv) & 15)
+        return ATTN_ERR_ALIGN;
+    if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+    const size_t qb = (size_t)n_q * hd * 2, kb = (size_t)n_kv * hd * 2, lb = (size_t)n_q * 4;
+    // outputs overlap no input and no other output
+    const void* ins[6] = {q, k, v, o, dO, lse};
+    const size_t insz[6] = {qb, kb, kb, qb, qb, lb};
+    const void* outs[3] = {dq, dk, dv};
+    const size_t outsz[3] = {qb, kb, kb};
+    for (int a = 0; a < 3; a++) {
+        for (int i = 0; i < 6; i++)
+            if (ranges_overlap(outs[a], outsz[a], ins[i], insz[i])) return ATTN_ERR_ALIAS;
+        for (int c = a + 1; c < 3; c++)
+            if (ranges_overlap(outs[a], outsz[a], outs[c], outsz[c])) return ATTN_ERR_ALIAS;
+    }
+    int dev = -1;
+    DeviceInfo info;
+    const int drc = probe_device(&dev, &info);
+    if (drc != ATTN_OK) return drc;
+
+    attn_bwd::BwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+    p.o = (const uint16_t*)o; p.dO = (const uint16_t*)dO; p.lse = lse;
+    p.dq = (uint16_t*)dq; p.dk = (uint16_t*)dk; p.dv = (uint16_t*)dv;
+    if (layout == ATTN_LAYOUT_BSHD) {
+        p.q_row = H * hd; p.q_head = hd; p.q_batch = Sq * H * hd;
+        p.kv_row = H * hd; p.kv_head = hd; p.kv_batch = Skv * H * hd;
+    } else {
+        p.q_row = hd; p.q_head = Sq * hd; p.q_batch = H * Sq * hd;
+        p.kv_row = hd; p.kv_head = Skv * hd; p.kv_batch = H * Skv * hd;
+    }
+    p.B = (int)B; p.H = (int)H; p.Sq = (int)Sq; p.Skv = (int)Skv;
+    p.n_qblocks = (int)((Sq + 255) / 256);
+    p.n_kblocks = (int)((Skv + 127) / 128);
+    if (B * H * std::max(p.n_qblocks, p.n_kblocks) >= lim31) return ATTN_ERR_SHAPE;
+    p.c = (float)((double)scale * 1.4426950408889634073599246810018921);
+    p.scale = scale;
+    void* ws = nullptr;
+    const int wrc = get_workspace(dev, stream, (size_t)n_q * sizeof(float), &ws);
+    if (wrc != ATTN_OK) return wrc;
+    p.delta = (float*)ws;
+    if (attn_bwd::launch_bwd(p, (hipStream_t)stream) != 0) return ATTN_ERR_LAUNCH;
+    return ATTN_OK;
 }
 
 extern "C" int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float* lse,

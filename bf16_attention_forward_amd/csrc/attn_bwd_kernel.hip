@@ -1,0 +1,429 @@
+// attn_bwd_kernel.hip -- gfx950 (MI355X, CDNA4) kernels for the backward pass
+// of bf16 attention, head dimension 128, for O = softmax(Q K^T * scale) V.
+//
+// The HipKittens summary's kernel suite pairs the attention forward kernels
+// with their backward; the gradients follow from the chain rule on the
+// forward's definition, restated here with the forward's saved output O and
+// its per-row log-sum-exp L (natural log):
+//     P = exp(S * scale - L),  dV = P^T dO,  dP = dO V^T,
+//     dS = P o (dP - delta),   delta_i = <dO_i, O_i>,
+//     dQ = scale dS K,         dK = scale dS^T Q.
+// Three kernels:
+//  * attn_bwd_delta: delta_i, one thread per query row (fp32 from bf16).
+//  * attn_bwd_dq: one work-group of 8 waves owns 256 query rows (32 per wave,
+//    Q and dO fragments in registers as MFMA operand B) and streams 64-key
+//    K and V tiles through LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T (K and
+//    V read as operand A, the forward's K-as-A layout, so each lane holds one
+//    query), then dS^T elementwise, then dQ^T += K^T dS^T with K^T read by
+//    ds_read_b64_tr_b16 in the order of dS^T's keys (the forward's V^T read).
+//  * attn_bwd_dkdv: the mirror image -- a work-group of 8 waves owns 128 keys
+//    (16 per wave, K and V fragments in registers as operand B) and streams
+//    64-query Q and dO tiles.  Per tile: S = Q K^T and dP = dO V^T (Q and dO as
+//    operand A: each lane holds one key), then P and dS, then dV^T += dO^T P
+//    and dK^T += Q^T dS with dO^T and Q^T transposed out of LDS.
+// Every LDS tile is read both straight (ds_read_b128) and transposed, so all
+// tiles keep one layout: chunk c of row r at c ^ (r & 15).  P and dS enter the
+// MFMAs as bf16 (round to nearest-even); all sums are fp32; the gradients are
+// rounded to bf16 (nearest-even).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_bwd_internal.h"
+
+namespace attn_bwd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int D = 128;
+constexpr int ROW_BYTES = D * 2;
+constexpr int TILE_ROWS = 64;
+constexpr int TILE_BYTES = TILE_ROWS * ROW_BYTES;   // 16 KiB
+constexpr int NW = 8;
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest-even; NaN -> 0x7FC0
+__device__ __forceinline__ uint32_t rtne_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// LDS barrier: this wave's LDS reads are done (lgkmcnt) and every wave has
+// arrived; each wave waits for its own DMA (vmcnt) before it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The 64-row tile at row r0 of a tensor (row stride row_elems) into LDS with
+// buffer_load ... lds, 8 waves x 2 rounds of 32 rows: lane (g, j) of wave w in
+// round i writes row 32*i + 4*w + g, chunk position j, holding the source
+// chunk j ^ (row & 15); rows past `rows` read as zero (buffer range check).
+struct TileSrc {
+    __amdgpu_buffer_rsrc_t rs;
+    int row_bytes;
+};
+__device__ __forceinline__ TileSrc tile_src(const uint16_t* base, int64_t row_elems, int rows) {
+    TileSrc t;
+    t.row_bytes = (int)(row_elems * 2);
+    const uint32_t nrec = (uint32_t)((int64_t)(rows - 1) * t.row_bytes + ROW_BYTES);
+    t.rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
+    return t;
+}
+__device__ __forceinline__ void issue_tile(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
+    const int row = wave * 4 + g;                        // + 32 * i (same swizzle)
+    const int voff = row * s.row_bytes + ((j ^ (row & 15)) << 4);
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
+                                                 voff, (r0 + 32 * i) * s.row_bytes, 0, 0);
+}
+
+// Straight fragment (operand A): lane (g, j) gets row 16*rb + j, dims
+// 32*ks + 8*g .. +7.
+__device__ __forceinline__ bf16x8 read_rows(const uint8_t* tile, int addr0, int rb) {
+    return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(tile + addr0 + rb * 16 * ROW_BYTES);
+}
+// Transposed fragment (operand A of a product over the tile's rows): lane
+// (g, j) gets, as elements 4*hf + e, rows 32*ks + 16*hf + 4*g + e of dim
+// 16*db + j (the order of the B operand built from a C fragment).
+__device__ __forceinline__ bf16x8 read_cols(const uint8_t* tile, int addr0, int ks) {
+    bf16x4 half[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+        const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(tile + addr0 + (32 * ks + 16 * hf) * ROW_BYTES);
+        half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
+    }
+    return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Packs a C fragment pair (row blocks 2*ks, 2*ks+1 of 16 rows, 4 per lane)
+// into the bf16 B operand whose k index runs over those 32 rows.
+__device__ __forceinline__ bf16x8 pack_b(const float* lo4, const float* hi4) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        r[e] = __builtin_bit_cast(__bf16, (uint16_t)rtne_bits(lo4[e]));
+        r[4 + e] = __builtin_bit_cast(__bf16, (uint16_t)rtne_bits(hi4[e]));
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------- delta
+__global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (b*H + h)*Sq + i
+    if (r >= (int64_t)p.B * p.H * p.Sq) return;
+    const int i = (int)(r % p.Sq);
+    const int64_t bh = r / p.Sq;
+    const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+    const int64_t off = (int64_t)b * p.q_batch + (int64_t)h * p.q_head + (int64_t)i * p.q_row;
+    const uint4* op = (const uint4*)(p.o + off);
+    const uint4* gp = (const uint4*)(p.dO + off);
+    float acc = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < D / 8; c++) {
+        const uint4 a = op[c], g = gp[c];
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            acc = __builtin_fmaf(__uint_as_float(av[e] << 16), __uint_as_float(gv[e] << 16), acc);
+            acc = __builtin_fmaf(__uint_as_float(av[e] & 0xffff0000u), __uint_as_float(gv[e] & 0xffff0000u), acc);
+        }
+    }
+    p.delta[r] = acc;
+}
+
+// ------------------------------------------------------------------- dQ
+__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) uint8_t sk0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sk1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sv0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sv1[TILE_BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, j = lane & 15;
+    constexpr int BMQ = NW * 32;
+    const int qt = blockIdx.x % p.n_qblocks;
+    const int bh = blockIdx.x / p.n_qblocks;
+    const int h = bh % p.H, b = bh / p.H;
+    const int qrow0 = qt * BMQ + wave * 32;
+    const int T = (p.Skv + TILE_ROWS - 1) / TILE_ROWS;
+
+    const TileSrc ks = tile_src(p.k + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
+    const TileSrc vs = tile_src(p.v + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
+    issue_tile(ks, 0, sk0, wave, g, j);
+    issue_tile(vs, 0, sv0, wave, g, j);
+
+    // Q and dO of query rows qrow0 + 16*qb + j (clamped; results of rows past
+    // Sq are never stored), dims 32*kk + 8*g .. +7: operand B.
+    const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
+    bf16x8 qf[2][4], gf[2][4];
+    float lse2[2], dlt[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+        const int row = min(qrow0 + qb * 16 + j, p.Sq - 1);
+        const uint16_t* qs = p.q + qoff + (int64_t)row * p.q_row + 8 * g;
+        const uint16_t* gs = p.dO + qoff + (int64_t)row * p.q_row + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            qf[qb][kk] = *(const bf16x8*)(qs + 32 * kk);
+            gf[qb][kk] = *(const bf16x8*)(gs + 32 * kk);
+        }
+        const int64_t ri = ((int64_t)b * p.H + h) * p.Sq + row;
+        lse2[qb] = p.lse[ri] * LOG2E;
+        dlt[qb] = p.delta[ri];
+    }
+    f32x4 dq[8][2];
+#pragma unroll
+    for (int db = 0; db < 8; db++)
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++) dq[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // per-lane fragment offsets: straight reads of row j, transposed reads of
+    // rows 4*g + j/4 (+ multiples of 16: same swizzle)
+    int a_row[4], a_col[8];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ (j & 15)) << 4);
+#pragma unroll
+    for (int db = 0; db < 8; db++) {
+        const int row = 4 * g + (j >> 2);
+        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ (row & 15)) << 4) + ((j & 1) << 3);
+    }
+    lds_barrier();
+
+    auto tile = [&](int t, const uint8_t* kt, const uint8_t* vt, uint8_t* kn, uint8_t* vn) __attribute__((always_inline)) {
+        if (t + 1 < T) {
+            issue_tile(ks, (t + 1) * TILE_ROWS, kn, wave, g, j);
+            issue_tile(vs, (t + 1) * TILE_ROWS, vn, wave, g, j);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
+#pragma unroll
+        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
+        // S^T = K Q^T and dP^T = V dO^T: lane (g, j) holds keys 16*kb + 4*g + r of query j
+        f32x4 s[4][2], dp[4][2];
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++) {
+                const bf16x8 kf = read_rows(kt, a_row[kk], kb);
+                const bf16x8 vf = read_rows(vt, a_row[kk], kb);
+#pragma unroll
+                for (int qb = 0; qb < 2; qb++) {
+                    s[kb][qb] = mfma(kf, qf[qb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][qb]);
+                    dp[kb][qb] = mfma(vf, gf[qb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[kb][qb]);
+                }
+            }
+        // dS^T = P^T o (dP^T - delta), P^T = 2^(c s - L log2 e); keys past Skv -> 0
+        bf16x8 dsf[2][2];
+        const int valid = p.Skv - t * TILE_ROWS - 4 * g;
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++) {
+            float dsv[4][4];
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.c, -lse2[qb]));
+                    dsv[kb][r] = (16 * kb + r < valid) ? pw * (dp[kb][qb][r] - dlt[qb]) : 0.f;
+                }
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++) dsf[qb][kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+            for (int db = 0; db < 8; db++) {
+                const bf16x8 kt_f = read_cols(kt, a_col[db], kk);
+#pragma unroll
+                for (int qb = 0; qb < 2; qb++) dq[db][qb] = mfma(kt_f, dsf[qb][kk], dq[db][qb]);
+            }
+        lds_barrier();
+    };
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+        tile(t, sk0, sv0, sk1, sv1);
+        tile(t + 1, sk1, sv1, sk0, sv0);
+    }
+    if (t < T) tile(t, sk0, sv0, sk1, sv1);
+
+    // dQ = scale (dQ^T)^T: lane (g, j) holds dims 16*db + 4*g + r of query j
+    uint16_t* dqb = p.dq + qoff;
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+        const int row = qrow0 + qb * 16 + j;
+        if (row >= p.Sq) continue;
+        uint16_t* dst = dqb + (int64_t)row * p.q_row + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 8; db++) {
+            uint2 pk;
+            pk.x = rtne_bits(dq[db][qb][0] * p.scale) | (rtne_bits(dq[db][qb][1] * p.scale) << 16);
+            pk.y = rtne_bits(dq[db][qb][2] * p.scale) | (rtne_bits(dq[db][qb][3] * p.scale) << 16);
+            *(uint2*)(dst + 16 * db) = pk;
+        }
+    }
+#endif
+}
+
+// ----------------------------------------------------------------- dK, dV
+__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) uint8_t sq0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sq1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sg0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sg1[TILE_BYTES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, j = lane & 15;
+    constexpr int BMK = NW * 16;
+    const int kt_ = blockIdx.x % p.n_kblocks;
+    const int bh = blockIdx.x / p.n_kblocks;
+    const int h = bh % p.H, b = bh / p.H;
+    const int krow = kt_ * BMK + wave * 16 + j;          // this lane's key
+    const int T = (p.Sq + TILE_ROWS - 1) / TILE_ROWS;
+
+    const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
+    const TileSrc qs = tile_src(p.q + qoff, p.q_row, p.Sq);
+    const TileSrc gs = tile_src(p.dO + qoff, p.q_row, p.Sq);
+    issue_tile(qs, 0, sq0, wave, g, j);
+    issue_tile(gs, 0, sg0, wave, g, j);
+
+    // K and V of key krow (clamped; rows past Skv are never stored): operand B
+    const int64_t koff = (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head;
+    bf16x8 kf[4], vf[4];
+    {
+        const int row = min(krow, p.Skv - 1);
+        const uint16_t* ksrc = p.k + koff + (int64_t)row * p.kv_row + 8 * g;
+        const uint16_t* vsrc = p.v + koff + (int64_t)row * p.kv_row + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            kf[kk] = *(const bf16x8*)(ksrc + 32 * kk);
+            vf[kk] = *(const bf16x8*)(vsrc + 32 * kk);
+        }
+    }
+    f32x4 dk[8], dv[8];
+#pragma unroll
+    for (int db = 0; db < 8; db++) { dk[db] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[db] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    int a_row[4], a_col[8];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ (j & 15)) << 4);
+#pragma unroll
+    for (int db = 0; db < 8; db++) {
+        const int row = 4 * g + (j >> 2);
+        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ (row & 15)) << 4) + ((j & 1) << 3);
+    }
+    const float* lse_bh = p.lse + ((int64_t)b * p.H + h) * p.Sq;
+    const float* dlt_bh = p.delta + ((int64_t)b * p.H + h) * p.Sq;
+    lds_barrier();
+
+    auto tile = [&](int t, const uint8_t* qt, const uint8_t* gt, uint8_t* qn, uint8_t* gn) __attribute__((always_inline)) {
+        // L log2 e and delta of queries 64*t + 16*mb + 4*g + r (0 past Sq)
+        float l2[4][4], dl[4][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int q = t * TILE_ROWS + 16 * mb + 4 * g + r;
+                const bool in = q < p.Sq;
+                l2[mb][r] = in ? lse_bh[in ? q : 0] * LOG2E : 0.f;
+                dl[mb][r] = in ? dlt_bh[in ? q : 0] : 0.f;
+            }
+        if (t + 1 < T) {
+            issue_tile(qs, (t + 1) * TILE_ROWS, qn, wave, g, j);
+            issue_tile(gs, (t + 1) * TILE_ROWS, gn, wave, g, j);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
+#pragma unroll
+        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
+        // S = Q K^T, dP = dO V^T: lane (g, j) holds queries 16*mb + 4*g + r of key j
+        f32x4 s[4], dp[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+                const bf16x8 qa = read_rows(qt, a_row[kk], mb);
+                const bf16x8 ga = read_rows(gt, a_row[kk], mb);
+                s[mb] = mfma(qa, kf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mb]);
+                dp[mb] = mfma(ga, vf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[mb]);
+            }
+        // P = 2^(c s - L log2 e), dS = P o (dP - delta); queries past Sq -> 0
+        const int valid = p.Sq - t * TILE_ROWS - 4 * g;
+        float pv[4][4], dsv[4][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const bool in = 16 * mb + r < valid;
+                const float pw = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], p.c, -l2[mb][r])) : 0.f;
+                pv[mb][r] = pw;
+                dsv[mb][r] = pw * (dp[mb][r] - dl[mb][r]);
+            }
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            pf[kk] = pack_b(pv[2 * kk], pv[2 * kk + 1]);
+            dsf[kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+            for (int db = 0; db < 8; db++) {
+                const bf16x8 gtf = read_cols(gt, a_col[db], kk);
+                const bf16x8 qtf = read_cols(qt, a_col[db], kk);
+                dv[db] = mfma(gtf, pf[kk], dv[db]);
+                dk[db] = mfma(qtf, dsf[kk], dk[db]);
+            }
+        lds_barrier();
+    };
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+        tile(t, sq0, sg0, sq1, sg1);
+        tile(t + 1, sq1, sg1, sq0, sg0);
+    }
+    if (t < T) tile(t, sq0, sg0, sq1, sg1);
+
+    // dK = scale (dK^T)^T, dV = (dV^T)^T: lane (g, j) holds dims 16*db + 4*g + r of key j
+    if (krow < p.Skv) {
+        uint16_t* dkd = p.dk + koff + (int64_t)krow * p.kv_row + 4 * g;
+        uint16_t* dvd = p.dv + koff + (int64_t)krow * p.kv_row + 4 * g;
+#pragma unroll
+        for (int db = 0; db < 8; db++) {
+            uint2 a, c;
+            a.x = rtne_bits(dk[db][0] * p.scale) | (rtne_bits(dk[db][1] * p.scale) << 16);
+            a.y = rtne_bits(dk[db][2] * p.scale) | (rtne_bits(dk[db][3] * p.scale) << 16);
+            c.x = rtne_bits(dv[db][0]) | (rtne_bits(dv[db][1]) << 16);
+            c.y = rtne_bits(dv[db][2]) | (rtne_bits(dv[db][3]) << 16);
+            *(uint2*)(dkd + 16 * db) = a;
+            *(uint2*)(dvd + 16 * db) = c;
+        }
+    }
+#endif
+}
+
+int launch_bwd(const BwdParams& p, hipStream_t stream) {
+    const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+    hipLaunchKernelGGL(attn_bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return -1;
+    hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)((int64_t)p.B * p.H * p.n_kblocks)), dim3(NW * 64), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return -1;
+    hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)((int64_t)p.B * p.H * p.n_qblocks)), dim3(NW * 64), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return -1;
+    return 0;
+}
+
+}  // namespace attn_bwd

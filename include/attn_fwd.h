@@ -175,6 +175,35 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
                      int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                      int64_t head_dim, float scale, int causal, int round_mode, void* stream);
 
+/*
+ * attn_bwd_bf16 -- backward pass of attn_fwd_bf16: dQ, dK, dV for a given dO.
+ *
+ * The gradients of O = softmax(Q K^T * scale) V follow from the chain rule on
+ * the forward's definition (the HipKittens summary's kernel suite pairs the
+ * attention forward with its backward); the pass starts, as usual, from the
+ * forward's saved output and per-row log-sum-exp:
+ *     P = exp(scale * Q K^T - lse),   dV = P^T dO,   dP = dO V^T,
+ *     dS = P o (dP - delta),  delta_i = <dO_i, O_i>,
+ *     dQ = scale * dS K,      dK = scale * dS^T Q.
+ *
+ *   q, o, dO   [B,Sq,H,128] or [B,H,Sq,128] bf16, device (read); o is the
+ *              forward output for these q, k, v, scale
+ *   k, v       [B,Skv,H,128] or [B,H,Skv,128] bf16, device (read)
+ *   lse        fp32 [B, H, Sq], device (read): the forward's log-sum-exp
+ *              (attn_fwd_bf16_gqa's lse output), 4-byte aligned
+ *   dq         shaped like q; dk, dv shaped like k (bf16, written, rounded to
+ *              nearest-even); no output may overlap an input or another output
+ *   layout, B, H, Sq, Skv, scale, stream  as attn_fwd_bf16 (H shared by all,
+ *              no mask)
+ *
+ * The accuracy of the gradients follows that of lse and o.  Errors as for
+ * attn_fwd_bf16 (pointers 16-byte aligned, lse 4-byte aligned); the library's
+ * per-device workspace holds delta.  Asynchronous on `stream`.
+ */
+int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, void* dq, void* dk, void* dv, int layout, int64_t B, int64_t H,
+                  int64_t Sq, int64_t Skv, float scale, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* attn_status_string(int status);
 

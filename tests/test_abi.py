@@ -127,3 +127,32 @@ def test_gqa_valid_arguments_reach_device_check():
     assert call_gqa(causal=0, Hkv=8) == -8
     assert call_gqa(lse=FAKE + (4 << 30)) == -8
     assert call_gqa(mode=0x102) == -8
+
+
+def call_bwd(**kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), do=FAKE + (4 << 30),
+             lse=FAKE + (5 << 30), dq=FAKE + (6 << 30), dk=FAKE + (7 << 30), dv=FAKE + (8 << 30), layout=1,
+             B=1, H=2, Sq=64, Skv=64, scale=0.088, stream=0)
+    a.update(kw)
+    return load_library().attn_bwd_bf16(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                                        a["dv"], a["layout"], a["B"], a["H"], a["Sq"], a["Skv"], a["scale"],
+                                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=0), -1), (dict(lse=0), -1), (dict(dv=0), -1), (dict(layout=3), -2), (dict(Sq=0), -4),
+    (dict(Skv=-1), -4), (dict(scale=math.nan), -5), (dict(dq=FAKE + (6 << 30) + 8), -6),
+    (dict(lse=FAKE + (5 << 30) + 2), -6),
+    (dict(dq=FAKE + 64), -7),                           # dq overlaps q
+    (dict(dk=FAKE + (6 << 30) + 16), -7),               # dk overlaps dq
+    (dict(dv=FAKE + (5 << 30)), -7),                    # dv overlaps lse
+])
+def test_bwd_argument_errors_before_device(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_valid_arguments_reach_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_bwd() == -8

@@ -1,0 +1,124 @@
+"""GPU parity of the backward pass (attn_bwd_bf16), through the C ABI.
+
+The backward starts from the forward's output O and log-sum-exp; here both
+come from the oracle (its fp64 output rounded to bf16, and its fp64 lse as
+fp32), and the oracle's gradients take delta_i = <dO_i, O_i> from that same O.
+Every gradient element is gated like the forward output: within 2 bf16 ULP
+and at least 99.9% within 1, the ULP taken at max(|exact|, 2 sigma), sigma the
+RMS size of the terms its sum adds.  The kernels feed P and dS to the MFMAs as
+bf16, which is what the sigma floor absorbs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import gate
+from bf16_attention_forward_amd import workloads as wl
+from tests.helpers import say, to_dev
+
+pytestmark = pytest.mark.gpu
+SCALE = wl.DEFAULT_SCALE
+
+
+def rows_first(bits, layout):
+    """[B,S,H,D] or [B,H,S,D] bits -> [(b*H + h)*S + s, D]."""
+    if layout == "bshd":
+        bits = bits.transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(bits).reshape(-1, bits.shape[-1])
+
+
+def case_inputs(layout, B, H, Sq, Skv, seed):
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, seed, 1.0, 2.0, 1.0)
+    do = wl.random_qkv(layout, B, H, Sq, 1, seed + 5000)[0]
+    fwd = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=SCALE, method=False)
+    o_rows = fwd.rounded("rtne").reshape(B, H, Sq, 128)
+    o_bits = o_rows.transpose(0, 2, 1, 3).copy() if layout == "bshd" else o_rows.copy()
+    o = torch.from_numpy(o_bits.view(np.int16)).view(torch.bfloat16)
+    lse = torch.from_numpy(fwd.lse.astype(np.float32).reshape(B, H, Sq))
+    return q, k, v, do, o, o_bits, lse
+
+
+def run_bwd(q, k, v, o, do, lse, layout):
+    from bf16_attention_forward_amd import attn_bwd_bf16
+    dq, dk, dv = attn_bwd_bf16(to_dev(q), to_dev(k), to_dev(v), to_dev(o), to_dev(do), to_dev(lse),
+                               layout=layout, scale=SCALE)
+    torch.cuda.synchronize()
+    return wl.bits(dq.cpu()), wl.bits(dk.cpu()), wl.bits(dv.cpu())
+
+
+CASES = [
+    ("bshd", 2, 3, 257, 130),    # ragged query and key tails
+    ("bhsd", 1, 2, 300, 1000),   # several key blocks and query tiles
+    ("bhsd", 1, 2, 64, 64),      # one tile each
+    ("bhsd", 1, 1, 700, 333),    # Sq > Skv
+    ("bshd", 1, 2, 1, 77),       # a single query
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}_B{c[1]}H{c[2]}_{c[3]}x{c[4]}")
+def test_backward_matches_oracle(case):
+    layout, B, H, Sq, Skv = case
+    q, k, v, do, o, o_bits, lse = case_inputs(layout, B, H, Sq, Skv, 300 + Sq + Skv)
+    say(f"[case] backward {case}")
+    gq, gk, gv = run_bwd(q, k, v, o, do, lse, layout)
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                               o=o_bits)
+    for name, g, exact, sig in (("dq", gq, ref.dq, ref.sdq), ("dk", gk, ref.dk, ref.sdk), ("dv", gv, ref.dv, ref.sdv)):
+        st = gate.compare(rows_first(g, layout), exact, sig, "rtne")
+        say(f"[gate] backward {case} {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
+        assert st["passed"], (name, st)
+
+
+@pytest.mark.parametrize("sq", [1, 70])
+def test_single_key_backward(sq):
+    """One key: the softmax is constant, so dS = P (dP - delta) = 0 and dQ = dK
+    = 0 exactly, while dV is the sum of dO over the queries.  The kernel forms
+    dP and delta as two fp32 dot products of the same 128 products in different
+    orders; each is within 128 u (u = 2^-24) of the sum of the absolute
+    products (at most 128 max|dO| max|V|), so |dP - delta| <= 2^-9 max|dO|
+    max|V|, and with P <= 1 the gradients stay below scale 2^-9 max|dO| max|V|
+    times max|K| (dQ) or Sq max|Q| (dK)."""
+    layout, B, H = "bhsd", 1, 2
+    q, k, v, do, o, o_bits, lse = case_inputs(layout, B, H, sq, 1, 57 + sq)
+    gq, gk, gv = run_bwd(q, k, v, o, do, lse, layout)
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                               o=o_bits)
+    assert np.all(ref.dq == 0) and np.all(ref.dk == 0)
+    mx = lambda t: float(t.float().abs().max())
+    noise = SCALE * 2.0 ** -9 * mx(do) * mx(v)
+    f = lambda bits: oracle.bf16_bits_to_f64(bits)
+    say(f"[gate] single key sq={sq}: max|dq| {np.abs(f(gq)).max():.2e} max|dk| {np.abs(f(gk)).max():.2e} "
+        f"bounds {noise * mx(k):.2e} {noise * mx(q) * sq:.2e}")
+    assert np.all(np.abs(f(gq)) <= noise * mx(k))
+    assert np.all(np.abs(f(gk)) <= noise * mx(q) * sq)
+    st = gate.compare(rows_first(gv, layout), ref.dv, ref.sdv, "rtne")
+    assert st["passed"], st
+
+
+def test_backward_deterministic():
+    layout, B, H, Sq, Skv = "bhsd", 1, 2, 300, 400
+    q, k, v, do, o, _, lse = case_inputs(layout, B, H, Sq, Skv, 41)
+    a = run_bwd(q, k, v, o, do, lse, layout)
+    b = run_bwd(q, k, v, o, do, lse, layout)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_forward_then_backward_on_the_gpu():
+    """End to end: the GPU forward's O and lse feed the GPU backward, compared
+    with the oracle's gradients for the exact output.  lse is formed from the
+    bf16 weights (error below 2^-8, a common factor on each row's weights) and O
+    is rounded, yet the gradients still meet the same gate."""
+    from bf16_attention_forward_amd import attn_fwd_bf16_gqa, attn_bwd_bf16
+    layout, B, H, Sq, Skv = "bhsd", 1, 2, 300, 500
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 47, 1.0, 2.0, 1.0)
+    do = wl.random_qkv(layout, B, H, Sq, 1, 5047)[0]
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = attn_fwd_bf16_gqa(qd, kd, vd, layout=layout, return_lse=True)
+    dq, dk, dv = attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=layout)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE)
+    for name, g, exact, sig in (("dq", dq, ref.dq, ref.sdq), ("dk", dk, ref.dk, ref.sdk), ("dv", dv, ref.dv, ref.sdv)):
+        st = gate.compare(rows_first(wl.bits(g.cpu()), layout), exact, sig, "rtne")
+        say(f"[gate] fwd+bwd {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f} >2={st['frac_D_gt2']:.5f}")
+        assert st["passed"], (name, st)
