@@ -88,6 +88,11 @@ def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
     return {"wall_s": wall, "ms": per, "flops": w.flops}
 
 
+# algorithmic FLOPs of the backward pass: five products of the forward's
+# size (the recomputed S, dP, dV, dQ, dK) against the forward's two
+BWD_FLOP_FACTOR = 2.5
+
+
 def time_backward(w, steps, warmup):
     """Median ms of attn_bwd_bf16 on workload w (O and lse from the forward)."""
     import torch
@@ -146,6 +151,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time only the backward pass of the workload (one JSON line of its own)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -161,6 +168,19 @@ def main():
         sys.exit(1)
 
     w = wl.WORKLOADS[args.workload]
+    if args.backward:
+        if w.D != 128 or w.causal or w.Hkv:
+            print(f"the backward pass covers non-causal attention with d=128 and H = Hkv; not {w.name}",
+                  file=sys.stderr)
+            sys.exit(2)
+        em = time_backward(w, steps=args.steps, warmup=args.warmup)
+        tf = BWD_FLOP_FACTOR * w.flops / (em * 1e-3) / 1e12
+        print(json.dumps({"metric": "attention bwd TFLOPS (2.5 x 4*B*H*Sq*Skv*d) and % of bf16 MFMA peak",
+                          "value": round(tf, 2), "unit": "TFLOP/s", "median_ms": round(em, 5),
+                          "steps": args.steps, "warmup": args.warmup,
+                          "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "config": {**w.describe(), "pass": "backward"}}), flush=True)
+        return
     r = time_workload(w, args.mode, args.steps, args.warmup)
     ms_step = r["wall_s"] * 1e3 / args.steps
     tflops = w.flops / (ms_step * 1e-3) / 1e12
@@ -193,13 +213,12 @@ def main():
             extra[f"{w.name}:{mode}+weights"] = {"mode": mode, "round_weights": True, "median_ms": round(em, 4),
                                                  "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
 
-        # backward pass of the default workload (algorithmic FLOPs 2.5x the forward's:
-        # five products of the forward's size, dV, dP, dQ, dK and the recomputed S)
+        # backward pass of the default workload
         if w.D == 128 and not w.causal and not w.Hkv:
             em = time_backward(w, steps=20, warmup=5)
-            extra[f"{w.name}:backward"] = {"median_ms": round(em, 4),
-                                           "tflops": round(2.5 * w.flops / (em * 1e-3) / 1e12, 1),
-                                           "frac_peak": round(2.5 * w.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+            tf = BWD_FLOP_FACTOR * w.flops / (em * 1e-3) / 1e12
+            extra[f"{w.name}:backward"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),
+                                           "frac_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
 

@@ -16,13 +16,18 @@
 //    V read as operand A, the forward's K-as-A layout, so each lane holds one
 //    query), then dS^T elementwise, then dQ^T += K^T dS^T with K^T read by
 //    ds_read_b64_tr_b16 in the order of dS^T's keys (the forward's V^T read).
-//  * attn_bwd_dkdv: the mirror image -- a work-group of 8 waves owns 128 keys
-//    (16 per wave, K and V fragments in registers as operand B) and streams
+//  * attn_bwd_dkdv: the mirror image -- a work-group owns 128 keys (8 waves x
+//    16 or 4 waves x 32, K and V fragments in registers as operand B) and streams
 //    64-query Q and dO tiles.  Per tile: S = Q K^T and dP = dO V^T (Q and dO as
 //    operand A: each lane holds one key), then P and dS, then dV^T += dO^T P
 //    and dK^T += Q^T dS with dO^T and Q^T transposed out of LDS.
 // Every LDS tile is read both straight (ds_read_b128) and transposed, so all
-// tiles keep one layout: chunk c of row r at c ^ (r & 15).  P and dS enter the
+// tiles keep one layout: 16-byte chunk c of row r at c ^ swz(r), where
+// swz(r) = 2 (r & 7) + ((r >> 3) & 1) takes 16 distinct values over any 16
+// rows in a row (straight reads: 16 rows at one chunk column, no two lanes in
+// one bank) and keeps chunk pairs together with 8 distinct pair positions
+// over any 8 rows in a row (transposed reads: 8 rows x one 32-byte pair per
+// half-wave).  P and dS enter the
 // MFMAs as bf16 (round to nearest-even); all sums are fp32; the gradients are
 // rounded to bf16 (nearest-even).
 #include <hip/hip_runtime.h>
@@ -38,6 +43,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int D = 128;
@@ -67,27 +73,53 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // The 64-row tile at row r0 of a tensor (row stride row_elems) into LDS with
-// buffer_load ... lds, 8 waves x 2 rounds of 32 rows: lane (g, j) of wave w in
-// round i writes row 32*i + 4*w + g, chunk position j, holding the source
-// chunk j ^ (row & 15); rows past `rows` read as zero (buffer range check).
+// buffer_load ... lds: NWK waves move it in 16 / NWK rounds of 4 * NWK rows;
+// lane (g, j) of wave w in round i writes row 4*NWK*i + 4*w + g, chunk
+// position j, holding the source chunk j ^ swz(row) (4*NWK is a multiple of
+// 16, so one swizzle serves every round).  Rows past `rows` read as zero (the
+// buffer's range check).  The loads are issued from inline assembly: the
+// compiler then adds no vmcnt waits of its own in front of the LDS reads of
+// the other buffer (it cannot tell the two buffers apart); every wave waits
+// for its own transfers in lds_barrier.
+// chunk swizzle of row r (only r mod 16 matters)
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 struct TileSrc {
-    __amdgpu_buffer_rsrc_t rs;
+    i32x4 rs;
     int row_bytes;
 };
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
 __device__ __forceinline__ TileSrc tile_src(const uint16_t* base, int64_t row_elems, int rows) {
     TileSrc t;
     t.row_bytes = (int)(row_elems * 2);
-    const uint32_t nrec = (uint32_t)((int64_t)(rows - 1) * t.row_bytes + ROW_BYTES);
-    t.rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, 0x00020000);
+    t.rs = buffer_rsrc(base, (uint32_t)((int64_t)(rows - 1) * t.row_bytes + ROW_BYTES));
     return t;
 }
-__device__ __forceinline__ void issue_tile(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
-    const int row = wave * 4 + g;                        // + 32 * i (same swizzle)
-    const int voff = row * s.row_bytes + ((j ^ (row & 15)) << 4);
+// 16 bytes per lane from rs at voff + soff to LDS dst + 16 * lane
+__device__ __forceinline__ void dma16(const i32x4 rs, uint8_t* dst, int voff, int soff) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst;
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+// 4 bytes per lane from rs at voff + soff to LDS dst + 4 * lane
+__device__ __forceinline__ void dma4(const i32x4 rs, uint8_t* dst, int voff, int soff) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst;
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+template <int NWK>
+__device__ __forceinline__ void issue_tile_n(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
+    static_assert(NWK == 4 || NWK == 8, "4 or 8 waves");
+    const int row = wave * 4 + g;
+    const int voff = row * s.row_bytes + ((j ^ swz(row)) << 4);
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rs, (LDS_AS void*)(dst + ((i * NW + wave) * 64) * 16), 16,
-                                                 voff, (r0 + 32 * i) * s.row_bytes, 0, 0);
+    for (int i = 0; i < 16 / NWK; i++)
+        dma16(s.rs, dst + ((i * NWK + wave) * 64) * 16, voff, (r0 + 4 * NWK * i) * s.row_bytes);
+}
+__device__ __forceinline__ void issue_tile(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
+    issue_tile_n<NW>(s, r0, dst, wave, g, j);
 }
 
 // Straight fragment (operand A): lane (g, j) gets row 16*rb + j, dims
@@ -109,15 +141,16 @@ __device__ __forceinline__ bf16x8 read_cols(const uint8_t* tile, int addr0, int 
 }
 
 // Packs a C fragment pair (row blocks 2*ks, 2*ks+1 of 16 rows, 4 per lane)
-// into the bf16 B operand whose k index runs over those 32 rows.
+// into the bf16 B operand whose k index runs over those 32 rows (hardware
+// conversion, round to nearest-even).
 __device__ __forceinline__ bf16x8 pack_b(const float* lo4, const float* hi4) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        r[e] = __builtin_bit_cast(__bf16, (uint16_t)rtne_bits(lo4[e]));
-        r[4 + e] = __builtin_bit_cast(__bf16, (uint16_t)rtne_bits(hi4[e]));
-    }
-    return r;
+    const bf16x2 a = __builtin_convertvector((f32x2{lo4[0], lo4[1]}), bf16x2);
+    const bf16x2 b = __builtin_convertvector((f32x2{lo4[2], lo4[3]}), bf16x2);
+    const bf16x2 c = __builtin_convertvector((f32x2{hi4[0], hi4[1]}), bf16x2);
+    const bf16x2 d = __builtin_convertvector((f32x2{hi4[2], hi4[3]}), bf16x2);
+    const bf16x4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const bf16x4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // ---------------------------------------------------------------- delta
@@ -145,14 +178,19 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
 }
 
 // ------------------------------------------------------------------- dQ
+// 8 waves, each owning 32 query rows (Q and dO fragments in registers as
+// operand B).  The same software pipeline and out-of-phase wave groups as the
+// dK/dV kernel below: iteration t runs dQ^T += K_{t-1}^T dS^T_{t-1} (K_{t-1}
+// read transposed) and S^T_t = K_t Q^T, dP^T_t = V_t dO^T (tiles t read
+// straight), then the elementwise step of tile t; three K/V slots.
+constexpr int NSLOT = 3;
+
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __shared__ __attribute__((aligned(1024))) uint8_t sk0[TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sk1[TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sv0[TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sv1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[NSLOT * 2 * TILE_BYTES];   // per slot: K, V
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool late = wave >= 4;
     const int g = lane >> 4, j = lane & 15;
     constexpr int BMQ = NW * 32;
     const int qt = blockIdx.x % p.n_qblocks;
@@ -163,8 +201,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 
     const TileSrc ks = tile_src(p.k + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
     const TileSrc vs = tile_src(p.v + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
-    issue_tile(ks, 0, sk0, wave, g, j);
-    issue_tile(vs, 0, sv0, wave, g, j);
+    auto kslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES); };
+    auto vslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
+    // tile 0: all 8 waves; later tiles: waves 0-3
+    issue_tile_n<NW>(ks, 0, kslot(0), wave, g, j);
+    issue_tile_n<NW>(vs, 0, vslot(0), wave, g, j);
+    auto issue_next = [&](int t) __attribute__((always_inline)) {
+        if (!late && t < T) {
+            const int sl = t % NSLOT;
+            issue_tile_n<4>(ks, t * TILE_ROWS, kslot(sl), wave, g, j);
+            issue_tile_n<4>(vs, t * TILE_ROWS, vslot(sl), wave, g, j);
+        }
+    };
 
     // Q and dO of query rows qrow0 + 16*qb + j (clamped; results of rows past
     // Sq are never stored), dims 32*kk + 8*g .. +7: operand B.
@@ -185,6 +233,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         lse2[qb] = p.lse[ri] * LOG2E;
         dlt[qb] = p.delta[ri];
     }
+    // Wait for these loads here, once: the register uses below make the
+    // compiler place the waits before the loop instead of inside it, where
+    // they would also wait for the tile transfers in flight.
+#pragma unroll
+    for (int qb = 0; qb < 2; qb++) {
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) __asm__ volatile("" : "+v"(qf[qb][kk]), "+v"(gf[qb][kk]));
+        __asm__ volatile("" : "+v"(lse2[qb]), "+v"(dlt[qb]));
+    }
     f32x4 dq[8][2];
 #pragma unroll
     for (int db = 0; db < 8; db++)
@@ -195,25 +252,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     // rows 4*g + j/4 (+ multiples of 16: same swizzle)
     int a_row[4], a_col[8];
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ (j & 15)) << 4);
+    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ swz(j)) << 4);
 #pragma unroll
     for (int db = 0; db < 8; db++) {
         const int row = 4 * g + (j >> 2);
-        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ (row & 15)) << 4) + ((j & 1) << 3);
+        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz(row)) << 4) + ((j & 1) << 3);
     }
     lds_barrier();
 
-    auto tile = [&](int t, const uint8_t* kt, const uint8_t* vt, uint8_t* kn, uint8_t* vn) __attribute__((always_inline)) {
-        if (t + 1 < T) {
-            issue_tile(ks, (t + 1) * TILE_ROWS, kn, wave, g, j);
-            issue_tile(vs, (t + 1) * TILE_ROWS, vn, wave, g, j);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
-#pragma unroll
-        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
-        // S^T = K Q^T and dP^T = V dO^T: lane (g, j) holds keys 16*kb + 4*g + r of query j
-        f32x4 s[4][2], dp[4][2];
+    f32x4 s[4][2], dp[4][2];   // S^T, dP^T of tile t: lane (g, j) holds keys 16*kb + 4*g + r of query j
+    bf16x8 dsf[2][2];          // dS^T of the previous tile as operand B (k = keys)
+    // S^T = K Q^T and dP^T = V dO^T of the tiles in slot sl
+    auto products_a = [&](int sl) __attribute__((always_inline)) {
+        const uint8_t* kt = kslot(sl);
+        const uint8_t* vt = vslot(sl);
 #pragma unroll
         for (int kk = 0; kk < 4; kk++)
 #pragma unroll
@@ -226,8 +278,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
                     dp[kb][qb] = mfma(vf, gf[qb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[kb][qb]);
                 }
             }
-        // dS^T = P^T o (dP^T - delta), P^T = 2^(c s - L log2 e); keys past Skv -> 0
-        bf16x8 dsf[2][2];
+    };
+    // dQ^T += K^T dS^T with the K tile in slot sl
+    auto products_b = [&](int sl) __attribute__((always_inline)) {
+        const uint8_t* kt = kslot(sl);
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+            for (int db = 0; db < 8; db++) {
+                const bf16x8 kt_f = read_cols(kt, a_col[db], kk);
+#pragma unroll
+                for (int qb = 0; qb < 2; qb++) dq[db][qb] = mfma(kt_f, dsf[qb][kk], dq[db][qb]);
+            }
+    };
+    // dS^T = P^T o (dP^T - delta), P^T = 2^(c s - L log2 e) of tile t; keys past Skv -> 0
+    auto elementwise = [&](int t) __attribute__((always_inline)) {
         const int valid = p.Skv - t * TILE_ROWS - 4 * g;
 #pragma unroll
         for (int qb = 0; qb < 2; qb++) {
@@ -242,23 +307,46 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) dsf[qb][kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
         }
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-            for (int db = 0; db < 8; db++) {
-                const bf16x8 kt_f = read_cols(kt, a_col[db], kk);
-#pragma unroll
-                for (int qb = 0; qb < 2; qb++) dq[db][qb] = mfma(kt_f, dsf[qb][kk], dq[db][qb]);
-            }
+    };
+    // barrier of waves 0-3: after their elementwise step (the operands keep the
+    // compiler from sinking that step below the barrier)
+    auto early_barrier = [&]() __attribute__((always_inline)) {
+        __asm__ volatile("" :: "v"(dsf[0][0]), "v"(dsf[0][1]), "v"(dsf[1][0]), "v"(dsf[1][1]));
         lds_barrier();
     };
-    int t = 0;
-    for (; t + 1 < T; t += 2) {
-        tile(t, sk0, sv0, sk1, sv1);
-        tile(t + 1, sk1, sv1, sk0, sv0);
+    auto pin_addr = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
+#pragma unroll
+        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
+    };
+
+    // iteration 0: products of tile 0 only
+    issue_next(1);
+    pin_addr();
+    __builtin_amdgcn_s_setprio(1);
+    products_a(0);
+    __builtin_amdgcn_s_setprio(0);
+    if (late) lds_barrier();
+    elementwise(0);
+    if (!late) early_barrier();
+    int cur = 1 % NSLOT, prev = 0;
+    for (int t = 1; t < T; t++) {
+        issue_next(t + 1);
+        pin_addr();
+        __builtin_amdgcn_s_setprio(1);
+        products_b(prev);   // first: dS^T of tile t-1 is then dead while S^T, dP^T accumulate
+        products_a(cur);
+        __builtin_amdgcn_s_setprio(0);
+        if (late) lds_barrier();
+        elementwise(t);
+        if (!late) early_barrier();
+        prev = cur;
+        cur = cur == NSLOT - 1 ? 0 : cur + 1;
     }
-    if (t < T) tile(t, sk0, sv0, sk1, sv1);
+    // the last tile's dQ products (no LDS writes follow: no barrier)
+    pin_addr();
+    products_b(prev);
 
     // dQ = scale (dQ^T)^T: lane (g, j) holds dims 16*db + 4*g + r of query j
     uint16_t* dqb = p.dq + qoff;
@@ -279,33 +367,67 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 }
 
 // ----------------------------------------------------------------- dK, dV
+// 8 waves, each owning 16 keys (K and V fragments in registers as operand B).
+// Software pipeline over the 64-query tiles: iteration t runs the products of
+// two tiles back to back -- S_t = Q_t K^T and dP_t = dO_t V^T (tile t read
+// straight), then dV^T += dO_{t-1}^T P_{t-1} and dK^T += Q_{t-1}^T dS_{t-1}
+// (tile t-1 read transposed) -- and then the elementwise step of tile t
+// (P_t, dS_t), so LDS holds three tiles (t-1, t, and t+1 in flight).  The two
+// waves of a SIMD are out of phase: waves 0-3 take the iteration's barrier
+// after the elementwise step, waves 4-7 before it, so one wave's exp and
+// packing run while the other's products keep the matrix core busy.  Waves
+// 0-3 issue all transfers of tile t+1 at the start of iteration t and wait
+// for them before their barrier.
+// (4 waves x 32 keys halves the LDS bytes per product but needs more than 256
+// registers per wave, one wave per SIMD; measured slower.)
+constexpr int LS_BYTES = 2 * TILE_ROWS * 4;   // L and delta of a tile's 64 queries
+
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __shared__ __attribute__((aligned(1024))) uint8_t sq0[TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sq1[TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sg0[TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sg1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[NSLOT * 2 * TILE_BYTES];   // per slot: Q, dO
+    __shared__ __attribute__((aligned(16))) uint8_t lsd[NSLOT * LS_BYTES];           // per slot: L, delta
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool late = wave >= 4;
     const int g = lane >> 4, j = lane & 15;
-    constexpr int BMK = NW * 16;
     const int kt_ = blockIdx.x % p.n_kblocks;
     const int bh = blockIdx.x / p.n_kblocks;
     const int h = bh % p.H, b = bh / p.H;
-    const int krow = kt_ * BMK + wave * 16 + j;          // this lane's key
+    const int kbase = kt_ * (NW * 16) + wave * 16;       // this wave's first key
     const int T = (p.Sq + TILE_ROWS - 1) / TILE_ROWS;
 
     const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
     const TileSrc qs = tile_src(p.q + qoff, p.q_row, p.Sq);
     const TileSrc gs = tile_src(p.dO + qoff, p.q_row, p.Sq);
-    issue_tile(qs, 0, sq0, wave, g, j);
-    issue_tile(gs, 0, sg0, wave, g, j);
+    // L and delta of queries past Sq read as zero (range check)
+    const int64_t rbh = ((int64_t)b * p.H + h) * p.Sq;
+    const i32x4 lrs = buffer_rsrc(p.lse + rbh, (uint32_t)p.Sq * 4u);
+    const i32x4 drs = buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u);
+    auto qslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES); };
+    auto gslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
+    auto lslot = [&](int sl) { return lsd + sl * LS_BYTES; };
+    auto issue_ls = [&](int q0, int sl) {
+        dma4(lrs, lslot(sl), lane * 4, q0 * 4);
+        dma4(drs, lslot(sl) + TILE_ROWS * 4, lane * 4, q0 * 4);
+    };
+    // tile 0: all 8 waves; later tiles: waves 0-3
+    issue_tile_n<NW>(qs, 0, qslot(0), wave, g, j);
+    issue_tile_n<NW>(gs, 0, gslot(0), wave, g, j);
+    if (wave == 0) issue_ls(0, 0);
+    auto issue_next = [&](int t) __attribute__((always_inline)) {
+        if (!late && t < T) {
+            const int sl = t % NSLOT;
+            issue_tile_n<4>(qs, t * TILE_ROWS, qslot(sl), wave, g, j);
+            issue_tile_n<4>(gs, t * TILE_ROWS, gslot(sl), wave, g, j);
+            if (wave == 0) issue_ls(t * TILE_ROWS, sl);
+        }
+    };
 
-    // K and V of key krow (clamped; rows past Skv are never stored): operand B
+    // K and V of keys kbase + j (clamped; rows past Skv are never stored)
     const int64_t koff = (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head;
     bf16x8 kf[4], vf[4];
     {
-        const int row = min(krow, p.Skv - 1);
+        const int row = min(kbase + j, p.Skv - 1);
         const uint16_t* ksrc = p.k + koff + (int64_t)row * p.kv_row + 8 * g;
         const uint16_t* vsrc = p.v + koff + (int64_t)row * p.kv_row + 8 * g;
 #pragma unroll
@@ -314,43 +436,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
             vf[kk] = *(const bf16x8*)(vsrc + 32 * kk);
         }
     }
+    // wait for these loads here, once (as in the dQ kernel)
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) __asm__ volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
     f32x4 dk[8], dv[8];
 #pragma unroll
     for (int db = 0; db < 8; db++) { dk[db] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[db] = f32x4{0.f, 0.f, 0.f, 0.f}; }
     int a_row[4], a_col[8];
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ (j & 15)) << 4);
+    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ swz(j)) << 4);
 #pragma unroll
     for (int db = 0; db < 8; db++) {
         const int row = 4 * g + (j >> 2);
-        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ (row & 15)) << 4) + ((j & 1) << 3);
+        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz(row)) << 4) + ((j & 1) << 3);
     }
-    const float* lse_bh = p.lse + ((int64_t)b * p.H + h) * p.Sq;
-    const float* dlt_bh = p.delta + ((int64_t)b * p.H + h) * p.Sq;
     lds_barrier();
 
-    auto tile = [&](int t, const uint8_t* qt, const uint8_t* gt, uint8_t* qn, uint8_t* gn) __attribute__((always_inline)) {
-        // L log2 e and delta of queries 64*t + 16*mb + 4*g + r (0 past Sq)
-        float l2[4][4], dl[4][4];
-#pragma unroll
-        for (int mb = 0; mb < 4; mb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int q = t * TILE_ROWS + 16 * mb + 4 * g + r;
-                const bool in = q < p.Sq;
-                l2[mb][r] = in ? lse_bh[in ? q : 0] * LOG2E : 0.f;
-                dl[mb][r] = in ? dlt_bh[in ? q : 0] : 0.f;
-            }
-        if (t + 1 < T) {
-            issue_tile(qs, (t + 1) * TILE_ROWS, qn, wave, g, j);
-            issue_tile(gs, (t + 1) * TILE_ROWS, gn, wave, g, j);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
-#pragma unroll
-        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
-        // S = Q K^T, dP = dO V^T: lane (g, j) holds queries 16*mb + 4*g + r of key j
-        f32x4 s[4], dp[4];
+    f32x4 s[4], dp[4];        // S and dP of tile t: lane (g, j) holds queries 16*mb + 4*g + r of key j
+    bf16x8 pf[2], dsf[2];     // P and dS of the previous tile as operand B (k = queries)
+    // S = Q K^T, dP = dO V^T of the tile in slot sl
+    auto products_a = [&](int sl) __attribute__((always_inline)) {
+        const uint8_t* qt = qslot(sl);
+        const uint8_t* gt = gslot(sl);
 #pragma unroll
         for (int kk = 0; kk < 4; kk++)
 #pragma unroll
@@ -360,25 +467,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
                 s[mb] = mfma(qa, kf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mb]);
                 dp[mb] = mfma(ga, vf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[mb]);
             }
-        // P = 2^(c s - L log2 e), dS = P o (dP - delta); queries past Sq -> 0
-        const int valid = p.Sq - t * TILE_ROWS - 4 * g;
-        float pv[4][4], dsv[4][4];
-#pragma unroll
-        for (int mb = 0; mb < 4; mb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const bool in = 16 * mb + r < valid;
-                const float pw = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], p.c, -l2[mb][r])) : 0.f;
-                pv[mb][r] = pw;
-                dsv[mb][r] = pw * (dp[mb][r] - dl[mb][r]);
-            }
-        bf16x8 pf[2], dsf[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            pf[kk] = pack_b(pv[2 * kk], pv[2 * kk + 1]);
-            dsf[kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS
+    };
+    // dV^T += dO^T P, dK^T += Q^T dS with the tile in slot sl
+    auto products_b = [&](int sl) __attribute__((always_inline)) {
+        const uint8_t* qt = qslot(sl);
+        const uint8_t* gt = gslot(sl);
 #pragma unroll
         for (int kk = 0; kk < 2; kk++)
 #pragma unroll
@@ -388,16 +481,72 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
                 dv[db] = mfma(gtf, pf[kk], dv[db]);
                 dk[db] = mfma(qtf, dsf[kk], dk[db]);
             }
+    };
+    // P = 2^(c s - L log2 e), dS = P o (dP - delta) of tile t; queries past Sq -> 0
+    auto elementwise = [&](int t, int sl) __attribute__((always_inline)) {
+        const uint8_t* lt = lslot(sl);
+        const int valid = p.Sq - t * TILE_ROWS - 4 * g;
+        float pv[4][4], dsv[4][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+            const f32x4 l2 = *(const LDS_AS f32x4*)(LDS_AS const uint8_t*)(lt + (16 * mb + 4 * g) * 4) * LOG2E;
+            const f32x4 dl = *(const LDS_AS f32x4*)(LDS_AS const uint8_t*)(lt + TILE_ROWS * 4 + (16 * mb + 4 * g) * 4);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const bool in = 16 * mb + r < valid;
+                const float pw = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], p.c, -l2[r])) : 0.f;
+                pv[mb][r] = pw;
+                dsv[mb][r] = pw * (dp[mb][r] - dl[r]);
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            pf[kk] = pack_b(pv[2 * kk], pv[2 * kk + 1]);
+            dsf[kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
+        }
+    };
+    // barrier of waves 0-3: after their elementwise step (the operands keep the
+    // compiler from sinking that step below the barrier)
+    auto early_barrier = [&]() __attribute__((always_inline)) {
+        __asm__ volatile("" :: "v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
         lds_barrier();
     };
-    int t = 0;
-    for (; t + 1 < T; t += 2) {
-        tile(t, sq0, sg0, sq1, sg1);
-        tile(t + 1, sq1, sg1, sq0, sg0);
+    auto pin_addr = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
+#pragma unroll
+        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
+    };
+
+    // iteration 0: products of tile 0 only
+    issue_next(1);
+    pin_addr();
+    __builtin_amdgcn_s_setprio(1);
+    products_a(0);
+    __builtin_amdgcn_s_setprio(0);
+    if (late) lds_barrier();
+    elementwise(0, 0);
+    if (!late) early_barrier();
+    int cur = 1 % NSLOT, prev = 0;
+    for (int t = 1; t < T; t++) {
+        issue_next(t + 1);
+        pin_addr();
+        __builtin_amdgcn_s_setprio(1);
+        products_a(cur);
+        products_b(prev);
+        __builtin_amdgcn_s_setprio(0);
+        if (late) lds_barrier();
+        elementwise(t, cur);
+        if (!late) early_barrier();
+        prev = cur;
+        cur = cur == NSLOT - 1 ? 0 : cur + 1;
     }
-    if (t < T) tile(t, sq0, sg0, sq1, sg1);
+    // the last tile's dV, dK products (no LDS writes follow: no barrier)
+    pin_addr();
+    products_b(prev);
 
     // dK = scale (dK^T)^T, dV = (dV^T)^T: lane (g, j) holds dims 16*db + 4*g + r of key j
+    const int krow = kbase + j;
     if (krow < p.Skv) {
         uint16_t* dkd = p.dk + koff + (int64_t)krow * p.kv_row + 4 * g;
         uint16_t* dvd = p.dv + koff + (int64_t)krow * p.kv_row + 4 * g;
@@ -419,7 +568,7 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.B * p.H * p.Sq;
     hipLaunchKernelGGL(attn_bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
-    hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)((int64_t)p.B * p.H * p.n_kblocks)), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)((int64_t)p.B * p.H * p.n_kblocks)), dim3(8 * 64), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
     hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)((int64_t)p.B * p.H * p.n_qblocks)), dim3(NW * 64), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
