@@ -117,7 +117,7 @@ extern "C" const char* attn_status_string(int status) {
         case ATTN_ERR_DEVICE: return "the current device is not a gfx950 GPU";
         case ATTN_ERR_WORKSPACE: return "split workspace unavailable (allocation failed or stream is being captured)";
         case ATTN_ERR_LAUNCH: return "kernel launch failed";
-        case ATTN_ERR_OPTION: return "kv_splits, block_order or causal out of range";
+        case ATTN_ERR_OPTION: return "kv_splits, block_order, waves or causal out of range";
         default: return "unknown status";
     }
 }
@@ -128,7 +128,7 @@ namespace {
 int run_attention(const void* q, const void* k, const void* v, void* o, float* lse,
                   int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t head_dim,
                   float scale, int causal, int round_mode, void* stream,
-                  int kv_splits, int block_order) {
+                  int kv_splits, int block_order, int waves) {
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
     const int out_mode = round_mode & ~ATTN_ROUND_WEIGHTS;
@@ -146,7 +146,14 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     if (n_q > ((int64_t)1 << 52) / kHeadDim || n_kv > ((int64_t)1 << 52) / kHeadDim) return ATTN_ERR_SHAPE;
     const int64_t kv_row = (layout == ATTN_LAYOUT_BSHD) ? Hkv * kHeadDim : kHeadDim;
     if ((Skv - 1) * kv_row * 2 + kHeadDim * 2 >= lim31) return ATTN_ERR_SHAPE;
-    const int64_t n_qtiles = (Sq + KERNEL_BM - 1) / KERNEL_BM;
+    // work-group size: the 4-wave group (two per CU) for short key ranges
+    const int64_t n_kv_tiles64 = (Skv + kKeyTile - 1) / kKeyTile;
+    const bool short_ok = head_dim == 128 && !causal;   // where the 4-wave variant exists
+    if (waves != 0 && waves != KERNEL_NW && !(waves == KERNEL_NW_SHORT && short_ok)) return ATTN_ERR_OPTION;
+    const int nw = waves ? waves
+                         : ((short_ok && n_kv_tiles64 <= KERNEL_SHORT_KV_TILES) ? KERNEL_NW_SHORT : KERNEL_NW);
+    const int64_t bm = (int64_t)nw * 16 * KERNEL_NQB;   // query rows per work item
+    const int64_t n_qtiles = (Sq + bm - 1) / bm;
     if (B * H * n_qtiles * kMaxSplits >= lim31) return ATTN_ERR_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return ATTN_ERR_ALIGN;
@@ -193,16 +200,18 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.round_mode = out_mode;
     p.p_mode = (round_mode & ATTN_ROUND_WEIGHTS) ? out_mode : ATTN_ROUND_RTNE;
     p.head_dim = (int)head_dim;
+    p.nw = nw;
     p.c = (float)((double)scale * 1.4426950408889634073599246810018921);
 
     // ---- plan the key-range split
-    // One work-group fills a CU (two waves per SIMD), so a launch runs in
-    // rounds of n_cu items.  When the last round is ragged, the items of that
+    // The resident work-groups (one 8-wave or two 4-wave groups per CU: two
+    // waves per SIMD) run the items in rounds of `slots` items.  When the
+    // last round is ragged, the items of that
     // round have their key range split so that the round fills the chip (the
     // tail split); when there is less than one round of items, every item is
     // split.  A forced kv_splits = n splits every item n ways.
     const int n_kv_tiles = (int)((Skv + kKeyTile - 1) / kKeyTile);
-    const int slots = info.n_cu * KERNEL_WG_PER_CU;
+    const int slots = info.n_cu * (8 / nw);   // resident work-groups: two waves per SIMD
     int n_full = p.n_items, splits = 1;
     if (causal) {
         // Causal items differ in length (the diagonal): they run unsplit,
@@ -232,12 +241,12 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
 
     if (n_full < p.n_items) {
         const size_t n_part = (size_t)(p.n_items - n_full) * splits;
-        const size_t need = n_part * KERNEL_BM * (kHeadDim + 2) * sizeof(float);
+        const size_t need = n_part * bm * (kHeadDim + 2) * sizeof(float);
         void* ws = nullptr;
         const int wrc = get_workspace(dev, stream, need, &ws);
         if (wrc != ATTN_OK) return wrc;
         p.ws_o = (float*)ws;
-        p.ws_ml = (float*)((char*)ws + n_part * KERNEL_BM * kHeadDim * sizeof(float));
+        p.ws_ml = (float*)((char*)ws + n_part * bm * kHeadDim * sizeof(float));
     }
 
     if (attn::launch(p, (hipStream_t)stream) != 0) return ATTN_ERR_LAUNCH;
@@ -249,15 +258,15 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
 extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
                                 int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                                 float scale, int round_mode, void* stream,
-                                int kv_splits, int block_order) {
+                                int kv_splits, int block_order, int waves) {
     return run_attention(q, k, v, o, nullptr, layout, B, H, H, Sq, Skv, 128, scale, 0, round_mode, stream,
-                         kv_splits, block_order);
+                         kv_splits, block_order, waves);
 }
 
 extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                  float scale, int causal, int round_mode, void* stream) {
-    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, 128, scale, causal, round_mode, stream, 0, 0);
+    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, 128, scale, causal, round_mode, stream, 0, 0, 0);
 }
 
 extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -324,11 +333,11 @@ extern "C" int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, voi
                                 int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                 int64_t head_dim, float scale, int causal, int round_mode, void* stream) {
     return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, head_dim, scale, causal, round_mode,
-                         stream, 0, 0);
+                         stream, 0, 0, 0);
 }
 
 extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                              int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                              float scale, int round_mode, void* stream) {
-    return attn_fwd_bf16_ex(q, k, v, o, layout, B, H, Sq, Skv, scale, round_mode, stream, 0, 0);
+    return attn_fwd_bf16_ex(q, k, v, o, layout, B, H, Sq, Skv, scale, round_mode, stream, 0, 0, 0);
 }

@@ -3,13 +3,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Tiling of the compiled kernel: KERNEL_NW waves per work-group, each owning
+// Tiling of the kernels: KERNEL_NW waves per work-group, each owning
 // KERNEL_NQB blocks of 16 query rows; KERNEL_BM query rows per work item.
+// Short key ranges (at most KERNEL_SHORT_KV_TILES tiles of 64 keys, head
+// dimension 128, no causal mask) use work-groups of KERNEL_NW_SHORT waves
+// instead, two per CU: a work item then spends a large share of its time
+// loading Q and storing O, and a second resident work-group keeps the
+// matrix cores busy meanwhile.
 #ifndef KERNEL_NQB
 #define KERNEL_NQB 2
 #endif
 #ifndef KERNEL_NW
 #define KERNEL_NW 8
+#endif
+#ifndef KERNEL_NW_SHORT
+#define KERNEL_NW_SHORT 4
+#endif
+#ifndef KERNEL_SHORT_KV_TILES
+#define KERNEL_SHORT_KV_TILES 16
 #endif
 #define KERNEL_BM (KERNEL_NW * 16 * KERNEL_NQB)
 // work-groups resident per CU: two waves per SIMD in total (the register
@@ -45,6 +56,7 @@ struct AttnParams {
     int round_mode;
     int head_dim;      // 128 or 64
     int p_mode;        // rounding of the in-loop bf16 weights (ROUND_RTNE unless asked otherwise)
+    int nw;            // waves per work-group: KERNEL_NW, or KERNEL_NW_SHORT (query tile nw * 16 * KERNEL_NQB rows)
     float c;           // fp32(scale * log2(e))
 };
 

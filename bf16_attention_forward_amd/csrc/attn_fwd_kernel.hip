@@ -80,9 +80,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BN = 64;          // keys per K/V tile
-constexpr int NW = KERNEL_NW;   // waves per work-group
 constexpr int NQB = KERNEL_NQB; // 16-row query blocks per wave
-constexpr int BM = KERNEL_BM;   // query rows per work item
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float WEIGHT_LIMIT = 65536.0f;    // a lane's tile sum of weights above this triggers a new offset
 
@@ -159,11 +157,14 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// 8 waves, each owning 32 query rows of the work item; see the file header
-// for the per-tile schedule.
-template <int HD, bool CPOS, bool CAUSAL, int PMODE>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_main(const AttnParams p) {
+// NWT waves (8, or 4 for short key ranges), each owning 32 query rows of the
+// work item; see the file header for the per-tile schedule.
+template <int HD, bool CPOS, bool CAUSAL, int PMODE, int NWT>
+__global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+    static_assert(NWT == 8 || NWT == 4, "8 waves (one work-group per CU) or 4 (two)");
+    constexpr int NW = NWT;                      // waves per work-group
+    constexpr int BM = NW * 16 * NQB;            // query rows per work item
     static_assert(HD == 128 || HD == 64, "head dimension 128 or 64");
     constexpr int ROW_BYTES = HD * 2;
     constexpr int TILE_BYTES = BN * ROW_BYTES;   // 16 KiB (HD = 128) or 8 KiB
@@ -748,19 +749,33 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
 
 // ------------------------------------------------------------------ launch
 int launch(const AttnParams& p, hipStream_t stream) {
-    dim3 grid(p.n_blocks), block(NW * 64);
-    // The head dimension, c > 0 (the usual positive scale), the causal mask
-    // and the weights' rounding mode are compile-time variants, so the plain
-    // path carries no code for any alternative.
-    auto go = [&](auto hd, auto cpos, auto causal) {
-        constexpr int H_ = decltype(hd)::value;
+    // The head dimension, c > 0 (the usual positive scale), the causal mask,
+    // the weights' rounding mode and the work-group size are compile-time
+    // variants, so the plain path carries no code for any alternative.  The
+    // 4-wave work-group exists for head dimension 128 without the causal mask.
+    const bool short_wg = p.nw == KERNEL_NW_SHORT;
+    if (p.nw != KERNEL_NW && !(short_wg && p.head_dim == 128 && !p.causal)) return -1;
+    dim3 grid(p.n_blocks), block(p.nw * 64);
+    auto go_nw = [&](auto hd, auto cpos, auto causal, auto nw) {
+        constexpr int H_ = decltype(hd)::value, N_ = decltype(nw)::value;
         constexpr bool CP = decltype(cpos)::value, CA = decltype(causal)::value;
         if (p.p_mode == ROUND_RTNA)
-            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNA>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNA, N_>), grid, block, 0, stream, p);
         else if (p.p_mode == ROUND_RTZ)
-            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTZ>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTZ, N_>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNE>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNE, N_>), grid, block, 0, stream, p);
+    };
+    auto go = [&](auto hd, auto cpos, auto causal) {
+        constexpr int H_ = decltype(hd)::value;
+        constexpr bool CA = decltype(causal)::value;
+        if constexpr (H_ == 128 && !CA) {
+            if (short_wg) {
+                go_nw(hd, cpos, causal, std::integral_constant<int, KERNEL_NW_SHORT>{});
+                return;
+            }
+        }
+        go_nw(hd, cpos, causal, std::integral_constant<int, KERNEL_NW>{});
     };
     auto go_hd = [&](auto hd) {
         if (p.causal) {
@@ -775,10 +790,13 @@ int launch(const AttnParams& p, hipStream_t stream) {
     else go_hd(std::integral_constant<int, 128>{});
     if (hipGetLastError() != hipSuccess) return -1;
     if (p.n_full < p.n_items) {
-        const int64_t total = (int64_t)(p.n_items - p.n_full) * KERNEL_BM * (p.head_dim / 4);
+        const int bm = p.nw * 16 * KERNEL_NQB;
+        const int64_t total = (int64_t)(p.n_items - p.n_full) * bm * (p.head_dim / 4);
         dim3 cgrid((unsigned)((total + 255) / 256));
         if (p.head_dim == 64)
             hipLaunchKernelGGL((attn_fwd_combine<KERNEL_BM, 64>), cgrid, dim3(256), 0, stream, p);
+        else if (short_wg)
+            hipLaunchKernelGGL((attn_fwd_combine<KERNEL_NW_SHORT * 16 * KERNEL_NQB, 128>), cgrid, dim3(256), 0, stream, p);
         else
             hipLaunchKernelGGL((attn_fwd_combine<KERNEL_BM, 128>), cgrid, dim3(256), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return -1;

@@ -104,23 +104,29 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
  * attn_fwd_bf16_ex -- attn_fwd_bf16 with planner overrides, for tests and
  * ablations.
  *
- * The planner (kv_splits = 0) runs one work-group per CU per round; when the
- * last round of query tiles is ragged (or there is less than one round), the
- * query tiles of that round have their key range split so the round fills
- * the GPU, and a combine kernel merges the partial results in a fixed order
- * (the flash-decoding style tail split of "MoonMath AI open-sources a HIP
- * attention kernel for AMD MI300X", section on the two later improvements).
+ * The planner (kv_splits = 0) runs the work items in rounds that fill every
+ * CU; when the last round of query tiles is ragged (or there is less than
+ * one round), the query tiles of that round have their key range split so
+ * the round fills the GPU, and a combine kernel merges the partial results
+ * in a fixed order (the flash-decoding style tail split of "MoonMath AI
+ * open-sources a HIP attention kernel for AMD MI300X", section on the two
+ * later improvements).  Work-groups have 8 waves (256 query rows, one per
+ * CU), or, for key ranges of at most 16 tiles of 64 keys, 4 waves (128
+ * rows, two per CU, so one's Q loads and O stores overlap the other's
+ * matrix work).
  *
  * kv_splits: 0 = planner's choice; 1 = never split; n >= 2 splits every
  * query tile's keys into n contiguous ranges of whole 64-key tiles (n must
  * not exceed the number of 64-key tiles, n <= 64).  block_order: 0 =
  * planner's choice (XCD-aware), 1 = naive (work item = block id), 2 =
- * XCD-aware.  Other values return ATTN_ERR_OPTION.
+ * XCD-aware.  waves: 0 = planner's choice, 8 or 4 waves per work-group.
+ * Other values return ATTN_ERR_OPTION.  The result does not depend on
+ * block_order or waves; it may differ in the last bits with kv_splits.
  */
 int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
                      int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                      float scale, int round_mode, void* stream,
-                     int kv_splits, int block_order);
+                     int kv_splits, int block_order, int waves);
 
 /*
  * attn_fwd_bf16_gqa -- attn_fwd_bf16 with grouped-query heads and an optional

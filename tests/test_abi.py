@@ -45,10 +45,10 @@ FAKE = 1 << 40   # 16-byte aligned, never dereferenced: validation fails first
 
 def call(**kw):
     a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), layout=0, B=1, H=2,
-             Sq=64, Skv=64, scale=0.088, mode=0, stream=0, splits=0, order=0)
+             Sq=64, Skv=64, scale=0.088, mode=0, stream=0, splits=0, order=0, waves=0)
     a.update(kw)
     return attn_fwd_bf16_raw(a["q"], a["k"], a["v"], a["o"], a["layout"], a["B"], a["H"], a["Sq"], a["Skv"],
-                             a["scale"], a["mode"], a["stream"], a["splits"], a["order"])
+                             a["scale"], a["mode"], a["stream"], a["splits"], a["order"], a["waves"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -58,6 +58,7 @@ def call(**kw):
     (dict(Skv=-5), -4), (dict(Sq=1 << 40), -4), (dict(scale=math.nan), -5), (dict(scale=math.inf), -5),
     (dict(q=FAKE + 8), -6), (dict(o=FAKE + (3 << 30) + 2), -6), (dict(o=FAKE), -7),
     (dict(o=FAKE + 64 * 2 * 128 * 2 - 16), -7), (dict(splits=65), -11), (dict(order=3), -11),
+    (dict(waves=3), -11), (dict(waves=16), -11), (dict(waves=-4), -11), (dict(waves=2), -11),
 ])
 def test_argument_errors_before_device(kw, code):
     assert call(**kw) == code
@@ -71,6 +72,8 @@ def test_valid_arguments_reach_device_check():
     assert call() == -8
     for m in (0x100, 0x101, 0x102):   # ATTN_ROUND_WEIGHTS with each output mode is valid
         assert call(mode=m) == -8
+    for w in (4, 8):                  # both work-group sizes are valid for any length
+        assert call(waves=w) == -8 and call(waves=w, Skv=5000) == -8
 
 
 def call_gqa(**kw):

@@ -14,6 +14,7 @@ from tests.helpers import check, run_hip, say
 pytestmark = pytest.mark.gpu
 
 MODES = ("rtne", "rtna", "rtz")
+WAVES = (8, 4)   # work-group sizes of the kernel (the planner picks 4 for at most 16 key tiles)
 
 
 def assert_gate(st):
@@ -38,23 +39,25 @@ SMALL = [
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}_B{c[1]}H{c[2]}_{c[3]}x{c[4]}")
 @pytest.mark.parametrize("mode", MODES)
-def test_small_shapes_all_rows(case, mode):
+@pytest.mark.parametrize("waves", WAVES)
+def test_small_shapes_all_rows(case, mode, waves):
     layout, B, H, Sq, Skv, qf, kf, vf = case
-    say(f"[case] small {case} {mode}")
+    say(f"[case] small {case} {mode} waves={waves}")
     q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 100 + Sq + Skv, qf, kf, vf)
-    o = run_hip(q, k, v, layout, mode)
-    st, _ = check(o, q, k, v, layout, mode, label=str(case))
+    o = run_hip(q, k, v, layout, mode, waves=waves)
+    st, _ = check(o, q, k, v, layout, mode, label=f"{case} waves={waves}")
     assert_gate(st)
 
 
 @pytest.mark.parametrize("splits", [2, 3, 5])
-def test_forced_kv_split_matches_oracle(splits):
+@pytest.mark.parametrize("waves", WAVES)
+def test_forced_kv_split_matches_oracle(splits, waves):
     layout, B, H, Sq, Skv = "bhsd", 1, 2, 200, 1000
-    say(f"[case] forced split {splits}")
+    say(f"[case] forced split {splits} waves={waves}")
     q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 55, 1.0, 2.0, 1.0)
     for mode in MODES:
-        o = run_hip(q, k, v, layout, mode, kv_splits=splits)
-        st, _ = check(o, q, k, v, layout, mode, label=f"split{splits}")
+        o = run_hip(q, k, v, layout, mode, kv_splits=splits, waves=waves)
+        st, _ = check(o, q, k, v, layout, mode, label=f"split{splits} waves={waves}")
         assert_gate(st)
 
 
@@ -98,11 +101,24 @@ def test_nonfinite_instance_positions():
 
 
 @pytest.mark.parametrize("splits", [0, 3])
-def test_bitwise_deterministic(splits):
+@pytest.mark.parametrize("waves", WAVES)
+def test_bitwise_deterministic(splits, waves):
     layout, B, H, Sq, Skv = "bshd", 1, 4, 700, 900
     q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 77, 1.0, 2.0, 1.0)
-    outs = [run_hip(q, k, v, layout, "rtne", kv_splits=splits) for _ in range(3)]
+    outs = [run_hip(q, k, v, layout, "rtne", kv_splits=splits, waves=waves) for _ in range(3)]
     assert all(np.array_equal(outs[0], x) for x in outs[1:])
+
+
+@pytest.mark.parametrize("layout,Skv", [("bshd", 900), ("bhsd", 3000)])
+def test_work_group_sizes_agree_bitwise(layout, Skv):
+    """A query row's arithmetic is the same in the 8-wave and the 4-wave
+    work-group (same key tiles, same offsets): unsplit, the outputs are
+    bitwise equal in every mode."""
+    q, k, v = wl.random_qkv(layout, 1, 3, 600, Skv, 79, 1.0, 2.0, 1.0)
+    for mode in MODES:
+        a = run_hip(q, k, v, layout, mode, kv_splits=1, waves=8)
+        b = run_hip(q, k, v, layout, mode, kv_splits=1, waves=4)
+        assert np.array_equal(a, b), mode
 
 
 def test_layouts_give_identical_bits():
@@ -114,9 +130,9 @@ def test_layouts_give_identical_bits():
 
 
 def test_planner_tail_split_ragged_round():
-    """270 query tiles of 256 rows on 256 CUs: the planner splits the keys of
-    the 14 tiles of the ragged last round; both the split and the unsplit
-    tiles must pass the gate."""
+    """270 query tiles of 256 rows on 256 CUs (8-wave work-groups): the
+    planner splits the keys of the 14 tiles of the ragged last round; both
+    the split and the unsplit tiles must pass the gate."""
     layout, B, H, Sq, Skv = "bhsd", 1, 3, 256 * 90, 1024
     q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 91, 1.0, 2.0, 1.0)
     rng = np.random.default_rng(5)
@@ -125,8 +141,26 @@ def test_planner_tail_split_ragged_round():
     rows = np.unique(np.concatenate([tail_rows, head_rows, [B * H * Sq - 1]]))
     res = None
     for splits in (0, 1):
-        o = run_hip(q, k, v, layout, "rtne", kv_splits=splits)
+        o = run_hip(q, k, v, layout, "rtne", kv_splits=splits, waves=8)
         st, res = check(o, q, k, v, layout, "rtne", rows=rows, label=f"tail planner splits={splits}", oracle_res=res)
+        assert_gate(st)
+
+
+def test_planner_tail_split_ragged_round_4_waves():
+    """The planner's own choice for 1024 keys: 4-wave work-groups, two per
+    CU.  526 query tiles of 128 rows on 512 slots: the 14 tiles of the
+    ragged last round (the last 14 of head 1) are split and merged."""
+    layout, B, H, Sq, Skv = "bhsd", 1, 2, 128 * 263, 1024
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 93, 1.0, 2.0, 1.0)
+    rng = np.random.default_rng(6)
+    tail_rows = Sq + 249 * 128 + rng.integers(0, 14 * 128, size=96)     # items 512..525
+    head_rows = rng.integers(0, Sq + 249 * 128, size=64)
+    rows = np.unique(np.concatenate([tail_rows, head_rows, [B * H * Sq - 1]]))
+    res = None
+    for splits in (0, 1):
+        o = run_hip(q, k, v, layout, "rtne", kv_splits=splits)
+        st, res = check(o, q, k, v, layout, "rtne", rows=rows, label=f"tail planner 4 waves splits={splits}",
+                        oracle_res=res)
         assert_gate(st)
 
 
