@@ -278,16 +278,21 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     const uint64_t ka = (uint64_t)(uintptr_t)kbase, va = (uint64_t)(uintptr_t)vbase;
     const i32x4 krs4 = {(int)(uint32_t)ka, (int)((ka >> 32) & 0xffffu), (int)nrec, 0x00020000};
     const i32x4 vrs4 = {(int)(uint32_t)va, (int)((va >> 32) & 0xffffu), (int)nrec, 0x00020000};
-    auto dma16 = [&](const i32x4 rs, uint8_t* dst, int voff, int soff) {
-        const uint32_t lds = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst;
+    auto dma16 = [&](const i32x4 rs, uint8_t* dst, int voff, int soff) __attribute__((always_inline)) {
+        // the LDS address, the descriptor and the tile offset are
+        // wave-uniform; say so, so they stay in scalar registers
+        const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
+        const int so = __builtin_amdgcn_readfirstlane(soff);
+        const i32x4 rsu = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                           __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
         __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                         :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+                         :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
     };
     // round r of the K (or V) tile that starts at key k0
-    auto dma_k = [&](int r, int k0, uint8_t* dst) {
+    auto dma_k = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
         dma16(krs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 + RPR * r) * kv_row_bytes);
     };
-    auto dma_v = [&](int r, int k0, uint8_t* dst) {
+    auto dma_v = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
         dma16(vrs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 + RPR * r) * kv_row_bytes);
     };
     if (!late) {
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v<HD>(row);
         v_addr[db] = row * ROW_BYTES + (chunk << 4) + ((j & 1) << 3);
     }
-    auto read_frag = [&](int st, const uint8_t* kt, const uint8_t* vt) -> bf16x8 {
+    auto read_frag = [&](int st, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) -> bf16x8 {
         if (st < SS) {
             const int kb = st & 3, ks = st >> 2;
             return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(kt + k_addr[ks] + kb * 16 * ROW_BYTES);
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         }
         return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    auto use_frag = [&](int st, const bf16x8 f) {
+    auto use_frag = [&](int st, const bf16x8 f) __attribute__((always_inline)) {
         if (st < SS) {
             const int kb = st & 3, ks = st >> 2;
 #pragma unroll
@@ -385,8 +390,13 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // CU's address unit drains it while the matrix core runs instead of
     // stalling a wave that issues all of it at once.
     constexpr int NDMA = 2 * DMA_ROUNDS;   // instructions per wave and tile
-    auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c, int t, uint8_t* kn, uint8_t* vc) {
+    // The phase has no branch: the issuing group is a compile-time choice
+    // (LATE), and past the last tile the K DMA re-reads that tile into the
+    // free buffer, so the scheduler sees the whole phase as one region.
+    auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c, int t, uint8_t* kn, uint8_t* vc,
+                          auto latec) __attribute__((always_inline)) {
         constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
+        constexpr bool LATE = decltype(latec)::value;
         constexpr int STRIDE = (S1 - S0) / NDMA;
         static_assert(S0 != 0 || STRIDE * NDMA <= S1 - S0, "the DMA fits the phase");
         // Opaque per-lane offsets: stops the compiler from hoisting every
@@ -403,10 +413,10 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         for (int st = S0; st < S1; st++) {
             const bf16x8 cur = fr[(st - S0) % PF];
             if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
-            if (S0 == 0 && (st - S0) % STRIDE == 0 && (st - S0) / STRIDE < NDMA && !late) {
+            if (S0 == 0 && (st - S0) % STRIDE == 0 && (st - S0) / STRIDE < NDMA && !LATE) {
                 const int k = (st - S0) / STRIDE;     // K and V rounds alternate
                 if (k & 1) dma_v(k >> 1, kv_begin + t * BN, vc);
-                else if (t + 1 < T) dma_k(k >> 1, kv_begin + (t + 1) * BN, kn);
+                else dma_k(k >> 1, kv_begin + min(t + 1, T - 1) * BN, kn);
             }
             use_frag(st, cur);
         }
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // become NaN, but it only arises in rows whose output is NaN anyway).
     // Toward zero: the high half of the bit pattern, after clamping every NaN
     // to the canonical one so truncation cannot make it an infinity.
-    auto weight_pair = [&](const f32x2 two) -> bf16x2 {
+    auto weight_pair = [&](const f32x2 two) __attribute__((always_inline)) -> bf16x2 {
         if (PMODE == ROUND_RTNE) return __builtin_convertvector(two, bf16x2);
         if (PMODE == ROUND_RTNA) {
             const f32x2 up = {__uint_as_float(__float_as_uint(two[0]) | 1u), __uint_as_float(__float_as_uint(two[1]) | 1u)};
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // rounded to bf16 pairs for the P.V product (pf), and this lane's sum of
     // those bf16 weights -- the row sum adds the same values the product uses,
     // so O is normalised by exactly its own weights.
-    auto weights = [&](int qb, float m, auto biasc) -> float {
+    auto weights = [&](int qb, float m, auto biasc) __attribute__((always_inline)) -> float {
         constexpr bool BIASED = decltype(biasc)::value;   // S^T already holds s - moff/c: exponent = c * S^T
         const float negm = -m;
         f32x4 pv4[4];
@@ -489,7 +499,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     };
     // ceil of the tile's largest x for query block qb (NaN-propagating
     // v_maximum3_f32 in the lane, then across the 4 lanes of a row)
-    auto tile_max_ceil = [&](int qb) -> float {
+    auto tile_max_ceil = [&](int qb) __attribute__((always_inline)) -> float {
         float mx = -__builtin_inff();
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
@@ -499,7 +509,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         if (CPOS) mx *= c;
         return ceilf(mx);
     };
-    auto set_bias = [&](int qb) {
+    auto set_bias = [&](int qb) __attribute__((always_inline)) {
         if (CPOS) {
             const float bb = -moff[qb] * rc;
             bias4[qb] = f32x4{bb, bb, bb, bb};
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     };
 
     // ---- online softmax of S_t with a power-of-two running offset.
-    auto softmax = [&](int t, auto firstc) {
+    auto softmax = [&](int t, auto firstc) __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(firstc)::value;
         const int valid = kv_end - (kv_begin + t * BN);   // keys of this tile inside the range
         // Keys outside the range are masked by select, never by arithmetic:
@@ -614,34 +624,40 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // and one's softmax fills the gaps of the other's MFMAs.  Both groups
     // read K_t and V_{t-1} between the same two barriers, so the buffer
     // protocol is the same for both.
-    auto sync = [&]() {
+    auto sync = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0x0f70);
         lds_barrier();
     };
-    auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c) {
+    auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c, auto latec) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(latec)::value;
         // A wave in its MFMA phase takes issue priority over one in its
         // softmax, so the matrix core of a SIMD stays fed; the softmax VALU
         // work fills the MFMA phase's gaps.
         __builtin_amdgcn_s_setprio(1);
-        mfma_phase(kc, vp, s0c, s1c, t, kn, vc);
+        mfma_phase(kc, vp, s0c, s1c, t, kn, vc, latec);
         __builtin_amdgcn_s_setprio(0);
-        if (late) sync();
+        if (LATE) sync();
         if (decltype(s0c)::value == 0)
             softmax(t, std::integral_constant<bool, decltype(s1c)::value == SS>{});
-        if (!late) sync();
+        if (!LATE) sync();
     };
-    iter(0, sk0, sk1, sv0, sv1, C0{}, CS{});
-    int t = 1;
-    for (; t + 1 < T; t += 2) {
-        iter(t, sk1, sk0, sv1, sv0, C0{}, CT{});
-        iter(t + 1, sk0, sk1, sv0, sv1, C0{}, CT{});
-    }
-    if (t < T) {
-        iter(t, sk1, sk0, sv1, sv0, C0{}, CT{});
-        t++;
-    }
-    if (T & 1) iter(T, sk1, sk0, sv1, sv0, CS{}, CT{});
-    else iter(T, sk0, sk1, sv0, sv1, CS{}, CT{});
+    // the key loop, compiled once per wave group
+    auto key_loop = [&](auto latec) __attribute__((always_inline)) {
+        iter(0, sk0, sk1, sv0, sv1, C0{}, CS{}, latec);
+        int t = 1;
+        for (; t + 1 < T; t += 2) {
+            iter(t, sk1, sk0, sv1, sv0, C0{}, CT{}, latec);
+            iter(t + 1, sk0, sk1, sv0, sv1, C0{}, CT{}, latec);
+        }
+        if (t < T) {
+            iter(t, sk1, sk0, sv1, sv0, C0{}, CT{}, latec);
+            t++;
+        }
+        if (T & 1) iter(T, sk1, sk0, sv1, sv0, CS{}, CT{}, latec);
+        else iter(T, sk0, sk1, sv0, sv1, CS{}, CT{}, latec);
+    };
+    if (late) key_loop(std::true_type{});
+    else key_loop(std::false_type{});
 
     // ---- epilogue: the 4 lanes of a row hold partial row sums
     float l_row[NQB];
