@@ -205,13 +205,13 @@ def main():
         for mode in w.modes:
             if mode == args.mode:
                 continue
-            rr = time_workload(w, mode, steps=50, warmup=20)
+            rr = time_workload(w, mode, steps=100, warmup=200)
             em = statistics.median(rr["ms"])
             extra[f"{w.name}:{mode}"] = {"mode": mode, "median_ms": round(em, 4),
                                          "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
         # the option that rounds the in-loop weights with the output's mode
         for mode in w.modes:
-            rr = time_workload(w, mode, steps=50, warmup=20, round_weights=True)
+            rr = time_workload(w, mode, steps=100, warmup=200, round_weights=True)
             em = statistics.median(rr["ms"])
             extra[f"{w.name}:{mode}+weights"] = {"mode": mode, "round_weights": True, "median_ms": round(em, 4),
                                                  "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}

@@ -64,6 +64,23 @@ def test_argument_errors_before_device(kw, code):
     assert call(**kw) == code
 
 
+def test_key_extent_limit_edge():
+    """A head's K/V rows are addressed with 32-bit byte offsets: the last
+    row must start below 2^31 - 256.  BSHD with 16 heads (4096-byte rows):
+    524288 keys are accepted (they reach the device probe), 524289 are not."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    G = 1 << 33
+    kw = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, o=FAKE + 3 * G, layout=0, H=16, Sq=300)
+    assert call(Skv=524288, **kw) == -8
+    assert call(Skv=524289, **kw) == -4
+    # BHSD rows are 256 bytes: 2^23 - 1 keys per head
+    kw.update(layout=1, H=1)
+    assert call(Skv=(1 << 23) - 1, **kw) == -8
+    assert call(Skv=1 << 23, **kw) == -4
+
+
 def test_valid_arguments_reach_device_check():
     # no GPU here: a valid call stops at the device probe (-8); on a GPU box this test is skipped
     import torch

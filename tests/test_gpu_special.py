@@ -181,3 +181,31 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(out, ref), f"splits={splits} replay {rep}"
             attn_fwd_bf16(qd, kd, vd, layout="bhsd")   # eager work between replays
             torch.cuda.synchronize()
+
+
+def test_largest_key_extent_reads_the_last_rows():
+    """The largest key extent the 32-bit offsets allow (BSHD, 16 heads,
+    524288 keys: 2 GiB each of K and V).  Head h's one dominant key sits
+    among the last rows (the last one for head 0), every other score is 0,
+    so every output row is that key's V row bitwise -- through the planner's
+    split and unsplit."""
+    B, H, Sq, Skv = 1, 16, 130, 524288
+    say(f"[case] largest key extent bshd B{B} H{H} Sq{Sq} Skv{Skv}")
+    dev = torch.device("cuda")
+    k = torch.zeros((B, Skv, H, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    q = torch.zeros((B, Sq, H, 128), dtype=torch.bfloat16, device=dev)
+    q[..., 0] = 128.0
+    j0 = [Skv - 1 - 37 * h for h in range(H)]
+    rows = wl.random_qkv("bshd", 1, H, 1, 1, 41)[2]          # [1, 1, H, 128] random bf16 rows
+    for h in range(H):
+        k[0, j0[h], h, 0] = 128.0
+        v[0, j0[h], h] = rows[0, 0, h].to(dev)
+    expect = np.broadcast_to(wl.bits(rows)[0, 0][None, :, :], (Sq, H, 128))
+    for splits in (0, 1):
+        for mode in ("rtne", "rtz"):
+            o = attn_fwd_bf16(q, k, v, layout="bshd", round_mode=mode, kv_splits=splits)
+            torch.cuda.synchronize()
+            got = wl.bits(o.cpu()).reshape(Sq, H, 128)
+            assert np.array_equal(got, expect), (splits, mode, int((got != expect).sum()))
+
