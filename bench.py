@@ -88,6 +88,76 @@ def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
     return {"wall_s": wall, "ms": per, "flops": w.flops}
 
 
+def time_cold(w, mode, steps, warmup=20):
+    """Per-launch ms of workload w with the caches cleared before every launch:
+    a 512 MiB fill on the launch stream (outside the events) evicts the L2s
+    and the last-level cache, so every launch reads Q, K, V from HBM."""
+    import torch
+    from bf16_attention_forward_amd import attn_fwd_bf16
+    from bf16_attention_forward_amd import workloads as wl
+
+    q, k, v = wl.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        flush.fill_(i & 0xff)
+        a.record(stream)
+        attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def read_sclk_mhz():
+    """The GPU's current shader clock in MHz from rocm-smi (a child process),
+    or None when the tool is unavailable or prints no sclk."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    for card in d.values():
+        if isinstance(card, dict):
+            for key, val in card.items():
+                if "sclk" in key.lower():
+                    m = re.search(r"(\d+)\s*mhz", str(val).lower())
+                    if m:
+                        return int(m.group(1))
+    return None
+
+
+def sclk_under_load(w, mode, seconds=2.0):
+    """Shader clock read while the workload runs back to back for `seconds`
+    (a thread runs rocm-smi in the middle of the run)."""
+    import threading
+    import torch
+    from bf16_attention_forward_amd import attn_fwd_bf16
+    from bf16_attention_forward_amd import workloads as wl
+
+    q, k, v = wl.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    got = {}
+    t = threading.Timer(seconds / 2, lambda: got.setdefault("mhz", read_sclk_mhz()))
+    t0 = time.perf_counter()
+    t.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode)
+        torch.cuda.synchronize()
+    t.join()
+    return got.get("mhz")
+
+
 # algorithmic FLOPs of the backward pass: five products of the forward's
 # size (the recomputed S, dP, dV, dQ, dK) against the forward's two
 BWD_FLOP_FACTOR = 2.5
@@ -181,6 +251,7 @@ def main():
                           "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                           "config": {**w.describe(), "pass": "backward"}}), flush=True)
         return
+    sclk_idle = read_sclk_mhz()
     r = time_workload(w, args.mode, args.steps, args.warmup)
     ms_step = r["wall_s"] * 1e3 / args.steps
     tflops = w.flops / (ms_step * 1e-3) / 1e12
@@ -190,7 +261,17 @@ def main():
     traffic = measured_traffic(w.name)
 
     extra = {}
+    clocks = None
     if not args.no_extra:
+        # caches cleared before every launch (the timed value above runs warm,
+        # as the HipKittens experiments do)
+        cold = sorted(time_cold(w, args.mode, steps=30))
+        em = statistics.median(cold)
+        extra[f"{w.name}:cold_cache"] = {"mode": args.mode, "median_ms": round(em, 4), "min_ms": round(cold[0], 4),
+                                         "tflops": round(w.flops / (em * 1e-3) / 1e12, 1),
+                                         "frac_peak": round(w.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        clocks = {"sclk_mhz_idle_before": sclk_idle, "sclk_mhz_under_load": sclk_under_load(w, args.mode),
+                  "sclk_mhz_after": read_sclk_mhz(), "source": "rocm-smi --showgpuclocks"}
         for num in (3, 4, 5, 6, 7, 8, 9):
             ww = wl.WORKLOADS[num]
             # sub-millisecond launches need more warm-up than the long ones
@@ -247,6 +328,7 @@ def main():
                      "traffic": traffic, "kernel": "attn_fwd_main",
                      "algorithmic_flops_per_launch": w.flops},
         "cpu_baseline": cpu,
+        "clocks": clocks,
         "workloads": extra,
     }
     print(json.dumps(out), flush=True)
