@@ -115,28 +115,29 @@ def time_cold(w, mode, steps, warmup=20):
 
 
 def read_sclk_mhz():
-    """The GPU's current shader clock in MHz from rocm-smi (a child process),
-    or None when the tool is unavailable or prints no sclk."""
+    """The GPU's current shader clock level in MHz, read from the driver's
+    sysfs table of clock levels (the line marked '*') for this device's PCI
+    address; None when it cannot be read.  A plain file read: no child
+    program is started."""
     import re
-    import subprocess
+    import torch
     try:
-        r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout)
+        pr = torch.cuda.get_device_properties(0)
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        with open(f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk") as fh:
+            text = fh.read()
     except Exception:
         return None
-    for card in d.values():
-        if isinstance(card, dict):
-            for key, val in card.items():
-                if "sclk" in key.lower():
-                    m = re.search(r"(\d+)\s*mhz", str(val).lower())
-                    if m:
-                        return int(m.group(1))
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*mhz", line.lower())
+            return int(m.group(1)) if m else None
     return None
 
 
 def sclk_under_load(w, mode, seconds=2.0):
     """Shader clock read while the workload runs back to back for `seconds`
-    (a thread runs rocm-smi in the middle of the run)."""
+    (a thread reads it in the middle of the run)."""
     import threading
     import torch
     from bf16_attention_forward_amd import attn_fwd_bf16
@@ -271,7 +272,7 @@ def main():
                                          "tflops": round(w.flops / (em * 1e-3) / 1e12, 1),
                                          "frac_peak": round(w.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         clocks = {"sclk_mhz_idle_before": sclk_idle, "sclk_mhz_under_load": sclk_under_load(w, args.mode),
-                  "sclk_mhz_after": read_sclk_mhz(), "source": "rocm-smi --showgpuclocks"}
+                  "sclk_mhz_after": read_sclk_mhz(), "source": "sysfs pp_dpm_sclk (current level)"}
         for num in (3, 4, 5, 6, 7, 8, 9):
             ww = wl.WORKLOADS[num]
             # sub-millisecond launches need more warm-up than the long ones

@@ -107,6 +107,11 @@ def derived_lines(cs: dict) -> list:
     av = cs.get("SQ_ACTIVE_INST_VALU")
     if av:
         out.append(f"  VALU active (quad-cycles x 4) / (cycles x {N_SIMD}) = {4 * av / (cyc * N_SIMD):.3f}")
+    hit, miss = cs.get("TCC_HIT_sum"), cs.get("TCC_MISS_sum")
+    if hit is not None and miss is not None and hit + miss > 0:
+        out.append(f"  L2 hit rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum) = {hit / (hit + miss):.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in cs and cs.get("SQ_INSTS_LDS"):
+        out.append(f"  LDS bank-conflict cycles per LDS instruction = {cs['SQ_LDS_BANK_CONFLICT'] / cs['SQ_INSTS_LDS']:.4f}")
     wl = cs.get("SQ_WAIT_INST_LDS")
     if wl is not None:
         out.append(f"  wave-cycles waiting for LDS issue (x 4) / (cycles x waves resident) = "
