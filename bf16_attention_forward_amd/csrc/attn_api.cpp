@@ -271,7 +271,7 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
 
 extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                              const float* lse, void* dq, void* dk, void* dv, int layout, int64_t B, int64_t H,
-                             int64_t Sq, int64_t Skv, float scale, void* stream) {
+                             int64_t Sq, int64_t Skv, float scale, int causal, void* stream) {
     if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
     if (B < 1 || H < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
@@ -282,6 +282,7 @@ extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const 
     const int64_t q_rowe = (layout == ATTN_LAYOUT_BSHD) ? H * hd : hd;
     if ((Sq - 1) * q_rowe * 2 + hd * 2 >= lim31 || (Skv - 1) * q_rowe * 2 + hd * 2 >= lim31) return ATTN_ERR_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv) & 15)
         return ATTN_ERR_ALIGN;
@@ -321,6 +322,8 @@ extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const 
     if (B * H * std::max(p.n_qblocks, p.n_kblocks) >= lim31) return ATTN_ERR_SHAPE;
     p.c = (float)((double)scale * 1.4426950408889634073599246810018921);
     p.scale = scale;
+    p.causal = causal;
+    p.causal_off = (int)(Skv - Sq);
     void* ws = nullptr;
     const int wrc = get_workspace(dev, stream, (size_t)n_q * sizeof(float), &ws);
     if (wrc != ATTN_OK) return wrc;

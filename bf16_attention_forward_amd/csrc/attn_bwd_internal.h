@@ -23,6 +23,8 @@ struct BwdParams {
     int n_kblocks;        // ceil(Skv / 128): work-groups per (b, h) of the dK/dV kernel
     float c;              // fp32(scale * log2(e))
     float scale;
+    int causal;           // 1: query i sees keys j <= i + causal_off (the forward's mask)
+    int causal_off;       // Skv - Sq
 };
 
 int launch_bwd(const BwdParams& p, hipStream_t stream);

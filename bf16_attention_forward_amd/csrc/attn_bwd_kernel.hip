@@ -21,6 +21,10 @@
 //    64-query Q and dO tiles.  Per tile: S = Q K^T and dP = dO V^T (Q and dO as
 //    operand A: each lane holds one key), then P and dS, then dV^T += dO^T P
 //    and dK^T += Q^T dS with dO^T and Q^T transposed out of LDS.
+// Under the causal mask (query i sees keys j <= i + Skv - Sq, the forward's
+// bottom-right alignment) the dQ key loop ends at the tile's diagonal and the
+// dK/dV query loop starts at it; the weights of masked pairs are zero by
+// select, and work-groups that see no pair write zeros and exit.
 // Every LDS tile is read both straight (ds_read_b128) and transposed, so all
 // tiles keep one layout: 16-byte chunk c of row r at c ^ swz(r), where
 // swz(r) = 2 (r & 7) + ((r >> 3) & 1) takes 16 distinct values over any 16
@@ -185,6 +189,7 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
 // straight), then the elementwise step of tile t; three K/V slots.
 constexpr int NSLOT = 3;
 
+template <bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[NSLOT * 2 * TILE_BYTES];   // per slot: K, V
@@ -193,11 +198,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     const bool late = wave >= 4;
     const int g = lane >> 4, j = lane & 15;
     constexpr int BMQ = NW * 32;
-    const int qt = blockIdx.x % p.n_qblocks;
-    const int bh = blockIdx.x / p.n_qblocks;
+    // under the mask a query tile's key range grows with its index: blocks
+    // take the longest first (the last query tile of every head, then the
+    // second last, ...) so the short ones fill the end of the launch
+    const int BH = p.B * p.H;
+    const int qt = CAUSAL ? p.n_qblocks - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x % p.n_qblocks);
+    const int bh = CAUSAL ? (int)(blockIdx.x % BH) : (int)(blockIdx.x / p.n_qblocks);
     const int h = bh % p.H, b = bh / p.H;
     const int qrow0 = qt * BMQ + wave * 32;
-    const int T = (p.Skv + TILE_ROWS - 1) / TILE_ROWS;
+    // keys up to the diagonal of the work-group's last row under the mask
+    const int kv_end = CAUSAL ? min(p.Skv, min(p.Sq, (qt + 1) * BMQ) - 1 + p.causal_off + 1) : p.Skv;
+    const int T = (kv_end + TILE_ROWS - 1) / TILE_ROWS;
+    if (kv_end <= 0) {
+        // no row of this work-group sees a key (Sq > Skv): dQ is zero
+        // (uniform across the work-group, before any transfer or barrier)
+        uint16_t* dqz = p.dq + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++) {
+            const int row = qrow0 + qb * 16 + j;
+            if (row >= p.Sq) continue;
+#pragma unroll
+            for (int db = 0; db < 8; db++) *(uint2*)(dqz + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
+        }
+        return;
+    }
 
     const TileSrc ks = tile_src(p.k + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
     const TileSrc vs = tile_src(p.v + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
@@ -291,18 +315,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
                 for (int qb = 0; qb < 2; qb++) dq[db][qb] = mfma(kt_f, dsf[qb][kk], dq[db][qb]);
             }
     };
-    // dS^T = P^T o (dP^T - delta), P^T = 2^(c s - L log2 e) of tile t; keys past Skv -> 0
+    // dS^T = P^T o (dP^T - delta), P^T = 2^(c s - L log2 e) of tile t; keys past
+    // Skv (and, under the mask, past the row's diagonal) -> 0 by select
     auto elementwise = [&](int t) __attribute__((always_inline)) {
         const int valid = p.Skv - t * TILE_ROWS - 4 * g;
 #pragma unroll
         for (int qb = 0; qb < 2; qb++) {
+            const int lim = CAUSAL ? min(valid, qrow0 + qb * 16 + j + p.causal_off + 1 - t * TILE_ROWS - 4 * g)
+                                   : valid;
             float dsv[4][4];
 #pragma unroll
             for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.c, -lse2[qb]));
-                    dsv[kb][r] = (16 * kb + r < valid) ? pw * (dp[kb][qb][r] - dlt[qb]) : 0.f;
+                    dsv[kb][r] = (16 * kb + r < lim) ? pw * (dp[kb][qb][r] - dlt[qb]) : 0.f;
                 }
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) dsf[qb][kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
@@ -382,6 +409,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 // registers per wave, one wave per SIMD; measured slower.)
 constexpr int LS_BYTES = 2 * TILE_ROWS * 4;   // L and delta of a tile's 64 queries
 
+template <bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[NSLOT * 2 * TILE_BYTES];   // per slot: Q, dO
@@ -390,11 +418,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool late = wave >= 4;
     const int g = lane >> 4, j = lane & 15;
-    const int kt_ = blockIdx.x % p.n_kblocks;
-    const int bh = blockIdx.x / p.n_kblocks;
+    // under the mask a key block's query range shrinks with its index:
+    // blocks take the longest (first key blocks of every head) first
+    const int BH = p.B * p.H;
+    const int kt_ = CAUSAL ? (int)(blockIdx.x / BH) : (int)(blockIdx.x % p.n_kblocks);
+    const int bh = CAUSAL ? (int)(blockIdx.x % BH) : (int)(blockIdx.x / p.n_kblocks);
     const int h = bh % p.H, b = bh / p.H;
     const int kbase = kt_ * (NW * 16) + wave * 16;       // this wave's first key
-    const int T = (p.Sq + TILE_ROWS - 1) / TILE_ROWS;
+    // query tiles [t0, t0 + T): under the mask the first query that sees the
+    // work-group's first key is k0 - (Skv - Sq)
+    const int q_first = CAUSAL ? max(0, kt_ * (NW * 16) - p.causal_off) : 0;
+    const int t0 = q_first / TILE_ROWS;
+    const int T = (p.Sq + TILE_ROWS - 1) / TILE_ROWS - t0;
+    if (T <= 0) {
+        // no query sees these keys: dK = dV = 0 (with the bottom-right mask
+        // the last query sees every key, so this is a guard only; uniform
+        // across the work-group, before any transfer or barrier)
+        const int krow = kbase + j;
+        if (krow < p.Skv) {
+            const int64_t ko = (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head + (int64_t)krow * p.kv_row + 4 * g;
+#pragma unroll
+            for (int db = 0; db < 8; db++) {
+                *(uint2*)(p.dk + ko + 16 * db) = uint2{0u, 0u};
+                *(uint2*)(p.dv + ko + 16 * db) = uint2{0u, 0u};
+            }
+        }
+        return;
+    }
+    const int q0 = t0 * TILE_ROWS;                       // first query row of tile 0
 
     const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
     const TileSrc qs = tile_src(p.q + qoff, p.q_row, p.Sq);
@@ -411,15 +462,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         dma4(drs, lslot(sl) + TILE_ROWS * 4, lane * 4, q0 * 4);
     };
     // tile 0: all 8 waves; later tiles: waves 0-3
-    issue_tile_n<NW>(qs, 0, qslot(0), wave, g, j);
-    issue_tile_n<NW>(gs, 0, gslot(0), wave, g, j);
-    if (wave == 0) issue_ls(0, 0);
+    issue_tile_n<NW>(qs, q0, qslot(0), wave, g, j);
+    issue_tile_n<NW>(gs, q0, gslot(0), wave, g, j);
+    if (wave == 0) issue_ls(q0, 0);
     auto issue_next = [&](int t) __attribute__((always_inline)) {
         if (!late && t < T) {
             const int sl = t % NSLOT;
-            issue_tile_n<4>(qs, t * TILE_ROWS, qslot(sl), wave, g, j);
-            issue_tile_n<4>(gs, t * TILE_ROWS, gslot(sl), wave, g, j);
-            if (wave == 0) issue_ls(t * TILE_ROWS, sl);
+            issue_tile_n<4>(qs, q0 + t * TILE_ROWS, qslot(sl), wave, g, j);
+            issue_tile_n<4>(gs, q0 + t * TILE_ROWS, gslot(sl), wave, g, j);
+            if (wave == 0) issue_ls(q0 + t * TILE_ROWS, sl);
         }
     };
 
@@ -482,10 +533,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
                 dk[db] = mfma(qtf, dsf[kk], dk[db]);
             }
     };
-    // P = 2^(c s - L log2 e), dS = P o (dP - delta) of tile t; queries past Sq -> 0
+    // P = 2^(c s - L log2 e), dS = P o (dP - delta) of tile t; queries past Sq
+    // (and, under the mask, queries before the key's diagonal) -> 0 by select
     auto elementwise = [&](int t, int sl) __attribute__((always_inline)) {
         const uint8_t* lt = lslot(sl);
-        const int valid = p.Sq - t * TILE_ROWS - 4 * g;
+        const int valid = p.Sq - q0 - t * TILE_ROWS - 4 * g;
+        // query 16*mb + 4*g + r of the tile sees key kbase + j iff
+        // 16*mb + r >= kbase + j - (Skv - Sq) - (first query of the tile) - 4*g
+        const int lo = CAUSAL ? kbase + j - p.causal_off - q0 - t * TILE_ROWS - 4 * g : -TILE_ROWS;
         float pv[4][4], dsv[4][4];
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
@@ -493,7 +548,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
             const f32x4 dl = *(const LDS_AS f32x4*)(LDS_AS const uint8_t*)(lt + TILE_ROWS * 4 + (16 * mb + 4 * g) * 4);
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const bool in = 16 * mb + r < valid;
+                const bool in = 16 * mb + r < valid && (!CAUSAL || 16 * mb + r >= lo);
                 const float pw = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], p.c, -l2[r])) : 0.f;
                 pv[mb][r] = pw;
                 dsv[mb][r] = pw * (dp[mb][r] - dl[r]);
@@ -568,9 +623,13 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.B * p.H * p.Sq;
     hipLaunchKernelGGL(attn_bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
-    hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)((int64_t)p.B * p.H * p.n_kblocks)), dim3(8 * 64), 0, stream, p);
+    // the causal mask is a compile-time variant: the unmasked kernels carry none of it
+    const dim3 gk((unsigned)((int64_t)p.B * p.H * p.n_kblocks)), gq((unsigned)((int64_t)p.B * p.H * p.n_qblocks));
+    if (p.causal) hipLaunchKernelGGL(attn_bwd_dkdv<true>, gk, dim3(NW * 64), 0, stream, p);
+    else hipLaunchKernelGGL(attn_bwd_dkdv<false>, gk, dim3(NW * 64), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
-    hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)((int64_t)p.B * p.H * p.n_qblocks)), dim3(NW * 64), 0, stream, p);
+    if (p.causal) hipLaunchKernelGGL(attn_bwd_dq<true>, gq, dim3(NW * 64), 0, stream, p);
+    else hipLaunchKernelGGL(attn_bwd_dq<false>, gq, dim3(NW * 64), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
     return 0;
 }

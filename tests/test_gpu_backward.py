@@ -27,10 +27,11 @@ def rows_first(bits, layout):
     return np.ascontiguousarray(bits).reshape(-1, bits.shape[-1])
 
 
-def case_inputs(layout, B, H, Sq, Skv, seed):
+def case_inputs(layout, B, H, Sq, Skv, seed, causal=False):
     q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, seed, 1.0, 2.0, 1.0)
     do = wl.random_qkv(layout, B, H, Sq, 1, seed + 5000)[0]
-    fwd = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=SCALE, method=False)
+    fwd = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=SCALE, method=False,
+                           causal=causal)
     o_rows = fwd.rounded("rtne").reshape(B, H, Sq, 128)
     o_bits = o_rows.transpose(0, 2, 1, 3).copy() if layout == "bshd" else o_rows.copy()
     o = torch.from_numpy(o_bits.view(np.int16)).view(torch.bfloat16)
@@ -38,10 +39,10 @@ def case_inputs(layout, B, H, Sq, Skv, seed):
     return q, k, v, do, o, o_bits, lse
 
 
-def run_bwd(q, k, v, o, do, lse, layout):
+def run_bwd(q, k, v, o, do, lse, layout, causal=False):
     from bf16_attention_forward_amd import attn_bwd_bf16
     dq, dk, dv = attn_bwd_bf16(to_dev(q), to_dev(k), to_dev(v), to_dev(o), to_dev(do), to_dev(lse),
-                               layout=layout, scale=SCALE)
+                               layout=layout, scale=SCALE, causal=causal)
     torch.cuda.synchronize()
     return wl.bits(dq.cpu()), wl.bits(dk.cpu()), wl.bits(dv.cpu())
 
@@ -66,6 +67,79 @@ def test_backward_matches_oracle(case):
     for name, g, exact, sig in (("dq", gq, ref.dq, ref.sdq), ("dk", gk, ref.dk, ref.sdk), ("dv", gv, ref.dv, ref.sdv)):
         st = gate.compare(rows_first(g, layout), exact, sig, "rtne")
         say(f"[gate] backward {case} {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
+        assert st["passed"], (name, st)
+
+
+CAUSAL_CASES = [
+    ("bhsd", 1, 2, 300, 300),    # square: the diagonal crosses tiles of both kernels
+    ("bshd", 2, 3, 200, 333),    # Sq < Skv: queries are the last positions
+    ("bhsd", 1, 2, 333, 130),    # Sq > Skv: leading rows see no key (lse -inf, dQ = 0)
+    ("bhsd", 1, 1, 600, 100),    # a whole dQ work-group of rows sees no key
+    ("bshd", 1, 2, 64, 1000),    # most keys before the queries; dK/dV work-groups start late
+    ("bhsd", 1, 2, 70, 700),     # the first dK/dV work-groups see every query
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL_CASES, ids=lambda c: f"{c[0]}_B{c[1]}H{c[2]}_{c[3]}x{c[4]}_causal")
+def test_causal_backward_matches_oracle(case):
+    """The causal mask of the forward (bottom-right aligned): O and lse from
+    the oracle's masked forward, gradients against its masked backward."""
+    layout, B, H, Sq, Skv = case
+    q, k, v, do, o, o_bits, lse = case_inputs(layout, B, H, Sq, Skv, 700 + Sq + Skv, causal=True)
+    say(f"[case] causal backward {case}")
+    gq, gk, gv = run_bwd(q, k, v, o, do, lse, layout, causal=True)
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                               o=o_bits, causal=True)
+    # A row that sees exactly one key (row Sq - Skv) is the single-key case:
+    # its exact dQ is 0, the kernel's is fp32 rounding noise (bound as in
+    # test_single_key_backward); every other element meets the gate.
+    one = Skv - Sq
+    seen1 = np.zeros((B * H, Sq), bool)
+    if 0 <= -one < Sq:
+        seen1[:, -one] = True
+    gq_rows = rows_first(gq, layout)
+    keep = ~seen1.reshape(-1)
+    for name, g, exact, sig in (("dq", gq_rows[keep], ref.dq[keep], ref.sdq[keep]),
+                                ("dk", rows_first(gk, layout), ref.dk, ref.sdk),
+                                ("dv", rows_first(gv, layout), ref.dv, ref.sdv)):
+        st = gate.compare(g, exact, sig, "rtne")
+        say(f"[gate] causal backward {case} {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
+        assert st["passed"], (name, st)
+    if seen1.any():
+        assert np.all(ref.dq[~keep] == 0)
+        mx = lambda t: float(t.float().abs().max())
+        bound = SCALE * 2.0 ** -9 * mx(do) * mx(v) * mx(k)
+        assert np.all(np.abs(oracle.bf16_bits_to_f64(gq_rows[~keep])) <= bound)
+    # rows that see no key (Sq > Skv) have dQ = 0 exactly
+    no_key = np.arange(Sq) + (Skv - Sq) < 0
+    assert np.all(gq_rows.reshape(B * H, Sq, 128)[:, no_key] == 0)
+
+
+def test_causal_forward_then_backward_on_the_gpu():
+    """End to end under the mask: the GPU causal forward's O and lse feed the
+    GPU causal backward, against the oracle's gradients for that same O (its
+    delta from the GPU's O).  Against the gradients of the exact output the
+    first rows fail the gate: a row that sees few keys has dP - delta
+    cancel, which magnifies the rounding of O inside delta."""
+    from bf16_attention_forward_amd import attn_fwd_bf16_gqa, attn_bwd_bf16
+    layout, B, H, Sq, Skv = "bshd", 1, 2, 400, 400
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 49, 1.0, 2.0, 1.0)
+    do = wl.random_qkv(layout, B, H, Sq, 1, 5049)[0]
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = attn_fwd_bf16_gqa(qd, kd, vd, layout=layout, causal=True, return_lse=True)
+    dq, dk, dv = attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=layout, causal=True)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                               o=wl.bits(o.cpu()), causal=True)
+    # row 0 sees one key: its exact dQ is 0 (checked in the test above)
+    keep = np.ones(B * H * Sq, bool)
+    keep[np.arange(B * H) * Sq] = False
+    dq_rows = rows_first(wl.bits(dq.cpu()), layout)
+    for name, g, exact, sig in (("dq", dq_rows[keep], ref.dq[keep], ref.sdq[keep]),
+                                ("dk", rows_first(wl.bits(dk.cpu()), layout), ref.dk, ref.sdk),
+                                ("dv", rows_first(wl.bits(dv.cpu()), layout), ref.dv, ref.sdv)):
+        st = gate.compare(g, exact, sig, "rtne")
+        say(f"[gate] causal fwd+bwd {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
         assert st["passed"], (name, st)
 
 

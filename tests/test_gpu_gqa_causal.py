@@ -31,6 +31,7 @@ CASES = [
     ("bhsd", 1, 3, 1, 1, 1, True),         # single query, single key
     ("bhsd", 2, 8, 2, 257, 257, False),    # grouped heads, no mask
     ("bshd", 1, 4, 4, 1000, 77, False),    # plain heads through the grouped entry
+    ("bshd", 1, 4, 2, 300, 2000, False),   # grouped heads, keys past 16 tiles: 8-wave work-groups
     ("bshd", 1, 4, 1, 64, 4096, True),     # short query block at the end of a long key range
 ]
 
@@ -98,7 +99,8 @@ LSE_CASES = [
     # layout, B, Hq, Hkv, Sq, Skv, causal
     ("bhsd", 1, 4, 2, 300, 300, True),
     ("bshd", 1, 2, 1, 333, 130, True),     # leading rows see no key: -inf
-    ("bhsd", 1, 2, 2, 300, 1000, False),   # few work items: the planner splits the keys
+    ("bhsd", 1, 2, 2, 300, 1000, False),   # few work items: the planner splits the keys (4-wave groups)
+    ("bhsd", 1, 2, 2, 300, 1500, False),   # the same on 8-wave groups (more than 16 key tiles)
     ("bshd", 2, 8, 2, 257, 513, False),
 ]
 
