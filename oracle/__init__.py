@@ -70,7 +70,7 @@ def configure(lib):
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.oracle_attention_bwd.restype = ctypes.c_int
-    lib.oracle_attention_bwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
+    lib.oracle_attention_bwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int] + [ctypes.c_void_p] * 6 + [ctypes.c_int]
     lib.oracle_version.restype = ctypes.c_int
     return lib
@@ -178,7 +178,9 @@ def attention_bwd(q, k, v, do, *, layout: str, scale: float, o=None, causal: boo
     """Gradients of the plain operation for the output gradient ``do`` (bf16
     bit patterns like q).  ``o``: the forward output the backward starts from
     (bf16 bits; its row dot product with do enters the softmax gradient), or
-    None for the exact output.  Heads of q and k/v are equal."""
+    None for the exact output.  k and v may have fewer heads than q (query
+    head h reads key/value head h // (Hq // Hkv)); dk and dv then sum over
+    each key/value head's query heads."""
     lib = _load()
     q, k, v, do = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q, k, v, do))
     if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or do.shape != q.shape:
@@ -192,16 +194,17 @@ def attention_bwd(q, k, v, do, *, layout: str, scale: float, o=None, causal: boo
         Hk, Skv = k.shape[1], k.shape[2]
     else:
         raise ValueError(layout)
-    if Hk != H or k.shape[0] != B or k.shape[-1] != D:
-        raise ValueError("q and k/v must share batch, heads and head dimension")
+    if H % Hk != 0 or k.shape[0] != B or k.shape[-1] != D:
+        raise ValueError("q and k/v must share batch and head dimension; Hq a multiple of Hkv")
     if o is not None:
         o = np.ascontiguousarray(o, dtype=np.uint16)
         if o.shape != q.shape:
             raise ValueError("o must be shaped like q")
-    out = [np.empty((B * H * n, D), np.float64) for n in (Sq, Sq, Skv, Skv, Skv, Skv)]
+    out = [np.empty((B * h * n, D), np.float64) for h, n in ((H, Sq), (H, Sq), (Hk, Skv), (Hk, Skv), (Hk, Skv),
+                                                             (Hk, Skv))]
     rc = lib.oracle_attention_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data,
                                   o.ctypes.data if o is not None else None, do.ctypes.data,
-                                  LAYOUTS[layout], B, H, Sq, Skv, D, ctypes.c_float(scale), 1 if causal else 0,
+                                  LAYOUTS[layout], B, H, Hk, Sq, Skv, D, ctypes.c_float(scale), 1 if causal else 0,
                                   *[a.ctypes.data for a in out], int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_bwd failed ({rc})")

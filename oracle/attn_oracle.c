@@ -316,21 +316,24 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * rounding.  Everything in fp64, rows in ascending order, no blocking.
  *
  *   q, o, dO : [B,Sq,H,D] or [B,H,Sq,D] bf16 bits (o may be NULL);
- *   k, v     : [B,Skv,H,D] or [B,H,Skv,D]
+ *   k, v     : [B,Skv,Hkv,D] or [B,Hkv,Skv,D]; query head h reads key/value
+ *              head h / (H / Hkv), H a multiple of Hkv (Hkv = H: plain heads)
  *   dq, sdq  : [B*H*Sq, D] doubles, rows (b*H + h)*Sq + i: the gradient and
  *              the RMS size of the terms its sum adds (scale |ds_ij k_jd|)
- *   dk, sdk, dv, sdv : [B*H*Skv, D] doubles, rows (b*H + h)*Skv + j
+ *   dk, sdk, dv, sdv : [B*Hkv*Skv, D] doubles, rows (b*Hkv + hk)*Skv + j; a
+ *              key/value head's gradient sums the terms of all its query heads
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
 int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                         const uint16_t* dO, int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
-                         int64_t D, float scale, int causal,
+                         const uint16_t* dO, int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq,
+                         int64_t Skv, int64_t D, float scale, int causal,
                          double* dq, double* sdq, double* dk, double* sdk, double* dv, double* sdv,
                          int nthreads) {
     if (!q || !k || !v || !dO || !dq || !sdq || !dk || !sdk || !dv || !sdv) return -1;
     if (layout != OR_LAYOUT_BSHD && layout != OR_LAYOUT_BHSD) return -1;
-    if (B < 1 || H < 1 || Sq < 1 || Skv < 1 || D < 1 || D > ORACLE_DMAX) return -1;
+    if (B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || Sq < 1 || Skv < 1 || D < 1 || D > ORACLE_DMAX) return -1;
     if (causal != 0 && causal != 1) return -1;
+    const int64_t group = H / Hkv;   /* query head h reads key/value head h / group */
     const double sc = (double)scale;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -340,8 +343,12 @@ int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
     double* P = (double*)malloc(sizeof(double) * (size_t)(Sq * Skv));
     double* dS = (double*)malloc(sizeof(double) * (size_t)(Sq * Skv));
     if (!P || !dS) { free(P); free(dS); return -1; }
+    /* dk, dv (and the sums of squares behind sdk, sdv) add up over the query
+       heads of each key/value head */
+    for (int64_t r = 0; r < B * Hkv * Skv * D; r++) { dk[r] = 0.0; sdk[r] = 0.0; dv[r] = 0.0; sdv[r] = 0.0; }
     for (int64_t b = 0; b < B; b++) {
         for (int64_t h = 0; h < H; h++) {
+            const int64_t kvh = h / group;
             /* weights p_ij (masked pairs 0), per row */
 #pragma omp parallel for schedule(dynamic, 8)
             for (int64_t i = 0; i < Sq; i++) {
@@ -356,7 +363,7 @@ int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
                 double* pr = P + i * Skv;
                 for (int64_t j = 0; j < Skv; j++) {
                     if (j >= n_keys) { pr[j] = 0.0; continue; }
-                    const uint16_t* kp = k + row_offset(layout, b, h, j, H, Skv, D);
+                    const uint16_t* kp = k + row_offset(layout, b, kvh, j, Hkv, Skv, D);
                     double acc = 0.0;
                     for (int d = 0; d < D; d++) acc += bf16_to_double(qp[d]) * bf16_to_double(kp[d]);
                     pr[j] = sc * acc;
@@ -375,7 +382,7 @@ int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
                     } else {
                         od = 0.0;
                         for (int64_t j = 0; j < n_keys; j++)
-                            od += pr[j] * bf16_to_double(v[row_offset(layout, b, h, j, H, Skv, D) + d]);
+                            od += pr[j] * bf16_to_double(v[row_offset(layout, b, kvh, j, Hkv, Skv, D) + d]);
                     }
                     delta += bf16_to_double(gp[d]) * od;
                 }
@@ -383,7 +390,7 @@ int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
                 double* dr = dS + i * Skv;
                 for (int64_t j = 0; j < Skv; j++) {
                     if (j >= n_keys) { dr[j] = 0.0; continue; }
-                    const uint16_t* vp = v + row_offset(layout, b, h, j, H, Skv, D);
+                    const uint16_t* vp = v + row_offset(layout, b, kvh, j, Hkv, Skv, D);
                     double dp = 0.0;
                     for (int d = 0; d < D; d++) dp += bf16_to_double(gp[d]) * bf16_to_double(vp[d]);
                     dr[j] = pr[j] * (dp - delta);
@@ -398,7 +405,7 @@ int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
                 for (int64_t j = 0; j < Skv; j++) {
                     const double w = dS[i * Skv + j];
                     if (w == 0.0) continue;
-                    const uint16_t* kp = k + row_offset(layout, b, h, j, H, Skv, D);
+                    const uint16_t* kp = k + row_offset(layout, b, kvh, j, Hkv, Skv, D);
                     for (int d = 0; d < D; d++) {
                         const double t = sc * w * bf16_to_double(kp[d]);
                         g[d] += t;
@@ -410,11 +417,10 @@ int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
             /* dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij do_i */
 #pragma omp parallel for schedule(dynamic, 8)
             for (int64_t j = 0; j < Skv; j++) {
-                double* gk = dk + ((b * H + h) * Skv + j) * D;
-                double* sk = sdk + ((b * H + h) * Skv + j) * D;
-                double* gv = dv + ((b * H + h) * Skv + j) * D;
-                double* sv = sdv + ((b * H + h) * Skv + j) * D;
-                for (int d = 0; d < D; d++) { gk[d] = 0.0; sk[d] = 0.0; gv[d] = 0.0; sv[d] = 0.0; }
+                double* gk = dk + ((b * Hkv + kvh) * Skv + j) * D;
+                double* sk = sdk + ((b * Hkv + kvh) * Skv + j) * D;
+                double* gv = dv + ((b * Hkv + kvh) * Skv + j) * D;
+                double* sv = sdv + ((b * Hkv + kvh) * Skv + j) * D;
                 for (int64_t i = 0; i < Sq; i++) {
                     const double w = dS[i * Skv + j], pw = P[i * Skv + j];
                     const uint16_t* qp = q + row_offset(layout, b, h, i, H, Sq, D);
@@ -426,10 +432,10 @@ int oracle_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v
                         gv[d] += tv; sv[d] += tv * tv;
                     }
                 }
-                for (int d = 0; d < D; d++) { sk[d] = sqrt(sk[d]); sv[d] = sqrt(sv[d]); }
             }
         }
     }
+    for (int64_t r = 0; r < B * Hkv * Skv * D; r++) { sdk[r] = sqrt(sdk[r]); sdv[r] = sqrt(sdv[r]); }
     free(P);
     free(dS);
     return 0;

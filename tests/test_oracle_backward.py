@@ -25,7 +25,11 @@ def heads_first(t, layout):
 
 def autograd_grads(q, k, v, do, layout, scale, causal):
     Q, K, V, G = (heads_first(f64(t), layout).clone().requires_grad_(i < 3) for i, t in enumerate((q, k, v, do)))
-    S = scale * (Q @ K.transpose(-1, -2))
+    group = Q.shape[1] // K.shape[1]
+    # grouped heads: each key/value head serves `group` consecutive query
+    # heads; autograd adds the repeated heads' gradients into the original
+    Kr, Vr = K.repeat_interleave(group, dim=1), V.repeat_interleave(group, dim=1)
+    S = scale * (Q @ Kr.transpose(-1, -2))
     keep = torch.ones(S.shape[-2:], dtype=torch.bool)
     if causal:
         sq, skv = Q.shape[2], K.shape[2]
@@ -36,7 +40,7 @@ def autograd_grads(q, k, v, do, layout, scale, causal):
     has_key = keep.any(dim=-1, keepdim=True)
     S = torch.where(keep | ~has_key, S, torch.full_like(S, float("-inf")))
     P = torch.softmax(S, dim=-1) * has_key
-    O = P @ V
+    O = P @ Vr
     (O * G).sum().backward()
     D = q.shape[-1]
     return (Q.grad.reshape(-1, D).numpy(), K.grad.reshape(-1, D).numpy(), V.grad.reshape(-1, D).numpy(),
@@ -56,6 +60,23 @@ def test_matches_torch_autograd_float64(layout, causal, sq, skv):
     g = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
                              causal=causal)
     dq, dk, dv, _ = autograd_grads(q, k, v, do, layout, SCALE, causal)
+    for got, ref in ((g.dq, dq), (g.dk, dk), (g.dv, dv)):
+        assert np.allclose(got, ref, rtol=1e-11, atol=1e-12), np.abs(got - ref).max()
+
+
+@pytest.mark.parametrize("layout,hkv,causal", [("bhsd", 1, False), ("bshd", 2, True), ("bhsd", 3, True)])
+def test_grouped_heads_match_torch_autograd_float64(layout, hkv, causal):
+    """Grouped-query heads (6 query heads on hkv key/value heads): dK and dV of
+    a key/value head sum over its query heads -- autograd through the
+    repeated heads, a derivation independent of the oracle's loops."""
+    q, k, v, do = inputs(layout, 2, 6, 29, 35, 13)
+    keep = slice(0, hkv)
+    k, v = (t[:, :, keep] if layout == "bshd" else t[:, keep] for t in (k, v))
+    k, v = k.contiguous(), v.contiguous()
+    g = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                             causal=causal)
+    dq, dk, dv, _ = autograd_grads(q, k, v, do, layout, SCALE, causal)
+    assert g.dk.shape == (2 * hkv * 35, 128)
     for got, ref in ((g.dq, dq), (g.dk, dk), (g.dv, dv)):
         assert np.allclose(got, ref, rtol=1e-11, atol=1e-12), np.abs(got - ref).max()
 

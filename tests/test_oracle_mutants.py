@@ -40,6 +40,7 @@ MUTANTS = {
     "gqa_head_modulo": ("int64_t hk = h / group;", "int64_t hk = h % Hkv;"),
     "causal_off_by_one": ("\n                n_keys = i + (Skv - Sq) + 1;", "\n                n_keys = i + (Skv - Sq);"),
     "causal_top_left": ("\n                n_keys = i + (Skv - Sq) + 1;", "\n                n_keys = i + 1;"),
+    "bwd_gqa_head_modulo": ("const int64_t kvh = h / group;", "const int64_t kvh = h % Hkv;"),
     "bwd_causal_off_by_one": ("\n                    n_keys = i + (Skv - Sq) + 1;", "\n                    n_keys = i + (Skv - Sq);"),
     "empty_rows_not_zero": ("if (n_keys <= 0) {", "if (n_keys < 0) {"),
     "lse_drops_max": ("if (lse) lse[t] = m + log(l);", "if (lse) lse[t] = log(l);"),
@@ -83,6 +84,7 @@ def pins():
     out.append(("bwd_autograd", lambda: BW.test_matches_torch_autograd_float64("bhsd", False, 23, 41)))
     out.append(("bwd_single_key", BW.test_single_key_closed_form))
     out.append(("bwd_causal", lambda: BW.test_matches_torch_autograd_float64("bshd", True, 37, 37)))
+    out.append(("bwd_gqa", lambda: BW.test_grouped_heads_match_torch_autograd_float64("bshd", 2, True)))
     return out
 
 
