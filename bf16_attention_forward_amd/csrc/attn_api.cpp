@@ -271,16 +271,18 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
 
 extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                              const float* lse, void* dq, void* dk, void* dv, int layout, int64_t B, int64_t H,
-                             int64_t Sq, int64_t Skv, float scale, int causal, void* stream) {
+                             int64_t Hkv, int64_t Sq, int64_t Skv, float scale, int causal, void* stream) {
     if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
-    if (B < 1 || H < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
+    if (B < 1 || H < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
+    if (H % Hkv != 0) return ATTN_ERR_SHAPE;
     const int64_t lim31 = (int64_t)1 << 31, hd = 128;
     if (B >= lim31 || H >= lim31 || Sq >= lim31 || Skv >= lim31 || B * H >= lim31) return ATTN_ERR_SHAPE;
-    const int64_t n_q = B * H * Sq, n_kv = B * H * Skv;
+    const int64_t n_q = B * H * Sq, n_kv = B * Hkv * Skv;
     if (n_q > ((int64_t)1 << 52) / hd || n_kv > ((int64_t)1 << 52) / hd) return ATTN_ERR_SHAPE;
     const int64_t q_rowe = (layout == ATTN_LAYOUT_BSHD) ? H * hd : hd;
-    if ((Sq - 1) * q_rowe * 2 + hd * 2 >= lim31 || (Skv - 1) * q_rowe * 2 + hd * 2 >= lim31) return ATTN_ERR_SHAPE;
+    const int64_t kv_rowe = (layout == ATTN_LAYOUT_BSHD) ? Hkv * hd : hd;
+    if ((Sq - 1) * q_rowe * 2 + hd * 2 >= lim31 || (Skv - 1) * kv_rowe * 2 + hd * 2 >= lim31) return ATTN_ERR_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO | (uintptr_t)dq |
@@ -311,12 +313,13 @@ extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const 
     p.dq = (uint16_t*)dq; p.dk = (uint16_t*)dk; p.dv = (uint16_t*)dv;
     if (layout == ATTN_LAYOUT_BSHD) {
         p.q_row = H * hd; p.q_head = hd; p.q_batch = Sq * H * hd;
-        p.kv_row = H * hd; p.kv_head = hd; p.kv_batch = Skv * H * hd;
+        p.kv_row = Hkv * hd; p.kv_head = hd; p.kv_batch = Skv * Hkv * hd;
     } else {
         p.q_row = hd; p.q_head = Sq * hd; p.q_batch = H * Sq * hd;
-        p.kv_row = hd; p.kv_head = Skv * hd; p.kv_batch = H * Skv * hd;
+        p.kv_row = hd; p.kv_head = Skv * hd; p.kv_batch = Hkv * Skv * hd;
     }
     p.B = (int)B; p.H = (int)H; p.Sq = (int)Sq; p.Skv = (int)Skv;
+    p.Hkv = (int)Hkv; p.group = (int)(H / Hkv);
     p.n_qblocks = (int)((Sq + 255) / 256);
     p.n_kblocks = (int)((Skv + 127) / 128);
     if (B * H * std::max(p.n_qblocks, p.n_kblocks) >= lim31) return ATTN_ERR_SHAPE;

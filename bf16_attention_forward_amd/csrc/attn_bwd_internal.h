@@ -18,9 +18,11 @@ struct BwdParams {
     uint16_t* dv;
     int64_t q_row, q_head, q_batch;      // element strides of q, o, dO, dq
     int64_t kv_row, kv_head, kv_batch;   // element strides of k, v, dk, dv
-    int B, H, Sq, Skv;
+    int B, H, Sq, Skv;    // H = query heads
+    int Hkv;              // key/value heads (H a multiple of Hkv)
+    int group;            // H / Hkv: query head h reads key/value head h / group
     int n_qblocks;        // ceil(Sq / 256): work-groups per (b, h) of the dQ kernel
-    int n_kblocks;        // ceil(Skv / 128): work-groups per (b, h) of the dK/dV kernel
+    int n_kblocks;        // ceil(Skv / 128): work-groups per (b, key/value head) of the dK/dV kernel
     float c;              // fp32(scale * log2(e))
     float scale;
     int causal;           // 1: query i sees keys j <= i + causal_off (the forward's mask)

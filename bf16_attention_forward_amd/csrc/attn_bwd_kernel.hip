@@ -21,6 +21,10 @@
 //    64-query Q and dO tiles.  Per tile: S = Q K^T and dP = dO V^T (Q and dO as
 //    operand A: each lane holds one key), then P and dS, then dV^T += dO^T P
 //    and dK^T += Q^T dS with dO^T and Q^T transposed out of LDS.
+// With grouped-query heads (query head h reads key/value head h / group) the
+// dQ kernel reads its head's key/value head, and a dK/dV work-group streams
+// the query tiles of every query head of its group in turn, so dK and dV add
+// up over the group in registers.
 // Under the causal mask (query i sees keys j <= i + Skv - Sq, the forward's
 // bottom-right alignment) the dQ key loop ends at the tile's diagonal and the
 // dK/dV query loop starts at it; the weights of masked pairs are zero by
@@ -36,6 +40,8 @@
 // rounded to bf16 (nearest-even).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_bwd_internal.h"
 
@@ -102,16 +108,26 @@ __device__ __forceinline__ TileSrc tile_src(const uint16_t* base, int64_t row_el
     return t;
 }
 // 16 bytes per lane from rs at voff + soff to LDS dst + 16 * lane
+// (the LDS address, the descriptor and the offset are wave-uniform: say so,
+// so they stay in scalar registers)
+__device__ __forceinline__ i32x4 uniform4(const i32x4 rs) {
+    return i32x4{__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                 __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
+}
 __device__ __forceinline__ void dma16(const i32x4 rs, uint8_t* dst, int voff, int soff) {
-    const uint32_t lds = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
+    const i32x4 rsu = uniform4(rs);
+    const int so = __builtin_amdgcn_readfirstlane(soff);
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+                     :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }
 // 4 bytes per lane from rs at voff + soff to LDS dst + 4 * lane
 __device__ __forceinline__ void dma4(const i32x4 rs, uint8_t* dst, int voff, int soff) {
-    const uint32_t lds = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
+    const i32x4 rsu = uniform4(rs);
+    const int so = __builtin_amdgcn_readfirstlane(soff);
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+                     :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }
 template <int NWK>
 __device__ __forceinline__ void issue_tile_n(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
@@ -223,8 +239,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         return;
     }
 
-    const TileSrc ks = tile_src(p.k + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
-    const TileSrc vs = tile_src(p.v + (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head, p.kv_row, p.Skv);
+    const int hk = h / p.group;                          // key/value head of query head h
+    const TileSrc ks = tile_src(p.k + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
+    const TileSrc vs = tile_src(p.v + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
     auto kslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES); };
     auto vslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
     // tile 0: all 8 waves; later tiles: waves 0-3
@@ -420,10 +437,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
     const int g = lane >> 4, j = lane & 15;
     // under the mask a key block's query range shrinks with its index:
     // blocks take the longest (first key blocks of every head) first
-    const int BH = p.B * p.H;
+    const int BH = p.B * p.Hkv;
     const int kt_ = CAUSAL ? (int)(blockIdx.x / BH) : (int)(blockIdx.x % p.n_kblocks);
-    const int bh = CAUSAL ? (int)(blockIdx.x % BH) : (int)(blockIdx.x / p.n_kblocks);
-    const int h = bh % p.H, b = bh / p.H;
+    const int bh = CAUSAL ? (int)(blockIdx.x % BH) : (int)(blockIdx.x / p.n_kblocks);   // (b, key/value head)
+    const int hk = bh % p.Hkv, b = bh / p.Hkv;
     const int kbase = kt_ * (NW * 16) + wave * 16;       // this wave's first key
     // query tiles [t0, t0 + T): under the mask the first query that sees the
     // work-group's first key is k0 - (Skv - Sq)
@@ -436,7 +453,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         // across the work-group, before any transfer or barrier)
         const int krow = kbase + j;
         if (krow < p.Skv) {
-            const int64_t ko = (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head + (int64_t)krow * p.kv_row + 4 * g;
+            const int64_t ko = (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head + (int64_t)krow * p.kv_row + 4 * g;
 #pragma unroll
             for (int db = 0; db < 8; db++) {
                 *(uint2*)(p.dk + ko + 16 * db) = uint2{0u, 0u};
@@ -446,36 +463,39 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         return;
     }
     const int q0 = t0 * TILE_ROWS;                       // first query row of tile 0
+    // steps u = 0 .. TT-1 run over the query heads of the group (outer) and
+    // their query tiles [t0, t0 + T) (inner): step u is tile u % T of query
+    // head hk * group + u / T, whose first row is q0 + (u % T) * 64
+    const int TT = T * p.group;
 
-    const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
-    const TileSrc qs = tile_src(p.q + qoff, p.q_row, p.Sq);
-    const TileSrc gs = tile_src(p.dO + qoff, p.q_row, p.Sq);
-    // L and delta of queries past Sq read as zero (range check)
-    const int64_t rbh = ((int64_t)b * p.H + h) * p.Sq;
-    const i32x4 lrs = buffer_rsrc(p.lse + rbh, (uint32_t)p.Sq * 4u);
-    const i32x4 drs = buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u);
     auto qslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES); };
     auto gslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
     auto lslot = [&](int sl) { return lsd + sl * LS_BYTES; };
-    auto issue_ls = [&](int q0, int sl) {
-        dma4(lrs, lslot(sl), lane * 4, q0 * 4);
-        dma4(drs, lslot(sl) + TILE_ROWS * 4, lane * 4, q0 * 4);
-    };
-    // tile 0: all 8 waves; later tiles: waves 0-3
-    issue_tile_n<NW>(qs, q0, qslot(0), wave, g, j);
-    issue_tile_n<NW>(gs, q0, gslot(0), wave, g, j);
-    if (wave == 0) issue_ls(q0, 0);
-    auto issue_next = [&](int t) __attribute__((always_inline)) {
-        if (!late && t < T) {
-            const int sl = t % NSLOT;
-            issue_tile_n<4>(qs, q0 + t * TILE_ROWS, qslot(sl), wave, g, j);
-            issue_tile_n<4>(gs, q0 + t * TILE_ROWS, gslot(sl), wave, g, j);
-            if (wave == 0) issue_ls(q0 + t * TILE_ROWS, sl);
+    // the Q, dO, L and delta tiles of step u into slot u % NSLOT, moved by NWK
+    // waves; each query head's tensors get their own buffer ranges, so rows
+    // past Sq read as zero (the range check), never the next head's rows
+    auto issue_step = [&](int u, auto nwk) __attribute__((always_inline)) {
+        constexpr int NWK = decltype(nwk)::value;
+        const int hq = hk * p.group + u / T;
+        const int r0 = q0 + (u % T) * TILE_ROWS;
+        const int sl = u % NSLOT;
+        const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)hq * p.q_head;
+        issue_tile_n<NWK>(tile_src(p.q + qoff, p.q_row, p.Sq), r0, qslot(sl), wave, g, j);
+        issue_tile_n<NWK>(tile_src(p.dO + qoff, p.q_row, p.Sq), r0, gslot(sl), wave, g, j);
+        if (wave == 0) {
+            const int64_t rbh = ((int64_t)b * p.H + hq) * p.Sq;
+            dma4(buffer_rsrc(p.lse + rbh, (uint32_t)p.Sq * 4u), lslot(sl), lane * 4, r0 * 4);
+            dma4(buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u), lslot(sl) + TILE_ROWS * 4, lane * 4, r0 * 4);
         }
+    };
+    // step 0: all 8 waves; later steps: waves 0-3
+    issue_step(0, std::integral_constant<int, NW>{});
+    auto issue_next = [&](int t) __attribute__((always_inline)) {
+        if (!late && t < TT) issue_step(t, std::integral_constant<int, 4>{});
     };
 
     // K and V of keys kbase + j (clamped; rows past Skv are never stored)
-    const int64_t koff = (int64_t)b * p.kv_batch + (int64_t)h * p.kv_head;
+    const int64_t koff = (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head;
     bf16x8 kf[4], vf[4];
     {
         const int row = min(kbase + j, p.Skv - 1);
@@ -533,14 +553,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
                 dk[db] = mfma(qtf, dsf[kk], dk[db]);
             }
     };
-    // P = 2^(c s - L log2 e), dS = P o (dP - delta) of tile t; queries past Sq
+    // P = 2^(c s - L log2 e), dS = P o (dP - delta) of step u; queries past Sq
     // (and, under the mask, queries before the key's diagonal) -> 0 by select
-    auto elementwise = [&](int t, int sl) __attribute__((always_inline)) {
+    auto elementwise = [&](int u, int sl) __attribute__((always_inline)) {
         const uint8_t* lt = lslot(sl);
-        const int valid = p.Sq - q0 - t * TILE_ROWS - 4 * g;
+        const int r0 = q0 + (u % T) * TILE_ROWS;        // first query row of the step's tile
+        const int valid = p.Sq - r0 - 4 * g;
         // query 16*mb + 4*g + r of the tile sees key kbase + j iff
         // 16*mb + r >= kbase + j - (Skv - Sq) - (first query of the tile) - 4*g
-        const int lo = CAUSAL ? kbase + j - p.causal_off - q0 - t * TILE_ROWS - 4 * g : -TILE_ROWS;
+        const int lo = CAUSAL ? kbase + j - p.causal_off - r0 - 4 * g : -TILE_ROWS;
         float pv[4][4], dsv[4][4];
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
@@ -583,7 +604,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
     elementwise(0, 0);
     if (!late) early_barrier();
     int cur = 1 % NSLOT, prev = 0;
-    for (int t = 1; t < T; t++) {
+    for (int t = 1; t < TT; t++) {
         issue_next(t + 1);
         pin_addr();
         __builtin_amdgcn_s_setprio(1);
@@ -624,7 +645,7 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(attn_bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;
     // the causal mask is a compile-time variant: the unmasked kernels carry none of it
-    const dim3 gk((unsigned)((int64_t)p.B * p.H * p.n_kblocks)), gq((unsigned)((int64_t)p.B * p.H * p.n_qblocks));
+    const dim3 gk((unsigned)((int64_t)p.B * p.Hkv * p.n_kblocks)), gq((unsigned)((int64_t)p.B * p.H * p.n_qblocks));
     if (p.causal) hipLaunchKernelGGL(attn_bwd_dkdv<true>, gk, dim3(NW * 64), 0, stream, p);
     else hipLaunchKernelGGL(attn_bwd_dkdv<false>, gk, dim3(NW * 64), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return -1;

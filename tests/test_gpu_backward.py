@@ -27,8 +27,8 @@ def rows_first(bits, layout):
     return np.ascontiguousarray(bits).reshape(-1, bits.shape[-1])
 
 
-def case_inputs(layout, B, H, Sq, Skv, seed, causal=False):
-    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, seed, 1.0, 2.0, 1.0)
+def case_inputs(layout, B, H, Sq, Skv, seed, causal=False, Hkv=None):
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, seed, 1.0, 2.0, 1.0, Hkv=Hkv)
     do = wl.random_qkv(layout, B, H, Sq, 1, seed + 5000)[0]
     fwd = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=SCALE, method=False,
                            causal=causal)
@@ -140,6 +140,62 @@ def test_causal_forward_then_backward_on_the_gpu():
                                 ("dv", rows_first(wl.bits(dv.cpu()), layout), ref.dv, ref.sdv)):
         st = gate.compare(g, exact, sig, "rtne")
         say(f"[gate] causal fwd+bwd {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
+        assert st["passed"], (name, st)
+
+
+GQA_CASES = [
+    # layout, B, Hq, Hkv, Sq, Skv, causal
+    ("bhsd", 1, 4, 1, 300, 500, False),    # one key/value head for four query heads
+    ("bshd", 2, 6, 2, 257, 130, False),    # ragged tails, three query heads per group
+    ("bhsd", 1, 4, 2, 300, 300, True),     # with the causal mask
+    ("bshd", 1, 8, 2, 200, 333, True),     # Sq < Skv under the mask
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=lambda c: f"{c[0]}_B{c[1]}Hq{c[2]}Hkv{c[3]}_{c[4]}x{c[5]}_{'causal' if c[6] else 'full'}")
+def test_grouped_heads_backward_matches_oracle(case):
+    """Grouped-query heads: dQ per query head from its key/value head, dK and
+    dV of a key/value head summed over its query heads (O and lse from the
+    oracle's grouped forward)."""
+    layout, B, Hq, Hkv, Sq, Skv, causal = case
+    q, k, v, do, o, o_bits, lse = case_inputs(layout, B, Hq, Sq, Skv, 900 + Sq + Skv, causal=causal, Hkv=Hkv)
+    say(f"[case] grouped backward {case}")
+    gq, gk, gv = run_bwd(q, k, v, o, do, lse, layout, causal=causal)
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                               o=o_bits, causal=causal)
+    gq_rows = rows_first(gq, layout)
+    keep = np.ones(B * Hq * Sq, bool)
+    if causal and 0 <= Sq - Skv < Sq:
+        keep.reshape(B * Hq, Sq)[:, Sq - Skv] = False     # rows that see one key: exact dQ 0 (noise bound below)
+    for name, g, exact, sig in (("dq", gq_rows[keep], ref.dq[keep], ref.sdq[keep]),
+                                ("dk", rows_first(gk, layout), ref.dk, ref.sdk),
+                                ("dv", rows_first(gv, layout), ref.dv, ref.sdv)):
+        st = gate.compare(g, exact, sig, "rtne")
+        say(f"[gate] grouped backward {case} {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
+        assert st["passed"], (name, st)
+    if not keep.all():
+        mx = lambda t: float(t.float().abs().max())
+        bound = SCALE * 2.0 ** -9 * mx(do) * mx(v) * mx(k)
+        assert np.all(np.abs(oracle.bf16_bits_to_f64(gq_rows[~keep])) <= bound)
+
+
+def test_grouped_forward_then_backward_on_the_gpu():
+    """End to end with grouped heads: the GPU grouped forward's O and lse feed
+    the GPU backward; the oracle's gradients for that same O."""
+    from bf16_attention_forward_amd import attn_fwd_bf16_gqa, attn_bwd_bf16
+    layout, B, Hq, Hkv, Sq, Skv = "bhsd", 1, 4, 2, 300, 700
+    q, k, v = wl.random_qkv(layout, B, Hq, Sq, Skv, 51, 1.0, 2.0, 1.0, Hkv=Hkv)
+    do = wl.random_qkv(layout, B, Hq, Sq, 1, 5051)[0]
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = attn_fwd_bf16_gqa(qd, kd, vd, layout=layout, return_lse=True)
+    dq, dk, dv = attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=layout)
+    torch.cuda.synchronize()
+    assert dk.shape == k.shape and dv.shape == v.shape
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE,
+                               o=wl.bits(o.cpu()))
+    for name, g, exact, sig in (("dq", dq, ref.dq, ref.sdq), ("dk", dk, ref.dk, ref.sdk), ("dv", dv, ref.dv, ref.sdv)):
+        st = gate.compare(rows_first(wl.bits(g.cpu()), layout), exact, sig, "rtne")
+        say(f"[gate] grouped fwd+bwd {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
         assert st["passed"], (name, st)
 
 
