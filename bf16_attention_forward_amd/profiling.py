@@ -39,6 +39,9 @@ def short_name(name: str) -> str:
         return "attn_fwd_main"
     if "attn_fwd_combine" in name:
         return "attn_fwd_combine"
+    for k in ("attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_delta"):
+        if k in name:
+            return k + ("<causal>" if "<true>" in name else "")
     if "copy" in name.lower() or "elementwise" in name.lower():
         return "copy:" + name[:60]
     return name[:80]
