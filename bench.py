@@ -167,22 +167,24 @@ BWD_FLOP_FACTOR = 2.5
 def time_backward(w, steps, warmup):
     """Median ms of attn_bwd_bf16 on workload w (O and lse from the forward)."""
     import torch
-    from bf16_attention_forward_amd import attn_bwd_bf16, attn_fwd_bf16_gqa
+    from bf16_attention_forward_amd import attn_bwd_bf16, attn_fwd_bf16_hd
     from bf16_attention_forward_amd import workloads as wl
 
     q, k, v = wl.make_inputs(w)
-    do = wl.random_qkv(w.layout, w.B, w.H, w.Sq, 1, w.seed + 5000)[0]
+    do = wl.random_qkv(w.layout, w.B, w.H, w.Sq, 1, w.seed + 5000, D=w.D)[0]
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
-    o, lse = attn_fwd_bf16_gqa(qd, kd, vd, layout=w.layout, causal=w.causal, return_lse=True)
+    o, lse = attn_fwd_bf16_hd(qd, kd, vd, layout=w.layout, scale=w.scale, causal=w.causal, return_lse=True)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    bwd = lambda: attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=w.layout, scale=w.scale, causal=w.causal,
+                                dq=dq, dk=dk, dv=dv)
     for _ in range(warmup):
-        attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=w.layout, causal=w.causal, dq=dq, dk=dk, dv=dv)
+        bwd()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         a.record()
-        attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=w.layout, causal=w.causal, dq=dq, dk=dk, dv=dv)
+        bwd()
         b.record()
     torch.cuda.synchronize()
     return statistics.median([a.elapsed_time(b) for a, b in evs])
@@ -240,8 +242,8 @@ def main():
 
     w = wl.WORKLOADS[args.workload]
     if args.backward:
-        if w.D != 128:
-            print(f"the backward pass covers head dimension 128; not {w.name}", file=sys.stderr)
+        if w.D not in (128, 64):
+            print(f"the backward pass covers head dimensions 128 and 64; not {w.name}", file=sys.stderr)
             sys.exit(2)
         em = time_backward(w, steps=args.steps, warmup=args.warmup)
         tf = BWD_FLOP_FACTOR * w.flops / (em * 1e-3) / 1e12
@@ -298,8 +300,8 @@ def main():
                                                  "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
 
         # backward pass of the default workload and of the causal 4096^2 one
-        for ww in (w, wl.WORKLOADS[7], wl.WORKLOADS[6]):
-            if ww.D == 128:
+        for ww in (w, wl.WORKLOADS[7], wl.WORKLOADS[6], wl.WORKLOADS[8]):
+            if ww.D in (128, 64):
                 em = time_backward(ww, steps=20, warmup=5)
                 tf = BWD_FLOP_FACTOR * ww.flops / (em * 1e-3) / 1e12
                 extra[f"{ww.name}:backward"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),

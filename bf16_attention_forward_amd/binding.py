@@ -58,7 +58,7 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16_hd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_bf16_hd.restype = ctypes.c_int
-    lib.attn_bwd_bf16.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
+    lib.attn_bwd_bf16.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_bwd_bf16.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -227,12 +227,13 @@ def attn_bwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
                   dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
     """Backward pass (attn_bwd_bf16): returns (dq, dk, dv) for the output
     gradient ``do``, from the forward's output ``o`` and log-sum-exp ``lse``
-    (float32 [B, Hq, Sq]).  Head dimension 128; k and v may have fewer heads
+    (float32 [B, Hq, Sq]).  Head dimension 128 or 64; k and v may have fewer heads
     than q (the forward's grouping; dk, dv then sum over each group);
     causal: the forward's mask (query i sees keys j <= i + Skv - Sq)."""
     lib = load_library()
     _check_tensors(q, k, v, o)
-    B, H, Hkv, Sq, Skv = _dims(q, k, layout, grouped=True)
+    B, H, Hkv, Sq, Skv = _dims(q, k, layout, grouped=True, head_dims=HEAD_DIMS)
+    D = q.shape[-1]
     for name, t in (("do", do),):
         if t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous bfloat16 device tensor shaped like q")
@@ -244,12 +245,12 @@ def attn_bwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t.dtype != torch.bfloat16 or t.shape != ref.shape or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous bfloat16 device tensor shaped like its input")
-    sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
+    sc = float(1.0 / math.sqrt(D)) if scale is None else float(scale)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
         rc = lib.attn_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ATTN_LAYOUT[layout],
-                               B, H, Hkv, Sq, Skv, sc, 1 if causal else 0, st.cuda_stream)
+                               B, H, Hkv, Sq, Skv, D, sc, 1 if causal else 0, st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
     return dq, dk, dv

@@ -271,12 +271,14 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
 
 extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                              const float* lse, void* dq, void* dk, void* dv, int layout, int64_t B, int64_t H,
-                             int64_t Hkv, int64_t Sq, int64_t Skv, float scale, int causal, void* stream) {
+                             int64_t Hkv, int64_t Sq, int64_t Skv, int64_t head_dim, float scale, int causal,
+                             void* stream) {
     if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
     if (B < 1 || H < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return ATTN_ERR_SHAPE;
     if (H % Hkv != 0) return ATTN_ERR_SHAPE;
-    const int64_t lim31 = (int64_t)1 << 31, hd = 128;
+    if (head_dim != 128 && head_dim != 64) return ATTN_ERR_SHAPE;
+    const int64_t lim31 = (int64_t)1 << 31, hd = head_dim;
     if (B >= lim31 || H >= lim31 || Sq >= lim31 || Skv >= lim31 || B * H >= lim31) return ATTN_ERR_SHAPE;
     const int64_t n_q = B * H * Sq, n_kv = B * Hkv * Skv;
     if (n_q > ((int64_t)1 << 52) / hd || n_kv > ((int64_t)1 << 52) / hd) return ATTN_ERR_SHAPE;
@@ -327,6 +329,7 @@ extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const 
     p.scale = scale;
     p.causal = causal;
     p.causal_off = (int)(Skv - Sq);
+    p.head_dim = (int)head_dim;
     void* ws = nullptr;
     const int wrc = get_workspace(dev, stream, (size_t)n_q * sizeof(float), &ws);
     if (wrc != ATTN_OK) return wrc;

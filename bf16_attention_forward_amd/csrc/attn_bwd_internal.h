@@ -27,6 +27,7 @@ struct BwdParams {
     float scale;
     int causal;           // 1: query i sees keys j <= i + causal_off (the forward's mask)
     int causal_off;       // Skv - Sq
+    int head_dim;         // 128 or 64
 };
 
 int launch_bwd(const BwdParams& p, hipStream_t stream);

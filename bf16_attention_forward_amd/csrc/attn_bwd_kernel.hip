@@ -1,5 +1,5 @@
 // attn_bwd_kernel.hip -- gfx950 (MI355X, CDNA4) kernels for the backward pass
-// of bf16 attention, head dimension 128, for O = softmax(Q K^T * scale) V.
+// of bf16 attention, head dimension 128 or 64, for O = softmax(Q K^T * scale) V.
 //
 // The HipKittens summary's kernel suite pairs the attention forward kernels
 // with their backward; the gradients follow from the chain rule on the
@@ -30,12 +30,15 @@
 // dK/dV query loop starts at it; the weights of masked pairs are zero by
 // select, and work-groups that see no pair write zeros and exit.
 // Every LDS tile is read both straight (ds_read_b128) and transposed, so all
-// tiles keep one layout: 16-byte chunk c of row r at c ^ swz(r), where
+// tiles keep one layout: 16-byte chunk c of row r at c ^ swz(r).  With
+// 256-byte rows (head dimension 128)
 // swz(r) = 2 (r & 7) + ((r >> 3) & 1) takes 16 distinct values over any 16
 // rows in a row (straight reads: 16 rows at one chunk column, no two lanes in
 // one bank) and keeps chunk pairs together with 8 distinct pair positions
 // over any 8 rows in a row (transposed reads: 8 rows x one 32-byte pair per
-// half-wave).  P and dS enter the
+// half-wave).  With 128-byte rows (head dimension 64) two rows share a
+// 256-byte bank pass and swz(r) = 2 ((r >> 1) & 3) + ((r >> 3) & 1) over 8
+// chunk positions does the same.  P and dS enter the
 // MFMAs as bf16 (round to nearest-even); all sums are fp32; the gradients are
 // rounded to bf16 (nearest-even).
 #include <hip/hip_runtime.h>
@@ -56,10 +59,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int D = 128;
-constexpr int ROW_BYTES = D * 2;
 constexpr int TILE_ROWS = 64;
-constexpr int TILE_BYTES = TILE_ROWS * ROW_BYTES;   // 16 KiB
 constexpr int NW = 8;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -92,7 +92,9 @@ __device__ __forceinline__ void lds_barrier() {
 // the other buffer (it cannot tell the two buffers apart); every wave waits
 // for its own transfers in lds_barrier.
 // chunk swizzle of row r (only r mod 16 matters)
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+template <int HD> __device__ __forceinline__ int swz(int r) {
+    return HD == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
 struct TileSrc {
     i32x4 rs;
     int row_bytes;
@@ -101,10 +103,10 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
     const uint64_t a = (uint64_t)(uintptr_t)base;
     return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
-__device__ __forceinline__ TileSrc tile_src(const uint16_t* base, int64_t row_elems, int rows) {
+template <int HD> __device__ __forceinline__ TileSrc tile_src(const uint16_t* base, int64_t row_elems, int rows) {
     TileSrc t;
     t.row_bytes = (int)(row_elems * 2);
-    t.rs = buffer_rsrc(base, (uint32_t)((int64_t)(rows - 1) * t.row_bytes + ROW_BYTES));
+    t.rs = buffer_rsrc(base, (uint32_t)((int64_t)(rows - 1) * t.row_bytes + 2 * HD));
     return t;
 }
 // 16 bytes per lane from rs at voff + soff to LDS dst + 16 * lane
@@ -129,32 +131,31 @@ __device__ __forceinline__ void dma4(const i32x4 rs, uint8_t* dst, int voff, int
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                      :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }
-template <int NWK>
+template <int HD, int NWK>
 __device__ __forceinline__ void issue_tile_n(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
     static_assert(NWK == 4 || NWK == 8, "4 or 8 waves");
-    const int row = wave * 4 + g;
-    const int voff = row * s.row_bytes + ((j ^ swz(row)) << 4);
+    constexpr int CPR = HD / 8, RPW = 64 / CPR;      // 16-byte chunks per row, rows per wave and round
+    const int lane = 16 * g + j;
+    const int row = wave * RPW + lane / CPR;
+    const int voff = row * s.row_bytes + (((lane % CPR) ^ swz<HD>(row)) << 4);
 #pragma unroll
-    for (int i = 0; i < 16 / NWK; i++)
-        dma16(s.rs, dst + ((i * NWK + wave) * 64) * 16, voff, (r0 + 4 * NWK * i) * s.row_bytes);
-}
-__device__ __forceinline__ void issue_tile(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
-    issue_tile_n<NW>(s, r0, dst, wave, g, j);
+    for (int i = 0; i < TILE_ROWS / (RPW * NWK); i++)
+        dma16(s.rs, dst + ((i * NWK + wave) * 64) * 16, voff, (r0 + RPW * NWK * i) * s.row_bytes);
 }
 
 // Straight fragment (operand A): lane (g, j) gets row 16*rb + j, dims
 // 32*ks + 8*g .. +7.
-__device__ __forceinline__ bf16x8 read_rows(const uint8_t* tile, int addr0, int rb) {
-    return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(tile + addr0 + rb * 16 * ROW_BYTES);
+template <int HD> __device__ __forceinline__ bf16x8 read_rows(const uint8_t* tile, int addr0, int rb) {
+    return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(tile + addr0 + rb * 16 * (2 * HD));
 }
 // Transposed fragment (operand A of a product over the tile's rows): lane
 // (g, j) gets, as elements 4*hf + e, rows 32*ks + 16*hf + 4*g + e of dim
 // 16*db + j (the order of the B operand built from a C fragment).
-__device__ __forceinline__ bf16x8 read_cols(const uint8_t* tile, int addr0, int ks) {
+template <int HD> __device__ __forceinline__ bf16x8 read_cols(const uint8_t* tile, int addr0, int ks) {
     bf16x4 half[2];
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-        const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(tile + addr0 + (32 * ks + 16 * hf) * ROW_BYTES);
+        const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(tile + addr0 + (32 * ks + 16 * hf) * (2 * HD));
         half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
     }
     return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -174,6 +175,7 @@ __device__ __forceinline__ bf16x8 pack_b(const float* lo4, const float* hi4) {
 }
 
 // ---------------------------------------------------------------- delta
+template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
     const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (b*H + h)*Sq + i
     if (r >= (int64_t)p.B * p.H * p.Sq) return;
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
     const uint4* gp = (const uint4*)(p.dO + off);
     float acc = 0.f;
 #pragma unroll 4
-    for (int c = 0; c < D / 8; c++) {
+    for (int c = 0; c < HD / 8; c++) {
         const uint4 a = op[c], g = gp[c];
         const uint32_t av[4] = {a.x, a.y, a.z, a.w}, gv[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
@@ -205,9 +207,12 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
 // straight), then the elementwise step of tile t; three K/V slots.
 constexpr int NSLOT = 3;
 
-template <bool CAUSAL>
+template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(HD == 128 || HD == 64, "head dimension 128 or 64");
+    constexpr int ROW_BYTES = 2 * HD, TILE_BYTES = TILE_ROWS * ROW_BYTES;
+    constexpr int NKK = HD / 32, NDB = HD / 16;   // k-steps over the dims, 16-dim blocks
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[NSLOT * 2 * TILE_BYTES];   // per slot: K, V
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -234,31 +239,31 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
             const int row = qrow0 + qb * 16 + j;
             if (row >= p.Sq) continue;
 #pragma unroll
-            for (int db = 0; db < 8; db++) *(uint2*)(dqz + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
+            for (int db = 0; db < NDB; db++) *(uint2*)(dqz + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
         }
         return;
     }
 
     const int hk = h / p.group;                          // key/value head of query head h
-    const TileSrc ks = tile_src(p.k + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
-    const TileSrc vs = tile_src(p.v + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
+    const TileSrc ks = tile_src<HD>(p.k + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
+    const TileSrc vs = tile_src<HD>(p.v + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
     auto kslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES); };
     auto vslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
     // tile 0: all 8 waves; later tiles: waves 0-3
-    issue_tile_n<NW>(ks, 0, kslot(0), wave, g, j);
-    issue_tile_n<NW>(vs, 0, vslot(0), wave, g, j);
+    issue_tile_n<HD, NW>(ks, 0, kslot(0), wave, g, j);
+    issue_tile_n<HD, NW>(vs, 0, vslot(0), wave, g, j);
     auto issue_next = [&](int t) __attribute__((always_inline)) {
         if (!late && t < T) {
             const int sl = t % NSLOT;
-            issue_tile_n<4>(ks, t * TILE_ROWS, kslot(sl), wave, g, j);
-            issue_tile_n<4>(vs, t * TILE_ROWS, vslot(sl), wave, g, j);
+            issue_tile_n<HD, 4>(ks, t * TILE_ROWS, kslot(sl), wave, g, j);
+            issue_tile_n<HD, 4>(vs, t * TILE_ROWS, vslot(sl), wave, g, j);
         }
     };
 
     // Q and dO of query rows qrow0 + 16*qb + j (clamped; results of rows past
     // Sq are never stored), dims 32*kk + 8*g .. +7: operand B.
     const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
-    bf16x8 qf[2][4], gf[2][4];
+    bf16x8 qf[2][NKK], gf[2][NKK];
     float lse2[2], dlt[2];
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
@@ -266,7 +271,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         const uint16_t* qs = p.q + qoff + (int64_t)row * p.q_row + 8 * g;
         const uint16_t* gs = p.dO + qoff + (int64_t)row * p.q_row + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
+        for (int kk = 0; kk < NKK; kk++) {
             qf[qb][kk] = *(const bf16x8*)(qs + 32 * kk);
             gf[qb][kk] = *(const bf16x8*)(gs + 32 * kk);
         }
@@ -280,24 +285,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < 2; qb++) {
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) __asm__ volatile("" : "+v"(qf[qb][kk]), "+v"(gf[qb][kk]));
+        for (int kk = 0; kk < NKK; kk++) __asm__ volatile("" : "+v"(qf[qb][kk]), "+v"(gf[qb][kk]));
         __asm__ volatile("" : "+v"(lse2[qb]), "+v"(dlt[qb]));
     }
-    f32x4 dq[8][2];
+    f32x4 dq[NDB][2];
 #pragma unroll
-    for (int db = 0; db < 8; db++)
+    for (int db = 0; db < NDB; db++)
 #pragma unroll
         for (int qb = 0; qb < 2; qb++) dq[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // per-lane fragment offsets: straight reads of row j, transposed reads of
     // rows 4*g + j/4 (+ multiples of 16: same swizzle)
-    int a_row[4], a_col[8];
+    int a_row[NKK], a_col[NDB];
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ swz(j)) << 4);
+    for (int kk = 0; kk < NKK; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ swz<HD>(j)) << 4);
 #pragma unroll
-    for (int db = 0; db < 8; db++) {
+    for (int db = 0; db < NDB; db++) {
         const int row = 4 * g + (j >> 2);
-        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz(row)) << 4) + ((j & 1) << 3);
+        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz<HD>(row)) << 4) + ((j & 1) << 3);
     }
     lds_barrier();
 
@@ -308,11 +313,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         const uint8_t* kt = kslot(sl);
         const uint8_t* vt = vslot(sl);
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++)
+        for (int kk = 0; kk < NKK; kk++)
 #pragma unroll
             for (int kb = 0; kb < 4; kb++) {
-                const bf16x8 kf = read_rows(kt, a_row[kk], kb);
-                const bf16x8 vf = read_rows(vt, a_row[kk], kb);
+                const bf16x8 kf = read_rows<HD>(kt, a_row[kk], kb);
+                const bf16x8 vf = read_rows<HD>(vt, a_row[kk], kb);
 #pragma unroll
                 for (int qb = 0; qb < 2; qb++) {
                     s[kb][qb] = mfma(kf, qf[qb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][qb]);
@@ -326,8 +331,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < 2; kk++)
 #pragma unroll
-            for (int db = 0; db < 8; db++) {
-                const bf16x8 kt_f = read_cols(kt, a_col[db], kk);
+            for (int db = 0; db < NDB; db++) {
+                const bf16x8 kt_f = read_cols<HD>(kt, a_col[db], kk);
 #pragma unroll
                 for (int qb = 0; qb < 2; qb++) dq[db][qb] = mfma(kt_f, dsf[qb][kk], dq[db][qb]);
             }
@@ -360,9 +365,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     };
     auto pin_addr = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
+        for (int i = 0; i < NKK; i++) __asm__ volatile("" : "+v"(a_row[i]));
 #pragma unroll
-        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
+        for (int i = 0; i < NDB; i++) __asm__ volatile("" : "+v"(a_col[i]));
     };
 
     // iteration 0: products of tile 0 only
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         if (row >= p.Sq) continue;
         uint16_t* dst = dqb + (int64_t)row * p.q_row + 4 * g;
 #pragma unroll
-        for (int db = 0; db < 8; db++) {
+        for (int db = 0; db < NDB; db++) {
             uint2 pk;
             pk.x = rtne_bits(dq[db][qb][0] * p.scale) | (rtne_bits(dq[db][qb][1] * p.scale) << 16);
             pk.y = rtne_bits(dq[db][qb][2] * p.scale) | (rtne_bits(dq[db][qb][3] * p.scale) << 16);
@@ -426,9 +431,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 // registers per wave, one wave per SIMD; measured slower.)
 constexpr int LS_BYTES = 2 * TILE_ROWS * 4;   // L and delta of a tile's 64 queries
 
-template <bool CAUSAL>
+template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(HD == 128 || HD == 64, "head dimension 128 or 64");
+    constexpr int ROW_BYTES = 2 * HD, TILE_BYTES = TILE_ROWS * ROW_BYTES;
+    constexpr int NKK = HD / 32, NDB = HD / 16;   // k-steps over the dims, 16-dim blocks
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[NSLOT * 2 * TILE_BYTES];   // per slot: Q, dO
     __shared__ __attribute__((aligned(16))) uint8_t lsd[NSLOT * LS_BYTES];           // per slot: L, delta
     const int lane = threadIdx.x & 63;
@@ -455,7 +463,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         if (krow < p.Skv) {
             const int64_t ko = (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head + (int64_t)krow * p.kv_row + 4 * g;
 #pragma unroll
-            for (int db = 0; db < 8; db++) {
+            for (int db = 0; db < NDB; db++) {
                 *(uint2*)(p.dk + ko + 16 * db) = uint2{0u, 0u};
                 *(uint2*)(p.dv + ko + 16 * db) = uint2{0u, 0u};
             }
@@ -480,8 +488,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         const int r0 = q0 + (u % T) * TILE_ROWS;
         const int sl = u % NSLOT;
         const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)hq * p.q_head;
-        issue_tile_n<NWK>(tile_src(p.q + qoff, p.q_row, p.Sq), r0, qslot(sl), wave, g, j);
-        issue_tile_n<NWK>(tile_src(p.dO + qoff, p.q_row, p.Sq), r0, gslot(sl), wave, g, j);
+        issue_tile_n<HD, NWK>(tile_src<HD>(p.q + qoff, p.q_row, p.Sq), r0, qslot(sl), wave, g, j);
+        issue_tile_n<HD, NWK>(tile_src<HD>(p.dO + qoff, p.q_row, p.Sq), r0, gslot(sl), wave, g, j);
         if (wave == 0) {
             const int64_t rbh = ((int64_t)b * p.H + hq) * p.Sq;
             dma4(buffer_rsrc(p.lse + rbh, (uint32_t)p.Sq * 4u), lslot(sl), lane * 4, r0 * 4);
@@ -496,30 +504,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
 
     // K and V of keys kbase + j (clamped; rows past Skv are never stored)
     const int64_t koff = (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head;
-    bf16x8 kf[4], vf[4];
+    bf16x8 kf[NKK], vf[NKK];
     {
         const int row = min(kbase + j, p.Skv - 1);
         const uint16_t* ksrc = p.k + koff + (int64_t)row * p.kv_row + 8 * g;
         const uint16_t* vsrc = p.v + koff + (int64_t)row * p.kv_row + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
+        for (int kk = 0; kk < NKK; kk++) {
             kf[kk] = *(const bf16x8*)(ksrc + 32 * kk);
             vf[kk] = *(const bf16x8*)(vsrc + 32 * kk);
         }
     }
     // wait for these loads here, once (as in the dQ kernel)
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) __asm__ volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
-    f32x4 dk[8], dv[8];
+    for (int kk = 0; kk < NKK; kk++) __asm__ volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
+    f32x4 dk[NDB], dv[NDB];
 #pragma unroll
-    for (int db = 0; db < 8; db++) { dk[db] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[db] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-    int a_row[4], a_col[8];
+    for (int db = 0; db < NDB; db++) { dk[db] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[db] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    int a_row[NKK], a_col[NDB];
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ swz(j)) << 4);
+    for (int kk = 0; kk < NKK; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ swz<HD>(j)) << 4);
 #pragma unroll
-    for (int db = 0; db < 8; db++) {
+    for (int db = 0; db < NDB; db++) {
         const int row = 4 * g + (j >> 2);
-        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz(row)) << 4) + ((j & 1) << 3);
+        a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz<HD>(row)) << 4) + ((j & 1) << 3);
     }
     lds_barrier();
 
@@ -530,11 +538,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         const uint8_t* qt = qslot(sl);
         const uint8_t* gt = gslot(sl);
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++)
+        for (int kk = 0; kk < NKK; kk++)
 #pragma unroll
             for (int mb = 0; mb < 4; mb++) {
-                const bf16x8 qa = read_rows(qt, a_row[kk], mb);
-                const bf16x8 ga = read_rows(gt, a_row[kk], mb);
+                const bf16x8 qa = read_rows<HD>(qt, a_row[kk], mb);
+                const bf16x8 ga = read_rows<HD>(gt, a_row[kk], mb);
                 s[mb] = mfma(qa, kf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mb]);
                 dp[mb] = mfma(ga, vf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[mb]);
             }
@@ -546,9 +554,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < 2; kk++)
 #pragma unroll
-            for (int db = 0; db < 8; db++) {
-                const bf16x8 gtf = read_cols(gt, a_col[db], kk);
-                const bf16x8 qtf = read_cols(qt, a_col[db], kk);
+            for (int db = 0; db < NDB; db++) {
+                const bf16x8 gtf = read_cols<HD>(gt, a_col[db], kk);
+                const bf16x8 qtf = read_cols<HD>(qt, a_col[db], kk);
                 dv[db] = mfma(gtf, pf[kk], dv[db]);
                 dk[db] = mfma(qtf, dsf[kk], dk[db]);
             }
@@ -589,9 +597,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
     };
     auto pin_addr = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) __asm__ volatile("" : "+v"(a_row[i]));
+        for (int i = 0; i < NKK; i++) __asm__ volatile("" : "+v"(a_row[i]));
 #pragma unroll
-        for (int i = 0; i < 8; i++) __asm__ volatile("" : "+v"(a_col[i]));
+        for (int i = 0; i < NDB; i++) __asm__ volatile("" : "+v"(a_col[i]));
     };
 
     // iteration 0: products of tile 0 only
@@ -627,7 +635,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         uint16_t* dkd = p.dk + koff + (int64_t)krow * p.kv_row + 4 * g;
         uint16_t* dvd = p.dv + koff + (int64_t)krow * p.kv_row + 4 * g;
 #pragma unroll
-        for (int db = 0; db < 8; db++) {
+        for (int db = 0; db < NDB; db++) {
             uint2 a, c;
             a.x = rtne_bits(dk[db][0] * p.scale) | (rtne_bits(dk[db][1] * p.scale) << 16);
             a.y = rtne_bits(dk[db][2] * p.scale) | (rtne_bits(dk[db][3] * p.scale) << 16);
@@ -641,18 +649,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
 }
 
 int launch_bwd(const BwdParams& p, hipStream_t stream) {
-    const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-    hipLaunchKernelGGL(attn_bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return -1;
-    // the causal mask is a compile-time variant: the unmasked kernels carry none of it
-    const dim3 gk((unsigned)((int64_t)p.B * p.Hkv * p.n_kblocks)), gq((unsigned)((int64_t)p.B * p.H * p.n_qblocks));
-    if (p.causal) hipLaunchKernelGGL(attn_bwd_dkdv<true>, gk, dim3(NW * 64), 0, stream, p);
-    else hipLaunchKernelGGL(attn_bwd_dkdv<false>, gk, dim3(NW * 64), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return -1;
-    if (p.causal) hipLaunchKernelGGL(attn_bwd_dq<true>, gq, dim3(NW * 64), 0, stream, p);
-    else hipLaunchKernelGGL(attn_bwd_dq<false>, gq, dim3(NW * 64), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return -1;
-    return 0;
+    // head dimension and causal mask are compile-time variants
+    auto go = [&](auto hd) -> int {
+        constexpr int H_ = decltype(hd)::value;
+        const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+        hipLaunchKernelGGL(attn_bwd_delta<H_>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return -1;
+        const dim3 gk((unsigned)((int64_t)p.B * p.Hkv * p.n_kblocks)), gq((unsigned)((int64_t)p.B * p.H * p.n_qblocks));
+        if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv<H_, true>), gk, dim3(NW * 64), 0, stream, p);
+        else hipLaunchKernelGGL((attn_bwd_dkdv<H_, false>), gk, dim3(NW * 64), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return -1;
+        if (p.causal) hipLaunchKernelGGL((attn_bwd_dq<H_, true>), gq, dim3(NW * 64), 0, stream, p);
+        else hipLaunchKernelGGL((attn_bwd_dq<H_, false>), gq, dim3(NW * 64), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return -1;
+        return 0;
+    };
+    if (p.head_dim == 64) return go(std::integral_constant<int, 64>{});
+    if (p.head_dim == 128) return go(std::integral_constant<int, 128>{});
+    return -1;
 }
 
 }  // namespace attn_bwd

@@ -182,8 +182,8 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
                      int64_t head_dim, float scale, int causal, int round_mode, void* stream);
 
 /*
- * attn_bwd_bf16 -- backward pass of attn_fwd_bf16 / attn_fwd_bf16_gqa (head
- * dimension 128): dQ, dK, dV for a given dO.
+ * attn_bwd_bf16 -- backward pass of attn_fwd_bf16 / attn_fwd_bf16_gqa /
+ * attn_fwd_bf16_hd: dQ, dK, dV for a given dO.
  *
  * The gradients of O = softmax(Q K^T * scale) V follow from the chain rule on
  * the forward's definition (the HipKittens summary's kernel suite pairs the
@@ -193,9 +193,9 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
  *     dS = P o (dP - delta),  delta_i = <dO_i, O_i>,
  *     dQ = scale * dS K,      dK = scale * dS^T Q.
  *
- *   q, o, dO   [B,Sq,H,128] or [B,H,Sq,128] bf16, device (read); o is the
- *              forward output for these q, k, v, scale
- *   k, v       [B,Skv,Hkv,128] or [B,Hkv,Skv,128] bf16, device (read); query
+ *   q, o, dO   [B,Sq,H,D] or [B,H,Sq,D] bf16, device (read), D = head_dim;
+ *              o is the forward output for these q, k, v, scale
+ *   k, v       [B,Skv,Hkv,D] or [B,Hkv,Skv,D] bf16, device (read); query
  *              head h reads key/value head h / (H / Hkv) (attn_fwd_bf16_gqa's
  *              grouping; H a multiple of Hkv, else ATTN_ERR_SHAPE), and dK, dV
  *              of a key/value head sum over its query heads
@@ -203,6 +203,7 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
  *              (attn_fwd_bf16_gqa's lse output), 4-byte aligned
  *   dq         shaped like q; dk, dv shaped like k (bf16, written, rounded to
  *              nearest-even); no output may overlap an input or another output
+ *   head_dim   128 or 64 (else ATTN_ERR_SHAPE)
  *   layout, B, H, Sq, Skv, scale, stream  as attn_fwd_bf16 (H: query heads)
  *   causal     0: every key; 1: the mask of attn_fwd_bf16_gqa (query i sees
  *              keys j <= i + Skv - Sq); lse must come from the forward with
@@ -216,7 +217,8 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
  */
 int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, void* dq, void* dk, void* dv, int layout, int64_t B, int64_t H,
-                  int64_t Hkv, int64_t Sq, int64_t Skv, float scale, int causal, void* stream);
+                  int64_t Hkv, int64_t Sq, int64_t Skv, int64_t head_dim, float scale, int causal,
+                  void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* attn_status_string(int status);

@@ -152,11 +152,11 @@ def test_gqa_valid_arguments_reach_device_check():
 def call_bwd(**kw):
     a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), do=FAKE + (4 << 30),
              lse=FAKE + (5 << 30), dq=FAKE + (6 << 30), dk=FAKE + (7 << 30), dv=FAKE + (8 << 30), layout=1,
-             B=1, H=2, Hkv=2, Sq=64, Skv=64, scale=0.088, causal=0, stream=0)
+             B=1, H=2, Hkv=2, Sq=64, Skv=64, hd=128, scale=0.088, causal=0, stream=0)
     a.update(kw)
     return load_library().attn_bwd_bf16(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
                                         a["dv"], a["layout"], a["B"], a["H"], a["Hkv"], a["Sq"], a["Skv"],
-                                        a["scale"], a["causal"], a["stream"])
+                                        a["hd"], a["scale"], a["causal"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -167,7 +167,7 @@ def call_bwd(**kw):
     (dict(dk=FAKE + (6 << 30) + 16), -7),               # dk overlaps dq
     (dict(dv=FAKE + (5 << 30)), -7),                    # dv overlaps lse
     (dict(causal=2), -11), (dict(causal=-1), -11),
-    (dict(Hkv=0), -4), (dict(Hkv=3), -4), (dict(H=4, Hkv=3), -4),
+    (dict(Hkv=0), -4), (dict(Hkv=3), -4), (dict(H=4, Hkv=3), -4), (dict(hd=96), -4), (dict(hd=256), -4),
 ])
 def test_bwd_argument_errors_before_device(kw, code):
     assert call_bwd(**kw) == code
@@ -180,3 +180,4 @@ def test_bwd_valid_arguments_reach_device_check():
     assert call_bwd() == -8
     assert call_bwd(causal=1) == -8
     assert call_bwd(H=4, Hkv=1) == -8 and call_bwd(H=4, Hkv=2, causal=1) == -8
+    assert call_bwd(hd=64) == -8

@@ -27,22 +27,22 @@ def rows_first(bits, layout):
     return np.ascontiguousarray(bits).reshape(-1, bits.shape[-1])
 
 
-def case_inputs(layout, B, H, Sq, Skv, seed, causal=False, Hkv=None):
-    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, seed, 1.0, 2.0, 1.0, Hkv=Hkv)
-    do = wl.random_qkv(layout, B, H, Sq, 1, seed + 5000)[0]
-    fwd = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=SCALE, method=False,
+def case_inputs(layout, B, H, Sq, Skv, seed, causal=False, Hkv=None, D=128, scale=SCALE):
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, seed, 1.0, 2.0, 1.0, Hkv=Hkv, D=D)
+    do = wl.random_qkv(layout, B, H, Sq, 1, seed + 5000, D=D)[0]
+    fwd = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=scale, method=False,
                            causal=causal)
-    o_rows = fwd.rounded("rtne").reshape(B, H, Sq, 128)
+    o_rows = fwd.rounded("rtne").reshape(B, H, Sq, D)
     o_bits = o_rows.transpose(0, 2, 1, 3).copy() if layout == "bshd" else o_rows.copy()
     o = torch.from_numpy(o_bits.view(np.int16)).view(torch.bfloat16)
     lse = torch.from_numpy(fwd.lse.astype(np.float32).reshape(B, H, Sq))
     return q, k, v, do, o, o_bits, lse
 
 
-def run_bwd(q, k, v, o, do, lse, layout, causal=False):
+def run_bwd(q, k, v, o, do, lse, layout, causal=False, scale=SCALE):
     from bf16_attention_forward_amd import attn_bwd_bf16
     dq, dk, dv = attn_bwd_bf16(to_dev(q), to_dev(k), to_dev(v), to_dev(o), to_dev(do), to_dev(lse),
-                               layout=layout, scale=SCALE, causal=causal)
+                               layout=layout, scale=scale, causal=causal)
     torch.cuda.synchronize()
     return wl.bits(dq.cpu()), wl.bits(dk.cpu()), wl.bits(dv.cpu())
 
@@ -196,6 +196,65 @@ def test_grouped_forward_then_backward_on_the_gpu():
     for name, g, exact, sig in (("dq", dq, ref.dq, ref.sdq), ("dk", dk, ref.dk, ref.sdk), ("dv", dv, ref.dv, ref.sdv)):
         st = gate.compare(rows_first(wl.bits(g.cpu()), layout), exact, sig, "rtne")
         say(f"[gate] grouped fwd+bwd {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
+        assert st["passed"], (name, st)
+
+
+D64_CASES = [
+    # layout, B, Hq, Hkv, Sq, Skv, causal
+    ("bhsd", 1, 2, 2, 300, 500, False),
+    ("bshd", 2, 3, 3, 257, 130, False),    # ragged tails
+    ("bshd", 1, 4, 2, 257, 257, True),     # grouped heads and the causal mask
+    ("bhsd", 1, 2, 1, 333, 130, True),     # Sq > Skv: rows without keys
+]
+SCALE64 = float(np.float32(0.125))
+
+
+@pytest.mark.parametrize("case", D64_CASES, ids=lambda c: f"{c[0]}_B{c[1]}Hq{c[2]}Hkv{c[3]}_{c[4]}x{c[5]}_{'causal' if c[6] else 'full'}_d64")
+def test_head_dim_64_backward_matches_oracle(case):
+    """Head dimension 64 (128-byte rows, the backward's 8-position LDS
+    swizzle), against the oracle's backward at D = 64."""
+    layout, B, Hq, Hkv, Sq, Skv, causal = case
+    q, k, v, do, o, o_bits, lse = case_inputs(layout, B, Hq, Sq, Skv, 1100 + Sq + Skv, causal=causal, Hkv=Hkv,
+                                              D=64, scale=SCALE64)
+    say(f"[case] d64 backward {case}")
+    gq, gk, gv = run_bwd(q, k, v, o, do, lse, layout, causal=causal, scale=SCALE64)
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE64,
+                               o=o_bits, causal=causal)
+    gq_rows = rows_first(gq, layout)
+    keep = np.ones(B * Hq * Sq, bool)
+    if causal and 0 <= Sq - Skv < Sq:
+        keep.reshape(B * Hq, Sq)[:, Sq - Skv] = False     # rows that see one key: exact dQ 0
+    for name, g, exact, sig in (("dq", gq_rows[keep], ref.dq[keep], ref.sdq[keep]),
+                                ("dk", rows_first(gk, layout), ref.dk, ref.sdk),
+                                ("dv", rows_first(gv, layout), ref.dv, ref.sdv)):
+        st = gate.compare(g, exact, sig, "rtne")
+        say(f"[gate] d64 backward {case} {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
+        assert st["passed"], (name, st)
+    if not keep.all():
+        mx = lambda t: float(t.float().abs().max())
+        bound = SCALE64 * 2.0 ** -9 * mx(do) * mx(v) * mx(k)
+        assert np.all(np.abs(oracle.bf16_bits_to_f64(gq_rows[~keep])) <= bound)
+    if causal:   # rows that see no key (Sq > Skv under the mask) have dQ = 0 exactly
+        no_key = np.arange(Sq) + (Skv - Sq) < 0
+        assert np.all(gq_rows.reshape(B * Hq, Sq, 64)[:, no_key] == 0)
+
+
+def test_head_dim_64_forward_then_backward_on_the_gpu():
+    """End to end at head dimension 64: attn_fwd_bf16_hd's O and lse feed the
+    backward; the oracle's gradients for that same O."""
+    from bf16_attention_forward_amd import attn_fwd_bf16_hd, attn_bwd_bf16
+    layout, B, H, Sq, Skv = "bshd", 1, 4, 400, 600
+    q, k, v = wl.random_qkv(layout, B, H, Sq, Skv, 53, 1.0, 2.0, 1.0, D=64)
+    do = wl.random_qkv(layout, B, H, Sq, 1, 5053, D=64)[0]
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = attn_fwd_bf16_hd(qd, kd, vd, layout=layout, scale=SCALE64, return_lse=True)
+    dq, dk, dv = attn_bwd_bf16(qd, kd, vd, o, dod, lse, layout=layout, scale=SCALE64)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do), layout=layout, scale=SCALE64,
+                               o=wl.bits(o.cpu()))
+    for name, g, exact, sig in (("dq", dq, ref.dq, ref.sdq), ("dk", dk, ref.dk, ref.sdk), ("dv", dv, ref.dv, ref.sdv)):
+        st = gate.compare(rows_first(wl.bits(g.cpu()), layout), exact, sig, "rtne")
+        say(f"[gate] d64 fwd+bwd {name} max_D={st['max_D']:.2f} >1={st['frac_D_gt1']:.5f}")
         assert st["passed"], (name, st)
 
 

@@ -147,60 +147,72 @@ def test_forward_weight_key_order():
 
 
 # ---------------------------------------------------------------- backward
-def swz_b(row):
-    return ((row & 7) << 1) | ((row >> 3) & 1)
+def swz_b(hd, row):
+    """256-byte rows: 2 (r & 7) + ((r >> 3) & 1) over 16 chunk positions;
+    128-byte rows (two rows per 256-byte bank pass): 2 ((r >> 1) & 3) +
+    ((r >> 3) & 1) over 8."""
+    if hd == 128:
+        return ((row & 7) << 1) | ((row >> 3) & 1)
+    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1)
 
 
-def bwd_dma_image(nwk):
-    """The backward's issue_tile_n: NWK waves, 16 / NWK rounds of 4 NWK rows;
-    lane (g, j) of wave w in round i writes row 4 NWK i + 4 w + g, chunk
-    position j, holding source chunk j ^ swz(row)."""
+def bwd_dma_image(hd, nwk):
+    """The backward's issue_tile_n: NWK waves move a 64-row tile in rounds of
+    64 NWK / CPR rows (CPR = 16-byte chunks per row); lane l of wave w in
+    round i writes row (64 / CPR) (NWK i + w) + l / CPR, chunk position
+    l % CPR, holding source chunk (l % CPR) ^ swz(row)."""
+    cpr = hd // 8
+    rpw = 64 // cpr                  # rows per wave and round
     image = {}
-    for i in range(16 // nwk):
+    for i in range(TILE_ROWS // (rpw * nwk)):
         for w in range(nwk):
             for lane in range(64):
-                g, j = lane >> 4, lane & 15
-                row = 4 * w + g
-                src_row = 4 * nwk * i + row
+                row = rpw * w + lane // cpr
+                pos = lane % cpr
+                src_row = rpw * nwk * i + row
                 lds = ((i * nwk + w) * 64 + lane) * 16
                 assert lds not in image
-                image[lds] = (src_row, j ^ swz_b(row))
+                image[lds] = (src_row, pos ^ swz_b(hd, row))
     return image
 
 
+@pytest.mark.parametrize("hd", [128, 64])
 @pytest.mark.parametrize("nwk", [8, 4])
-def test_backward_dma_places_every_chunk_once(nwk):
-    image = bwd_dma_image(nwk)
-    assert sorted(image.values()) == [(r, c) for r in range(TILE_ROWS) for c in range(16)]
+def test_backward_dma_places_every_chunk_once(hd, nwk):
+    image = bwd_dma_image(hd, nwk)
+    row_bytes = 2 * hd
+    assert sorted(image.values()) == [(r, c) for r in range(TILE_ROWS) for c in range(hd // 8)]
     for lds, (row, chunk) in image.items():
-        assert lds == row * 256 + ((chunk ^ swz_b(row)) << 4)
+        assert lds == row * row_bytes + ((chunk ^ swz_b(hd, row)) << 4)
 
 
-def test_backward_straight_and_transposed_reads():
+@pytest.mark.parametrize("hd", [128, 64])
+def test_backward_straight_and_transposed_reads(hd):
     """One layout serves both reads of every backward tile: read_rows (lane
     (g, j) of step (kk, rb): row 16 rb + j, dims 32 kk + 8 g .. + 7) and
     read_cols (lane (g, j), element 4 hf + e: row 32 ks + 16 hf + 4 g + e,
     dim 16 db + j), both bank-spread as in the forward."""
-    image = bwd_dma_image(8)
-    for kk in range(4):
+    image = bwd_dma_image(hd, 8)
+    rb_ = 2 * hd
+    for kk in range(hd // 32):
         for rb in range(4):
             for g in range(4):
                 slots = set()
                 for j in range(16):
-                    addr = j * 256 + (((4 * kk + g) ^ swz_b(j)) << 4) + rb * 16 * 256
+                    addr = j * rb_ + (((4 * kk + g) ^ swz_b(hd, j)) << 4) + rb * 16 * rb_
                     assert [element(image, addr + 2 * e) for e in range(8)] == \
                         [(16 * rb + j, 32 * kk + 8 * g + e) for e in range(8)]
                     slots.add((addr % 256) // 16)
                 assert len(slots) == 16
     for ks in range(2):
-        for db in range(8):
+        for db in range(hd // 16):
             for hf in range(2):
                 lane_addr = {}
                 for g in range(4):
                     for j in range(16):
                         row = 4 * g + (j >> 2)
-                        a_col = row * 256 + (((2 * db + ((j & 3) >> 1)) ^ swz_b(row)) << 4) + ((j & 1) << 3)
-                        lane_addr[(g, j)] = a_col + (32 * ks + 16 * hf) * 256
+                        a_col = row * rb_ + (((2 * db + ((j & 3) >> 1)) ^ swz_b(hd, row)) << 4) + ((j & 1) << 3)
+                        lane_addr[(g, j)] = a_col + (32 * ks + 16 * hf) * rb_
                 for g in range(4):
                     out = tr16([lane_addr[(g, s)] for s in range(16)], image)
                     for j in range(16):
