@@ -1,10 +1,12 @@
 // attn_fwd_kernel.hip -- gfx950 (MI355X, CDNA4) kernels for bf16 attention forward.
 //
-// Computes O = softmax(Q K^T * scale) V for head dimension 128 (the fused
-// operation of "MoonMath AI open-sources a HIP attention kernel for AMD
+// Computes O = softmax(Q K^T * scale) V for head dimension 128 or 64 (the
+// fused operation of "MoonMath AI open-sources a HIP attention kernel for AMD
 // MI300X that beats AITER", opening paragraphs), streaming K/V tiles with an
 // online softmax.  Design, per work-group (8 waves, 256 query rows of one
-// (batch, head), one work-group per CU):
+// (batch, head), one work-group per CU; for key ranges of at most 16 tiles a
+// 4-wave variant with 128 rows, two work-groups per CU, so one's Q loads and
+// O stores overlap the other's matrix work):
 //
 //  * Each wave owns 32 query rows; its Q fragments stay in VGPRs for the
 //    whole key loop and O accumulates in registers (the MI300X article's data
