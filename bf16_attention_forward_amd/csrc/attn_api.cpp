@@ -102,7 +102,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-extern "C" int attn_version(void) { return 10400; }
+extern "C" int attn_version(void) { return 10500; }
 
 extern "C" const char* attn_status_string(int status) {
     switch (status) {
