@@ -49,7 +49,7 @@ def measured_traffic(workload_name: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
+def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False, block_order=0):
     import torch
     from bf16_attention_forward_amd import attn_fwd_bf16, attn_fwd_bf16_gqa, attn_fwd_bf16_hd
     from bf16_attention_forward_amd import workloads as wl
@@ -69,6 +69,7 @@ def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False):
                               round_weights=round_weights)
         else:
             attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode, stream=stream, kv_splits=kv_splits,
+                          block_order=block_order,
                           round_weights=round_weights)
 
     for _ in range(warmup):
@@ -219,7 +220,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", type=int, default=2, help="workload number (1..5)")
+    ap.add_argument("--workload", type=int, default=2, help="workload number (1..9)")
+    ap.add_argument("--block-order", choices=["planner", "naive", "xcd"], default="planner",
+                    help="work-group order of the plain entry point (an ablation of the XCD-aware order)")
     ap.add_argument("--mode", default="rtne")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -254,7 +257,8 @@ def main():
                           "config": {**w.describe(), "pass": "backward"}}), flush=True)
         return
     sclk_idle = read_sclk_mhz()
-    r = time_workload(w, args.mode, args.steps, args.warmup)
+    order = {"planner": 0, "naive": 1, "xcd": 2}[args.block_order]
+    r = time_workload(w, args.mode, args.steps, args.warmup, block_order=order)
     ms_step = r["wall_s"] * 1e3 / args.steps
     tflops = w.flops / (ms_step * 1e-3) / 1e12
     ev_mean = statistics.fmean(r["ms"])
@@ -322,7 +326,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 inputs, K x2)",
-        "config": {**w.describe(), "round_mode": args.mode, "parallelism": "single GPU"},
+        "config": {**w.describe(), "round_mode": args.mode, "parallelism": "single GPU",
+                   **({"block_order": args.block_order} if args.block_order != "planner" else {})},
         "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernel_ms": {"mean": round(ev_mean, 5), "median": round(statistics.median(srt), 5),
                       "min": round(srt[0], 5), "p90": round(srt[int(0.9 * (len(srt) - 1))], 5)},
