@@ -223,6 +223,10 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="workload number (1..9)")
     ap.add_argument("--block-order", choices=["planner", "naive", "xcd"], default="planner",
                     help="work-group order of the plain entry point (an ablation of the XCD-aware order)")
+    ap.add_argument("--sq", type=int, default=0,
+                    help="override the workload's query length (e.g. for a ragged last round of work items)")
+    ap.add_argument("--kv-splits", type=int, default=0,
+                    help="key splits of the plain entry point: 0 = planner, 1 = never (an ablation of the tail split)")
     ap.add_argument("--mode", default="rtne")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -244,6 +248,9 @@ def main():
         sys.exit(1)
 
     w = wl.WORKLOADS[args.workload]
+    if args.sq:
+        import dataclasses
+        w = dataclasses.replace(w, Sq=args.sq, name=f"{w.name}_sq{args.sq}")
     if args.backward:
         if w.D not in (128, 64):
             print(f"the backward pass covers head dimensions 128 and 64; not {w.name}", file=sys.stderr)
@@ -258,7 +265,7 @@ def main():
         return
     sclk_idle = read_sclk_mhz()
     order = {"planner": 0, "naive": 1, "xcd": 2}[args.block_order]
-    r = time_workload(w, args.mode, args.steps, args.warmup, block_order=order)
+    r = time_workload(w, args.mode, args.steps, args.warmup, block_order=order, kv_splits=args.kv_splits)
     ms_step = r["wall_s"] * 1e3 / args.steps
     tflops = w.flops / (ms_step * 1e-3) / 1e12
     ev_mean = statistics.fmean(r["ms"])
@@ -327,7 +334,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 inputs, K x2)",
         "config": {**w.describe(), "round_mode": args.mode, "parallelism": "single GPU",
-                   **({"block_order": args.block_order} if args.block_order != "planner" else {})},
+                   **({"block_order": args.block_order} if args.block_order != "planner" else {}),
+                   **({"kv_splits": args.kv_splits} if args.kv_splits else {})},
         "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernel_ms": {"mean": round(ev_mean, 5), "median": round(statistics.median(srt), 5),
                       "min": round(srt[0], 5), "p90": round(srt[int(0.9 * (len(srt) - 1))], 5)},
