@@ -285,7 +285,7 @@ def main():
                                          "frac_peak": round(w.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         clocks = {"sclk_mhz_idle_before": sclk_idle, "sclk_mhz_under_load": sclk_under_load(w, args.mode),
                   "sclk_mhz_after": read_sclk_mhz(), "source": "sysfs pp_dpm_sclk (current level)"}
-        for num in (3, 4, 5, 6, 7, 8, 9):
+        for num in (1, 3, 4, 5, 6, 7, 8, 9):   # 1: the tiny 128x128 case (launch-latency bound)
             ww = wl.WORKLOADS[num]
             # sub-millisecond launches need more warm-up than the long ones
             # to reach a steady clock (100 launches of them take < 0.1 s)
