@@ -83,10 +83,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // The 64-row tile at row r0 of a tensor (row stride row_elems) into LDS with
-// buffer_load ... lds: NWK waves move it in 16 / NWK rounds of 4 * NWK rows;
-// lane (g, j) of wave w in round i writes row 4*NWK*i + 4*w + g, chunk
-// position j, holding the source chunk j ^ swz(row) (4*NWK is a multiple of
-// 16, so one swizzle serves every round).  Rows past `rows` read as zero (the
+// buffer_load ... lds: one instruction moves RPW rows (RPW = 64 / CPR, CPR
+// the 16-byte chunks of a row: 4 rows at head dimension 128, 8 at 64), and NWK
+// waves move the tile in 64 / (RPW * NWK) rounds; lane l of wave w in round i
+// writes row RPW*(NWK*i + w) + l / CPR, chunk position l % CPR, holding the
+// source chunk (l % CPR) ^ swz(row) (RPW*NWK is a multiple of 16, so one
+// swizzle serves every round).  Rows past `rows` read as zero (the
 // buffer's range check).  The loads are issued from inline assembly: the
 // compiler then adds no vmcnt waits of its own in front of the LDS reads of
 // the other buffer (it cannot tell the two buffers apart); every wave waits

@@ -82,7 +82,7 @@ def test_key_extent_limit_edge():
 
 
 def test_valid_arguments_reach_device_check():
-    # no GPU here: a valid call stops at the device probe (-8); on a GPU machine this test is skipped
+    # without a GPU a valid call stops at the device probe (-8); with one this test is skipped
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
