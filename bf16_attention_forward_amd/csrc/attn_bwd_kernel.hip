@@ -122,6 +122,9 @@ __device__ __forceinline__ void dma16(const i32x4 rs, uint8_t* dst, int voff, in
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
     const i32x4 rsu = uniform4(rs);
     const int so = __builtin_amdgcn_readfirstlane(soff);
+    // m0 is written in the same statement as the load (as in the forward
+    // kernel): nothing can be scheduled between them, and no other code of
+    // these kernels uses m0.
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                      :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }

@@ -287,6 +287,11 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         const int so = __builtin_amdgcn_readfirstlane(soff);
         const i32x4 rsu = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
                            __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
+        // m0 (the LDS destination) is written in the same statement as the
+        // load, so nothing is scheduled between the two; no other code of the
+        // kernel uses m0, which makes the clobber safe.  Handing the address
+        // in as an {m0} operand lets the compiler move the write away from
+        // the load, and that form gave wrong results here.
         __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                          :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
     };
