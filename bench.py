@@ -6,14 +6,17 @@ staging, both MFMA products, the online softmax, the rounding epilogue and,
 when the planner splits keys, the combine kernel) over one batch of seeded
 synthetic input already resident in HBM.
 
-Default workload: self-attention, BHSD, B=2, H=16, Sq=Skv=4096, head dim
-128, K scaled x2, RTNE output.  The other large workloads are timed too and
-reported under "workloads".  Methodology follows the HipKittens summary's
+Default workload: the largest single-GPU configuration, video-diffusion
+self-attention, BSHD, B=1, H=12, Sq=Skv=32760 (a 21x30x52 latent grid), head
+dim 128, Q/K/V ~ N(0,1)*0.5, RTNE output.  The other workloads are timed too
+and reported under "workloads".  Methodology follows the HipKittens summary's
 experiments section: warm-up launches, then timed launches on N(0,1)-style
-inputs.
+inputs; before the warm-up the workload runs back to back for a few seconds
+so the timed launches see the clock the GPU settles at under this load, and
+the shader clock is sampled during the timed launches.
 
 Prints ONE JSON line:
-  value        = algorithmic TFLOP/s (4*B*H*Sq*Skv*128 / time per step)
+  value        = algorithmic TFLOP/s (4*B*H*Sq*Skv*128 / wall time per step)
   roofline     = the main kernel's achieved TFLOP/s (HIP events around each
                  launch on the launch stream) against the dense bf16 MFMA peak
   cpu_baseline = the fp64 oracle timed on a bounded row sample on the host
@@ -49,7 +52,14 @@ def measured_traffic(workload_name: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False, block_order=0):
+def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False, block_order=0, settle_s=0.0,
+                  sample_clock=False):
+    """Time `steps` launches of workload w after `warmup` untimed ones (and,
+    with settle_s > 0, after running it back to back for that many seconds
+    first).  Returns wall seconds of the timed launches, per-launch ms from
+    HIP events recorded on the launch stream, and (sample_clock) the shader
+    clock levels read while the timed launches ran."""
+    import threading
     import torch
     from bf16_attention_forward_amd import attn_fwd_bf16, attn_fwd_bf16_gqa, attn_fwd_bf16_hd
     from bf16_attention_forward_amd import workloads as wl
@@ -72,12 +82,29 @@ def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False, bloc
                           block_order=block_order,
                           round_weights=round_weights)
 
+    if settle_s > 0:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     # per-launch HIP events on the launch stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    clocks, done = [], threading.Event()
+
+    def sampler():
+        while not done.wait(0.05):
+            mhz = read_sclk_mhz()
+            if mhz is not None:
+                clocks.append(mhz)
+
+    th = threading.Thread(target=sampler, daemon=True) if sample_clock else None
     torch.cuda.synchronize()
+    if th:
+        th.start()
     t0 = time.perf_counter()
     for a, b in evs:
         a.record(stream)
@@ -85,8 +112,11 @@ def time_workload(w, mode, steps, warmup, kv_splits=0, round_weights=False, bloc
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if th:
+        done.set()
+        th.join()
     per = [a.elapsed_time(b) for a, b in evs]   # ms
-    return {"wall_s": wall, "ms": per, "flops": w.flops}
+    return {"wall_s": wall, "ms": per, "flops": w.flops, "sclk_mhz": clocks}
 
 
 def time_cold(w, mode, steps, warmup=20):
@@ -134,30 +164,6 @@ def read_sclk_mhz():
             m = re.search(r"(\d+)\s*mhz", line.lower())
             return int(m.group(1)) if m else None
     return None
-
-
-def sclk_under_load(w, mode, seconds=2.0):
-    """Shader clock read while the workload runs back to back for `seconds`
-    (a thread reads it in the middle of the run)."""
-    import threading
-    import torch
-    from bf16_attention_forward_amd import attn_fwd_bf16
-    from bf16_attention_forward_amd import workloads as wl
-
-    q, k, v = wl.make_inputs(w)
-    dev = torch.device("cuda:0")
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    od = torch.empty_like(qd)
-    got = {}
-    t = threading.Timer(seconds / 2, lambda: got.setdefault("mhz", read_sclk_mhz()))
-    t0 = time.perf_counter()
-    t.start()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(20):
-            attn_fwd_bf16(qd, kd, vd, od, layout=w.layout, round_mode=mode)
-        torch.cuda.synchronize()
-    t.join()
-    return got.get("mhz")
 
 
 # algorithmic FLOPs of the backward pass: five products of the forward's
@@ -220,7 +226,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", type=int, default=2, help="workload number (1..9)")
+    ap.add_argument("--workload", type=int, default=3, help="workload number (1..9)")
+    ap.add_argument("--settle", type=float, default=3.0,
+                    help="seconds of back-to-back launches before the warm-up (clock settling)")
     ap.add_argument("--block-order", choices=["planner", "naive", "xcd"], default="planner",
                     help="work-group order of the plain entry point (an ablation of the XCD-aware order)")
     ap.add_argument("--sq", type=int, default=0,
@@ -265,61 +273,70 @@ def main():
         return
     sclk_idle = read_sclk_mhz()
     order = {"planner": 0, "naive": 1, "xcd": 2}[args.block_order]
-    r = time_workload(w, args.mode, args.steps, args.warmup, block_order=order, kv_splits=args.kv_splits)
+    r = time_workload(w, args.mode, args.steps, args.warmup, block_order=order, kv_splits=args.kv_splits,
+                      settle_s=args.settle, sample_clock=True)
     ms_step = r["wall_s"] * 1e3 / args.steps
     tflops = w.flops / (ms_step * 1e-3) / 1e12
     ev_mean = statistics.fmean(r["ms"])
     achieved = w.flops / (ev_mean * 1e-3) / 1e12
     srt = sorted(r["ms"])
     traffic = measured_traffic(w.name)
+    sk = sorted(r["sclk_mhz"])
+    clocks = {"sclk_mhz_idle_before": sclk_idle,
+              "sclk_mhz_timed_median": sk[len(sk) // 2] if sk else None,
+              "sclk_mhz_timed_min": sk[0] if sk else None, "sclk_mhz_timed_max": sk[-1] if sk else None,
+              "sclk_samples": len(sk), "settle_s": args.settle,
+              "source": "sysfs pp_dpm_sclk (current level), sampled every 50 ms during the timed launches"}
+    if sk:
+        # dense bf16 peak at the clock the timed launches ran at
+        clocks["peak_tflops_at_timed_median_clock"] = round(MFMA_BF16_PEAK_TFLOPS * clocks["sclk_mhz_timed_median"]
+                                                            / 2400.0, 1)
 
     extra = {}
-    clocks = None
     if not args.no_extra:
         # caches cleared before every launch (the timed value above runs warm,
         # as the HipKittens experiments do)
-        cold = sorted(time_cold(w, args.mode, steps=30))
+        cold = sorted(time_cold(w, args.mode, steps=10 if w.flops > 2e12 else 30))
         em = statistics.median(cold)
         extra[f"{w.name}:cold_cache"] = {"mode": args.mode, "median_ms": round(em, 4), "min_ms": round(cold[0], 4),
                                          "tflops": round(w.flops / (em * 1e-3) / 1e12, 1),
                                          "frac_peak": round(w.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-        clocks = {"sclk_mhz_idle_before": sclk_idle, "sclk_mhz_under_load": sclk_under_load(w, args.mode),
-                  "sclk_mhz_after": read_sclk_mhz(), "source": "sysfs pp_dpm_sclk (current level)"}
-        for num in (1, 3, 4, 5, 6, 7, 8, 9):   # 1: the tiny 128x128 case (launch-latency bound)
+        # every other workload in each of its rounding modes
+        for num in sorted(wl.WORKLOADS):
             ww = wl.WORKLOADS[num]
             # sub-millisecond launches need more warm-up than the long ones
             # to reach a steady clock (100 launches of them take < 0.1 s)
             short = ww.flops < 2e12
-            for mode in ww.modes[:1]:
-                rr = time_workload(ww, mode, steps=100 if short else 20, warmup=100 if short else 10)
+            for mode in ww.modes:
+                if ww.name == w.name and mode == args.mode:
+                    continue
+                rr = time_workload(ww, mode, steps=100 if short else 20, warmup=200 if short else 10,
+                                   settle_s=0.5)
                 em = statistics.median(rr["ms"])
-                extra[ww.name] = {"mode": mode, "median_ms": round(em, 4),
-                                  "tflops": round(ww.flops / (em * 1e-3) / 1e12, 1),
-                                  "frac_peak": round(ww.flops / (em * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-        for mode in w.modes:
-            if mode == args.mode:
-                continue
-            rr = time_workload(w, mode, steps=100, warmup=200)
+                extra[f"{ww.name}:{mode}"] = {"mode": mode, "median_ms": round(em, 4),
+                                              "tflops": round(ww.flops / (em * 1e-3) / 1e12, 1),
+                                              "frac_peak": round(ww.flops / (em * 1e-3) / 1e12 /
+                                                                 MFMA_BF16_PEAK_TFLOPS, 4)}
+        # the option that rounds the in-loop weights with the output's mode,
+        # on the 4096^2 self-attention workload
+        w2 = wl.WORKLOADS[2]
+        for mode in w2.modes:
+            rr = time_workload(w2, mode, steps=100, warmup=200, round_weights=True, settle_s=0.5)
             em = statistics.median(rr["ms"])
-            extra[f"{w.name}:{mode}"] = {"mode": mode, "median_ms": round(em, 4),
-                                         "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
-        # the option that rounds the in-loop weights with the output's mode
-        for mode in w.modes:
-            rr = time_workload(w, mode, steps=100, warmup=200, round_weights=True)
-            em = statistics.median(rr["ms"])
-            extra[f"{w.name}:{mode}+weights"] = {"mode": mode, "round_weights": True, "median_ms": round(em, 4),
-                                                 "tflops": round(w.flops / (em * 1e-3) / 1e12, 1)}
+            extra[f"{w2.name}:{mode}+weights"] = {"mode": mode, "round_weights": True, "median_ms": round(em, 4),
+                                                  "tflops": round(w2.flops / (em * 1e-3) / 1e12, 1)}
 
-        # backward pass of the default workload and of the causal 4096^2 one
-        for ww in (w, wl.WORKLOADS[7], wl.WORKLOADS[6], wl.WORKLOADS[8]):
-            if ww.D in (128, 64):
-                em = time_backward(ww, steps=20, warmup=5)
-                tf = BWD_FLOP_FACTOR * ww.flops / (em * 1e-3) / 1e12
-                extra[f"{ww.name}:backward"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),
-                                                "frac_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        # backward pass of the 4096^2 workloads (plain, causal, head dim 64) and the grouped causal one
+        for ww in (wl.WORKLOADS[2], wl.WORKLOADS[7], wl.WORKLOADS[6], wl.WORKLOADS[8]):
+            em = time_backward(ww, steps=20, warmup=5)
+            tf = BWD_FLOP_FACTOR * ww.flops / (em * 1e-3) / 1e12
+            extra[f"{ww.name}:backward"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),
+                                            "frac_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
 
+    factors = {"q": w.q_factor, "k": w.k_factor, "v": w.v_factor}
+    scaled = ", ".join(f"{n.upper()} x{f:g}" for n, f in factors.items() if f != 1.0)
     out = {
         "metric": "attention fwd TFLOPS (4*B*H*Sq*Skv*d) and % of bf16 MFMA peak, d=128",
         "value": round(tflops, 2),
@@ -332,7 +349,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 inputs, K x2)",
+        "data": "synthetic (seeded N(0,1) bf16 inputs" + (f", {scaled}" if scaled else "") + ")",
         "config": {**w.describe(), "round_mode": args.mode, "parallelism": "single GPU",
                    **({"block_order": args.block_order} if args.block_order != "planner" else {}),
                    **({"kv_splits": args.kv_splits} if args.kv_splits else {})},

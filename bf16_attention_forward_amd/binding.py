@@ -141,8 +141,10 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     q, k, v, o: contiguous bfloat16 CUDA tensors in the given layout.  o is
     allocated when None.  scale defaults to 1/sqrt(128) (as fp32).  The
     launch goes to ``stream`` (default: torch's current stream) and is
-    asynchronous.  kv_splits/block_order/waves are the planner overrides of
-    attn_fwd_bf16_ex (0 = automatic; waves 8 or 4 per work-group).  round_weights: round the in-loop
+    asynchronous.  With kv_splits, block_order and waves all 0 (automatic)
+    the call goes to the C entry point attn_fwd_bf16; otherwise to
+    attn_fwd_bf16_ex with those planner overrides (waves 8 or 4 per
+    work-group).  round_weights: round the in-loop
     softmax weights with ``round_mode`` too (ATTN_ROUND_WEIGHTS; default:
     nearest-even).
     """
@@ -152,9 +154,15 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
-        rc = lib.attn_fwd_bf16_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                  ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, _mode(round_mode, round_weights),
-                                  st.cuda_stream, int(kv_splits), int(block_order), int(waves))
+        if kv_splits == 0 and block_order == 0 and waves == 0:
+            # the planner's own choices: the plain entry point
+            rc = lib.attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, _mode(round_mode, round_weights),
+                                   st.cuda_stream)
+        else:
+            rc = lib.attn_fwd_bf16_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, _mode(round_mode, round_weights),
+                                      st.cuda_stream, int(kv_splits), int(block_order), int(waves))
     if rc != ATTN_OK:
         _raise(rc)
     return o

@@ -1,20 +1,26 @@
 """Build the gfx950 HIP library (libattn_fwd.so) in-tree with hipcc.
 
-Usage: python -m bf16_attention_forward_amd.build   (or build() from Python)
-The resource-usage report of the kernels (VGPR/AGPR/SGPR counts, LDS,
-scratch, occupancy) is written next to the library as
-libattn_fwd.resource-usage.txt.
+Usage: python -m bf16_attention_forward_amd.build            (or build() from Python)
+       python -m bf16_attention_forward_amd.build --table    (build, then print a
+                                                               per-kernel resource table)
+The compiler's raw resource-usage remarks (VGPR/AGPR/SGPR counts, LDS,
+scratch, occupancy per kernel) are written to _build/ at the repository root,
+a build folder kept out of version control; resource_table() condenses them
+into one markdown row per kernel.
 """
 from __future__ import annotations
 
 import os
+import re
+import shutil
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_fwd.so")
-REPORT = os.path.join(HERE, "libattn_fwd.resource-usage.txt")
+BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
+REPORT = os.path.join(BUILD_DIR, "libattn_fwd.resource-usage.txt")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
@@ -36,12 +42,58 @@ def build(extra_flags=None, out=None, quiet=True) -> str:
         raise RuntimeError("hipcc failed building libattn_fwd.so")
     os.replace(out + ".tmp", out)
     lines = [ln for ln in res.stderr.splitlines() if "remark:" in ln]
-    with open(REPORT if out == LIB else out + ".resource-usage.txt", "w") as f:
+    report = REPORT if out == LIB else out + ".resource-usage.txt"
+    os.makedirs(os.path.dirname(report), exist_ok=True)
+    with open(report, "w") as f:
         f.write("\n".join(lines) + "\n")
     if not quiet:
         print("\n".join(lines))
     return out
 
 
+FIELDS = (("VGPRs", "VGPRs"), ("AGPRs", "AGPRs"), ("TotalSGPRs", "SGPRs"), ("VGPRs Spill", "VGPR spill"),
+          ("ScratchSize [bytes/lane]", "scratch B/lane"), ("LDS Size [bytes/block]", "LDS B/block"),
+          ("Occupancy [waves/SIMD]", "waves/SIMD"))
+
+
+def _demangle(names):
+    tool = shutil.which("llvm-cxxfilt") or "/opt/rocm/llvm/bin/llvm-cxxfilt"
+    if not os.path.exists(tool):
+        tool = shutil.which("c++filt")
+    if not tool:
+        return names
+    res = subprocess.run([tool], input="\n".join(names), capture_output=True, text=True)
+    out = res.stdout.splitlines()
+    return out if len(out) == len(names) else names
+
+
+def resource_table(report: str = REPORT) -> str:
+    """One markdown row per kernel from the compiler's resource-usage remarks."""
+    kernels, cur = [], None
+    pat = re.compile(r"remark:\s+(.*?):\s+(\S+)\s+\[-Rpass")
+    for ln in open(report):
+        m = pat.search(ln)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = {"name": val}
+            kernels.append(cur)
+        elif cur is not None:
+            cur[key] = val
+    names = _demangle([k["name"] for k in kernels])
+    head = "| kernel | " + " | ".join(h for _, h in FIELDS) + " |"
+    rows = [head, "|" + "---|" * (len(FIELDS) + 1)]
+    for k, nm in sorted(zip(kernels, names), key=lambda kn: kn[1]):
+        nm = nm.replace("attn::", "").replace("attn_bwd::", "").replace("(attn::AttnParams)", "")
+        nm = re.sub(r"\(attn_bwd::BwdParams\)", "", nm)
+        rows.append(f"| `{nm}` | " + " | ".join(k.get(f, "") for f, _ in FIELDS) + " |")
+    return "\n".join(rows) + "\n"
+
+
 if __name__ == "__main__":
-    print(build(quiet=False))
+    path = build(quiet="--table" in sys.argv)
+    if "--table" in sys.argv:
+        print(resource_table())
+    else:
+        print(path)

@@ -40,12 +40,10 @@ struct Workspace {
     size_t bytes;
 };
 std::vector<Workspace> g_ws;
-std::vector<void*> g_retired;   // outgrown buffers, freed at unload (a queued launch may still use them)
 
 struct Cleanup {
     ~Cleanup() {
         for (auto& w : g_ws) if (w.ptr) (void)hipFree(w.ptr);
-        for (void* p : g_retired) (void)hipFree(p);
     }
 } g_cleanup;
 
@@ -66,31 +64,37 @@ int probe_device(int* dev_out, DeviceInfo* info) {
     return d.gfx950 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
-// Workspace of at least `bytes` for (device, stream).  Never allocates while
-// the stream is being captured into a graph.
+// Workspace of at least `bytes` for (device, stream).  Buffers come from the
+// stream-ordered allocator on that stream: an outgrown buffer is released
+// with hipFreeAsync on the same stream, so the release waits for the launches
+// already queued there (the only users of a per-stream buffer) without the
+// host waiting for anything.  Grows to at least twice the old size.  Never
+// allocates while the stream is being captured into a graph.
 int get_workspace(int dev, void* stream, size_t bytes, void** out) {
     std::lock_guard<std::mutex> lk(g_mu);
-    for (auto& w : g_ws) {
-        if (w.device == dev && w.stream == stream) {
-            if (w.bytes >= bytes) { *out = w.ptr; return ATTN_OK; }
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
-                return ATTN_ERR_WORKSPACE;
-            void* p = nullptr;
-            if (hipMalloc(&p, bytes) != hipSuccess) return ATTN_ERR_WORKSPACE;
-            g_retired.push_back(w.ptr);
-            w.ptr = p;
-            w.bytes = bytes;
-            *out = p;
-            return ATTN_OK;
-        }
+    Workspace* w = nullptr;
+    for (auto& e : g_ws)
+        if (e.device == dev && e.stream == stream) w = &e;
+    if (w && w->bytes >= bytes) {
+        *out = w->ptr;
+        return ATTN_OK;
     }
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
         return ATTN_ERR_WORKSPACE;
+    const size_t want = w ? std::max(bytes, 2 * w->bytes) : bytes;
     void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) return ATTN_ERR_WORKSPACE;
-    g_ws.push_back(Workspace{dev, stream, p, bytes});
+    if (hipMallocAsync(&p, want, (hipStream_t)stream) != hipSuccess) return ATTN_ERR_WORKSPACE;
+    if (w) {
+        if (hipFreeAsync(w->ptr, (hipStream_t)stream) != hipSuccess) {
+            (void)hipFreeAsync(p, (hipStream_t)stream);
+            return ATTN_ERR_WORKSPACE;
+        }
+        w->ptr = p;
+        w->bytes = want;
+    } else {
+        g_ws.push_back(Workspace{dev, stream, p, want});
+    }
     *out = p;
     return ATTN_OK;
 }

@@ -124,8 +124,10 @@ __device__ __forceinline__ void dma16(const i32x4 rs, uint8_t* dst, int voff, in
     const int so = __builtin_amdgcn_readfirstlane(soff);
     // m0 is written in the same statement as the load (as in the forward
     // kernel): nothing can be scheduled between them, and no other code of
-    // these kernels uses m0.
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    // these kernels uses m0.  The s_nop is the one wait state an LDS-bound
+    // buffer load needs after a scalar write of m0 (the hazard recognizer
+    // does not see into inline assembly).
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                      :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }
 // 4 bytes per lane from rs at voff + soff to LDS dst + 4 * lane
@@ -133,7 +135,7 @@ __device__ __forceinline__ void dma4(const i32x4 rs, uint8_t* dst, int voff, int
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
     const i32x4 rsu = uniform4(rs);
     const int so = __builtin_amdgcn_readfirstlane(soff);
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                      :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }
 template <int HD, int NWK>
@@ -585,7 +587,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
                 const bool in = 16 * mb + r < valid && (!CAUSAL || 16 * mb + r >= lo);
                 const float pw = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], p.c, -l2[r])) : 0.f;
                 pv[mb][r] = pw;
-                dsv[mb][r] = pw * (dp[mb][r] - dl[r]);
+                // by select, like the weight: 0 * (dP - delta) would be NaN
+                // where a pair outside the mask meets a non-finite dP or delta
+                dsv[mb][r] = in ? pw * (dp[mb][r] - dl[r]) : 0.f;
             }
         }
 #pragma unroll

@@ -291,8 +291,12 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         // load, so nothing is scheduled between the two; no other code of the
         // kernel uses m0, which makes the clobber safe.  Handing the address
         // in as an {m0} operand lets the compiler move the write away from
-        // the load, and that form gave wrong results here.
-        __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+        // the load, and that form gave wrong results here.  An LDS-bound
+        // buffer load reads m0 one wait state after a scalar write of it at
+        // the earliest (the compiler puts the same s_nop after its own m0
+        // write for the builtin form of this load); inline assembly is opaque
+        // to the hazard recognizer, so the statement carries the nop itself.
+        __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                          :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
     };
     // round r of the K (or V) tile that starts at key k0

@@ -227,14 +227,19 @@ def gather_rows(o_bits: np.ndarray, layout: str, B: int, H: int, Sq: int, rows) 
     return o_bits.reshape(B, H, Sq, -1)[b, h, i]
 
 
-def sample_rows(B: int, H: int, Sq: int, n_per_head: int, seed: int, tile: int = 128) -> np.ndarray:
-    """Seeded row sample: per head the first and last rows, the first row of
-    the last (ragged) tile, and n_per_head random rows."""
+def sample_rows(B: int, H: int, Sq: int, n_per_head: int, seed: int, tile: int = 256) -> np.ndarray:
+    """Seeded row sample: per head the first and last rows, the last row of
+    the first query tile, every row of the last query tile when it is ragged
+    (Sq not a multiple of `tile`; otherwise its first row), and n_per_head
+    random rows.  With tile = 256, the query tile of the 8-wave kernel, the
+    ragged tail also holds the whole last tile of the 128-row kernel."""
     rng = np.random.default_rng(seed)
     out = []
+    last0 = (Sq - 1) // tile * tile
+    tail = set(range(last0, Sq)) if Sq % tile else {last0}
     for bh in range(B * H):
         base = bh * Sq
-        fixed = {0, Sq - 1, (Sq - 1) // tile * tile, min(Sq - 1, tile - 1)}
+        fixed = {0, Sq - 1, min(Sq - 1, tile - 1)} | tail
         rnd = rng.integers(0, Sq, size=n_per_head)
         out.extend(base + np.array(sorted(fixed | set(int(x) for x in rnd))))
     return np.array(out, dtype=np.int64)

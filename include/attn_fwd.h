@@ -87,8 +87,13 @@ enum {
  *   stream       hipStream_t to launch on (NULL = default stream)
  *
  * Ownership: the caller owns q, k, v, o and keeps them alive until the
- * stream's work completes.  The library keeps a per-device workspace for the
- * split-KV partial results; it grows on demand and lives until unload.
+ * stream's work completes.  The library keeps a workspace per (device,
+ * stream) for the split-KV partial results.  It comes from the stream-ordered
+ * allocator on that stream and grows on demand (at least doubling; the
+ * outgrown buffer is released in stream order, after the launches already
+ * queued on the stream); it is never allocated while the stream is being
+ * captured into a graph (ATTN_ERR_WORKSPACE instead, so capture needs one
+ * eager call of the same shape first), and lives until unload.
  *
  * Returns ATTN_OK or an ATTN_ERR_* code.  The call never synchronizes:
  * device faults surface at the caller's next synchronization.  NaN and Inf
@@ -142,6 +147,13 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
  *            the queries are the last Sq positions of the key sequence
  *            (for Sq == Skv the usual lower-triangular mask).  A query row
  *            that sees no key (only when Sq > Skv) is written as zeros.
+ *            Non-finite values under the mask: a 256-row query tile runs
+ *            every key below its last row's diagonal through the P.V
+ *            product with zero weights for the keys a row does not see, so
+ *            a NaN or Inf in V[j, d] makes column d NaN (0 * Inf) in the
+ *            rows of such a tile that do not see key j.  Rows that see j,
+ *            rows of tiles whose key range ends before j, and every finite
+ *            input follow the definition.
  *   lse      NULL, or fp32 [B, Hq, Sq] (this order in both layouts), device
  *            memory, 4-byte aligned, not overlapping q/k/v/o: receives each
  *            row's natural-log log-sum-exp of its scaled scores,
@@ -213,7 +225,7 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
  *
  * The accuracy of the gradients follows that of lse and o.  Errors as for
  * attn_fwd_bf16 (pointers 16-byte aligned, lse 4-byte aligned); the library's
- * per-device workspace holds delta.  Asynchronous on `stream`.
+ * workspace for (device, stream) holds delta.  Asynchronous on `stream`.
  */
 int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, void* dq, void* dk, void* dv, int layout, int64_t B, int64_t H,

@@ -6,14 +6,31 @@ identical".  Read literally (ULP of each exact output value) it cannot be
 met by any kernel that feeds bf16 probabilities into the p.V product:
 outputs that cancel to near zero have a tiny ULP while the bf16 rounding of
 the weights perturbs them by about 2^-9 of the terms being summed.  The
-reading used here takes the ULP at the larger of |o| and twice the RMS size
-sigma of those terms:
+reading used here takes the ULP at the larger of |o| and a multiple f of the
+RMS size sigma of those terms:
 
-    D = |g - round(o)| / ulp_bf16(max(|o|, 2 sigma))
+    D = |g - round(o)| / ulp_bf16(max(|o|, f sigma))
 
-with ulp_bf16(x) = 2^(max(floor(log2 x), -126) - 7).  Where |o| >= 2 sigma
-(almost every element) this is the literal ULP distance.  The literal
-distance in bf16 steps is reported as well.
+with ulp_bf16(x) = 2^(max(floor(log2 x), -126) - 7).  This floor is not a
+rare correction.  An attention output is a weighted mean of many values of
+both signs, so |o| is typically of the order of sigma.  Measured with the
+oracle on the workloads' input recipes (N(0,1)-type Q, K, V; 128 to 4096
+keys), the definition gate's floor (f = 2) governs 95-97% of the elements.
+It widens the median element's ULP unit 2-4 times over the literal one
+(16 times at the 90th percentile).  On those elements the gate reads as an
+absolute bound of 1-2 ULP of 2 sigma, not as a relative one.  Where
+|o| >= 2 sigma (3-5% of elements) D is the literal ULP distance.  The
+tests pin these shares (tests/test_gate.py).
+
+So every forward parity test also applies a second, tighter gate.  It
+compares against the oracle's method companion: the same operation with
+the weights rounded to bf16 the way the kernel rounds them, normalised by
+the sum of those rounded weights.  Its floor is f = 1 times that
+companion's sigma, and it governs about two thirds of the elements.  What
+separates the kernel from the companion is fp32 accumulation order and rare
+weights whose fp32 exponential rounds to the other bf16 neighbour, so that
+gate also holds it to D <= 2 everywhere and D <= 1 for >= 99.9%.  The
+literal distance in bf16 steps is reported as well.
 """
 from __future__ import annotations
 

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from bf16_attention_forward_amd import workloads as wl
-from tests.helpers import check, run_hip, run_hip_gqa, say
+from tests.helpers import assert_gates, check, run_hip, run_hip_gqa, say
 
 pytestmark = pytest.mark.gpu
 
@@ -15,9 +15,7 @@ MODES = ("rtne", "rtna", "rtz")
 
 
 def assert_gate(st):
-    assert st["nonfinite_match"], st
-    assert st["max_D"] <= 2.0, st
-    assert st["frac_D_gt1"] <= 1e-3, st
+    assert_gates(st)
 
 
 # every row checked; shapes span several query and key tiles with ragged
@@ -129,4 +127,50 @@ def test_lse_matches_oracle(case):
     assert np.all(err <= 2.0 ** -8 + 2.0 ** -20 * np.abs(ref[fin]))
     # the output is unchanged by asking for the statistic
     st, _ = check(wl.bits(o.cpu()), q, k, v, layout, "rtne", label=f"lse {case}", causal=causal)
+    assert_gate(st)
+
+
+def test_causal_nonfinite_values_documented_pattern():
+    """Under the causal mask a query tile of 256 rows runs every key below its
+    last row's diagonal through the P.V product, with the weights of keys a
+    row does not see set to 0.  A non-finite V[j, d] therefore reaches, as
+    0 * Inf = NaN, column d of the rows of such a tile that do not see key j
+    (the documented limitation; finite inputs are unaffected).  Pinned
+    exactly: rows that see j follow the definition's closed form, rows of a
+    tile that holds a row seeing j but that do not see it themselves are NaN
+    in column d, rows of tiles whose key range ends before j are untouched,
+    and everything finite passes the gates."""
+    import torch
+    layout, B, H, S = "bhsd", 1, 2, 600
+    q, k, v = wl.random_qkv(layout, B, H, S, S, 811)
+    sites = [(0, 300, 5, float("inf")), (0, 100, 7, float("nan")), (1, 550, 9, float("-inf")),
+             (1, 20, 3, float("inf")), (1, 21, 3, float("-inf"))]
+    for h, j, d, val in sites:
+        v[0, h, j, d] = val
+    o = run_hip_gqa(q, k, v, layout, "rtne", causal=True).reshape(B, H, S, 128)
+    vals = (o.astype(np.uint32) << 16).view(np.float32)
+    off = 0                                    # Skv - Sq
+    want = np.zeros((H, S, 128), np.int8)     # 0 finite, 1 NaN, 2 +Inf, 3 -Inf
+    for h in range(H):
+        for d in range(128):
+            col = [(j, val) for (hh, j, dd, val) in sites if hh == h and dd == d]
+            if not col:
+                continue
+            for i in range(S):
+                seen = [val for (j, val) in col if j <= i + off]
+                tile_end = min(S, (i // 256) * 256 + 256 + off)      # the tile's key range end
+                reached = [val for (j, val) in col if j < tile_end and j > i + off]
+                if any(np.isnan(x) for x in seen) or (np.inf in seen and -np.inf in seen) or reached:
+                    want[h, i, d] = 1
+                elif np.inf in seen:
+                    want[h, i, d] = 2
+                elif -np.inf in seen:
+                    want[h, i, d] = 3
+    got = np.where(np.isnan(vals), 1, np.where(np.isposinf(vals), 2, np.where(np.isneginf(vals), 3, 0)))[0]
+    assert np.array_equal(got, want), f"pattern differs in {(got != want).sum()} places"
+    assert (want == 1).sum() > 0 and ((want == 1) & (got == 1)).sum() == (want == 1).sum()
+    # rows untouched by any non-finite value pass both gates
+    clean = np.where(~np.any(want != 0, axis=2).reshape(-1))[0]
+    st, _ = check(o.reshape(-1), q, k, v, layout, "rtne", rows=clean, label="causal nonfinite clean rows",
+                  causal=True)
     assert_gate(st)

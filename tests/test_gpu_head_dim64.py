@@ -36,10 +36,15 @@ def gate_all(o_bits, q, k, v, layout, mode, causal=False, scale=SCALE64, rows=No
         B, Sq, H, _ = q.shape
     else:
         B, H, Sq, _ = q.shape
-    res = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=scale, method=False,
-                           causal=causal, rows=rows)
+    res = oracle.attention(wl.bits(q), wl.bits(k), wl.bits(v), layout=layout, scale=scale, method=True,
+                           l_from_rounded=True, causal=causal, rows=rows)
     g = wl.gather_rows(o_bits, layout, B, H, Sq, np.arange(B * H * Sq) if rows is None else rows)
-    return gate.compare(g, res.o_exact, res.sigma, mode), res
+    st = gate.compare(g, res.o_exact, res.sigma, mode)
+    # the tighter gate against the method companion (bf16 weights, their own sum)
+    sm = gate.compare(g, res.o_method, res.sigma_method, mode, floor_factor=1.0)
+    st["method"] = sm
+    st["passed"] = bool(st["passed"] and sm["passed"])
+    return st, res
 
 
 CASES = [

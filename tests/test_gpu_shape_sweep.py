@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from bf16_attention_forward_amd import workloads as wl
-from tests.helpers import check, run_hip, run_hip_gqa, say
+from tests.helpers import assert_gates, check, run_hip, run_hip_gqa, say
 
 pytestmark = pytest.mark.gpu
 
@@ -69,9 +69,7 @@ def grouped_cases():
 
 
 def _gate(st):
-    assert st["nonfinite_match"], st
-    assert st["max_D"] <= 2.0, st
-    assert st["frac_D_gt1"] <= 1e-3, st
+    assert_gates(st)
 
 
 @pytest.mark.parametrize("case", plain_cases(), ids=lambda c: f"s{c[0]}_{c[1]}_B{c[2]}H{c[3]}_{c[4]}x{c[5]}")

@@ -279,6 +279,45 @@ def test_method_weights_rounded_in_mode(mode):
     assert (differs_from_rtne > 0) == (mode == "rtz")
 
 
+@pytest.mark.parametrize("mode", ["rtne", "rtna", "rtz"])
+@pytest.mark.parametrize("l_from_rounded", [True, False])
+def test_method_companion_and_its_sigma_rebuilt(mode, l_from_rounded):
+    """o_method and sigma_method for general V, rebuilt from exact (rational)
+    scores, the grid-search rounding of the weights pt_j = mode(2^(x_j - M))
+    and plain matrix products: o_method = (pt V) / L and sigma_method =
+    sqrt(pt^2 V^2) / L, L = sum pt (l_from_rounded) or sum 2^(x_j - M).
+    sigma_method sets the ULP floor of the method gate."""
+    from tests.test_oracle_round import reference_round
+    sq, skv = 3, 70
+    q, k, v = wl.random_qkv("bhsd", 1, 1, sq, skv, 67, k_factor=2.0)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), method=True, l_from_rounded=l_from_rounded, p_round=mode)
+    Q, K, V = (f64(wl.bits(t))[0, 0] for t in (q, k, v))
+    log2e = 1.4426950408889634
+    for i in range(sq):
+        s = np.array([float(sum(Fraction(Q[i, d]) * Fraction(K[j, d]) for d in range(128)) * Fraction(float(SCALE)))
+                      for j in range(skv)])
+        x = s * log2e
+        pm = np.exp2(x - np.ceil(x.max()))
+        pt = oracle.bf16_bits_to_f64(reference_round(pm, mode))
+        L = pt.sum() if l_from_rounded else pm.sum()
+        assert np.allclose(res.o_method[i], (pt @ V) / L, rtol=1e-12, atol=1e-14 * np.abs(V).max())
+        assert np.allclose(res.sigma_method[i], np.sqrt((pt * pt) @ (V * V)) / L, rtol=1e-12, atol=0)
+    # the companion's sigma stays within the weights' rounding of the exact one
+    assert np.all(np.abs(res.sigma_method - res.sigma) <= 2.0 ** -7 * res.sigma + 1e-300) or not l_from_rounded
+
+
+def test_sigma_bounds_the_output():
+    """|o_d| <= sqrt(Skv) sigma_d (Cauchy-Schwarz on the sum of Skv terms) and
+    sigma_d <= max_j |v_jd| (the weights sum to one), for o and o_method."""
+    skv = 50
+    q, k, v = wl.random_qkv("bshd", 1, 2, 20, skv, 69, k_factor=2.0)
+    res = run(wl.bits(q), wl.bits(k), wl.bits(v), layout="bshd", method=True, l_from_rounded=True)
+    vmax = np.abs(f64(wl.bits(v))).max(axis=1).reshape(2, 128)           # [h, d]
+    for o, sg in ((res.o_exact, res.sigma), (res.o_method, res.sigma_method)):
+        assert np.all(np.abs(o) <= np.sqrt(skv) * sg * (1 + 1e-12))
+        assert np.all(sg.reshape(2, 20, 128) <= vmax[:, None, :] * (1 + 1e-12))
+
+
 # ------------------------------------------- grouped-query heads, causal mask
 # The pages list causal masking and grouped-query attention as limitations of
 # the kernel they describe (MoonMath article, limitations paragraph); the

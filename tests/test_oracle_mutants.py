@@ -45,6 +45,12 @@ MUTANTS = {
     "empty_rows_not_zero": ("if (n_keys <= 0) {", "if (n_keys < 0) {"),
     "lse_drops_max": ("if (lse) lse[t] = m + log(l);", "if (lse) lse[t] = log(l);"),
     "weights_mode_ignored": ("pt = round_trip_bf16(pm, p_round);", "pt = round_trip_bf16(pm, OR_RTNE);"),
+    # the sigmas that set the gates' ULP floors
+    "bwd_sdk_unsquared": ("gk[d] += tk; sk[d] += tk * tk;", "gk[d] += tk; sk[d] += tk;"),
+    "bwd_sdq_no_scale": ("sg[d] += t * t;", "sg[d] += (t / sc) * (t / sc);"),
+    "bwd_sdv_from_ds": ("gv[d] += tv; sv[d] += tv * tv;", "gv[d] += tv; sv[d] += tk * tk;"),
+    "sigma_method_from_unrounded": ("sqm[d] += (pt * vv) * (pt * vv);", "sqm[d] += (pm * vv) * (pm * vv);"),
+    "sigma_method_unnormalised": ("if (sm) sm[d] = sqrt(sqm[d]) / L;", "if (sm) sm[d] = sqrt(sqm[d]);"),
 }
 
 
@@ -85,6 +91,10 @@ def pins():
     out.append(("bwd_single_key", BW.test_single_key_closed_form))
     out.append(("bwd_causal", lambda: BW.test_matches_torch_autograd_float64("bshd", True, 37, 37)))
     out.append(("bwd_gqa", lambda: BW.test_grouped_heads_match_torch_autograd_float64("bshd", 2, True)))
+    out.append(("bwd_sigmas", lambda: BW.test_gradient_sigmas_match_float64_products("bshd", 6, 2, True, 29, 35)))
+    out.append(("bwd_brute", lambda: BW.test_gradients_and_sigmas_bruteforce_decimal(2, 3)))
+    out.append(("sigma_method", lambda: A.test_method_companion_and_its_sigma_rebuilt("rtne", True)))
+    out.append(("sigma_bounds", A.test_sigma_bounds_the_output))
     return out
 
 
