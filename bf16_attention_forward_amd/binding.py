@@ -23,8 +23,9 @@ ARGUMENT_ERRORS = {-1, -2, -3, -4, -5, -6, -7, -11}
 HEAD_DIM = 128
 
 # names of every entry point the header declares
-EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_bwd_bf16",
-           "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_fwd_bf16_hd_noalloc",
+           "attn_bwd_bf16", "attn_status_string", "attn_version")
+NOALLOC_SCRATCH_BYTES = 34078720   # ATTN_NOALLOC_SCRATCH_BYTES
 HEAD_DIMS = (128, 64)
 
 _lib = None
@@ -58,6 +59,8 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16_hd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_bf16_hd.restype = ctypes.c_int
+    lib.attn_fwd_bf16_hd_noalloc.argtypes = lib.attn_fwd_bf16_hd.argtypes
+    lib.attn_fwd_bf16_hd_noalloc.restype = ctypes.c_int
     lib.attn_bwd_bf16.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_bwd_bf16.restype = ctypes.c_int
@@ -224,6 +227,35 @@ def attn_fwd_bf16_hd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
                                   lse.data_ptr() if lse is not None else None,
                                   ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, hd, sc, 1 if causal else 0,
                                   _mode(round_mode, round_weights), st.cuda_stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return (o, lse) if lse is not None else o
+
+
+def attn_fwd_bf16_hd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, *,
+                             layout: str = "bshd", scale: float | None = None, causal: bool = False,
+                             round_mode: str = "rtne", stream: torch.cuda.Stream | None = None,
+                             lse: torch.Tensor | None = None, round_weights: bool = False):
+    """attn_fwd_bf16_hd through the allocation-free entry point
+    (attn_fwd_bf16_hd_noalloc): the split partials go to the library's fixed
+    device array, so nothing is allocated -- o (and lse, if wanted) must be
+    passed in.  Calls on one GPU that overlap in time race on that array."""
+    lib = load_library()
+    if o is None:
+        raise ValueError("o must be given: the allocation-free call allocates nothing")
+    o = _check_tensors(q, k, v, o)
+    B, Hq, Hkv, Sq, Skv = _dims(q, k, layout, grouped=True, head_dims=HEAD_DIMS)
+    hd = int(q.shape[-1])
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq)
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 device tensor shaped [B, Hq, Sq]")
+    sc = float(1.0 / math.sqrt(hd)) if scale is None else float(scale)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_bf16_hd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                          lse.data_ptr() if lse is not None else None,
+                                          ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, hd, sc, 1 if causal else 0,
+                                          _mode(round_mode, round_weights), st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (o, lse) if lse is not None else o

@@ -18,6 +18,8 @@
 #include "attn_fwd_internal.h"
 #include "../../include/attn_fwd.h"
 
+static_assert(NOALLOC_SCRATCH_BYTES == ATTN_NOALLOC_SCRATCH_BYTES, "the header states the fixed array's size");
+
 namespace {
 
 constexpr int kKeyTile = 64;
@@ -106,7 +108,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-extern "C" int attn_version(void) { return 10500; }
+extern "C" int attn_version(void) { return 10600; }
 
 extern "C" const char* attn_status_string(int status) {
     switch (status) {
@@ -122,6 +124,8 @@ extern "C" const char* attn_status_string(int status) {
         case ATTN_ERR_WORKSPACE: return "split workspace unavailable (allocation failed or stream is being captured)";
         case ATTN_ERR_LAUNCH: return "kernel launch failed";
         case ATTN_ERR_OPTION: return "kv_splits, block_order, waves or causal out of range";
+        case ATTN_ERR_SCRATCH: return "the call's split partials need more than the fixed scratch array of the "
+                                      "allocation-free entry point holds (ATTN_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -132,7 +136,7 @@ namespace {
 int run_attention(const void* q, const void* k, const void* v, void* o, float* lse,
                   int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t head_dim,
                   float scale, int causal, int round_mode, void* stream,
-                  int kv_splits, int block_order, int waves) {
+                  int kv_splits, int block_order, int waves, bool noalloc = false) {
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
     const int out_mode = round_mode & ~ATTN_ROUND_WEIGHTS;
@@ -247,8 +251,14 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
         const size_t n_part = (size_t)(p.n_items - n_full) * splits;
         const size_t need = n_part * bm * (kHeadDim + 2) * sizeof(float);
         void* ws = nullptr;
-        const int wrc = get_workspace(dev, stream, need, &ws);
-        if (wrc != ATTN_OK) return wrc;
+        if (noalloc) {
+            // the fixed device array; nothing is allocated
+            if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+            if (attn::scratch_address(dev, &ws) != 0) return ATTN_ERR_DEVICE;
+        } else {
+            const int wrc = get_workspace(dev, stream, need, &ws);
+            if (wrc != ATTN_OK) return wrc;
+        }
         p.ws_o = (float*)ws;
         p.ws_ml = (float*)((char*)ws + n_part * bm * kHeadDim * sizeof(float));
     }
@@ -353,4 +363,11 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
                              int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                              float scale, int round_mode, void* stream) {
     return attn_fwd_bf16_ex(q, k, v, o, layout, B, H, Sq, Skv, scale, round_mode, stream, 0, 0, 0);
+}
+
+extern "C" int attn_fwd_bf16_hd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                        int64_t head_dim, float scale, int causal, int round_mode, void* stream) {
+    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, head_dim, scale, causal, round_mode,
+                         stream, 0, 0, 0, true);
 }

@@ -27,7 +27,17 @@
 // budget of a wave is then 256 VGPRs)
 #define KERNEL_WG_PER_CU (8 / KERNEL_NW)
 
+// Size of the fixed device array behind the allocation-free entry point: the
+// largest split workspace the planner asks for on a 256-CU device (256
+// partial query tiles of 256 rows, fp32 O of 128 dims plus (M, l)).
+#define NOALLOC_SCRATCH_BYTES (256 * 256 * (128 + 2) * 4)
+#define NOALLOC_MAX_DEVICES 64
+
 namespace attn {
+
+// Address of the fixed scratch array on device `dev` (which must be the
+// current device); looked up once per device.  0 on success.
+int scratch_address(int dev, void** out);
 
 enum { ROUND_RTNE = 0, ROUND_RTNA = 1, ROUND_RTZ = 2 };
 enum { ORDER_NAIVE = 1, ORDER_XCD = 2 };

@@ -66,6 +66,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn_fwd_internal.h"
@@ -828,6 +829,28 @@ int launch(const AttnParams& p, hipStream_t stream) {
             hipLaunchKernelGGL((attn_fwd_combine<KERNEL_BM, 128>), cgrid, dim3(256), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return -1;
     }
+    return 0;
+}
+
+// ------------------------------------------------- fixed scratch array
+// Split partials of the allocation-free entry point.  Each GPU holds its own
+// copy at its own address, until the process ends.  In host code the name
+// `scratch` is a host-side stand-in, not a device address: host code only ever
+// uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+int scratch_address(int dev, void** out) {
+    static std::mutex mu;
+    static void* addr[NOALLOC_MAX_DEVICES] = {};
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return -1;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        // once per device, with that device current (the caller's)
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return -1;
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
     return 0;
 }
 

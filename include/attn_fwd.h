@@ -67,7 +67,9 @@ enum {
     ATTN_ERR_DEVICE = -8,      /* current device is not gfx950, or no device        */
     ATTN_ERR_WORKSPACE = -9,   /* split workspace could not be obtained             */
     ATTN_ERR_LAUNCH = -10,     /* the HIP runtime rejected a launch                 */
-    ATTN_ERR_OPTION = -11      /* kv_splits, block_order or causal out of range     */
+    ATTN_ERR_OPTION = -11,     /* kv_splits, block_order or causal out of range     */
+    ATTN_ERR_SCRATCH = -12     /* attn_fwd_bf16_hd_noalloc: the split partials need
+                                  more than ATTN_NOALLOC_SCRATCH_BYTES              */
 };
 
 /*
@@ -192,6 +194,35 @@ int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, floa
 int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                      int64_t head_dim, float scale, int causal, int round_mode, void* stream);
+
+/* Size in bytes of the fixed device array behind attn_fwd_bf16_hd_noalloc:
+ * 256 partial query tiles x 256 rows x (128 + 2) fp32 values, the largest
+ * split workspace the planner asks for on a 256-CU gfx950 device. */
+#define ATTN_NOALLOC_SCRATCH_BYTES 34078720
+
+/*
+ * attn_fwd_bf16_hd_noalloc -- attn_fwd_bf16_hd for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It makes the same plan and gives the
+ * same result bit for bit, but the split partials go to a fixed device
+ * array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends, instead of a workspace it allocates.  The
+ * call itself allocates nothing (no hipMalloc, no library allocation).
+ *
+ * Arguments, ownership of q, k, v, o and lse, asynchrony and errors are
+ * those of attn_fwd_bf16_hd.  A call whose split partials would need more
+ * than the array holds returns ATTN_ERR_SCRATCH and launches nothing; on a
+ * 256-CU gfx950 the planner never asks for more.
+ *
+ * The array is shared by every call on the same GPU and keeps the last
+ * call's partials (each call writes every partial it reads, so nothing has
+ * to start at zero).  Calls on one GPU that overlap in time, e.g. on two
+ * streams without ordering between them, race on it: order them on one
+ * stream or through events.
+ */
+int attn_fwd_bf16_hd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                             int64_t head_dim, float scale, int causal, int round_mode, void* stream);
 
 /*
  * attn_bwd_bf16 -- backward pass of attn_fwd_bf16 / attn_fwd_bf16_gqa /

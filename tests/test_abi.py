@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert pkg.attn_version() >= 10000
-    for code in range(-11, 1):
+    for code in range(-12, 1):
         assert pkg.attn_status_string(code)
     assert pkg.attn_status_string(-999) == "unknown status"
 
