@@ -59,7 +59,7 @@ def test_exact_means_round_bit_for_bit(skv, kw):
     v64 = one_binade_values(rng, (B, H, skv, 128), exps=[-20, -3, 0, 1, 7, 30])
     v = bf16_tensor(v64)
     q = torch.zeros((B, H, Sq, 128), dtype=torch.bfloat16)
-    k = bf16_tensor(rng.standard_normal((B, H, skv, 128)))
+    k = torch.from_numpy(rng.standard_normal((B, H, skv, 128)).astype(np.float32)).to(torch.bfloat16)
     mean = v64.mean(axis=2)                                    # exact: power-of-two count, bounded bits
     q_d, k_d, v_d = to_dev(q), to_dev(k), to_dev(v)
     ties = 0
