@@ -30,15 +30,14 @@
 // dK/dV query loop starts at it; the weights of masked pairs are zero by
 // select, and work-groups that see no pair write zeros and exit.
 // Every LDS tile is read both straight (ds_read_b128) and transposed, so all
-// tiles keep one layout: 16-byte chunk c of row r at c ^ swz(r).  With
-// 256-byte rows (head dimension 128)
-// swz(r) = 2 (r & 7) + ((r >> 3) & 1) takes 16 distinct values over any 16
-// rows in a row (straight reads: 16 rows at one chunk column, no two lanes in
-// one bank) and keeps chunk pairs together with 8 distinct pair positions
-// over any 8 rows in a row (transposed reads: 8 rows x one 32-byte pair per
-// half-wave).  With 128-byte rows (head dimension 64) two rows share a
-// 256-byte bank pass and swz(r) = 2 ((r >> 1) & 3) + ((r >> 3) & 1) over 8
-// chunk positions does the same.  P and dS enter the
+// tiles keep one layout: 16-byte chunk c of row r at c ^ swz(r), with
+// swz(r) = 2 (r & 7) for 256-byte rows (head dimension 128) and
+// 2 ((r >> 1) & 3) for 128-byte rows (64), the forward's V layouts.  It
+// keeps chunk pairs together with 8 distinct pair positions over any 8 rows
+// (transposed reads: 8 rows x one 32-byte pair per half-wave), and the
+// straight reads of 16 rows at one chunk column showed no bank conflicts
+// either (SQ_LDS_BANK_CONFLICT; a swizzle that also flipped the low chunk
+// bit on rows 8..15 conflicted on them).  P and dS enter the
 // MFMAs as bf16 (round to nearest-even); all sums are fp32; the gradients are
 // rounded to bf16 (nearest-even).
 #include <hip/hip_runtime.h>
@@ -95,7 +94,7 @@ __device__ __forceinline__ void lds_barrier() {
 // for its own transfers in lds_barrier.
 // chunk swizzle of row r (only r mod 16 matters)
 template <int HD> __device__ __forceinline__ int swz(int r) {
-    return HD == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    return HD == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1);
 }
 struct TileSrc {
     i32x4 rs;

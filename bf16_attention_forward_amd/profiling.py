@@ -81,7 +81,7 @@ N_XCD, N_CU, N_SIMD = 8, 256, 1024
 
 
 def derived_lines(cs: dict) -> list:
-    """Utilisation figures from the per-dispatch means of attn_fwd_main."""
+    """Utilisation figures from the per-dispatch means of one kernel."""
     out = []
     gui = cs.get("GRBM_GUI_ACTIVE")
     if not gui:
@@ -224,7 +224,7 @@ def main():
             lines.append(f"[{k}] per-dispatch means")
             for cn, val in sorted(cs.items()):
                 lines.append(f"  {cn:40s} {val:20.3f}")
-            if k == "attn_fwd_main":
+            if "GRBM_GUI_ACTIVE" in cs and not k.startswith("copy:"):
                 lines += ["", "Derived:"] + derived_lines(cs)
             lines.append("")
     text = "\n".join(lines) + "\n"

@@ -16,9 +16,15 @@ tiles (each element tagged with its (row, dim)) and checks:
     layout needs (16x16x32 bf16: A lane (g, j) holds row j, k = 8 g .. 8 g +
     7; the score fragment's keys 16 kb + 4 g + r fix the k order of the
     weights, which the transposed V reads must match);
-  * banks: the lanes served together read distinct 4-byte banks (16 lanes
-    of a ds_read_b128, 256 bytes per pass; 32 lanes of a ds_read_b64_tr_b16,
-    256 bytes per pass).
+  * banks, transposed reads: the 32 lanes of a half-wave, which one
+    ds_read_b64_tr_b16 serves together, read 32 distinct 8-byte slots of a
+    256-byte bank pass (this rule matched every swizzle measured with the
+    SQ_LDS_BANK_CONFLICT counter);
+  * banks, straight reads: no simple lane-grouping rule matched the
+    ds_read_b128 conflicts measured for five candidate swizzles (a layout
+    whose 16 rows take 16 distinct 16-byte slots conflicted, one with 8
+    did not), so the straight-read layouts are pinned to the swizzles
+    measured conflict-free, and the kernels' own counters confirm it.
 
 The formulas restate the kernels' (attn_fwd_kernel.hip, attn_bwd_kernel.hip);
 the invariants they must satisfy come from the operand layouts.
@@ -26,6 +32,17 @@ the invariants they must satisfy come from the operand layouts.
 import pytest
 
 TILE_ROWS = 64
+
+
+# Chunk swizzles whose straight ds_read_b128 fragment reads (lane (g, j):
+# row j, 16-byte chunk 4 kk + g) showed zero SQ_LDS_BANK_CONFLICT cycles on
+# gfx950, by head dimension, over rows 0..15.  Measured and found
+# conflicting: 2 (r & 7) + ((r >> 3) & 1) at 128 (2.7 conflict cycles per
+# read) and 2 ((r >> 1) & 3) + ((r >> 3) & 1) at 64 (2.0).
+STRAIGHT_CONFLICT_FREE = {
+    128: [[r & 15 for r in range(16)], [(r & 7) << 1 for r in range(16)]],
+    64: [[(r >> 1) & 7 for r in range(16)], [((r >> 1) & 3) << 1 for r in range(16)]],
+}
 
 
 # ---------------------------------------------------------------- forward
@@ -78,21 +95,19 @@ def test_forward_dma_places_every_chunk_once(hd, which):
 @pytest.mark.parametrize("hd", [128, 64])
 def test_forward_k_fragments(hd):
     """S^T = K Q^T, K as operand A: lane (g, j) of step (ks, kb) must read
-    key 16 kb + j, dims 32 ks + 8 g .. + 7; the 16 lanes of a group hit 16
-    distinct 16-byte bank slots of a 256-byte pass."""
+    key 16 kb + j, dims 32 ks + 8 g .. + 7, through a swizzle measured
+    conflict-free for these reads."""
     image = fwd_dma_image(hd, swz_k)
     row_bytes = hd * 2
+    assert [swz_k(hd, r) for r in range(16)] in STRAIGHT_CONFLICT_FREE[hd]
     for ks in range(hd // 32):
         for kb in range(4):
             for g in range(4):
-                slots = set()
                 for j in range(16):
                     k_addr = j * row_bytes + (((4 * ks + g) ^ swz_k(hd, j)) << 4)
                     addr = k_addr + kb * 16 * row_bytes
                     got = [element(image, addr + 2 * e) for e in range(8)]
                     assert got == [(16 * kb + j, 32 * ks + 8 * g + e) for e in range(8)]
-                    slots.add((addr % 256) // 16)
-                assert len(slots) == 16
 
 
 def tr16(addrs, image):
@@ -148,12 +163,12 @@ def test_forward_weight_key_order():
 
 # ---------------------------------------------------------------- backward
 def swz_b(hd, row):
-    """256-byte rows: 2 (r & 7) + ((r >> 3) & 1) over 16 chunk positions;
-    128-byte rows (two rows per 256-byte bank pass): 2 ((r >> 1) & 3) +
-    ((r >> 3) & 1) over 8."""
+    """256-byte rows: 2 (r & 7); 128-byte rows (two rows per 256-byte bank
+    pass): 2 ((r >> 1) & 3) -- the forward's V layouts, which serve both
+    read kinds without conflicts."""
     if hd == 128:
-        return ((row & 7) << 1) | ((row >> 3) & 1)
-    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1)
+        return (row & 7) << 1
+    return ((row >> 1) & 3) << 1
 
 
 def bwd_dma_image(hd, nwk):
@@ -191,19 +206,18 @@ def test_backward_straight_and_transposed_reads(hd):
     """One layout serves both reads of every backward tile: read_rows (lane
     (g, j) of step (kk, rb): row 16 rb + j, dims 32 kk + 8 g .. + 7) and
     read_cols (lane (g, j), element 4 hf + e: row 32 ks + 16 hf + 4 g + e,
-    dim 16 db + j), both bank-spread as in the forward."""
+    dim 16 db + j); the straight reads through a swizzle measured
+    conflict-free, the transposed ones on 32 distinct slots per half-wave."""
     image = bwd_dma_image(hd, 8)
     rb_ = 2 * hd
+    assert [swz_b(hd, r) for r in range(16)] in STRAIGHT_CONFLICT_FREE[hd]
     for kk in range(hd // 32):
         for rb in range(4):
             for g in range(4):
-                slots = set()
                 for j in range(16):
                     addr = j * rb_ + (((4 * kk + g) ^ swz_b(hd, j)) << 4) + rb * 16 * rb_
                     assert [element(image, addr + 2 * e) for e in range(8)] == \
                         [(16 * rb + j, 32 * kk + 8 * g + e) for e in range(8)]
-                    slots.add((addr % 256) // 16)
-                assert len(slots) == 16
     for ks in range(2):
         for db in range(hd // 16):
             for hf in range(2):
