@@ -28,6 +28,12 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 ALU ops are kept off: hipcc must not emit v_pk_{add,mul,fma}_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # built-in MFMAs keep their results in VGPRs: the backward's dK/dV kernel
+    # binds its accumulators to AGPRs itself (inline assembly), and its S and
+    # dP feed VALU work; without the option the compiler moves every MFMA of
+    # that kernel to the AGPR form and copies S and dP back (the other kernels
+    # compile to the same code either way)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Rpass-analysis=kernel-resource-usage",
 ]
 

@@ -16,9 +16,9 @@
 //    V read as operand A, the forward's K-as-A layout, so each lane holds one
 //    query), then dS^T elementwise, then dQ^T += K^T dS^T with K^T read by
 //    ds_read_b64_tr_b16 in the order of dS^T's keys (the forward's V^T read).
-//  * attn_bwd_dkdv: the mirror image -- a work-group owns 128 keys (8 waves x
-//    16 or 4 waves x 32, K and V fragments in registers as operand B) and streams
-//    64-query Q and dO tiles.  Per tile: S = Q K^T and dP = dO V^T (Q and dO as
+//  * attn_bwd_dkdv: the mirror image -- a work-group owns 128 keys (4 waves x
+//    32, K and V fragments in registers as operand B) and streams 64-query Q
+//    and dO tiles.  Per tile: S = Q K^T and dP = dO V^T (Q and dO as
 //    operand A: each lane holds one key), then P and dS, then dV^T += dO^T P
 //    and dK^T += Q^T dS with dO^T and Q^T transposed out of LDS.
 // With grouped-query heads (query head h reads key/value head h / group) the
@@ -57,6 +57,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
+typedef LDS_AS uint8_t lds_u8;   // a byte of LDS (pointers to it are 32-bit LDS addresses)
 
 constexpr int TILE_ROWS = 64;
 constexpr int NW = 8;
@@ -117,8 +118,8 @@ __device__ __forceinline__ i32x4 uniform4(const i32x4 rs) {
     return i32x4{__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
                  __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
 }
-__device__ __forceinline__ void dma16(const i32x4 rs, uint8_t* dst, int voff, int soff) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
+__device__ __forceinline__ void dma16(const i32x4 rs, lds_u8* dst, int voff, int soff) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
     const i32x4 rsu = uniform4(rs);
     const int so = __builtin_amdgcn_readfirstlane(soff);
     // m0 is written in the same statement as the load (as in the forward
@@ -130,15 +131,15 @@ __device__ __forceinline__ void dma16(const i32x4 rs, uint8_t* dst, int voff, in
                      :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }
 // 4 bytes per lane from rs at voff + soff to LDS dst + 4 * lane
-__device__ __forceinline__ void dma4(const i32x4 rs, uint8_t* dst, int voff, int soff) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
+__device__ __forceinline__ void dma4(const i32x4 rs, lds_u8* dst, int voff, int soff) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
     const i32x4 rsu = uniform4(rs);
     const int so = __builtin_amdgcn_readfirstlane(soff);
     __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                      :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
 }
 template <int HD, int NWK>
-__device__ __forceinline__ void issue_tile_n(const TileSrc& s, int r0, uint8_t* dst, int wave, int g, int j) {
+__device__ __forceinline__ void issue_tile_n(const TileSrc& s, int r0, lds_u8* dst, int wave, int g, int j) {
     static_assert(NWK == 4 || NWK == 8, "4 or 8 waves");
     constexpr int CPR = HD / 8, RPW = 64 / CPR;      // 16-byte chunks per row, rows per wave and round
     const int lane = 16 * g + j;
@@ -151,17 +152,17 @@ __device__ __forceinline__ void issue_tile_n(const TileSrc& s, int r0, uint8_t* 
 
 // Straight fragment (operand A): lane (g, j) gets row 16*rb + j, dims
 // 32*ks + 8*g .. +7.
-template <int HD> __device__ __forceinline__ bf16x8 read_rows(const uint8_t* tile, int addr0, int rb) {
-    return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(tile + addr0 + rb * 16 * (2 * HD));
+template <int HD> __device__ __forceinline__ bf16x8 read_rows(const lds_u8* tile, int addr0, int rb) {
+    return *(const LDS_AS bf16x8*)(tile + addr0 + rb * 16 * (2 * HD));
 }
 // Transposed fragment (operand A of a product over the tile's rows): lane
 // (g, j) gets, as elements 4*hf + e, rows 32*ks + 16*hf + 4*g + e of dim
 // 16*db + j (the order of the B operand built from a C fragment).
-template <int HD> __device__ __forceinline__ bf16x8 read_cols(const uint8_t* tile, int addr0, int ks) {
+template <int HD> __device__ __forceinline__ bf16x8 read_cols(const lds_u8* tile, int addr0, int ks) {
     bf16x4 half[2];
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-        const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(tile + addr0 + (32 * ks + 16 * hf) * (2 * HD));
+        const LDS_AS s16x4* src = (const LDS_AS s16x4*)(tile + addr0 + (32 * ks + 16 * hf) * (2 * HD));
         half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
     }
     return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -253,8 +254,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     const int hk = h / p.group;                          // key/value head of query head h
     const TileSrc ks = tile_src<HD>(p.k + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
     const TileSrc vs = tile_src<HD>(p.v + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head, p.kv_row, p.Skv);
-    auto kslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES); };
-    auto vslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
+    auto kslot = [&](int sl) { return (lds_u8*)tiles + sl * (2 * TILE_BYTES); };
+    auto vslot = [&](int sl) { return (lds_u8*)tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
     // tile 0: all 8 waves; later tiles: waves 0-3
     issue_tile_n<HD, NW>(ks, 0, kslot(0), wave, g, j);
     issue_tile_n<HD, NW>(vs, 0, vslot(0), wave, g, j);
@@ -316,8 +317,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     bf16x8 dsf[2][2];          // dS^T of the previous tile as operand B (k = keys)
     // S^T = K Q^T and dP^T = V dO^T of the tiles in slot sl
     auto products_a = [&](int sl) __attribute__((always_inline)) {
-        const uint8_t* kt = kslot(sl);
-        const uint8_t* vt = vslot(sl);
+        const lds_u8* kt = kslot(sl);
+        const lds_u8* vt = vslot(sl);
 #pragma unroll
         for (int kk = 0; kk < NKK; kk++)
 #pragma unroll
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     };
     // dQ^T += K^T dS^T with the K tile in slot sl
     auto products_b = [&](int sl) __attribute__((always_inline)) {
-        const uint8_t* kt = kslot(sl);
+        const lds_u8* kt = kslot(sl);
 #pragma unroll
         for (int kk = 0; kk < 2; kk++)
 #pragma unroll
@@ -422,32 +423,87 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 }
 
 // ----------------------------------------------------------------- dK, dV
-// 8 waves, each owning 16 keys (K and V fragments in registers as operand B).
-// Software pipeline over the 64-query tiles: iteration t runs the products of
-// two tiles back to back -- S_t = Q_t K^T and dP_t = dO_t V^T (tile t read
-// straight), then dV^T += dO_{t-1}^T P_{t-1} and dK^T += Q_{t-1}^T dS_{t-1}
-// (tile t-1 read transposed) -- and then the elementwise step of tile t
-// (P_t, dS_t), so LDS holds three tiles (t-1, t, and t+1 in flight).  The two
-// waves of a SIMD are out of phase: waves 0-3 take the iteration's barrier
-// after the elementwise step, waves 4-7 before it, so one wave's exp and
-// packing run while the other's products keep the matrix core busy.  Waves
-// 0-3 issue all transfers of tile t+1 at the start of iteration t and wait
-// for them before their barrier.
-// (4 waves x 32 keys halves the LDS bytes per product but needs more than 256
-// registers per wave, one wave per SIMD; measured slower.)
+// 4 waves, one per SIMD, each owning 32 keys in two 16-key blocks kb (K and
+// V fragments in registers as operand B): every Q or dO fragment read from
+// LDS feeds two MFMAs.  With 16 keys per wave a 16-cycle MFMA needs a fresh
+// 1 KiB fragment, the whole LDS read rate of a CU when all four SIMDs do
+// it; 32 keys halve that.  One wave per SIMD has the 512-register budget
+// that the 32 keys' dK and dV accumulators (128 registers, kept in AGPRs)
+// need beside the rest.  With no second wave on the SIMD, the overlap of
+// the elementwise step with the products is built inside the wave: a step
+// (one 64-query tile) runs as a fixed sequence of chunks, each a few MFMAs
+// with the LDS reads of a later chunk and a share of the VALU work placed
+// between them:
+//     A0 | A1 + E0 + DMA | A2 + E1 + DMA | A3 + E2 | B0 + E3 |
+//     barrier | B1 + the next tile's A0 reads
+// (A mb: S and dP of query block mb; E mb: P and dS of block mb, packed to
+// bf16 as they are made; B ks: dV and dK over queries 32 ks .. 32 ks + 31;
+// DMA: the transfers of step t+2).  Four LDS slots: the Q, dO, L and delta
+// tiles of step t+2 go into the slot of step t-2, whose last reads ended
+// before the barrier of step t-1; the barrier of step t follows each wave's
+// wait for its own transfers of step t+1 (in-order completion: only those
+// of step t+2 may remain).  On gfx950 a lone wave's MFMAs overlap little of
+// its own other instructions (per-phase timestamps: a phase takes about the
+// MFMA time plus the issue time of the rest), so this layout is bound by
+// its instruction count more than by LDS; it runs 5-10% faster than eight
+// waves of 16 keys.
+constexpr int DKV_NW = 4;
+constexpr int DKV_NSLOT = 4;                   // a power of two
 constexpr int LS_BYTES = 2 * TILE_ROWS * 4;   // L and delta of a tile's 64 queries
 
+// dK and dV accumulate in the accumulation registers (AGPRs): the product
+// is written as inline assembly with its C/D operand bound to an AGPR, while
+// every other product (built-in, VGPR form) leaves S and dP in VGPRs for the
+// elementwise step.  The compiler's hazard checks do not see into inline
+// assembly, so the schedule itself keeps the distances these products need:
+// their P and dS operands are made a whole phase (or a barrier) before
+// their use, the fragments come from LDS reads (waited for by lgkmcnt), no
+// accumulator is used by two products less than 16 products apart, and the
+// AGPRs are read only after the settling wait at the end; a CPU test checks
+// the distances on the built code.
+__device__ __forceinline__ void mfma_acc(f32x4& acc, bf16x8 a, bf16x8 b) {
+    __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// LDS barrier that leaves this wave's last N transfers in flight
+template <int N> __device__ __forceinline__ void lds_barrier_vm() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Chunk boundary: the chunk's reads first, then its NM MFMAs each followed
+// by up to NV VALU instructions; nothing moves across the boundary.
+template <int NM, int NV> __device__ __forceinline__ void chunk_end(int nr) {
+    // LDS reads (nr is a constant once the chunk loops are unrolled)
+    switch (nr) {
+        case 2: __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); break;
+        case 4: __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); break;
+        case 6: __builtin_amdgcn_sched_group_barrier(0x100, 6, 0); break;
+        default: break;
+    }
+#pragma unroll
+    for (int i = 0; i < NM; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
+__global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(HD == 128 || HD == 64, "head dimension 128 or 64");
     constexpr int ROW_BYTES = 2 * HD, TILE_BYTES = TILE_ROWS * ROW_BYTES;
     constexpr int NKK = HD / 32, NDB = HD / 16;   // k-steps over the dims, 16-dim blocks
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[NSLOT * 2 * TILE_BYTES];   // per slot: Q, dO
-    __shared__ __attribute__((aligned(16))) uint8_t lsd[NSLOT * LS_BYTES];           // per slot: L, delta
+    constexpr int RPW = 64 / (HD / 8);            // rows per DMA instruction
+    constexpr int NDMA = 2 * TILE_ROWS / (RPW * DKV_NW);   // Q and dO transfers per wave and step
+    constexpr int PD = HD == 128 ? 3 : 2;         // B-fragment prefetch distance, in chunks (at most 15 LDS reads in flight)
+    static_assert(NKK <= NDB && PD <= NKK, "prefetch placement");
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[DKV_NSLOT * 2 * TILE_BYTES];   // per slot: Q, dO
+    __shared__ __attribute__((aligned(16))) uint8_t lsd[DKV_NSLOT * LS_BYTES];           // per slot: L, delta
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool late = wave >= 4;
     const int g = lane >> 4, j = lane & 15;
     // under the mask a key block's query range shrinks with its index:
     // blocks take the longest (first key blocks of every head) first
@@ -455,19 +511,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
     const int kt_ = CAUSAL ? (int)(blockIdx.x / BH) : (int)(blockIdx.x % p.n_kblocks);
     const int bh = CAUSAL ? (int)(blockIdx.x % BH) : (int)(blockIdx.x / p.n_kblocks);   // (b, key/value head)
     const int hk = bh % p.Hkv, b = bh / p.Hkv;
-    const int kbase = kt_ * (NW * 16) + wave * 16;       // this wave's first key
+    const int kbase = kt_ * 128 + wave * 32;             // key block kb of this wave: keys kbase + 16 kb + j
     // query tiles [t0, t0 + T): under the mask the first query that sees the
     // work-group's first key is k0 - (Skv - Sq)
-    const int q_first = CAUSAL ? max(0, kt_ * (NW * 16) - p.causal_off) : 0;
+    const int q_first = CAUSAL ? max(0, kt_ * 128 - p.causal_off) : 0;
     const int t0 = q_first / TILE_ROWS;
     const int T = (p.Sq + TILE_ROWS - 1) / TILE_ROWS - t0;
+    const int64_t koff = (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head;
     if (T <= 0) {
         // no query sees these keys: dK = dV = 0 (with the bottom-right mask
         // the last query sees every key, so this is a guard only; uniform
         // across the work-group, before any transfer or barrier)
-        const int krow = kbase + j;
-        if (krow < p.Skv) {
-            const int64_t ko = (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head + (int64_t)krow * p.kv_row + 4 * g;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            const int krow = kbase + 16 * kb + j;
+            if (krow >= p.Skv) continue;
+            const int64_t ko = koff + (int64_t)krow * p.kv_row + 4 * g;
 #pragma unroll
             for (int db = 0; db < NDB; db++) {
                 *(uint2*)(p.dk + ko + 16 * db) = uint2{0u, 0u};
@@ -482,51 +541,73 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
     // head hk * group + u / T, whose first row is q0 + (u % T) * 64
     const int TT = T * p.group;
 
-    auto qslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES); };
-    auto gslot = [&](int sl) { return tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
-    auto lslot = [&](int sl) { return lsd + sl * LS_BYTES; };
-    // the Q, dO, L and delta tiles of step u into slot u % NSLOT, moved by NWK
-    // waves; each query head's tensors get their own buffer ranges, so rows
-    // past Sq read as zero (the range check), never the next head's rows
-    auto issue_step = [&](int u, auto nwk) __attribute__((always_inline)) {
-        constexpr int NWK = decltype(nwk)::value;
-        const int hq = hk * p.group + u / T;
-        const int r0 = q0 + (u % T) * TILE_ROWS;
-        const int sl = u % NSLOT;
+    auto qslot = [&](int sl) { return (lds_u8*)tiles + sl * (2 * TILE_BYTES); };
+    auto gslot = [&](int sl) { return (lds_u8*)tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
+    auto lslot = [&](int sl) { return (lds_u8*)lsd + sl * LS_BYTES; };
+    // the L and delta, Q, and dO tiles of tile r0 of query head hq into slot
+    // sl, in three parts; each query head's tensors get their own buffer
+    // ranges, so rows past Sq read as zero (the range check), never the next
+    // head's rows.  Every wave issues the L and delta transfers (the same
+    // bytes to the same LDS words), so all waves issue NDMA + 2 transfers
+    // per step, L and delta first.
+    auto issue_ld = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
+        const int64_t rbh = ((int64_t)b * p.H + hq) * p.Sq;
+        dma4(buffer_rsrc(p.lse + rbh, (uint32_t)p.Sq * 4u), lslot(sl), lane * 4, r0 * 4);
+        dma4(buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u), lslot(sl) + TILE_ROWS * 4, lane * 4, r0 * 4);
+    };
+    auto issue_q = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
         const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)hq * p.q_head;
-        issue_tile_n<HD, NWK>(tile_src<HD>(p.q + qoff, p.q_row, p.Sq), r0, qslot(sl), wave, g, j);
-        issue_tile_n<HD, NWK>(tile_src<HD>(p.dO + qoff, p.q_row, p.Sq), r0, gslot(sl), wave, g, j);
-        if (wave == 0) {
-            const int64_t rbh = ((int64_t)b * p.H + hq) * p.Sq;
-            dma4(buffer_rsrc(p.lse + rbh, (uint32_t)p.Sq * 4u), lslot(sl), lane * 4, r0 * 4);
-            dma4(buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u), lslot(sl) + TILE_ROWS * 4, lane * 4, r0 * 4);
-        }
+        issue_tile_n<HD, DKV_NW>(tile_src<HD>(p.q + qoff, p.q_row, p.Sq), r0, qslot(sl), wave, g, j);
     };
-    // step 0: all 8 waves; later steps: waves 0-3
-    issue_step(0, std::integral_constant<int, NW>{});
-    auto issue_next = [&](int t) __attribute__((always_inline)) {
-        if (!late && t < TT) issue_step(t, std::integral_constant<int, 4>{});
+    auto issue_g = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
+        const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)hq * p.q_head;
+        issue_tile_n<HD, DKV_NW>(tile_src<HD>(p.dO + qoff, p.q_row, p.Sq), r0, gslot(sl), wave, g, j);
     };
+    // step u runs tile u % T of the group's query head u / T
+    auto step_hq = [&](int u) { return hk * p.group + u / T; };
+    auto step_r0 = [&](int u) { return q0 + (u % T) * TILE_ROWS; };
 
-    // K and V of keys kbase + j (clamped; rows past Skv are never stored)
-    const int64_t koff = (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head;
-    bf16x8 kf[NKK], vf[NKK];
-    {
-        const int row = min(kbase + j, p.Skv - 1);
+    // K and V of keys kbase + 16 kb + j (clamped; rows past Skv are never stored)
+    bf16x8 kf[2][NKK], vf[2][NKK];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+        const int row = min(kbase + 16 * kb + j, p.Skv - 1);
         const uint16_t* ksrc = p.k + koff + (int64_t)row * p.kv_row + 8 * g;
         const uint16_t* vsrc = p.v + koff + (int64_t)row * p.kv_row + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < NKK; kk++) {
-            kf[kk] = *(const bf16x8*)(ksrc + 32 * kk);
-            vf[kk] = *(const bf16x8*)(vsrc + 32 * kk);
+            kf[kb][kk] = *(const bf16x8*)(ksrc + 32 * kk);
+            vf[kb][kk] = *(const bf16x8*)(vsrc + 32 * kk);
         }
     }
-    // wait for these loads here, once (as in the dQ kernel)
+    // steps 0 and 1 (past the last step, the transfers of step t + 2 repeat
+    // the last step's tiles into the free slot, so every step issues the
+    // same transfers)
+    issue_ld(0, step_hq(0), step_r0(0));
+    issue_q(0, step_hq(0), step_r0(0));
+    issue_g(0, step_hq(0), step_r0(0));
+    {
+        const int u = min(1, TT - 1);
+        issue_ld(1, step_hq(u), step_r0(u));
+        issue_q(1, step_hq(u), step_r0(u));
+        issue_g(1, step_hq(u), step_r0(u));
+    }
+    int uh = min(2, TT - 1) / T, utq = min(2, TT - 1) % T;   // query head and tile of step min(t + 2, TT - 1)
+    // wait for the K and V loads here, once (not inside the loop, where the
+    // wait would also hold for the transfers in flight)
 #pragma unroll
-    for (int kk = 0; kk < NKK; kk++) __asm__ volatile("" : "+v"(kf[kk]), "+v"(vf[kk]));
-    f32x4 dk[NDB], dv[NDB];
+    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-    for (int db = 0; db < NDB; db++) { dk[db] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[db] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+        for (int kk = 0; kk < NKK; kk++) __asm__ volatile("" : "+v"(kf[kb][kk]), "+v"(vf[kb][kk]));
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int kk = 0; kk < NKK; kk++) __asm__ volatile("" : "+a"(kf[kb][kk]), "+a"(vf[kb][kk]));
+    f32x4 dk[2][NDB], dv[2][NDB];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int db = 0; db < NDB; db++) { dk[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f}; }
     int a_row[NKK], a_col[NDB];
 #pragma unroll
     for (int kk = 0; kk < NKK; kk++) a_row[kk] = j * ROW_BYTES + (((4 * kk + g) ^ swz<HD>(j)) << 4);
@@ -535,120 +616,203 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dkdv(const BwdParams p) {
         const int row = 4 * g + (j >> 2);
         a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz<HD>(row)) << 4) + ((j & 1) << 3);
     }
-    lds_barrier();
+    lds_barrier_vm<NDMA + 2>();
 
-    f32x4 s[4], dp[4];        // S and dP of tile t: lane (g, j) holds queries 16*mb + 4*g + r of key j
-    bf16x8 pf[2], dsf[2];     // P and dS of the previous tile as operand B (k = queries)
-    // S = Q K^T, dP = dO V^T of the tile in slot sl
-    auto products_a = [&](int sl) __attribute__((always_inline)) {
-        const uint8_t* qt = qslot(sl);
-        const uint8_t* gt = gslot(sl);
+    // the straight fragments of query block 0 of the first tile
+    bf16x8 fa0[NKK][2];
 #pragma unroll
-        for (int kk = 0; kk < NKK; kk++)
-#pragma unroll
-            for (int mb = 0; mb < 4; mb++) {
-                const bf16x8 qa = read_rows<HD>(qt, a_row[kk], mb);
-                const bf16x8 ga = read_rows<HD>(gt, a_row[kk], mb);
-                s[mb] = mfma(qa, kf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mb]);
-                dp[mb] = mfma(ga, vf[kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[mb]);
-            }
-    };
-    // dV^T += dO^T P, dK^T += Q^T dS with the tile in slot sl
-    auto products_b = [&](int sl) __attribute__((always_inline)) {
-        const uint8_t* qt = qslot(sl);
-        const uint8_t* gt = gslot(sl);
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-            for (int db = 0; db < NDB; db++) {
-                const bf16x8 gtf = read_cols<HD>(gt, a_col[db], kk);
-                const bf16x8 qtf = read_cols<HD>(qt, a_col[db], kk);
-                dv[db] = mfma(gtf, pf[kk], dv[db]);
-                dk[db] = mfma(qtf, dsf[kk], dk[db]);
-            }
-    };
-    // P = 2^(c s - L log2 e), dS = P o (dP - delta) of step u; queries past Sq
-    // (and, under the mask, queries before the key's diagonal) -> 0 by select
-    auto elementwise = [&](int u, int sl) __attribute__((always_inline)) {
-        const uint8_t* lt = lslot(sl);
-        const int r0 = q0 + (u % T) * TILE_ROWS;        // first query row of the step's tile
-        const int valid = p.Sq - r0 - 4 * g;
-        // query 16*mb + 4*g + r of the tile sees key kbase + j iff
-        // 16*mb + r >= kbase + j - (Skv - Sq) - (first query of the tile) - 4*g
-        const int lo = CAUSAL ? kbase + j - p.causal_off - r0 - 4 * g : -TILE_ROWS;
-        float pv[4][4], dsv[4][4];
-#pragma unroll
-        for (int mb = 0; mb < 4; mb++) {
-            const f32x4 l2 = *(const LDS_AS f32x4*)(LDS_AS const uint8_t*)(lt + (16 * mb + 4 * g) * 4) * LOG2E;
-            const f32x4 dl = *(const LDS_AS f32x4*)(LDS_AS const uint8_t*)(lt + TILE_ROWS * 4 + (16 * mb + 4 * g) * 4);
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const bool in = 16 * mb + r < valid && (!CAUSAL || 16 * mb + r >= lo);
-                const float pw = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], p.c, -l2[r])) : 0.f;
-                pv[mb][r] = pw;
-                // by select, like the weight: 0 * (dP - delta) would be NaN
-                // where a pair outside the mask meets a non-finite dP or delta
-                dsv[mb][r] = in ? pw * (dp[mb][r] - dl[r]) : 0.f;
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            pf[kk] = pack_b(pv[2 * kk], pv[2 * kk + 1]);
-            dsf[kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
-        }
-    };
-    // barrier of waves 0-3: after their elementwise step (the operands keep the
-    // compiler from sinking that step below the barrier)
-    auto early_barrier = [&]() __attribute__((always_inline)) {
-        __asm__ volatile("" :: "v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
-        lds_barrier();
-    };
-    auto pin_addr = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NKK; i++) __asm__ volatile("" : "+v"(a_row[i]));
-#pragma unroll
-        for (int i = 0; i < NDB; i++) __asm__ volatile("" : "+v"(a_col[i]));
-    };
-
-    // iteration 0: products of tile 0 only
-    issue_next(1);
-    pin_addr();
-    __builtin_amdgcn_s_setprio(1);
-    products_a(0);
-    __builtin_amdgcn_s_setprio(0);
-    if (late) lds_barrier();
-    elementwise(0, 0);
-    if (!late) early_barrier();
-    int cur = 1 % NSLOT, prev = 0;
-    for (int t = 1; t < TT; t++) {
-        issue_next(t + 1);
-        pin_addr();
-        __builtin_amdgcn_s_setprio(1);
-        products_a(cur);
-        products_b(prev);
-        __builtin_amdgcn_s_setprio(0);
-        if (late) lds_barrier();
-        elementwise(t, cur);
-        if (!late) early_barrier();
-        prev = cur;
-        cur = cur == NSLOT - 1 ? 0 : cur + 1;
+    for (int kk = 0; kk < NKK; kk++) {
+        fa0[kk][0] = read_rows<HD>(qslot(0), a_row[kk], 0);
+        fa0[kk][1] = read_rows<HD>(gslot(0), a_row[kk], 0);
     }
-    // the last tile's dV, dK products (no LDS writes follow: no barrier)
-    pin_addr();
-    products_b(prev);
 
-    // dK = scale (dK^T)^T, dV = (dV^T)^T: lane (g, j) holds dims 16*db + 4*g + r of key j
-    const int krow = kbase + j;
-    if (krow < p.Skv) {
+    // one step on the tile in slot sl (first query row r0), issuing the
+    // transfers of tile dr0 of head dhq into slot dsl among its products;
+    // MASK: apply the causal mask by select.  Rows past Sq need no select: their Q, dO, L
+    // and delta read as zero, so their weight is 2^0 = 1 and their dS is
+    // 1 * (0 - 0) = 0, and both meet zero rows of dO and Q in the dV and dK
+    // products.
+    auto run_step = [&](auto mask_c, int sl, int r0, int nsl, int dsl, int dhq, int dr0) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_c)::value;
+        const lds_u8* qt = qslot(sl);
+        const lds_u8* gt = gslot(sl);
+        const lds_u8* lt = lslot(sl);
+        f32x4 s[2][4], dp[2][4];   // S and dP: lane (g, j) holds queries 16*mb + 4*g + r of key 16*kb + j
+        bf16x2 pp[2][4][2], dsp[2][4][2];   // P and dS of queries 16*mb + 4*g + 2*h, +1, packed as they are made
+        bf16x8 fa[4][NKK][2];         // straight Q, dO fragments of query block mb
+        bf16x8 fb[2][NDB][2];         // transposed dO, Q fragments of half ks
+        f32x4 l2[4], dl[4];
+#pragma unroll
+        for (int kk = 0; kk < NKK; kk++) { fa[0][kk][0] = fa0[kk][0]; fa[0][kk][1] = fa0[kk][1]; }
+        auto read_a = [&](int mb, int kk) __attribute__((always_inline)) {
+            fa[mb][kk][0] = read_rows<HD>(qt, a_row[kk], mb);
+            fa[mb][kk][1] = read_rows<HD>(gt, a_row[kk], mb);
+        };
+        auto read_b = [&](int ks, int db) __attribute__((always_inline)) {
+            fb[ks][db][0] = read_cols<HD>(gt, a_col[db], ks);
+            fb[ks][db][1] = read_cols<HD>(qt, a_col[db], ks);
+        };
+        auto read_ld = [&](int mb) __attribute__((always_inline)) {
+            l2[mb] = *(const LDS_AS f32x4*)(lt + (16 * mb + 4 * g) * 4);
+            dl[mb] = *(const LDS_AS f32x4*)(lt + TILE_ROWS * 4 + (16 * mb + 4 * g) * 4);
+        };
+        auto mfma_a = [&](int mb, int kk) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                s[kb][mb] = mfma(fa[mb][kk][0], kf[kb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][mb]);
+                dp[kb][mb] = mfma(fa[mb][kk][1], vf[kb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[kb][mb]);
+            }
+        };
+        // P and dS as operand B of half ks: k = queries 32 ks + 16 hf + 4 g + e
+        // (elements 4 hf + e), the blocks mb = 2 ks, 2 ks + 1 in order
+        auto operand = [&](bf16x2 (&v)[2][4][2], int kb, int ks) __attribute__((always_inline)) {
+            const bf16x4 lo = __builtin_shufflevector(v[kb][2 * ks][0], v[kb][2 * ks][1], 0, 1, 2, 3);
+            const bf16x4 hi = __builtin_shufflevector(v[kb][2 * ks + 1][0], v[kb][2 * ks + 1][1], 0, 1, 2, 3);
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        auto mfma_b = [&](int ks, int db) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                mfma_acc(dv[kb][db], fb[ks][db][0], operand(pp, kb, ks));
+                mfma_acc(dk[kb][db], fb[ks][db][1], operand(dsp, kb, ks));
+            }
+        };
+        // P = 2^(c s - L log2 e), dS = P o (dP - delta) of the element pair
+        // e (kb = e / 2, rows r = 2 (e % 2), +1) of query block mb, rounded to
+        // bf16 (nearest-even) in pairs; under MASK, queries before the key's
+        // diagonal -> 0 by select
+        auto elem2 = [&](int mb, int e) __attribute__((always_inline)) {
+            const int kb = e >> 1, h = e & 1;
+            float pw[2], ds[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int r = 2 * h + i;
+                const float x = __builtin_fmaf(s[kb][mb][r], p.c, -l2[mb][r] * LOG2E);
+                if (MASK) {
+                    // query 16*mb + 4*g + r of the tile sees key kbase + 16*kb + j iff
+                    // 16*mb + r >= kbase + 16*kb + j - (Skv - Sq) - r0 - 4*g
+                    const int lo = kbase + 16 * kb + j - p.causal_off - r0 - 4 * g;
+                    const bool in = 16 * mb + r >= lo;
+                    pw[i] = in ? __builtin_amdgcn_exp2f(x) : 0.f;
+                    // by select, like the weight: 0 * (dP - delta) would be NaN
+                    // where a pair outside the mask meets a non-finite dP or delta
+                    ds[i] = in ? pw[i] * (dp[kb][mb][r] - dl[mb][r]) : 0.f;
+                } else {
+                    pw[i] = __builtin_amdgcn_exp2f(x);
+                    ds[i] = pw[i] * (dp[kb][mb][r] - dl[mb][r]);
+                }
+            }
+            pp[kb][mb][h] = __builtin_convertvector((f32x2{pw[0], pw[1]}), bf16x2);
+            dsp[kb][mb][h] = __builtin_convertvector((f32x2{ds[0], ds[1]}), bf16x2);
+            // made here, in this chunk: otherwise the compiler may move the
+            // conversions next to their use by an inline-assembly product,
+            // closer than the 2 wait states a VALU write needs before an
+            // MFMA reads the register
+            __asm__ volatile("" : "+v"(pp[kb][mb][h]), "+v"(dsp[kb][mb][h]));
+        };
+
+        // A0, with the reads of A1 and of L, delta
+        read_ld(0);
+#pragma unroll
+        for (int kk = 0; kk < NKK; kk++) {
+            read_a(1, kk);
+            mfma_a(0, kk);
+            chunk_end<4, 0>(2 + (kk == 0 ? 2 : 0));
+        }
+        // A mb + E mb-1, with the reads of A mb+1 (or, in A3, of B0's first chunks)
+#pragma unroll
+        for (int mb = 1; mb < 4; mb++) {
+#pragma unroll
+            for (int kk = 0; kk < NKK; kk++) {
+                if (kk == 0) read_ld(mb);
+                if (kk == 0 && mb == 1) { issue_ld(dsl, dhq, dr0); issue_q(dsl, dhq, dr0); }
+                if (kk == 0 && mb == 2) issue_g(dsl, dhq, dr0);
+                int nr = kk == 0 ? 2 : 0;
+                if (mb < 3) { read_a(mb + 1, kk); nr += 2; }
+                else if (kk < PD) { read_b(0, kk); nr += 4; }
+                mfma_a(mb, kk);
+#pragma unroll
+                for (int e = 0; e < 4 / NKK; e++) elem2(mb - 1, (4 / NKK) * kk + e);
+                chunk_end<4, 6>(nr);
+            }
+        }
+        // B0 + E3, with the reads of B0 (the rest) and B1's first chunks
+#pragma unroll
+        for (int db = 0; db < NDB; db++) {
+            if (db + PD < NDB) read_b(0, db + PD);
+            else read_b(1, db + PD - NDB);
+            mfma_b(0, db);
+            // (in the later chunks: S and dP of block 3 come from the last
+            // products of A3, whose results a VALU read has to wait for)
+            if (db >= NDB - 4) elem2(3, db - (NDB - 4));
+            chunk_end<4, 4>(4);
+        }
+        // P and dS of blocks 2 and 3 are used only after the barrier: the
+        // register uses keep the compiler from sinking their computation
+        // below it
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int mb = 2; mb < 4; mb++)
+#pragma unroll
+                for (int h = 0; h < 2; h++) __asm__ volatile("" : "+v"(pp[kb][mb][h]), "+v"(dsp[kb][mb][h]));
+        // every wave has its transfers of the next step in LDS, and has
+        // issued its last reads of the slot that step t+1's transfers reuse
+        lds_barrier_vm<NDMA + 2>();
+        // B1, with the reads of B1 (the rest) and of the next tile's A0
+        const lds_u8* qn = qslot(nsl);
+        const lds_u8* gn = gslot(nsl);
+#pragma unroll
+        for (int db = 0; db < NDB; db++) {
+            if (db + PD < NDB) read_b(1, db + PD);
+            // the NKK fragment pairs of the next A0, in the last NKK chunks
+            if (db >= NDB - NKK) {
+                const int kk = db - (NDB - NKK);
+                fa0[kk][0] = read_rows<HD>(qn, a_row[kk], 0);
+                fa0[kk][1] = read_rows<HD>(gn, a_row[kk], 0);
+            }
+            mfma_b(1, db);
+            chunk_end<4, 0>((db + PD < NDB ? 4 : 0) + (db >= NDB - NKK ? 2 : 0));
+        }
+    };
+
+    int sl = 0, tq = 0;                                  // slot and tile index (within its head) of step t
+    for (int t = 0; t < TT; t++) {
+        const int r0 = q0 + tq * TILE_ROWS;             // first query row of the step's tile
+        const int nsl = sl == DKV_NSLOT - 1 ? 0 : sl + 1;
+        run_step(std::integral_constant<bool, CAUSAL>{}, sl, r0, nsl, (t + 2) & (DKV_NSLOT - 1),
+                 hk * p.group + uh, q0 + utq * TILE_ROWS);
+        if (t + 3 < TT) {
+            utq = utq == T - 1 ? 0 : utq + 1;
+            uh += utq == 0;
+        }
+        sl = nsl;
+        tq = tq == T - 1 ? 0 : tq + 1;
+    }
+    // the repeated transfers of the last two steps land before the wave ends
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // the last MFMA's results settle before the AGPRs are read (a read of an
+    // MFMA result needs up to 18 wait states; 24 here)
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int db = 0; db < NDB; db++) __asm__ volatile("" : "+a"(dk[kb][db]), "+a"(dv[kb][db]));
+    __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    // dK = scale (dK^T)^T, dV = (dV^T)^T: lane (g, j) holds dims 16*db + 4*g + r of key 16*kb + j
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+        const int krow = kbase + 16 * kb + j;
+        if (krow >= p.Skv) continue;
         uint16_t* dkd = p.dk + koff + (int64_t)krow * p.kv_row + 4 * g;
         uint16_t* dvd = p.dv + koff + (int64_t)krow * p.kv_row + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; db++) {
             uint2 a, c;
-            a.x = rtne_bits(dk[db][0] * p.scale) | (rtne_bits(dk[db][1] * p.scale) << 16);
-            a.y = rtne_bits(dk[db][2] * p.scale) | (rtne_bits(dk[db][3] * p.scale) << 16);
-            c.x = rtne_bits(dv[db][0]) | (rtne_bits(dv[db][1]) << 16);
-            c.y = rtne_bits(dv[db][2]) | (rtne_bits(dv[db][3]) << 16);
+            a.x = rtne_bits(dk[kb][db][0] * p.scale) | (rtne_bits(dk[kb][db][1] * p.scale) << 16);
+            a.y = rtne_bits(dk[kb][db][2] * p.scale) | (rtne_bits(dk[kb][db][3] * p.scale) << 16);
+            c.x = rtne_bits(dv[kb][db][0]) | (rtne_bits(dv[kb][db][1]) << 16);
+            c.y = rtne_bits(dv[kb][db][2]) | (rtne_bits(dv[kb][db][3]) << 16);
             *(uint2*)(dkd + 16 * db) = a;
             *(uint2*)(dvd + 16 * db) = c;
         }
@@ -664,8 +828,8 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL(attn_bwd_delta<H_>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return -1;
         const dim3 gk((unsigned)((int64_t)p.B * p.Hkv * p.n_kblocks)), gq((unsigned)((int64_t)p.B * p.H * p.n_qblocks));
-        if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv<H_, true>), gk, dim3(NW * 64), 0, stream, p);
-        else hipLaunchKernelGGL((attn_bwd_dkdv<H_, false>), gk, dim3(NW * 64), 0, stream, p);
+        if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv<H_, true>), gk, dim3(DKV_NW * 64), 0, stream, p);
+        else hipLaunchKernelGGL((attn_bwd_dkdv<H_, false>), gk, dim3(DKV_NW * 64), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return -1;
         if (p.causal) hipLaunchKernelGGL((attn_bwd_dq<H_, true>), gq, dim3(NW * 64), 0, stream, p);
         else hipLaunchKernelGGL((attn_bwd_dq<H_, false>), gq, dim3(NW * 64), 0, stream, p);
