@@ -171,6 +171,33 @@ def read_sclk_mhz():
 BWD_FLOP_FACTOR = 2.5
 
 
+def time_paged(steps, warmup):
+    """Median ms of attn_fwd_bf16_paged on the paged-cache workload (the copy
+    of the cached keys and values into the library's workspace included)."""
+    import torch
+    from bf16_attention_forward_amd import attn_fwd_bf16_paged
+    from bf16_attention_forward_amd import workloads as wl
+
+    c = wl.PAGED
+    pk = wl.make_paged_kv(c["B"], c["H"], c["kv_lens"], c["page_size"], seed=c["seed"])
+    q = wl.random_qkv("bshd", c["B"], c["H"], c["Sq"], 1, c["seed"])[0]
+    dev = torch.device("cuda:0")
+    qd, kc, vc = q.to(dev), pk.k_cache.to(dev), pk.v_cache.to(dev)
+    bt, kl = pk.block_table.to(dev), pk.kv_lens.to(dev)
+    od = torch.empty_like(qd)
+    run = lambda: attn_fwd_bf16_paged(qd, kc, vc, bt, kl, od, max_kv_len=pk.max_kv_len, layout="bshd")
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) for a, b in evs])
+
+
 def time_backward(w, steps, warmup):
     """Median ms of attn_bwd_bf16 on workload w (O and lse from the forward)."""
     import torch
@@ -241,6 +268,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--backward", action="store_true",
                     help="time only the backward pass of the workload (one JSON line of its own)")
+    ap.add_argument("--paged", action="store_true",
+                    help="time only the paged key/value cache workload (one JSON line of its own)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -270,6 +299,19 @@ def main():
                           "steps": args.steps, "warmup": args.warmup,
                           "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                           "config": {**w.describe(), "pass": "backward"}}), flush=True)
+        return
+    if args.paged:
+        c = wl.PAGED
+        em = time_paged(steps=args.steps, warmup=args.warmup)
+        tf = wl.paged_flops(c["H"], c["Sq"], c["kv_lens"]) / (em * 1e-3) / 1e12
+        print(json.dumps({"metric": "paged-cache attention fwd TFLOPS (sum over entries of 4*H*Sq*kv_len*d), "
+                                    "copy into the workspace included",
+                          "value": round(tf, 2), "unit": "TFLOP/s", "median_ms": round(em, 5),
+                          "steps": args.steps, "warmup": args.warmup,
+                          "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "config": {"workload": c["name"], "B": c["B"], "H": c["H"], "Sq": c["Sq"],
+                                     "kv_lens": list(c["kv_lens"]), "page_size": c["page_size"],
+                                     "head_dim": 128, "layout": "bshd", "round_mode": "rtne"}}), flush=True)
         return
     sclk_idle = read_sclk_mhz()
     order = {"planner": 0, "naive": 1, "xcd": 2}[args.block_order]
@@ -332,6 +374,14 @@ def main():
             tf = BWD_FLOP_FACTOR * ww.flops / (em * 1e-3) / 1e12
             extra[f"{ww.name}:backward"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),
                                             "frac_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+        # the paged key/value cache (per-entry lengths, 256-token pages)
+        c = wl.PAGED
+        em = time_paged(steps=20, warmup=5)
+        tf = wl.paged_flops(c["H"], c["Sq"], c["kv_lens"]) / (em * 1e-3) / 1e12
+        extra[f"{c['name']}:rtne"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),
+                                      "frac_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                      "note": "copy of the cached keys and values into the workspace included"}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
 

@@ -24,6 +24,7 @@ HEAD_DIM = 128
 
 # names of every entry point the header declares
 EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_fwd_bf16_hd_noalloc",
+           "attn_fwd_bf16_paged",
            "attn_bwd_bf16", "attn_status_string", "attn_version")
 NOALLOC_SCRATCH_BYTES = 34078720   # ATTN_NOALLOC_SCRATCH_BYTES
 HEAD_DIMS = (128, 64)
@@ -61,6 +62,9 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16_hd.restype = ctypes.c_int
     lib.attn_fwd_bf16_hd_noalloc.argtypes = lib.attn_fwd_bf16_hd.argtypes
     lib.attn_fwd_bf16_hd_noalloc.restype = ctypes.c_int
+    lib.attn_fwd_bf16_paged.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_int64] * 9 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_fwd_bf16_paged.restype = ctypes.c_int
     lib.attn_bwd_bf16.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_bwd_bf16.restype = ctypes.c_int
@@ -227,6 +231,60 @@ def attn_fwd_bf16_hd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
                                   lse.data_ptr() if lse is not None else None,
                                   ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, Skv, hd, sc, 1 if causal else 0,
                                   _mode(round_mode, round_weights), st.cuda_stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return (o, lse) if lse is not None else o
+
+
+def attn_fwd_bf16_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                        kv_lens: torch.Tensor, o: torch.Tensor | None = None, *, max_kv_len: int,
+                        layout: str = "bshd", scale: float | None = None, causal: bool = False,
+                        round_mode: str = "rtne", stream: torch.cuda.Stream | None = None,
+                        lse: torch.Tensor | None = None, return_lse: bool = False,
+                        round_weights: bool = False):
+    """attn_fwd_bf16_hd on a paged key/value cache (attn_fwd_bf16_paged):
+    k_cache, v_cache [num_pages, page_size, Hkv, head_dim] bf16, block_table
+    int32 [B, pages_per_seq], kv_lens int32 [B] (keys per batch entry, at most
+    max_kv_len); q and o in `layout`.  Scale defaults to 1/sqrt(head_dim)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, page_size, Hkv, head_dim] of one shape")
+    for name, t in (("block_table", block_table), ("kv_lens", kv_lens)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if q.dim() != 4:
+        raise ValueError("q must be 4-D")
+    num_pages, page_size, Hkv, hd = (int(x) for x in k_cache.shape)
+    if layout == "bshd":
+        B, Sq, Hq, D = (int(x) for x in q.shape)
+    elif layout == "bhsd":
+        B, Hq, Sq, D = (int(x) for x in q.shape)
+    else:
+        raise ValueError(f"layout must be 'bshd' or 'bhsd', got {layout!r}")
+    if D != hd or hd not in HEAD_DIMS:
+        raise ValueError(f"head dimension must be one of {HEAD_DIMS} in q and the caches")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(kv_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, pages_per_seq] and kv_lens [B]")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous bfloat16 device tensor shaped like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq)
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 device tensor shaped [B, Hq, Sq]")
+    sc = float(1.0 / math.sqrt(hd)) if scale is None else float(scale)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_bf16_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                     kv_lens.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                     ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, int(max_kv_len), page_size,
+                                     int(block_table.shape[1]), num_pages, hd, sc, 1 if causal else 0,
+                                     _mode(round_mode, round_weights), st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (o, lse) if lse is not None else o

@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 REPORT = os.path.join(BUILD_DIR, "libattn_fwd.resource-usage.txt")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_gather_kernel.hip", "attn_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 ALU ops are kept off: hipcc must not emit v_pk_{add,mul,fma}_f32

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <algorithm>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <vector>
 
@@ -132,11 +133,23 @@ extern "C" const char* attn_status_string(int status) {
 
 namespace {
 
+// Options of run_attention beyond the operation itself.
+struct RunOpts {
+    int kv_splits = 0, block_order = 0, waves = 0;   // planner overrides (0: the planner's choice)
+    bool noalloc = false;          // split partials in the fixed device array
+    const int* kv_lens = nullptr;  // device [B]: keys of each batch entry (per-entry lengths run unsplit)
+    bool kv_internal = false;      // k, v: the library's own BSHD copy (no alias or alignment check)
+    bool check_only = false;       // validate the arguments, touch no device
+    std::function<int(int)> pre_launch;   // runs after every check, right before the kernels are queued
+};
+
 // Shared by every entry point: H = query heads, Hkv = key/value heads.
 int run_attention(const void* q, const void* k, const void* v, void* o, float* lse,
                   int layout, int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t head_dim,
-                  float scale, int causal, int round_mode, void* stream,
-                  int kv_splits, int block_order, int waves, bool noalloc = false) {
+                  float scale, int causal, int round_mode, void* stream, const RunOpts& opt) {
+    const int kv_splits = opt.kv_splits, block_order = opt.block_order, waves = opt.waves;
+    const bool noalloc = opt.noalloc;
+    const int* kv_lens = opt.kv_lens;
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
     const int out_mode = round_mode & ~ATTN_ROUND_WEIGHTS;
@@ -152,7 +165,8 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     if (B * H >= lim31) return ATTN_ERR_SHAPE;
     const int64_t n_q = B * H * Sq, n_kv = B * Hkv * Skv;
     if (n_q > ((int64_t)1 << 52) / kHeadDim || n_kv > ((int64_t)1 << 52) / kHeadDim) return ATTN_ERR_SHAPE;
-    const int64_t kv_row = (layout == ATTN_LAYOUT_BSHD) ? Hkv * kHeadDim : kHeadDim;
+    const bool kv_rows_bshd = opt.kv_internal || layout == ATTN_LAYOUT_BSHD;
+    const int64_t kv_row = kv_rows_bshd ? Hkv * kHeadDim : kHeadDim;
     if ((Skv - 1) * kv_row * 2 + kHeadDim * 2 >= lim31) return ATTN_ERR_SHAPE;
     // work-group size: the 4-wave group (two per CU) for short key ranges
     const int64_t n_kv_tiles64 = (Skv + kKeyTile - 1) / kKeyTile;
@@ -164,8 +178,9 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     const int64_t n_qtiles = (Sq + bm - 1) / bm;
     if (B * H * n_qtiles * kMaxSplits >= lim31) return ATTN_ERR_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
-    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return ATTN_ERR_ALIGN;
-    const size_t q_bytes = (size_t)n_q * kHeadDim * 2, kv_bytes = (size_t)n_kv * kHeadDim * 2;
+    if (((uintptr_t)q | (uintptr_t)o | (opt.kv_internal ? 0 : ((uintptr_t)k | (uintptr_t)v))) & 15) return ATTN_ERR_ALIGN;
+    // (the library's own key/value copy overlaps nothing of the caller's)
+    const size_t q_bytes = (size_t)n_q * kHeadDim * 2, kv_bytes = opt.kv_internal ? 0 : (size_t)n_kv * kHeadDim * 2;
     if (ranges_overlap(o, q_bytes, q, q_bytes) || ranges_overlap(o, q_bytes, k, kv_bytes) ||
         ranges_overlap(o, q_bytes, v, kv_bytes))
         return ATTN_ERR_ALIAS;
@@ -179,6 +194,9 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     if (kv_splits < 0 || kv_splits > kMaxSplits || block_order < 0 || block_order > 2) return ATTN_ERR_OPTION;
     if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
     if (causal && (kv_splits > 1 || block_order == 2)) return ATTN_ERR_OPTION;
+    if (kv_lens && kv_splits > 1) return ATTN_ERR_OPTION;
+    if (kv_lens && ((uintptr_t)kv_lens & 3)) return ATTN_ERR_ALIGN;
+    if (opt.check_only) return ATTN_OK;
 
     int dev = -1;
     DeviceInfo info;
@@ -192,11 +210,15 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.v = (const uint16_t*)v;
     p.o = (uint16_t*)o;
     p.lse = lse;
+    p.kv_lens = kv_lens;
     if (layout == ATTN_LAYOUT_BSHD) {
         p.q_row = H * kHeadDim; p.q_head = kHeadDim; p.q_batch = Sq * H * kHeadDim;
-        p.kv_row = Hkv * kHeadDim; p.kv_head = kHeadDim; p.kv_batch = Skv * Hkv * kHeadDim;
     } else {
         p.q_row = kHeadDim; p.q_head = Sq * kHeadDim; p.q_batch = H * Sq * kHeadDim;
+    }
+    if (kv_rows_bshd) {
+        p.kv_row = Hkv * kHeadDim; p.kv_head = kHeadDim; p.kv_batch = Skv * Hkv * kHeadDim;
+    } else {
         p.kv_row = kHeadDim; p.kv_head = Skv * kHeadDim; p.kv_batch = Hkv * Skv * kHeadDim;
     }
     p.B = (int)B; p.H = (int)H; p.Sq = (int)Sq; p.Skv = (int)Skv;
@@ -221,9 +243,11 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     const int n_kv_tiles = (int)((Skv + kKeyTile - 1) / kKeyTile);
     const int slots = info.n_cu * (8 / nw);   // resident work-groups: two waves per SIMD
     int n_full = p.n_items, splits = 1;
-    if (causal) {
-        // Causal items differ in length (the diagonal): they run unsplit,
-        // longest first, in naive block order (the kernel numbers them so).
+    if (causal || kv_lens) {
+        // Causal items differ in length (the diagonal), and so do the items
+        // of batch entries with their own key counts: they run unsplit
+        // (causal ones longest first, in naive block order: the kernel
+        // numbers them so).
     } else if (kv_splits > 0) {
         if (kv_splits > n_kv_tiles) return ATTN_ERR_OPTION;   // every range must hold a key
         splits = kv_splits;
@@ -263,6 +287,10 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
         p.ws_ml = (float*)((char*)ws + n_part * bm * kHeadDim * sizeof(float));
     }
 
+    if (opt.pre_launch) {
+        const int prc = opt.pre_launch(dev);
+        if (prc != ATTN_OK) return prc;
+    }
     if (attn::launch(p, (hipStream_t)stream) != 0) return ATTN_ERR_LAUNCH;
     return ATTN_OK;
 }
@@ -273,14 +301,79 @@ extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, voi
                                 int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                                 float scale, int round_mode, void* stream,
                                 int kv_splits, int block_order, int waves) {
-    return run_attention(q, k, v, o, nullptr, layout, B, H, H, Sq, Skv, 128, scale, 0, round_mode, stream,
-                         kv_splits, block_order, waves);
+    RunOpts opt;
+    opt.kv_splits = kv_splits; opt.block_order = block_order; opt.waves = waves;
+    return run_attention(q, k, v, o, nullptr, layout, B, H, H, Sq, Skv, 128, scale, 0, round_mode, stream, opt);
 }
 
 extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                  float scale, int causal, int round_mode, void* stream) {
-    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, 128, scale, causal, round_mode, stream, 0, 0, 0);
+    return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, 128, scale, causal, round_mode, stream, RunOpts());
+}
+
+extern "C" int attn_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* kv_lens, void* o, float* lse,
+                                   int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t max_kv_len,
+                                   int64_t page_size, int64_t pages_per_seq, int64_t num_pages, int64_t head_dim,
+                                   float scale, int causal, int round_mode, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !kv_lens || !o) return ATTN_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || max_kv_len < 1) return ATTN_ERR_SHAPE;
+    if (head_dim != 128 && head_dim != 64) return ATTN_ERR_SHAPE;
+    const int64_t lim31 = (int64_t)1 << 31;
+    if (B >= lim31 || Hq >= lim31 || Hkv >= lim31 || Sq >= lim31 || max_kv_len >= lim31) return ATTN_ERR_SHAPE;
+    if (page_size < 1 || page_size >= lim31 || num_pages < 1 || pages_per_seq < 1 || pages_per_seq >= lim31)
+        return ATTN_ERR_SHAPE;
+    if (pages_per_seq < (max_kv_len + page_size - 1) / page_size) return ATTN_ERR_SHAPE;   // the table covers max_kv_len
+    if (B * pages_per_seq >= lim31 || Hkv * head_dim >= lim31) return ATTN_ERR_SHAPE;
+    const int64_t row_elems = Hkv * head_dim;
+    if (num_pages > ((int64_t)1 << 52) / page_size / row_elems) return ATTN_ERR_SHAPE;
+    if (((uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return ATTN_ERR_ALIGN;
+    if (((uintptr_t)block_table | (uintptr_t)kv_lens) & 3) return ATTN_ERR_ALIGN;
+    const size_t cache_bytes = (size_t)num_pages * (size_t)page_size * (size_t)row_elems * 2;
+    const size_t q_bytes = (size_t)B * Hq * Sq * head_dim * 2;
+    if (ranges_overlap(o, q_bytes, k_cache, cache_bytes) || ranges_overlap(o, q_bytes, v_cache, cache_bytes))
+        return ATTN_ERR_ALIAS;
+    if (lse && (ranges_overlap(lse, (size_t)B * Hq * Sq * 4, k_cache, cache_bytes) ||
+                ranges_overlap(lse, (size_t)B * Hq * Sq * 4, v_cache, cache_bytes)))
+        return ATTN_ERR_ALIAS;
+    if (max_kv_len > ((int64_t)1 << 52) / row_elems / B) return ATTN_ERR_SHAPE;   // the copy's size
+    // every check of q, o, lse, the mode and the sizes before anything is
+    // allocated or queued (the key/value arguments are the library's copy)
+    RunOpts opt;
+    opt.kv_lens = kv_lens;
+    opt.kv_internal = true;
+    opt.kv_splits = 1;
+    opt.check_only = true;
+    const void* placeholder = k_cache;   // stands for the copy: not read while checking
+    const int crc = run_attention(q, placeholder, placeholder, o, lse, layout, B, Hq, Hkv, Sq, max_kv_len, head_dim,
+                                  scale, causal, round_mode, stream, opt);
+    if (crc != ATTN_OK) return crc;
+    int dev = -1;
+    DeviceInfo info;
+    const int drc = probe_device(&dev, &info);
+    if (drc != ATTN_OK) return drc;
+    // the contiguous copy of the keys and values the attention kernel reads
+    const size_t kv_bytes = (size_t)B * max_kv_len * row_elems * 2;
+    void* ws = nullptr;
+    const int wrc = get_workspace(dev, stream, 2 * kv_bytes, &ws);
+    if (wrc != ATTN_OK) return wrc;
+    uint16_t* kws = (uint16_t*)ws;
+    uint16_t* vws = (uint16_t*)((char*)ws + kv_bytes);
+    opt.check_only = false;
+    opt.pre_launch = [&](int) -> int {
+        attn::GatherParams g;
+        g.k_cache = (const uint16_t*)k_cache; g.v_cache = (const uint16_t*)v_cache;
+        g.block_table = block_table; g.kv_lens = kv_lens;
+        g.k_out = kws; g.v_out = vws;
+        g.num_pages = num_pages;
+        g.B = (int)B; g.max_kv = (int)max_kv_len; g.page_size = (int)page_size; g.pages_per_seq = (int)pages_per_seq;
+        g.row_elems = (int)row_elems;
+        return attn::launch_gather(g, (hipStream_t)stream) == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+    };
+    // the attention on the copy, unsplit, with the per-entry key counts
+    return run_attention(q, kws, vws, o, lse, layout, B, Hq, Hkv, Sq, max_kv_len, head_dim, scale, causal,
+                         round_mode, stream, opt);
 }
 
 extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -356,7 +449,7 @@ extern "C" int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, voi
                                 int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                 int64_t head_dim, float scale, int causal, int round_mode, void* stream) {
     return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, head_dim, scale, causal, round_mode,
-                         stream, 0, 0, 0);
+                         stream, RunOpts());
 }
 
 extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
@@ -368,6 +461,8 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
 extern "C" int attn_fwd_bf16_hd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                                         int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                         int64_t head_dim, float scale, int causal, int round_mode, void* stream) {
+    RunOpts opt;
+    opt.noalloc = true;
     return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, head_dim, scale, causal, round_mode,
-                         stream, 0, 0, 0, true);
+                         stream, opt);
 }

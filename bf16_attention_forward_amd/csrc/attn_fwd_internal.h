@@ -48,6 +48,7 @@ struct AttnParams {
     const uint16_t* v;
     uint16_t* o;
     float* lse;        // optional [B][H][Sq] natural-log log-sum-exp per query row (NULL: not written)
+    const int* kv_lens;  // optional [B] keys of each batch entry, clamped to [0, Skv] (NULL: Skv each)
     float* ws_o;       // split partial outputs [n_items - n_full][kv_splits][BM][128] (fp32)
     float* ws_ml;      // split partial (M, l) pairs [n_items - n_full][kv_splits][BM][2]
     int64_t q_row, q_head, q_batch;      // element strides of q and o
@@ -71,5 +72,22 @@ struct AttnParams {
 };
 
 int launch(const AttnParams& p, hipStream_t stream);
+
+// Copy of a paged key/value cache into contiguous BSHD rows, for the
+// attention kernel: row i < kv_lens[b] of batch entry b comes from row
+// i % page_size of page block_table[b][i / page_size] of the cache.
+struct GatherParams {
+    const uint16_t* k_cache;   // [num_pages][page_size][Hkv][D]
+    const uint16_t* v_cache;
+    const int* block_table;    // [B][pages_per_seq]
+    const int* kv_lens;        // [B]
+    uint16_t* k_out;           // [B][max_kv][Hkv][D]
+    uint16_t* v_out;
+    int64_t num_pages;
+    int B, max_kv, page_size, pages_per_seq;
+    int row_elems;             // Hkv * D
+};
+
+int launch_gather(const GatherParams& p, hipStream_t stream);
 
 }  // namespace attn

@@ -62,7 +62,8 @@
 //  * The block id -> work item map groups consecutive query tiles of a head
 //    onto one XCD (blocks are dealt to the 8 XCDs round-robin), so the K/V of
 //    a head is fetched into one XCD's L2 (HipKittens summary, chiplet-aware
-//    grid schedule).
+//    grid schedule).  With per-entry key counts every XCD takes an equal
+//    share of each batch entry, longest entry first.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -149,6 +150,47 @@ __device__ __forceinline__ int map_block(int bid, int n, int order) {
     return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// Work item at position pos of the map above when every batch entry has its
+// own key count (no mask).  All M = H * n_qtiles items of an entry cost the
+// same, but entries differ, so numbering the items entry by entry would
+// leave whole XCDs with the long entries.  Instead the positions are cut in
+// 8 groups (the eighth of the positions each XCD receives); group x holds,
+// for each entry, the items [x M / 8, (x + 1) M / 8) of that entry (runs of
+// consecutive query tiles, so a head's tiles share one XCD's L2), entry
+// after entry, the entry with the most keys first: a longest-first list
+// schedule on every XCD.  The entries are ranked in-wave when there are at
+// most 64 of them (ties by index); with more they run in index order.
+// Called with all 64 lanes of the wave active.
+__device__ __forceinline__ void kvlen_item(int pos, const AttnParams& p, int& qt, int& bh) {
+    const int64_t M = (int64_t)p.H * p.n_qtiles;
+    int x = 0;
+    int64_t base = 0;
+    for (; x < 7; x++) {
+        const int64_t c = ((x + 1) * M >> 3) - (x * M >> 3);
+        if (pos < base + p.B * c) break;
+        base += p.B * c;
+    }
+    // group x is never empty here: pos < B * M and group 7 holds M - 7M/8 >= 1 items per entry
+    const int64_t c = ((x + 1) * M >> 3) - (x * M >> 3);
+    const int64_t t = pos - base;
+    const int r = (int)(t / c);                              // rank of the entry
+    const int k = (int)((x * M >> 3) + t % c);               // item within the entry
+    int b = r;
+    if (p.B <= 64) {
+        const int lane = threadIdx.x & 63;
+        const int len = lane < p.B ? min(max(p.kv_lens[lane], 0), p.Skv) : -1;
+        int rank = 0;
+        for (int u = 0; u < p.B; u++) {
+            const int lu = __builtin_amdgcn_readlane(len, u);
+            rank += (lu > len || (lu == len && u < lane)) ? 1 : 0;
+        }
+        const unsigned long long m = __ballot(lane < p.B && rank == r);
+        b = __builtin_amdgcn_readfirstlane(__ffsll(m) - 1);
+    }
+    qt = k % p.n_qtiles;
+    bh = b * p.H + k / p.n_qtiles;
+}
+
 // ------------------------------------------------------------ main kernel
 // Workgroup barrier between key tiles.  Every wave waits for its own K/V DMA
 // (vmcnt) explicitly before it, so the barrier itself only needs the LDS
@@ -162,7 +204,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // NWT waves (8, or 4 for short key ranges), each owning 32 query rows of the
 // work item; see the file header for the per-tile schedule.
-template <int HD, bool CPOS, bool CAUSAL, int PMODE, int NWT>
+template <int HD, bool CPOS, bool CAUSAL, bool KVL, int PMODE, int NWT>
 __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     static_assert(NWT == 8 || NWT == 4, "8 waves (one work-group per CU) or 4 (two)");
@@ -218,6 +260,8 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         const int slot = item % BH;
         qt = p.n_qtiles - 1 - item / BH;
         bh = (BH % 8 == 0) ? (slot % 8) * (BH / 8) + slot / 8 : slot;
+    } else if (KVL) {
+        kvlen_item(item, p, qt, bh);
     } else {
         qt = item % p.n_qtiles;
         bh = item / p.n_qtiles;
@@ -225,14 +269,18 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     const int h = bh % p.H;
     const int b = bh / p.H;
     const int hk = h / p.group;                      // key/value head of query head h
+    // keys of this batch entry (per-entry lengths: never split) and the
+    // causal offset that aligns its queries with the last of them
+    const int kvl = KVL ? min(max(p.kv_lens[b], 0), p.Skv) : p.Skv;
+    const int coff = KVL ? kvl - p.Sq : p.causal_off;
 
     // split s covers key tiles [s*T/ns, (s+1)*T/ns) of the T tiles: never empty for ns <= T
     const int kv_begin = (int)(((int64_t)split * p.n_kv_tiles) / nsplit) * BN;
-    int kv_end = min(p.Skv, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / nsplit) * BN);
+    int kv_end = min(kvl, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / nsplit) * BN);
     if (CAUSAL) {
         // keys up to the diagonal of the tile's last row (never split)
         const int last_row = min(p.Sq, (qt + 1) * BM) - 1;
-        kv_end = min(kv_end, last_row + p.causal_off + 1);
+        kv_end = min(kv_end, last_row + coff + 1);
     }
     const int T = (kv_end - kv_begin + BN - 1) / BN;
 
@@ -241,9 +289,10 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     const char* vbase = (const char*)(p.v + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head);
     const int kv_row_bytes = (int)(p.kv_row * 2);
 
-    if (CAUSAL && kv_end <= kv_begin) {
-        // Causal tile entirely above the diagonal (Sq > Skv): no query row of
-        // it sees a key; its rows are zeros.  Uniform across the work-group,
+    if ((CAUSAL || KVL) && kv_end <= kv_begin) {
+        // No query row of the tile sees a key (a causal tile entirely above
+        // the diagonal, or a batch entry with no keys): its rows are zeros
+        // and their log-sum-exp is -inf.  Uniform across the work-group,
         // before any barrier or DMA.
         uint16_t* obase = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
 #pragma unroll
@@ -252,6 +301,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
             if (row >= p.Sq) continue;
 #pragma unroll
             for (int db = 0; db < NDB; db++) *(uint2*)(obase + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
+            if (p.lse && g == 0) p.lse[((int64_t)b * p.H + h) * p.Sq + row] = -__builtin_inff();
         }
         return;
     }
@@ -539,12 +589,12 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         // diagonal needs it, and one branch covers both query blocks so the
         // compares stay inside it.
         const int ts = kv_begin + t * BN;              // first key of the tile
-        const bool diag = CAUSAL && ts + BN - 1 > qrow0 + p.causal_off;
+        const bool diag = CAUSAL && ts + BN - 1 > qrow0 + coff;
         int lim[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
             lim[qb] = valid - 4 * g;
-            if (CAUSAL) lim[qb] = min(lim[qb], qrow0 + qb * 16 + j + p.causal_off - ts + 1 - 4 * g);
+            if (CAUSAL) lim[qb] = min(lim[qb], qrow0 + qb * 16 + j + coff - ts + 1 - 4 * g);
         }
         if (CPOS && (valid < BN || diag)) {
 #pragma unroll
@@ -684,7 +734,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 const int row = qrow0 + qb * 16 + j;
                 if (row >= p.Sq) continue;
                 float v = (moff[qb] + __builtin_amdgcn_logf(l_row[qb])) * LN2;
-                if (CAUSAL && row + p.causal_off < 0) v = -__builtin_inff();   // sees no key
+                if (CAUSAL && row + coff < 0) v = -__builtin_inff();   // sees no key
                 p.lse[((int64_t)b * p.H + h) * p.Sq + row] = v;
             }
         }
@@ -696,7 +746,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
             const float lr = l_row[qb];
             const float inv = 1.0f / lr;
             // a causal row that sees no key at all (Sq > Skv) is zeros
-            const bool no_key = CAUSAL && row + p.causal_off < 0;
+            const bool no_key = CAUSAL && row + coff < 0;
             uint16_t* dst = obase + (int64_t)row * p.q_row + 4 * g;
 #pragma unroll
             for (int db = 0; db < NDB; db++) {
@@ -778,21 +828,27 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
 // ------------------------------------------------------------------ launch
 int launch(const AttnParams& p, hipStream_t stream) {
     // The head dimension, c > 0 (the usual positive scale), the causal mask,
-    // the weights' rounding mode and the work-group size are compile-time
+    // per-entry key counts, the weights' rounding mode and the work-group size are compile-time
     // variants, so the plain path carries no code for any alternative.  The
     // 4-wave work-group exists for head dimension 128 without the causal mask.
     const bool short_wg = p.nw == KERNEL_NW_SHORT;
     if (p.nw != KERNEL_NW && !(short_wg && p.head_dim == 128 && !p.causal)) return -1;
     dim3 grid(p.n_blocks), block(p.nw * 64);
-    auto go_nw = [&](auto hd, auto cpos, auto causal, auto nw) {
+    auto go_kv = [&](auto hd, auto cpos, auto causal, auto kvl, auto nw) {
         constexpr int H_ = decltype(hd)::value, N_ = decltype(nw)::value;
-        constexpr bool CP = decltype(cpos)::value, CA = decltype(causal)::value;
+        constexpr bool CP = decltype(cpos)::value, CA = decltype(causal)::value, KV = decltype(kvl)::value;
         if (p.p_mode == ROUND_RTNA)
-            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNA, N_>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, KV, ROUND_RTNA, N_>), grid, block, 0, stream, p);
         else if (p.p_mode == ROUND_RTZ)
-            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTZ, N_>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, KV, ROUND_RTZ, N_>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, ROUND_RTNE, N_>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_main<H_, CP, CA, KV, ROUND_RTNE, N_>), grid, block, 0, stream, p);
+    };
+    // per-entry key counts are a variant of their own: the kernels without
+    // them carry none of their code
+    auto go_nw = [&](auto hd, auto cpos, auto causal, auto nw) {
+        if (p.kv_lens) go_kv(hd, cpos, causal, std::true_type{}, nw);
+        else go_kv(hd, cpos, causal, std::false_type{}, nw);
     };
     auto go = [&](auto hd, auto cpos, auto causal) {
         constexpr int H_ = decltype(hd)::value;

@@ -39,6 +39,8 @@ def short_name(name: str) -> str:
         return "attn_fwd_main"
     if "attn_fwd_combine" in name:
         return "attn_fwd_combine"
+    if "attn_gather_kv" in name:
+        return "attn_gather_kv"
     for k in ("attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_delta"):
         if k in name:
             return k + ("<causal>" if "<true>" in name else "")

@@ -119,6 +119,20 @@ WORKLOADS = {
 }
 
 
+# The paged-cache workload: the video self-attention's per-head size with its
+# keys and values in 256-token pages of a shared pool, four batch entries
+# with a mix of cached lengths (the longest the full 32760-token latent) and
+# 4096 new query tokens each, BSHD, no mask.
+PAGED = dict(name="paged_kv_bshd_b4_h12_sq4096_kvmix_page256", B=4, H=12, Sq=4096,
+             kv_lens=(32760, 20480, 12000, 4100), page_size=256, seed=1010,
+             note="keys and values in a paged cache, per-entry lengths")
+
+
+def paged_flops(H: int, Sq: int, kv_lens, D: int = HEAD_DIM) -> int:
+    """Algorithmic FLOPs of the paged workload: 4 * H * Sq * kv_len * D per entry."""
+    return sum(4 * H * Sq * int(n) * D for n in kv_lens)
+
+
 def shape(layout: str, B: int, H: int, S: int, D: int = HEAD_DIM) -> tuple:
     if layout == "bshd":
         return (B, S, H, D)
@@ -153,6 +167,50 @@ def make_inputs(w: Workload, *, Sq: int | None = None, Skv: int | None = None,
     return random_qkv(w.layout, B or w.B, H or w.H, Sq or w.Sq, Skv or w.Skv,
                       w.seed if seed is None else seed, w.q_factor, w.k_factor, w.v_factor,
                       Hkv=w.Hkv or None, D=w.D)
+
+
+@dataclass
+class PagedKV:
+    """A paged key/value cache and its index tables (CPU tensors).
+
+    k_cache, v_cache: bf16 [num_pages, page_size, Hkv, D]; block_table: int32
+    [B, pages_per_seq]; kv_lens: int32 [B].  Row i < kv_lens[b] of batch
+    entry b is row i % page_size of page block_table[b, i // page_size]."""
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor
+    kv_lens: torch.Tensor
+    page_size: int
+    max_kv_len: int
+
+
+def make_paged_kv(B: int, Hkv: int, kv_lens, page_size: int, seed: int, D: int = HEAD_DIM,
+                  k_factor: float = 1.0, v_factor: float = 1.0, spare_pages: int = 3,
+                  share_first_page: bool = False) -> PagedKV:
+    """Seeded paged cache: every batch entry's pages are drawn from one pool
+    in a seeded random order (so logical order never matches physical order),
+    with `spare_pages` pages that no entry uses; with share_first_page,
+    entries 0 and 1 share their first page (a common prefix).  Table slots
+    past an entry's length hold -1 (never read)."""
+    kv_lens = [int(x) for x in kv_lens]
+    max_kv = max(max(kv_lens), 1)
+    pps = (max_kv + page_size - 1) // page_size
+    need = [(n + page_size - 1) // page_size for n in kv_lens]
+    num_pages = sum(need) + spare_pages
+    g = torch.Generator(device="cpu")
+    g.manual_seed(4 * seed + 3)
+    order = torch.randperm(num_pages, generator=g)
+    table = torch.full((B, pps), -1, dtype=torch.int32)
+    pos = 0
+    for b in range(B):
+        for i in range(need[b]):
+            table[b, i] = int(order[pos])
+            pos += 1
+    if share_first_page and B >= 2 and need[0] > 0 and need[1] > 0:
+        table[1, 0] = table[0, 0]
+    k_cache = _draw((num_pages, page_size, Hkv, D), 4 * seed + 1, k_factor)
+    v_cache = _draw((num_pages, page_size, Hkv, D), 4 * seed + 2, v_factor)
+    return PagedKV(k_cache, v_cache, table, torch.tensor(kv_lens, dtype=torch.int32), page_size, max_kv)
 
 
 @dataclass

@@ -195,6 +195,46 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
                      int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                      int64_t head_dim, float scale, int causal, int round_mode, void* stream);
 
+/*
+ * attn_fwd_bf16_paged -- attn_fwd_bf16_hd with the keys and values in a paged
+ * cache and a key count per batch entry: the flexible and paged KV-cache
+ * layouts the FlyDSL diffusion-attention article lists among diffusion
+ * inference's needs (its section on what such a kernel must offer).
+ *
+ *   q, o        [B,Sq,Hq,head_dim] or [B,Hq,Sq,head_dim] bf16 (`layout`, as
+ *               attn_fwd_bf16_hd); lse as attn_fwd_bf16_gqa
+ *   k_cache, v_cache  [num_pages][page_size][Hkv][head_dim] bf16, device
+ *               memory, 16-byte aligned: page p holds page_size token rows
+ *   block_table int32 [B][pages_per_seq], device memory: token row i of
+ *               batch entry b is row i % page_size of page
+ *               block_table[b][i / page_size]; pages may be shared between
+ *               entries; an entry outside [0, num_pages) reads as zero rows
+ *   kv_lens     int32 [B], device memory: keys of batch entry b, clamped to
+ *               [0, max_kv_len]; a batch entry with no keys gives zero rows
+ *               (and lse -inf)
+ *   max_kv_len  >= 1, at least every kv_lens[b] that should count whole;
+ *               pages_per_seq must cover it (pages_per_seq * page_size >=
+ *               max_kv_len)
+ *   causal      0, or 1: query i of entry b sees keys j <= i + kv_lens[b] -
+ *               Sq (its queries are the last Sq positions of its keys)
+ *
+ * The library first copies each entry's kv_lens[b] key and value rows into
+ * a contiguous per-(device, stream) workspace of 2 * B * max_kv_len * Hkv *
+ * head_dim bf16 values (HIP's stream-ordered allocator, as for the split
+ * partials; ATTN_ERR_WORKSPACE while the stream is being captured), then
+ * runs the attention kernel on it with the per-entry key counts; the key
+ * range is never split.  Every other argument, ownership, asynchrony and
+ * error behaviour are those of attn_fwd_bf16_hd; page_size, pages_per_seq
+ * or num_pages below 1, or a table too narrow for max_kv_len, give
+ * ATTN_ERR_SHAPE; a misaligned cache, table or kv_lens ATTN_ERR_ALIGN; o or
+ * lse overlapping a cache ATTN_ERR_ALIAS.
+ */
+int attn_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_table, const int32_t* kv_lens, void* o, float* lse,
+                        int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t max_kv_len,
+                        int64_t page_size, int64_t pages_per_seq, int64_t num_pages, int64_t head_dim,
+                        float scale, int causal, int round_mode, void* stream);
+
 /* Size in bytes of the fixed device array behind attn_fwd_bf16_hd_noalloc:
  * 256 partial query tiles x 256 rows x (128 + 2) fp32 values, the largest
  * split workspace the planner asks for on a 256-CU gfx950 device. */

@@ -181,3 +181,35 @@ def test_bwd_valid_arguments_reach_device_check():
     assert call_bwd(causal=1) == -8
     assert call_bwd(H=4, Hkv=1) == -8 and call_bwd(H=4, Hkv=2, causal=1) == -8
     assert call_bwd(hd=64) == -8
+
+
+def call_paged(**kw):
+    a = dict(q=FAKE, kc=FAKE + (1 << 30), vc=FAKE + (2 << 30), bt=FAKE + (4 << 30), kl=FAKE + (5 << 30),
+             o=FAKE + (3 << 30), lse=None, layout=0, B=2, Hq=4, Hkv=2, Sq=64, max_kv=300, ps=64, pps=5, npages=10,
+             hd=128, scale=0.0883883, causal=0, mode=0, stream=0)
+    a.update(kw)
+    return load_library().attn_fwd_bf16_paged(a["q"], a["kc"], a["vc"], a["bt"], a["kl"], a["o"], a["lse"],
+                                              a["layout"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["max_kv"],
+                                              a["ps"], a["pps"], a["npages"], a["hd"], a["scale"], a["causal"],
+                                              a["mode"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=0), -1), (dict(kl=0), -1), (dict(kc=0), -1), (dict(q=0), -1),
+    (dict(ps=0), -4), (dict(npages=0), -4), (dict(pps=4), -4),          # 4 pages of 64 do not cover 300 keys
+    (dict(max_kv=0), -4), (dict(hd=96), -4), (dict(Hkv=3), -4), (dict(max_kv=1 << 31), -4),
+    (dict(kc=FAKE + (1 << 30) + 8), -6), (dict(bt=FAKE + (4 << 30) + 2), -6), (dict(kl=FAKE + (5 << 30) + 1), -6),
+    (dict(o=FAKE + (1 << 30) + 64), -7),                                # o inside the key cache
+    (dict(mode=5), -3), (dict(causal=2), -11), (dict(layout=7), -2), (dict(scale=float("nan")), -5),
+])
+def test_paged_argument_errors_before_device(kw, code):
+    assert call_paged(**kw) == code
+
+
+def test_paged_valid_arguments_reach_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_paged() == -8
+    assert call_paged(causal=1, hd=64, layout=1) == -8
+    assert call_paged(pps=5, max_kv=320) == -8                          # exactly covered
