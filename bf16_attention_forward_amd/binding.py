@@ -52,7 +52,7 @@ def load_library(path: str | None = None):
            [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_bf16.argtypes = args
     lib.attn_fwd_bf16.restype = ctypes.c_int
-    lib.attn_fwd_bf16_ex.argtypes = args + [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.attn_fwd_bf16_ex.argtypes = args + [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.attn_fwd_bf16_ex.restype = ctypes.c_int
     lib.attn_fwd_bf16_gqa.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] + [ctypes.c_int64] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -142,16 +142,17 @@ def _check_tensors(q, k, v, o):
 def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor | None = None, *,
                   layout: str = "bshd", scale: float | None = None, round_mode: str = "rtne",
                   stream: torch.cuda.Stream | None = None, kv_splits: int = 0,
-                  block_order: int = 0, waves: int = 0, round_weights: bool = False) -> torch.Tensor:
+                  block_order: int = 0, waves: int = 0, grid: int = 0,
+                  round_weights: bool = False) -> torch.Tensor:
     """O = softmax(Q K^T * scale) V on the gfx950 library (bf16 in/out).
 
     q, k, v, o: contiguous bfloat16 CUDA tensors in the given layout.  o is
     allocated when None.  scale defaults to 1/sqrt(128) (as fp32).  The
     launch goes to ``stream`` (default: torch's current stream) and is
-    asynchronous.  With kv_splits, block_order and waves all 0 (automatic)
-    the call goes to the C entry point attn_fwd_bf16; otherwise to
-    attn_fwd_bf16_ex with those planner overrides (waves 8 or 4 per
-    work-group).  round_weights: round the in-loop
+    asynchronous.  With kv_splits, block_order, waves and grid all 0
+    (automatic) the call goes to the C entry point attn_fwd_bf16; otherwise
+    to attn_fwd_bf16_ex with those planner overrides (waves 8 or 4 per
+    work-group; grid: at most that many work-groups).  round_weights: round the in-loop
     softmax weights with ``round_mode`` too (ATTN_ROUND_WEIGHTS; default:
     nearest-even).
     """
@@ -161,7 +162,7 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     sc = float(1.0 / math.sqrt(HEAD_DIM)) if scale is None else float(scale)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
-        if kv_splits == 0 and block_order == 0 and waves == 0:
+        if kv_splits == 0 and block_order == 0 and waves == 0 and grid == 0:
             # the planner's own choices: the plain entry point
             rc = lib.attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, _mode(round_mode, round_weights),
@@ -169,7 +170,7 @@ def attn_fwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
         else:
             rc = lib.attn_fwd_bf16_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                       ATTN_LAYOUT[layout], B, H, Sq, Skv, sc, _mode(round_mode, round_weights),
-                                      st.cuda_stream, int(kv_splits), int(block_order), int(waves))
+                                      st.cuda_stream, int(kv_splits), int(block_order), int(waves), int(grid))
     if rc != ATTN_OK:
         _raise(rc)
     return o
@@ -356,8 +357,8 @@ def attn_bwd_bf16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
 
 def attn_fwd_bf16_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, layout: int, B: int, H: int,
                       Sq: int, Skv: int, scale: float, round_mode: int, stream_ptr: int,
-                      kv_splits: int = 0, block_order: int = 0, waves: int = 0) -> int:
+                      kv_splits: int = 0, block_order: int = 0, waves: int = 0, grid: int = 0) -> int:
     """Call the C entry point with raw integers; returns the status code."""
     lib = load_library()
     return int(lib.attn_fwd_bf16_ex(q_ptr, k_ptr, v_ptr, o_ptr, layout, B, H, Sq, Skv, scale,
-                                    round_mode, stream_ptr, kv_splits, block_order, waves))
+                                    round_mode, stream_ptr, kv_splits, block_order, waves, grid))

@@ -57,7 +57,8 @@ def build(extra_flags=None, out=None, quiet=True) -> str:
     return out
 
 
-FIELDS = (("VGPRs", "VGPRs"), ("AGPRs", "AGPRs"), ("TotalSGPRs", "SGPRs"), ("VGPRs Spill", "VGPR spill"),
+FIELDS = (("VGPRs", "VGPRs"), ("AGPRs", "AGPRs"), ("TotalSGPRs", "SGPRs"), ("SGPRs Spill", "SGPR spill"),
+          ("VGPRs Spill", "VGPR spill"),
           ("ScratchSize [bytes/lane]", "scratch B/lane"), ("LDS Size [bytes/block]", "LDS B/block"),
           ("Occupancy [waves/SIMD]", "waves/SIMD"))
 

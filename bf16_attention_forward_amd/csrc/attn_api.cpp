@@ -136,6 +136,7 @@ namespace {
 // Options of run_attention beyond the operation itself.
 struct RunOpts {
     int kv_splits = 0, block_order = 0, waves = 0;   // planner overrides (0: the planner's choice)
+    int grid = 0;                  // at most this many work-groups (0: the planner's choice)
     bool noalloc = false;          // split partials in the fixed device array
     const int* kv_lens = nullptr;  // device [B]: keys of each batch entry (per-entry lengths run unsplit)
     bool kv_internal = false;      // k, v: the library's own BSHD copy (no alias or alignment check)
@@ -195,6 +196,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
     if (causal && (kv_splits > 1 || block_order == 2)) return ATTN_ERR_OPTION;
     if (kv_lens && kv_splits > 1) return ATTN_ERR_OPTION;
+    if (opt.grid < 0 || (opt.grid > 0 && (causal || kv_lens))) return ATTN_ERR_OPTION;
     if (kv_lens && ((uintptr_t)kv_lens & 3)) return ATTN_ERR_ALIGN;
     if (opt.check_only) return ATTN_OK;
 
@@ -269,6 +271,23 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.kv_splits = splits;
     p.n_kv_tiles = n_kv_tiles;
     p.n_blocks = n_full + (p.n_items - n_full) * splits;
+    // Without the causal mask or per-entry key counts every block of the
+    // plan costs the same (the split blocks of the last round alike), and an
+    // 8-wave plan at head dimension 128 with more blocks than resident
+    // work-groups runs on a persistent grid of one work-group per slot
+    // (the item loop does not pay at head dimension 64): each takes every grid-th
+    // block and fetches the next one's Q and first K tile under its current
+    // item's last iteration.  The grid is a multiple of 8, so each block
+    // keeps the XCD the XCD-aware order gave it.  Causal and
+    // per-entry-length items differ in cost and keep one block per
+    // work-group, so the hardware balances them as they finish; so do 4-wave
+    // work-groups, two per CU, whose item boundaries overlap the other's
+    // work only when they run out of step.
+    p.grid = p.n_blocks;
+    if (!causal && !kv_lens && nw == KERNEL_NW && head_dim == 128) {
+        const int cap = std::max(8, (opt.grid > 0 ? opt.grid : slots) & ~7);
+        if (cap < p.n_blocks) p.grid = cap;
+    }
     p.block_order = (block_order == 1 || causal) ? attn::ORDER_NAIVE : attn::ORDER_XCD;
 
     if (n_full < p.n_items) {
@@ -300,9 +319,9 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
 extern "C" int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
                                 int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                                 float scale, int round_mode, void* stream,
-                                int kv_splits, int block_order, int waves) {
+                                int kv_splits, int block_order, int waves, int grid) {
     RunOpts opt;
-    opt.kv_splits = kv_splits; opt.block_order = block_order; opt.waves = waves;
+    opt.kv_splits = kv_splits; opt.block_order = block_order; opt.waves = waves; opt.grid = grid;
     return run_attention(q, k, v, o, nullptr, layout, B, H, H, Sq, Skv, 128, scale, 0, round_mode, stream, opt);
 }
 
@@ -455,7 +474,7 @@ extern "C" int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, voi
 extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                              int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                              float scale, int round_mode, void* stream) {
-    return attn_fwd_bf16_ex(q, k, v, o, layout, B, H, Sq, Skv, scale, round_mode, stream, 0, 0, 0);
+    return attn_fwd_bf16_ex(q, k, v, o, layout, B, H, Sq, Skv, scale, round_mode, stream, 0, 0, 0, 0);
 }
 
 extern "C" int attn_fwd_bf16_hd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -63,6 +63,7 @@ struct AttnParams {
     int kv_splits;     // key ranges of each item in [n_full, n_items) (1 = no split)
     int n_kv_tiles;    // ceil(Skv / 64)
     int n_blocks;      // n_full + (n_items - n_full) * kv_splits
+    int grid;          // work-groups launched: n_blocks, or fewer (a multiple of 8) for a persistent grid
     int block_order;   // ORDER_NAIVE or ORDER_XCD
     int round_mode;
     int head_dim;      // 128 or 64

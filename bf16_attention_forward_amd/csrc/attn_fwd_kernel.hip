@@ -143,6 +143,19 @@ __device__ __forceinline__ float div_corrected(float o, float l, float r) {
 template <int HD> __device__ __forceinline__ int swz_k(int row) { return HD == 128 ? (row & 15) : ((row >> 1) & 7); }
 template <int HD> __device__ __forceinline__ int swz_v(int row) { return HD == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1); }
 
+// The kernel's arguments in the kernel-argument segment, through a pointer
+// the compiler cannot see through: values read from it are read again at
+// each use site instead of being held in scalar registers from the kernel's
+// entry, which keeps the item loop of a persistent work-group from holding
+// every argument across its key loop.
+typedef const __attribute__((address_space(4))) AttnParams KParams;
+template <bool OPAQUE>
+__device__ __forceinline__ KParams& kernel_params() {
+    auto kp = __builtin_amdgcn_kernarg_segment_ptr();
+    if (OPAQUE) __asm__ volatile("" : "+s"(kp));
+    return *(KParams*)kp;
+}
+
 __device__ __forceinline__ int map_block(int bid, int n, int order) {
     if (order != ORDER_XCD) return bid;
     const int xcd = bid & 7, slot = bid >> 3;
@@ -161,7 +174,8 @@ __device__ __forceinline__ int map_block(int bid, int n, int order) {
 // schedule on every XCD.  The entries are ranked in-wave when there are at
 // most 64 of them (ties by index); with more they run in index order.
 // Called with all 64 lanes of the wave active.
-__device__ __forceinline__ void kvlen_item(int pos, const AttnParams& p, int& qt, int& bh) {
+template <class PT>
+__device__ __forceinline__ void kvlen_item(int pos, PT& p, int& qt, int& bh) {
     const int64_t M = (int64_t)p.H * p.n_qtiles;
     int x = 0;
     int64_t base = 0;
@@ -230,553 +244,618 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     __shared__ __attribute__((aligned(1024))) uint8_t sv0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sv1[TILE_BYTES];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
-    const int g = lane >> 4;       // lane group (0..3)
-    const int j = lane & 15;       // lane within group
-
-    // ---- work item
+    // ---- work items
     // Blocks [0, n_full) take the unsplit items (in XCD-aware order); the
-    // remaining blocks take the key ranges of the split items.
-    int item, split, nsplit;
-    if ((int)blockIdx.x < p.n_full) {
-        item = map_block(blockIdx.x, p.n_full, p.block_order);
-        split = 0;
-        nsplit = 1;
-    } else {
-        const int tb = blockIdx.x - p.n_full;
-        item = p.n_full + tb / p.kv_splits;
-        split = tb % p.kv_splits;
-        nsplit = p.kv_splits;
-    }
-    int qt, bh;
-    if (CAUSAL) {
-        // Causal items run longest first: items [0, BH) are the last query
-        // tile of every head, then the second last, ...; the block order is
-        // naive, so the XCD of item i is i mod 8 and each XCD gets an equal
-        // share of every tile length.  Within a tile length, XCD x takes
-        // heads [x*BH/8, (x+1)*BH/8), which share key/value heads under GQA.
-        const int BH = p.B * p.H;
-        const int slot = item % BH;
-        qt = p.n_qtiles - 1 - item / BH;
-        bh = (BH % 8 == 0) ? (slot % 8) * (BH / 8) + slot / 8 : slot;
-    } else if (KVL) {
-        kvlen_item(item, p, qt, bh);
-    } else {
-        qt = item % p.n_qtiles;
-        bh = item / p.n_qtiles;
-    }
-    const int h = bh % p.H;
-    const int b = bh / p.H;
-    const int hk = h / p.group;                      // key/value head of query head h
-    // keys of this batch entry (per-entry lengths: never split) and the
-    // causal offset that aligns its queries with the last of them
-    const int kvl = KVL ? min(max(p.kv_lens[b], 0), p.Skv) : p.Skv;
-    const int coff = KVL ? kvl - p.Sq : p.causal_off;
-
-    // split s covers key tiles [s*T/ns, (s+1)*T/ns) of the T tiles: never empty for ns <= T
-    const int kv_begin = (int)(((int64_t)split * p.n_kv_tiles) / nsplit) * BN;
-    int kv_end = min(kvl, (int)(((int64_t)(split + 1) * p.n_kv_tiles) / nsplit) * BN);
-    if (CAUSAL) {
-        // keys up to the diagonal of the tile's last row (never split)
-        const int last_row = min(p.Sq, (qt + 1) * BM) - 1;
-        kv_end = min(kv_end, last_row + coff + 1);
-    }
-    const int T = (kv_end - kv_begin + BN - 1) / BN;
-
-    const uint16_t* qbase = p.q + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
-    const char* kbase = (const char*)(p.k + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head);
-    const char* vbase = (const char*)(p.v + (int64_t)b * p.kv_batch + (int64_t)hk * p.kv_head);
-    const int kv_row_bytes = (int)(p.kv_row * 2);
-
-    if ((CAUSAL || KVL) && kv_end <= kv_begin) {
-        // No query row of the tile sees a key (a causal tile entirely above
-        // the diagonal, or a batch entry with no keys): its rows are zeros
-        // and their log-sum-exp is -inf.  Uniform across the work-group,
-        // before any barrier or DMA.
-        uint16_t* obase = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
-#pragma unroll
-        for (int qb = 0; qb < NQB; qb++) {
-            const int row = qt * BM + wave * 16 * NQB + qb * 16 + j;
-            if (row >= p.Sq) continue;
-#pragma unroll
-            for (int db = 0; db < NDB; db++) *(uint2*)(obase + (int64_t)row * p.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
-            if (p.lse && g == 0) p.lse[((int64_t)b * p.H + h) * p.Sq + row] = -__builtin_inff();
+    // remaining blocks take the key ranges of the split items.  Without the
+    // causal mask or per-entry key counts every item costs the same, and an
+    // 8-wave grid of G blocks at head dimension 128, fewer than the plan's,
+    // is persistent: block i runs the plan's blocks i, i + G, i + 2G, ... (G
+    // a multiple of 8, so each lands on the XCD it would have had) and
+    // fetches the next one's Q and first K tile during the current item's
+    // last iteration.  (Two 4-wave work-groups per CU already overlap one's
+    // item boundary with the other's matrix work; kept persistent, they run
+    // in step and their epilogues coincide, which measured slower.  At head
+    // dimension 64 the item loop costs more registers than it saves time.)
+    constexpr bool PERSIST = !CAUSAL && !KVL && NWT == 8 && HD == 128;
+    struct Loc {
+        int item, split, nsplit, qt, b, h, hk, coff, kv_begin, kv_end;
+    };
+    auto locate = [&](KParams& p, int vb) __attribute__((always_inline)) -> Loc {
+        Loc L;
+        if (vb < p.n_full) {
+            L.item = map_block(vb, p.n_full, p.block_order);
+            L.split = 0;
+            L.nsplit = 1;
+        } else {
+            const int tb = vb - p.n_full;
+            L.item = p.n_full + tb / p.kv_splits;
+            L.split = tb % p.kv_splits;
+            L.nsplit = p.kv_splits;
         }
-        return;
-    }
-
-    // ---- K/V buffer resources: reads at or beyond kv_end return zero.
-    const uint32_t nrec = (uint32_t)((int64_t)(kv_end - 1) * kv_row_bytes + ROW_BYTES);
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, 0x00020000);
-
-    // The first four waves issue all K/V DMA: lane l of wave w in round r
-    // lands at LDS slot (4*r + w)*64 + l, i.e. row by row in order: row
-    // RPR*r + RPW*w + l / CPR, chunk l % CPR (CPR chunks per row, RPW rows per
-    // wave, RPR rows per round: 16, 4, 16 for HD = 128 and 8, 8, 32 for 64);
-    // rows RPR apart share the swizzle, so one per-lane source offset serves
-    // every round.  The DMA is issued with inline assembly:
-    // the compiler then does not track it and inserts no vmcnt wait before
-    // LDS reads of other buffers (its alias tracking is lost at loop heads);
-    // the issuing waves wait for their DMA explicitly (vmcnt(0)) before the
-    // barrier that publishes a tile.
-    const bool late = NW == 8 && wave >= 4;   // second wave of each SIMD (see the key loop)
-    constexpr int CPR = ROW_BYTES / 16, RPW = 64 / CPR, RPR = 4 * RPW;
-    constexpr int DMA_ROUNDS = BN / RPR;
-    static_assert(DMA_ROUNDS * RPR == BN && RPR % 16 == 0, "rounds of whole swizzle periods");
-    const int dma_row = (wave & 3) * RPW + lane / CPR, dma_chunk = lane % CPR;
-    const int dma_off_k = dma_row * kv_row_bytes + ((dma_chunk ^ swz_k<HD>(dma_row)) << 4);
-    const int dma_off_v = dma_row * kv_row_bytes + ((dma_chunk ^ swz_v<HD>(dma_row)) << 4);
-    const uint64_t ka = (uint64_t)(uintptr_t)kbase, va = (uint64_t)(uintptr_t)vbase;
-    const i32x4 krs4 = {(int)(uint32_t)ka, (int)((ka >> 32) & 0xffffu), (int)nrec, 0x00020000};
-    const i32x4 vrs4 = {(int)(uint32_t)va, (int)((va >> 32) & 0xffffu), (int)nrec, 0x00020000};
-    auto dma16 = [&](const i32x4 rs, uint8_t* dst, int voff, int soff) __attribute__((always_inline)) {
-        // the LDS address, the descriptor and the tile offset are
-        // wave-uniform; say so, so they stay in scalar registers
-        const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
-        const int so = __builtin_amdgcn_readfirstlane(soff);
-        const i32x4 rsu = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
-                           __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
-        // m0 (the LDS destination) is written in the same statement as the
-        // load, so nothing is scheduled between the two; no other code of the
-        // kernel uses m0, which makes the clobber safe.  Handing the address
-        // in as an {m0} operand lets the compiler move the write away from
-        // the load, and that form gave wrong results here.  An LDS-bound
-        // buffer load reads m0 one wait state after a scalar write of it at
-        // the earliest (the compiler puts the same s_nop after its own m0
-        // write for the builtin form of this load); inline assembly is opaque
-        // to the hazard recognizer, so the statement carries the nop itself.
-        __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                         :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
+        int bh;
+        if (CAUSAL) {
+            // Causal items run longest first: items [0, BH) are the last query
+            // tile of every head, then the second last, ...; the block order is
+            // naive, so the XCD of item i is i mod 8 and each XCD gets an equal
+            // share of every tile length.  Within a tile length, XCD x takes
+            // heads [x*BH/8, (x+1)*BH/8), which share key/value heads under GQA.
+            const int BH = p.B * p.H;
+            const int slot = L.item % BH;
+            L.qt = p.n_qtiles - 1 - L.item / BH;
+            bh = (BH % 8 == 0) ? (slot % 8) * (BH / 8) + slot / 8 : slot;
+        } else if (KVL) {
+            kvlen_item(L.item, p, L.qt, bh);
+        } else {
+            L.qt = L.item % p.n_qtiles;
+            bh = L.item / p.n_qtiles;
+        }
+        L.h = bh % p.H;
+        L.b = bh / p.H;
+        L.hk = L.h / p.group;                      // key/value head of query head h
+        // keys of this batch entry (per-entry lengths: never split) and the
+        // causal offset that aligns its queries with the last of them
+        const int kvl = KVL ? min(max(p.kv_lens[L.b], 0), p.Skv) : p.Skv;
+        L.coff = KVL ? kvl - p.Sq : p.causal_off;
+        // split s covers key tiles [s*T/ns, (s+1)*T/ns) of the T tiles: never empty for ns <= T
+        L.kv_begin = (int)(((int64_t)L.split * p.n_kv_tiles) / L.nsplit) * BN;
+        L.kv_end = min(kvl, (int)(((int64_t)(L.split + 1) * p.n_kv_tiles) / L.nsplit) * BN);
+        if (CAUSAL) {
+            // keys up to the diagonal of the tile's last row (never split)
+            const int last_row = min(p.Sq, (L.qt + 1) * BM) - 1;
+            L.kv_end = min(L.kv_end, last_row + L.coff + 1);
+        }
+        return L;
     };
-    // round r of the K (or V) tile that starts at key k0
-    auto dma_k = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
-        dma16(krs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 + RPR * r) * kv_row_bytes);
+    // Buffer descriptor of a head's K or V rows [0, kv_end) (rows of
+    // kv_row_bytes): reads at or beyond kv_end return zero.
+    auto kv_rsrc = [&](const char* base, int kv_end, int kv_row_bytes) __attribute__((always_inline)) -> i32x4 {
+        const uint32_t nrec = (uint32_t)((int64_t)(kv_end - 1) * kv_row_bytes + ROW_BYTES);
+        const uint64_t a = (uint64_t)(uintptr_t)base;
+        return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)nrec, 0x00020000};
     };
-    auto dma_v = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
-        dma16(vrs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 + RPR * r) * kv_row_bytes);
-    };
-    if (!late) {
-#pragma unroll
-        for (int r = 0; r < DMA_ROUNDS; r++) dma_k(r, kv_begin, sk0);
-    }
-
     // ---- Q fragments (operand B of S^T = K Q^T): lane (g, j) holds query row
     // 16*qb + j of this wave, dims 32*ks + 8*g .. +7, for the whole key loop.
     // Rows past Sq are clamped (their results are never stored).
-    const int qrow0 = qt * BM + wave * 16 * NQB;   // first query row of this wave
     bf16x8 qf[NQB][NKS];
-#pragma unroll
-    for (int qb = 0; qb < NQB; qb++) {
-        const int row = min(qrow0 + qb * 16 + j, p.Sq - 1);
-        const uint16_t* src = qbase + (int64_t)row * p.q_row + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ks++) qf[qb][ks] = *(const bf16x8*)(src + 32 * ks);
-    }
-    f32x4 o_acc[NDB][NQB];
-#pragma unroll
-    for (int db = 0; db < NDB; db++)
-#pragma unroll
-        for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float moff[NQB], l_run[NQB];    // power-of-two offset of the weights (integer-valued), row-sum partials
-    f32x4 l_acc[NQB];               // MFMA_SUM: row sums, every element the lane's query
-    f32x4 bias4[NQB];               // c > 0: S^T accumulates from -moff/c, so c * S^T = x - moff
-#pragma unroll
-    for (int qb = 0; qb < NQB; qb++) {
-        moff[qb] = 0.f; l_run[qb] = 0.f;
-        bias4[qb] = f32x4{0.f, 0.f, 0.f, 0.f}; l_acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                          (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-    const float rc = 1.0f / p.c;
-    f32x4 s_acc[4][NQB];
-    bf16x8 pf[NQB][2];
-    const float c = p.c;
 
-    // ---- MFMA phase: steps [S0, S1) of a fixed sequence of ST fragment steps.
-    // Steps 0..SS-1 compute S^T = K Q^T: step 4*ks + kb reads the K fragment of
-    // key block kb, k-step ks (one ds_read_b128: lane (g, j) gets row 16*kb + j,
-    // dims 32*ks + 8*g .. +7) and feeds NQB MFMAs; k-steps are the outer index
-    // so consecutive MFMAs hit different accumulators.  The score fragment of
-    // lane (g, j) then holds query j and keys 16*kb + 4*g + r, r = 0..3.
-    // Steps SS..ST-1 compute O^T += V^T P^T: step SS + NDB*ks + db reads the
-    // V^T fragment of dim block db for the 32 keys of step ks with two
-    // ds_read_b64_tr_b16 (rows 32*ks + 16*hf + 4*g + r), matching the keys
-    // of P's elements 4*hf + r.  Fragment reads run PF steps ahead of their
-    // MFMAs so LDS latency hides behind the matrix core.
-    int k_addr[NKS], v_addr[NDB];   // per-lane byte offsets within a tile
-#pragma unroll
-    for (int ks = 0; ks < NKS; ks++) k_addr[ks] = j * ROW_BYTES + ((((4 * ks + g) ^ swz_k<HD>(j))) << 4);
-#pragma unroll
-    for (int db = 0; db < NDB; db++) {
-        const int row = 4 * g + (j >> 2);                    // + 32*ks + 16*hf (multiples of 8)
-        const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v<HD>(row);
-        v_addr[db] = row * ROW_BYTES + (chunk << 4) + ((j & 1) << 3);
-    }
-    auto read_frag = [&](int st, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) -> bf16x8 {
-        if (st < SS) {
-            const int kb = st & 3, ks = st >> 2;
-            return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(kt + k_addr[ks] + kb * 16 * ROW_BYTES);
-        }
-        const int db = (st - SS) % NDB, ks = (st - SS) / NDB;
-        bf16x4 half[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; hf++) {
-            const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(vt + v_addr[db] + (32 * ks + 16 * hf) * ROW_BYTES);
-            half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
-        }
-        return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    auto use_frag = [&](int st, const bf16x8 f) __attribute__((always_inline)) {
-        if (st < SS) {
-            const int kb = st & 3, ks = st >> 2;
-#pragma unroll
-            for (int qb = 0; qb < NQB; qb++)
-                s_acc[kb][qb] = mfma16x16x32(f, qf[qb][ks], ks == 0 ? (CPOS ? bias4[qb] : f32x4{0.f, 0.f, 0.f, 0.f}) : s_acc[kb][qb]);
-        } else {
-            const int db = (st - SS) % NDB, ks = (st - SS) / NDB;
-#pragma unroll
-            for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = mfma16x16x32(f, pf[qb][ks], o_acc[db][qb]);
-            if (MFMA_SUM && db == NDB - 1) {
-                // ones^T P^T: every lane gets the sum of the step's 32 bf16
-                // weights of its query (exact products, fp32 sums)
-#pragma unroll
-                for (int qb = 0; qb < NQB; qb++) l_acc[qb] = mfma16x16x32(ones8, pf[qb][ks], l_acc[qb]);
-            }
-        }
-    };
-    constexpr int PF = 4;   // fragment prefetch distance (steps)
-    // The DMA of iteration t (K_{t+1} into kn, V_t into vc) is spread over the
-    // issuing waves' MFMA phase, one instruction every STRIDE steps, so the
-    // CU's address unit drains it while the matrix core runs instead of
-    // stalling a wave that issues all of it at once.
-    constexpr int NDMA = 2 * DMA_ROUNDS;   // instructions per wave and tile
-    // The phase has no branch: the issuing group is a compile-time choice
-    // (LATE), and past the last tile the K DMA re-reads that tile into the
-    // free buffer, so the scheduler sees the whole phase as one region.
-    auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c, int t, uint8_t* kn, uint8_t* vc,
-                          auto latec) __attribute__((always_inline)) {
-        constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
-        constexpr bool LATE = decltype(latec)::value;
-        constexpr int STRIDE = (S1 - S0) / NDMA;
-        static_assert(S0 != 0 || STRIDE * NDMA <= S1 - S0, "the DMA fits the phase");
-        // Opaque per-lane offsets: stops the compiler from hoisting every
-        // buffer x fragment address combination out of the loop (and spilling
-        // them); each phase adds its buffer base to these offsets instead.
-#pragma unroll
-        for (int i = 0; i < NKS; i++) __asm__ volatile("" : "+v"(k_addr[i]));
-#pragma unroll
-        for (int i = 0; i < NDB; i++) __asm__ volatile("" : "+v"(v_addr[i]));
-        bf16x8 fr[PF];
-#pragma unroll
-        for (int st = S0; st < S0 + PF && st < S1; st++) fr[(st - S0) % PF] = read_frag(st, kt, vt);
-#pragma unroll
-        for (int st = S0; st < S1; st++) {
-            const bf16x8 cur = fr[(st - S0) % PF];
-            if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
-            if (S0 == 0 && (st - S0) % STRIDE == 0 && (st - S0) / STRIDE < NDMA && !LATE) {
-                const int k = (st - S0) / STRIDE;     // K and V rounds alternate
-                if (k & 1) dma_v(k >> 1, kv_begin + t * BN, vc);
-                else dma_k(k >> 1, kv_begin + min(t + 1, T - 1) * BN, kn);
-            }
-            use_frag(st, cur);
-        }
-        // keep the interleave: the reads of step st+PF, then the MFMAs of step st
-#pragma unroll
-        for (int st = S0; st < S0 + PF && st < S1; st++) {
-            if (st < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-#pragma unroll
-        for (int st = S0; st < S1; st++) {
-            if (st + PF < S1) {
-                if (st + PF < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            if (MFMA_SUM && st >= SS && (st - SS) % NDB == NDB - 1) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);
-            else __builtin_amdgcn_sched_group_barrier(0x008, NQB, 0);
-        }
-    };
-    using C0 = std::integral_constant<int, 0>;
-    using CS = std::integral_constant<int, SS>;
-    using CT = std::integral_constant<int, ST>;
-
-    // Two weights (>= 0, or NaN) to packed bf16 in the weights' rounding mode.
-    // Nearest-even: the hardware conversion.  Ties away: the same conversion
-    // after setting the lowest fp32 bit, which turns an exact tie into a value
-    // just above it and changes no other decision (an infinite weight would
-    // become NaN, but it only arises in rows whose output is NaN anyway).
-    // Toward zero: the high half of the bit pattern, after clamping every NaN
-    // to the canonical one so truncation cannot make it an infinity.
-    auto weight_pair = [&](const f32x2 two) __attribute__((always_inline)) -> bf16x2 {
-        if (PMODE == ROUND_RTNE) return __builtin_convertvector(two, bf16x2);
-        if (PMODE == ROUND_RTNA) {
-            const f32x2 up = {__uint_as_float(__float_as_uint(two[0]) | 1u), __uint_as_float(__float_as_uint(two[1]) | 1u)};
-            return __builtin_convertvector(up, bf16x2);
-        }
-        const uint32_t u0 = min(__float_as_uint(two[0]), 0x7fc00000u);
-        const uint32_t u1 = min(__float_as_uint(two[1]), 0x7fc00000u);
-        return __builtin_bit_cast(bf16x2, (u1 & 0xffff0000u) | (u0 >> 16));
-    };
-    // Weights of query block qb against offset m: p = 2^(x - m) (v_exp_f32),
-    // rounded to bf16 pairs for the P.V product (pf), and this lane's sum of
-    // those bf16 weights -- the row sum adds the same values the product uses,
-    // so O is normalised by exactly its own weights.
-    auto weights = [&](int qb, float m, auto biasc) __attribute__((always_inline)) -> float {
-        constexpr bool BIASED = decltype(biasc)::value;   // S^T already holds s - moff/c: exponent = c * S^T
-        const float negm = -m;
-        f32x4 pv4[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float x = BIASED ? s_acc[kb][qb][r] * c
-                                       : (CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm));
-                pv4[kb][r] = __builtin_amdgcn_exp2f(x);
-            }
-        float tlo = 0.f, thi = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            bf16x2 pr[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const f32x4& src = pv4[2 * ks + (i >> 1)];
-                const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
-                pr[i] = weight_pair(two);
-                if (!MFMA_SUM) {
-                    // the two bf16 weights as fp32 (bit placement), summed with
-                    // plain adds: v_dot2c would wait for the matrix core a
-                    // co-resident wave keeps busy
-                    const uint32_t u = __builtin_bit_cast(uint32_t, pr[i]);
-                    tlo += __uint_as_float(u << 16);
-                    thi += __uint_as_float(u & 0xffff0000u);
-                }
-            }
-            const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
-            const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
-            pf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        return tlo + thi;
-    };
-    // ceil of the tile's largest x for query block qb (NaN-propagating
-    // v_maximum3_f32 in the lane, then across the 4 lanes of a row)
-    auto tile_max_ceil = [&](int qb) __attribute__((always_inline)) -> float {
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
-        mx = rowmax4(mx);
-        if (CPOS) mx *= c;
-        return ceilf(mx);
-    };
-    auto set_bias = [&](int qb) __attribute__((always_inline)) {
-        if (CPOS) {
-            const float bb = -moff[qb] * rc;
-            bias4[qb] = f32x4{bb, bb, bb, bb};
-        }
-    };
-
-    // ---- online softmax of S_t with a power-of-two running offset.
-    auto softmax = [&](int t, auto firstc) __attribute__((always_inline)) {
-        constexpr bool FIRST = decltype(firstc)::value;
-        const int valid = kv_end - (kv_begin + t * BN);   // keys of this tile inside the range
-        // Keys outside the range are masked by select, never by arithmetic:
-        // key 16*kb + 4*g + r of the tile is inside iff 16*kb + r < lim[qb],
-        // lim = valid - 4*g, and under the causal mask also key <= row + off.
-        // With c > 0 only a ragged last tile or a tile crossing this wave's
-        // diagonal needs it, and one branch covers both query blocks so the
-        // compares stay inside it.
-        const int ts = kv_begin + t * BN;              // first key of the tile
-        const bool diag = CAUSAL && ts + BN - 1 > qrow0 + coff;
-        int lim[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; qb++) {
-            lim[qb] = valid - 4 * g;
-            if (CAUSAL) lim[qb] = min(lim[qb], qrow0 + qb * 16 + j + coff - ts + 1 - 4 * g);
-        }
-        if (CPOS && (valid < BN || diag)) {
-#pragma unroll
-            for (int qb = 0; qb < NQB; qb++)
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        s_acc[kb][qb][r] = (16 * kb + r < lim[qb]) ? s_acc[kb][qb][r] : -__builtin_inff();
-        }
-        if (!CPOS) {
-            // general scale (c <= 0): x = s*c explicitly, masked keys -> -inf
-#pragma unroll
-            for (int qb = 0; qb < NQB; qb++)
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        s_acc[kb][qb][r] = (16 * kb + r < lim[qb]) ? s_acc[kb][qb][r] * c : -__builtin_inff();
-        }
-        if (FIRST) {
-            // first tile: the offset starts at ceil(max x) (0 for a row whose
-            // scores are all -inf or NaN; its weights are then 0 or NaN)
+    int vb = blockIdx.x;
+    bool prefetched = false;   // this item's Q and first K tile came with the previous item
+    for (;;) {
+        // The lane indices, from an opaque copy of the thread index: nothing
+        // derived from them (fragment and DMA addresses, row offsets) is
+        // hoisted out of the item loop and held across the key loop.
+        int tid = threadIdx.x;
+        if (PERSIST) __asm__ volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+        const int g = lane >> 4;       // lane group (0..3)
+        const int j = lane & 15;       // lane within group
+        auto load_q = [&](KParams& p, const uint16_t* qb_base, int qrow0) __attribute__((always_inline)) {
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) {
-                const float m = tile_max_ceil(qb);
-                moff[qb] = __builtin_isfinite(m) ? m : 0.f;
-                l_run[qb] = weights(qb, moff[qb], std::false_type{});
-                set_bias(qb);
+                const int row = min(qrow0 + qb * 16 + j, p.Sq - 1);
+                const uint16_t* src = qb_base + (int64_t)row * p.q_row + 8 * g;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++) qf[qb][ks] = *(const bf16x8*)(src + 32 * ks);
+            }
+        };
+        KParams& P = kernel_params<PERSIST>();
+        const Loc L = locate(P, vb);
+        const int kv_row_bytes = (int)(P.kv_row * 2);
+        const int item = L.item, split = L.split, nsplit = L.nsplit, qt = L.qt, b = L.b, h = L.h;
+        const int coff = L.coff, kv_begin = L.kv_begin, kv_end = L.kv_end;
+        const int T = (kv_end - kv_begin + BN - 1) / BN;
+
+        const uint16_t* qbase = P.q + (int64_t)b * P.q_batch + (int64_t)h * P.q_head;
+        const char* kbase = (const char*)(P.k + (int64_t)b * P.kv_batch + (int64_t)L.hk * P.kv_head);
+        const char* vbase = (const char*)(P.v + (int64_t)b * P.kv_batch + (int64_t)L.hk * P.kv_head);
+
+        if ((CAUSAL || KVL) && kv_end <= kv_begin) {
+            // No query row of the tile sees a key (a causal tile entirely above
+            // the diagonal, or a batch entry with no keys): its rows are zeros
+            // and their log-sum-exp is -inf.  Uniform across the work-group,
+            // before any barrier or DMA.
+            uint16_t* obase = P.o + (int64_t)b * P.q_batch + (int64_t)h * P.q_head;
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) {
+                const int row = qt * BM + wave * 16 * NQB + qb * 16 + j;
+                if (row >= P.Sq) continue;
+#pragma unroll
+                for (int db = 0; db < NDB; db++) *(uint2*)(obase + (int64_t)row * P.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
+                if (P.lse && g == 0) P.lse[((int64_t)b * P.H + h) * P.Sq + row] = -__builtin_inff();
             }
             return;
         }
-        // Later tiles: weights against the running offset, with no max.  A
-        // weight can exceed 2^16 only if its lane's tile sum does (with the
-        // MFMA row sums: only if the lane's largest exponent exceeds 16); then
-        // (rare: the row max moved far past the offset) the tile is redone with
-        // the offset at ceil(max) and O and l rescaled by the exact power of two.
-        float tsum[NQB];
-        bool big = false;
+
+        // The first four waves issue all K/V DMA: lane l of wave w in round r
+        // lands at LDS slot (4*r + w)*64 + l, i.e. row by row in order: row
+        // RPR*r + RPW*w + l / CPR, chunk l % CPR (CPR chunks per row, RPW rows per
+        // wave, RPR rows per round: 16, 4, 16 for HD = 128 and 8, 8, 32 for 64);
+        // rows RPR apart share the swizzle, so one per-lane source offset serves
+        // every round.  The DMA is issued with inline assembly:
+        // the compiler then does not track it and inserts no vmcnt wait before
+        // LDS reads of other buffers (its alias tracking is lost at loop heads);
+        // the issuing waves wait for their DMA explicitly (vmcnt(0)) before the
+        // barrier that publishes a tile.
+        const bool late = NW == 8 && wave >= 4;   // second wave of each SIMD (see the key loop)
+        constexpr int CPR = ROW_BYTES / 16, RPW = 64 / CPR, RPR = 4 * RPW;
+        constexpr int DMA_ROUNDS = BN / RPR;
+        static_assert(DMA_ROUNDS * RPR == BN && RPR % 16 == 0, "rounds of whole swizzle periods");
+        const int dma_row = (wave & 3) * RPW + lane / CPR, dma_chunk = lane % CPR;
+        const int dma_off_k = dma_row * kv_row_bytes + ((dma_chunk ^ swz_k<HD>(dma_row)) << 4);
+        const int dma_off_v = dma_row * kv_row_bytes + ((dma_chunk ^ swz_v<HD>(dma_row)) << 4);
+        const i32x4 krs4 = kv_rsrc(kbase, kv_end, kv_row_bytes), vrs4 = kv_rsrc(vbase, kv_end, kv_row_bytes);
+        auto dma16 = [&](const i32x4 rs, uint8_t* dst, int voff, int soff) __attribute__((always_inline)) {
+            // the LDS address, the descriptor and the tile offset are
+            // wave-uniform; say so, so they stay in scalar registers
+            const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
+            const int so = __builtin_amdgcn_readfirstlane(soff);
+            const i32x4 rsu = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                               __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
+            // m0 (the LDS destination) is written in the same statement as the
+            // load, so nothing is scheduled between the two; no other code of the
+            // kernel uses m0, which makes the clobber safe.  Handing the address
+            // in as an {m0} operand lets the compiler move the write away from
+            // the load, and that form gave wrong results here.  An LDS-bound
+            // buffer load reads m0 one wait state after a scalar write of it at
+            // the earliest (the compiler puts the same s_nop after its own m0
+            // write for the builtin form of this load); inline assembly is opaque
+            // to the hazard recognizer, so the statement carries the nop itself.
+            __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                             :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
+        };
+        // round r of the K (or V) tile that starts at key k0
+        auto dma_k = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
+            dma16(krs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 + RPR * r) * kv_row_bytes);
+        };
+        auto dma_v = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
+            dma16(vrs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 + RPR * r) * kv_row_bytes);
+        };
+        const int qrow0 = qt * BM + wave * 16 * NQB;   // first query row of this wave
+        if (!prefetched) {
+            if (!late) {
+#pragma unroll
+                for (int r = 0; r < DMA_ROUNDS; r++) dma_k(r, kv_begin, sk0);
+            }
+            load_q(P, qbase, qrow0);
+        }
+        f32x4 o_acc[NDB][NQB];
+#pragma unroll
+        for (int db = 0; db < NDB; db++)
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float moff[NQB], l_run[NQB];    // power-of-two offset of the weights (integer-valued), row-sum partials
+        f32x4 l_acc[NQB];               // MFMA_SUM: row sums, every element the lane's query
+        f32x4 bias4[NQB];               // c > 0: S^T accumulates from -moff/c, so c * S^T = x - moff
 #pragma unroll
         for (int qb = 0; qb < NQB; qb++) {
-            if (MFMA_SUM) {
-                float mx = -__builtin_inff();
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
-                big |= (CPOS ? mx * c : mx - moff[qb]) > 16.0f;
-            }
-            tsum[qb] = weights(qb, moff[qb], std::integral_constant<bool, CPOS>{});
-            if (!MFMA_SUM) big |= tsum[qb] > WEIGHT_LIMIT;
+            moff[qb] = 0.f; l_run[qb] = 0.f;
+            bias4[qb] = f32x4{0.f, 0.f, 0.f, 0.f}; l_acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (__builtin_amdgcn_ballot_w64(big) != 0) {
-            float alpha[NQB];
+        const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                              (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+        const float rc = 1.0f / P.c;
+        f32x4 s_acc[4][NQB];
+        bf16x8 pf[NQB][2];
+        const float c = P.c;
+
+        // ---- MFMA phase: steps [S0, S1) of a fixed sequence of ST fragment steps.
+        // Steps 0..SS-1 compute S^T = K Q^T: step 4*ks + kb reads the K fragment of
+        // key block kb, k-step ks (one ds_read_b128: lane (g, j) gets row 16*kb + j,
+        // dims 32*ks + 8*g .. +7) and feeds NQB MFMAs; k-steps are the outer index
+        // so consecutive MFMAs hit different accumulators.  The score fragment of
+        // lane (g, j) then holds query j and keys 16*kb + 4*g + r, r = 0..3.
+        // Steps SS..ST-1 compute O^T += V^T P^T: step SS + NDB*ks + db reads the
+        // V^T fragment of dim block db for the 32 keys of step ks with two
+        // ds_read_b64_tr_b16 (rows 32*ks + 16*hf + 4*g + r), matching the keys
+        // of P's elements 4*hf + r.  Fragment reads run PF steps ahead of their
+        // MFMAs so LDS latency hides behind the matrix core.
+        int k_addr[NKS], v_addr[NDB];   // per-lane byte offsets within a tile
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++) k_addr[ks] = j * ROW_BYTES + ((((4 * ks + g) ^ swz_k<HD>(j))) << 4);
+#pragma unroll
+        for (int db = 0; db < NDB; db++) {
+            const int row = 4 * g + (j >> 2);                    // + 32*ks + 16*hf (multiples of 8)
+            const int chunk = (2 * db + ((j & 3) >> 1)) ^ swz_v<HD>(row);
+            v_addr[db] = row * ROW_BYTES + (chunk << 4) + ((j & 1) << 3);
+        }
+        auto read_frag = [&](int st, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) -> bf16x8 {
+            if (st < SS) {
+                const int kb = st & 3, ks = st >> 2;
+                return *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(kt + k_addr[ks] + kb * 16 * ROW_BYTES);
+            }
+            const int db = (st - SS) % NDB, ks = (st - SS) / NDB;
+            bf16x4 half[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; hf++) {
+                const LDS_AS s16x4* src = (const LDS_AS s16x4*)(LDS_AS const uint8_t*)(vt + v_addr[db] + (32 * ks + 16 * hf) * ROW_BYTES);
+                half[hf] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)src));
+            }
+            return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        auto use_frag = [&](int st, const bf16x8 f) __attribute__((always_inline)) {
+            if (st < SS) {
+                const int kb = st & 3, ks = st >> 2;
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++)
+                    s_acc[kb][qb] = mfma16x16x32(f, qf[qb][ks], ks == 0 ? (CPOS ? bias4[qb] : f32x4{0.f, 0.f, 0.f, 0.f}) : s_acc[kb][qb]);
+            } else {
+                const int db = (st - SS) % NDB, ks = (st - SS) / NDB;
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] = mfma16x16x32(f, pf[qb][ks], o_acc[db][qb]);
+                if (MFMA_SUM && db == NDB - 1) {
+                    // ones^T P^T: every lane gets the sum of the step's 32 bf16
+                    // weights of its query (exact products, fp32 sums)
+#pragma unroll
+                    for (int qb = 0; qb < NQB; qb++) l_acc[qb] = mfma16x16x32(ones8, pf[qb][ks], l_acc[qb]);
+                }
+            }
+        };
+        constexpr int PF = 4;   // fragment prefetch distance (steps)
+        // The DMA of iteration t (K_{t+1} into kn, V_t into vc) is spread over the
+        // issuing waves' MFMA phase, one instruction every STRIDE steps, so the
+        // CU's address unit drains it while the matrix core runs instead of
+        // stalling a wave that issues all of it at once.
+        constexpr int NDMA = 2 * DMA_ROUNDS;   // instructions per wave and tile
+        // The phase has no branch: the issuing group is a compile-time choice
+        // (LATE), and past the last tile the K DMA re-reads that tile into the
+        // free buffer, so the scheduler sees the whole phase as one region.
+        auto mfma_phase = [&](const uint8_t* kt, const uint8_t* vt, auto s0c, auto s1c, int t, uint8_t* kn, uint8_t* vc,
+                              auto latec) __attribute__((always_inline)) {
+            constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
+            constexpr bool LATE = decltype(latec)::value;
+            constexpr int STRIDE = (S1 - S0) / NDMA;
+            static_assert(S0 != 0 || STRIDE * NDMA <= S1 - S0, "the DMA fits the phase");
+            // Opaque per-lane offsets: stops the compiler from hoisting every
+            // buffer x fragment address combination out of the loop (and spilling
+            // them); each phase adds its buffer base to these offsets instead.
+#pragma unroll
+            for (int i = 0; i < NKS; i++) __asm__ volatile("" : "+v"(k_addr[i]));
+#pragma unroll
+            for (int i = 0; i < NDB; i++) __asm__ volatile("" : "+v"(v_addr[i]));
+            bf16x8 fr[PF];
+#pragma unroll
+            for (int st = S0; st < S0 + PF && st < S1; st++) fr[(st - S0) % PF] = read_frag(st, kt, vt);
+#pragma unroll
+            for (int st = S0; st < S1; st++) {
+                const bf16x8 cur = fr[(st - S0) % PF];
+                if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
+                if (S0 == 0 && (st - S0) % STRIDE == 0 && (st - S0) / STRIDE < NDMA && !LATE) {
+                    const int k = (st - S0) / STRIDE;     // K and V rounds alternate
+                    if (k & 1) dma_v(k >> 1, kv_begin + t * BN, vc);
+                    else dma_k(k >> 1, kv_begin + min(t + 1, T - 1) * BN, kn);
+                }
+                use_frag(st, cur);
+            }
+            // keep the interleave: the reads of step st+PF, then the MFMAs of step st
+#pragma unroll
+            for (int st = S0; st < S0 + PF && st < S1; st++) {
+                if (st < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+#pragma unroll
+            for (int st = S0; st < S1; st++) {
+                if (st + PF < S1) {
+                    if (st + PF < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                if (MFMA_SUM && st >= SS && (st - SS) % NDB == NDB - 1) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);
+                else __builtin_amdgcn_sched_group_barrier(0x008, NQB, 0);
+            }
+        };
+        using C0 = std::integral_constant<int, 0>;
+        using CS = std::integral_constant<int, SS>;
+        using CT = std::integral_constant<int, ST>;
+
+        // Two weights (>= 0, or NaN) to packed bf16 in the weights' rounding mode.
+        // Nearest-even: the hardware conversion.  Ties away: the same conversion
+        // after setting the lowest fp32 bit, which turns an exact tie into a value
+        // just above it and changes no other decision (an infinite weight would
+        // become NaN, but it only arises in rows whose output is NaN anyway).
+        // Toward zero: the high half of the bit pattern, after clamping every NaN
+        // to the canonical one so truncation cannot make it an infinity.
+        auto weight_pair = [&](const f32x2 two) __attribute__((always_inline)) -> bf16x2 {
+            if (PMODE == ROUND_RTNE) return __builtin_convertvector(two, bf16x2);
+            if (PMODE == ROUND_RTNA) {
+                const f32x2 up = {__uint_as_float(__float_as_uint(two[0]) | 1u), __uint_as_float(__float_as_uint(two[1]) | 1u)};
+                return __builtin_convertvector(up, bf16x2);
+            }
+            const uint32_t u0 = min(__float_as_uint(two[0]), 0x7fc00000u);
+            const uint32_t u1 = min(__float_as_uint(two[1]), 0x7fc00000u);
+            return __builtin_bit_cast(bf16x2, (u1 & 0xffff0000u) | (u0 >> 16));
+        };
+        // Weights of query block qb against offset m: p = 2^(x - m) (v_exp_f32),
+        // rounded to bf16 pairs for the P.V product (pf), and this lane's sum of
+        // those bf16 weights -- the row sum adds the same values the product uses,
+        // so O is normalised by exactly its own weights.
+        auto weights = [&](int qb, float m, auto biasc) __attribute__((always_inline)) -> float {
+            constexpr bool BIASED = decltype(biasc)::value;   // S^T already holds s - moff/c: exponent = c * S^T
+            const float negm = -m;
+            f32x4 pv4[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float x = BIASED ? s_acc[kb][qb][r] * c
+                                           : (CPOS ? __builtin_fmaf(s_acc[kb][qb][r], c, negm) : (s_acc[kb][qb][r] + negm));
+                    pv4[kb][r] = __builtin_amdgcn_exp2f(x);
+                }
+            float tlo = 0.f, thi = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                bf16x2 pr[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const f32x4& src = pv4[2 * ks + (i >> 1)];
+                    const f32x2 two = {src[2 * (i & 1)], src[2 * (i & 1) + 1]};
+                    pr[i] = weight_pair(two);
+                    if (!MFMA_SUM) {
+                        // the two bf16 weights as fp32 (bit placement), summed with
+                        // plain adds: v_dot2c would wait for the matrix core a
+                        // co-resident wave keeps busy
+                        const uint32_t u = __builtin_bit_cast(uint32_t, pr[i]);
+                        tlo += __uint_as_float(u << 16);
+                        thi += __uint_as_float(u & 0xffff0000u);
+                    }
+                }
+                const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
+                const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
+                pf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            return tlo + thi;
+        };
+        // ceil of the tile's largest x for query block qb (NaN-propagating
+        // v_maximum3_f32 in the lane, then across the 4 lanes of a row)
+        auto tile_max_ceil = [&](int qb) __attribute__((always_inline)) -> float {
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
+            mx = rowmax4(mx);
+            if (CPOS) mx *= c;
+            return ceilf(mx);
+        };
+        auto set_bias = [&](int qb) __attribute__((always_inline)) {
+            if (CPOS) {
+                const float bb = -moff[qb] * rc;
+                bias4[qb] = f32x4{bb, bb, bb, bb};
+            }
+        };
+
+        // ---- online softmax of S_t with a power-of-two running offset.
+        auto softmax = [&](int t, auto firstc) __attribute__((always_inline)) {
+            constexpr bool FIRST = decltype(firstc)::value;
+            const int valid = kv_end - (kv_begin + t * BN);   // keys of this tile inside the range
+            // Keys outside the range are masked by select, never by arithmetic:
+            // key 16*kb + 4*g + r of the tile is inside iff 16*kb + r < lim[qb],
+            // lim = valid - 4*g, and under the causal mask also key <= row + off.
+            // With c > 0 only a ragged last tile or a tile crossing this wave's
+            // diagonal needs it, and one branch covers both query blocks so the
+            // compares stay inside it.
+            const int ts = kv_begin + t * BN;              // first key of the tile
+            const bool diag = CAUSAL && ts + BN - 1 > qrow0 + coff;
+            int lim[NQB];
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) {
-                // with c > 0 the scores hold s - moff/c: x = c * S^T + moff
-                const float m_new = fmaxf(moff[qb], tile_max_ceil(qb) + (CPOS ? moff[qb] : 0.f));
-                alpha[qb] = ldexpf(1.0f, (int)fmaxf(moff[qb] - m_new, -200.f));
-                tsum[qb] = weights(qb, CPOS ? m_new - moff[qb] : m_new, std::false_type{});
-                moff[qb] = m_new;
-                set_bias(qb);
-                l_run[qb] *= alpha[qb];
-                l_acc[qb] *= alpha[qb];
+                lim[qb] = valid - 4 * g;
+                if (CAUSAL) lim[qb] = min(lim[qb], qrow0 + qb * 16 + j + coff - ts + 1 - 4 * g);
+            }
+            if (CPOS && (valid < BN || diag)) {
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++)
+#pragma unroll
+                    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            s_acc[kb][qb][r] = (16 * kb + r < lim[qb]) ? s_acc[kb][qb][r] : -__builtin_inff();
+            }
+            if (!CPOS) {
+                // general scale (c <= 0): x = s*c explicitly, masked keys -> -inf
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++)
+#pragma unroll
+                    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++)
+                            s_acc[kb][qb][r] = (16 * kb + r < lim[qb]) ? s_acc[kb][qb][r] * c : -__builtin_inff();
+            }
+            if (FIRST) {
+                // first tile: the offset starts at ceil(max x) (0 for a row whose
+                // scores are all -inf or NaN; its weights are then 0 or NaN)
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++) {
+                    const float m = tile_max_ceil(qb);
+                    moff[qb] = __builtin_isfinite(m) ? m : 0.f;
+                    l_run[qb] = weights(qb, moff[qb], std::false_type{});
+                    set_bias(qb);
+                }
+                return;
+            }
+            // Later tiles: weights against the running offset, with no max.  A
+            // weight can exceed 2^16 only if its lane's tile sum does (with the
+            // MFMA row sums: only if the lane's largest exponent exceeds 16); then
+            // (rare: the row max moved far past the offset) the tile is redone with
+            // the offset at ceil(max) and O and l rescaled by the exact power of two.
+            float tsum[NQB];
+            bool big = false;
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) {
+                if (MFMA_SUM) {
+                    float mx = -__builtin_inff();
+#pragma unroll
+                    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++) mx = __builtin_elementwise_maximum(mx, s_acc[kb][qb][r]);
+                    big |= (CPOS ? mx * c : mx - moff[qb]) > 16.0f;
+                }
+                tsum[qb] = weights(qb, moff[qb], std::integral_constant<bool, CPOS>{});
+                if (!MFMA_SUM) big |= tsum[qb] > WEIGHT_LIMIT;
+            }
+            if (__builtin_amdgcn_ballot_w64(big) != 0) {
+                float alpha[NQB];
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++) {
+                    // with c > 0 the scores hold s - moff/c: x = c * S^T + moff
+                    const float m_new = fmaxf(moff[qb], tile_max_ceil(qb) + (CPOS ? moff[qb] : 0.f));
+                    alpha[qb] = ldexpf(1.0f, (int)fmaxf(moff[qb] - m_new, -200.f));
+                    tsum[qb] = weights(qb, CPOS ? m_new - moff[qb] : m_new, std::false_type{});
+                    moff[qb] = m_new;
+                    set_bias(qb);
+                    l_run[qb] *= alpha[qb];
+                    l_acc[qb] *= alpha[qb];
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; db++)
+#pragma unroll
+                    for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] *= alpha[qb];
             }
 #pragma unroll
-            for (int db = 0; db < NDB; db++)
-#pragma unroll
-                for (int qb = 0; qb < NQB; qb++) o_acc[db][qb] *= alpha[qb];
-        }
-#pragma unroll
-        for (int qb = 0; qb < NQB; qb++) l_run[qb] += tsum[qb];
-    };
+            for (int qb = 0; qb < NQB; qb++) l_run[qb] += tsum[qb];
+        };
 
-    // ---- key loop: one barrier per tile.  Iteration t computes S_t = K_t Q^T
-    // and O += V_{t-1}^T P_{t-1}^T (with the DMA of K_{t+1} into the buffer
-    // K_{t-1} used and of V_t into V_{t-2}'s), then the softmax of S_t; the
-    // issuing waves wait for their DMA before the barrier.  Iteration 0 has
-    // no P.V step and iteration T (past the last tile) only the P.V step; the
-    // steady-state loop in between is branch-free in vector state, which
-    // keeps the accumulators in place.
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's K_0 slice and its Q landed
-    lds_barrier();
-    // Waves w and w + 4 share a SIMD.  The second group takes the barrier
-    // between its MFMA phase and its softmax instead of after the softmax, so
-    // between two barriers it runs the softmax of S_{t-1} and then the MFMA
-    // phase of tile t while the first group runs the MFMA phase of tile t and
-    // then the softmax of S_t: the two waves of a SIMD are in opposite phases
-    // and one's softmax fills the gaps of the other's MFMAs.  Both groups
-    // read K_t and V_{t-1} between the same two barriers, so the buffer
-    // protocol is the same for both.
-    auto sync = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);
+        // ---- key loop: one barrier per tile.  Iteration t computes S_t = K_t Q^T
+        // and O += V_{t-1}^T P_{t-1}^T (with the DMA of K_{t+1} into the buffer
+        // K_{t-1} used and of V_t into V_{t-2}'s), then the softmax of S_t; the
+        // issuing waves wait for their DMA before the barrier.  Iteration 0 has
+        // no P.V step and iteration T (past the last tile) only the P.V step; the
+        // steady-state loop in between is branch-free in vector state, which
+        // keeps the accumulators in place.  Before it, this wave's share of K_0
+        // and its Q have landed (a prefetched item's before the previous item's
+        // stores, so no store is waited for here) and the barrier publishes K_0.
+        if (!prefetched) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         lds_barrier();
-    };
-    auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c, auto latec) __attribute__((always_inline)) {
-        constexpr bool LATE = decltype(latec)::value;
-        // A wave in its MFMA phase takes issue priority over one in its
-        // softmax, so the matrix core of a SIMD stays fed; the softmax VALU
-        // work fills the MFMA phase's gaps.
-        __builtin_amdgcn_s_setprio(1);
-        mfma_phase(kc, vp, s0c, s1c, t, kn, vc, latec);
-        __builtin_amdgcn_s_setprio(0);
-        if (LATE) sync();
-        if (decltype(s0c)::value == 0)
-            softmax(t, std::integral_constant<bool, decltype(s1c)::value == SS>{});
-        if (!LATE) sync();
-    };
-    // the key loop, compiled once per wave group
-    auto key_loop = [&](auto latec) __attribute__((always_inline)) {
-        iter(0, sk0, sk1, sv0, sv1, C0{}, CS{}, latec);
-        int t = 1;
-        for (; t + 1 < T; t += 2) {
-            iter(t, sk1, sk0, sv1, sv0, C0{}, CT{}, latec);
-            iter(t + 1, sk0, sk1, sv0, sv1, C0{}, CT{}, latec);
-        }
-        if (t < T) {
-            iter(t, sk1, sk0, sv1, sv0, C0{}, CT{}, latec);
-            t++;
-        }
-        if (T & 1) iter(T, sk1, sk0, sv1, sv0, CS{}, CT{}, latec);
-        else iter(T, sk0, sk1, sv0, sv1, CS{}, CT{}, latec);
-    };
-    if (late) key_loop(std::true_type{});
-    else key_loop(std::false_type{});
-
-    // ---- epilogue: the 4 lanes of a row hold partial row sums
-    float l_row[NQB];
+        // Waves w and w + 4 share a SIMD.  The second group takes the barrier
+        // between its MFMA phase and its softmax instead of after the softmax, so
+        // between two barriers it runs the softmax of S_{t-1} and then the MFMA
+        // phase of tile t while the first group runs the MFMA phase of tile t and
+        // then the softmax of S_t: the two waves of a SIMD are in opposite phases
+        // and one's softmax fills the gaps of the other's MFMAs.  Both groups
+        // read K_t and V_{t-1} between the same two barriers, so the buffer
+        // protocol is the same for both.
+        auto sync = [&]() __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+            lds_barrier();
+        };
+        auto iter = [&](int t, uint8_t* kc, uint8_t* kn, uint8_t* vc, uint8_t* vp, auto s0c, auto s1c, auto latec) __attribute__((always_inline)) {
+            constexpr bool LATE = decltype(latec)::value;
+            // A wave in its MFMA phase takes issue priority over one in its
+            // softmax, so the matrix core of a SIMD stays fed; the softmax VALU
+            // work fills the MFMA phase's gaps.
+            __builtin_amdgcn_s_setprio(1);
+            mfma_phase(kc, vp, s0c, s1c, t, kn, vc, latec);
+            __builtin_amdgcn_s_setprio(0);
+            // The last iteration (P.V only) ends without a barrier: no LDS
+            // buffer is written after it before the next item's first barrier.
+            constexpr bool LAST = decltype(s0c)::value != 0;
+            if (LATE && !LAST) sync();
+            if (!LAST)
+                softmax(t, std::integral_constant<bool, decltype(s1c)::value == SS>{});
+            if (!LATE && !LAST) sync();
+        };
+        // The next block of a persistent work-group: its Q fragments (this item's
+        // are dead during the last iteration, which only runs the P.V product)
+        // and, from the issuing waves, its first K tile into sk0 (no K buffer is
+        // read in the last iteration).
+        auto prefetch_next = [&]() __attribute__((always_inline)) {
+            KParams& PN = kernel_params<true>();
+            const int nv = vb + PN.grid;
+            if (nv >= PN.n_blocks) return;
+            const Loc N = locate(PN, nv);
+            const uint16_t* nq = PN.q + (int64_t)N.b * PN.q_batch + (int64_t)N.h * PN.q_head;
+            if (!late) {
+                const char* nk = (const char*)(PN.k + (int64_t)N.b * PN.kv_batch + (int64_t)N.hk * PN.kv_head);
+                const i32x4 nrs = kv_rsrc(nk, N.kv_end, (int)(PN.kv_row * 2));
 #pragma unroll
-    for (int qb = 0; qb < NQB; qb++) l_row[qb] = MFMA_SUM ? l_acc[qb][0] : rowsum4(l_run[qb]);
+                for (int r = 0; r < DMA_ROUNDS; r++)
+                    dma16(nrs, sk0 + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (N.kv_begin + RPR * r) * kv_row_bytes);
+            }
+            load_q(PN, nq, N.qt * BM + wave * 16 * NQB);
+        };
+        // the key loop, compiled once per wave group
+        auto key_loop = [&](auto latec) __attribute__((always_inline)) {
+            iter(0, sk0, sk1, sv0, sv1, C0{}, CS{}, latec);
+            int t = 1;
+            for (; t + 1 < T; t += 2) {
+                iter(t, sk1, sk0, sv1, sv0, C0{}, CT{}, latec);
+                iter(t + 1, sk0, sk1, sv0, sv1, C0{}, CT{}, latec);
+            }
+            if (t < T) {
+                iter(t, sk1, sk0, sv1, sv0, C0{}, CT{}, latec);
+                t++;
+            }
+            // the last iteration reads neither Q nor a K buffer: the next item's
+            // Q fragments and first K tile are fetched under it
+            if (PERSIST) prefetch_next();
+            if (T & 1) iter(T, sk1, sk0, sv1, sv0, CS{}, CT{}, latec);
+            else iter(T, sk0, sk1, sv0, sv1, CS{}, CT{}, latec);
+        };
+        if (late) key_loop(std::true_type{});
+        else key_loop(std::false_type{});
 
-    if (nsplit == 1) {
-        if (p.lse && g == 0) {
-            // log-sum-exp of the row's scaled scores: sum_j 2^x_j = l * 2^moff
+        // ---- epilogue: the 4 lanes of a row hold partial row sums
+        float l_row[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; qb++) l_row[qb] = MFMA_SUM ? l_acc[qb][0] : rowsum4(l_run[qb]);
+
+        // A persistent work-group's loads for the next item (issued in the last
+        // iteration) complete before this item's stores enter the same counter,
+        // so the next item's first barrier waits for no store.
+        if (PERSIST) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        if (nsplit == 1) {
+            if (P.lse && g == 0) {
+#pragma unroll
+                for (int qb = 0; qb < NQB; qb++) {
+                    const int row = qrow0 + qb * 16 + j;
+                    if (row >= P.Sq) continue;
+                    float v = (moff[qb] + __builtin_amdgcn_logf(l_row[qb])) * LN2;
+                    if (CAUSAL && row + coff < 0) v = -__builtin_inff();
+                    P.lse[((int64_t)b * P.H + h) * P.Sq + row] = v;
+                }
+            }
+            uint16_t* obase = P.o + (int64_t)b * P.q_batch + (int64_t)h * P.q_head;
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) {
                 const int row = qrow0 + qb * 16 + j;
-                if (row >= p.Sq) continue;
-                float v = (moff[qb] + __builtin_amdgcn_logf(l_row[qb])) * LN2;
-                if (CAUSAL && row + coff < 0) v = -__builtin_inff();   // sees no key
-                p.lse[((int64_t)b * p.H + h) * p.Sq + row] = v;
+                if (row >= P.Sq) continue;
+                const float lr = l_row[qb];
+                const float inv = 1.0f / lr;
+                const bool no_key = CAUSAL && row + coff < 0;
+                uint16_t* dst = obase + (int64_t)row * P.q_row + 4 * g;
+#pragma unroll
+                for (int db = 0; db < NDB; db++) {
+                    f32x4 ov;
+#pragma unroll
+                    for (int r = 0; r < 4; r++) ov[r] = no_key ? 0.f : div_corrected(o_acc[db][qb][r], lr, inv);
+                    const uint32_t b0 = to_bf16_bits(ov[0], P.round_mode), b1 = to_bf16_bits(ov[1], P.round_mode);
+                    const uint32_t b2 = to_bf16_bits(ov[2], P.round_mode), b3 = to_bf16_bits(ov[3], P.round_mode);
+                    uint2 packed;
+                    packed.x = b0 | (b1 << 16);
+                    packed.y = b2 | (b3 << 16);
+                    *(uint2*)(dst + 16 * db) = packed;
+                }
+            }
+        } else {
+            // partial results: O (unnormalised, fp32) [item][split][BM][HD], M and l [item][split][BM]
+            // (items counted from n_full)
+            const int64_t part = (int64_t)(item - P.n_full) * nsplit + split;
+            float* ow = P.ws_o + part * (int64_t)BM * HD;
+            float* mw = P.ws_ml + part * (int64_t)BM * 2;
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++) {
+                const int lrow = wave * 16 * NQB + qb * 16 + j;   // row within the tile
+#pragma unroll
+                for (int db = 0; db < NDB; db++) *(f32x4*)(ow + (int64_t)lrow * HD + 16 * db + 4 * g) = o_acc[db][qb];
+                if (g == 0) {
+                    mw[2 * lrow] = moff[qb];
+                    mw[2 * lrow + 1] = l_row[qb];
+                }
             }
         }
-        uint16_t* obase = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head;
-#pragma unroll
-        for (int qb = 0; qb < NQB; qb++) {
-            const int row = qrow0 + qb * 16 + j;
-            if (row >= p.Sq) continue;
-            const float lr = l_row[qb];
-            const float inv = 1.0f / lr;
-            // a causal row that sees no key at all (Sq > Skv) is zeros
-            const bool no_key = CAUSAL && row + coff < 0;
-            uint16_t* dst = obase + (int64_t)row * p.q_row + 4 * g;
-#pragma unroll
-            for (int db = 0; db < NDB; db++) {
-                f32x4 ov;
-#pragma unroll
-                for (int r = 0; r < 4; r++) ov[r] = no_key ? 0.f : div_corrected(o_acc[db][qb][r], lr, inv);
-                const uint32_t b0 = to_bf16_bits(ov[0], p.round_mode), b1 = to_bf16_bits(ov[1], p.round_mode);
-                const uint32_t b2 = to_bf16_bits(ov[2], p.round_mode), b3 = to_bf16_bits(ov[3], p.round_mode);
-                uint2 packed;
-                packed.x = b0 | (b1 << 16);
-                packed.y = b2 | (b3 << 16);
-                *(uint2*)(dst + 16 * db) = packed;
-            }
-        }
-    } else {
-        // partial results: O (unnormalised, fp32) [item][split][BM][HD], M and l [item][split][BM]
-        // (items counted from n_full)
-        const int64_t part = (int64_t)(item - p.n_full) * nsplit + split;
-        float* ow = p.ws_o + part * (int64_t)BM * HD;
-        float* mw = p.ws_ml + part * (int64_t)BM * 2;
-#pragma unroll
-        for (int qb = 0; qb < NQB; qb++) {
-            const int lrow = wave * 16 * NQB + qb * 16 + j;   // row within the tile
-#pragma unroll
-            for (int db = 0; db < NDB; db++) *(f32x4*)(ow + (int64_t)lrow * HD + 16 * db + 4 * g) = o_acc[db][qb];
-            if (g == 0) {
-                mw[2 * lrow] = moff[qb];
-                mw[2 * lrow + 1] = l_row[qb];
-            }
-        }
+        if (!PERSIST) break;
+        vb += P.grid;
+        if (vb >= P.n_blocks) break;
+        prefetched = true;
     }
 #endif
 }
@@ -833,7 +912,7 @@ int launch(const AttnParams& p, hipStream_t stream) {
     // 4-wave work-group exists for head dimension 128 without the causal mask.
     const bool short_wg = p.nw == KERNEL_NW_SHORT;
     if (p.nw != KERNEL_NW && !(short_wg && p.head_dim == 128 && !p.causal)) return -1;
-    dim3 grid(p.n_blocks), block(p.nw * 64);
+    dim3 grid(p.grid), block(p.nw * 64);
     auto go_kv = [&](auto hd, auto cpos, auto causal, auto kvl, auto nw) {
         constexpr int H_ = decltype(hd)::value, N_ = decltype(nw)::value;
         constexpr bool CP = decltype(cpos)::value, CA = decltype(causal)::value, KV = decltype(kvl)::value;

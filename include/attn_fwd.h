@@ -127,13 +127,18 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
  * not exceed the number of 64-key tiles, n <= 64).  block_order: 0 =
  * planner's choice (XCD-aware), 1 = naive (work item = block id), 2 =
  * XCD-aware.  waves: 0 = planner's choice, 8 or 4 waves per work-group.
- * Other values return ATTN_ERR_OPTION.  The result does not depend on
- * block_order or waves; it may differ in the last bits with kv_splits.
+ * grid: 0 = planner's choice (an 8-wave plan of more work-groups than the
+ * GPU holds at once runs on a persistent grid of one work-group per CU,
+ * each taking every grid-th block of the plan); n >= 1 = at most n 8-wave
+ * work-groups (n rounded down to a multiple of 8, at least 8; 4-wave
+ * work-groups always run one per block).  Other values return
+ * ATTN_ERR_OPTION.  The result does not depend on block_order, waves or
+ * grid; it may differ in the last bits with kv_splits.
  */
 int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
                      int layout, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                      float scale, int round_mode, void* stream,
-                     int kv_splits, int block_order, int waves);
+                     int kv_splits, int block_order, int waves, int grid);
 
 /*
  * attn_fwd_bf16_gqa -- attn_fwd_bf16 with grouped-query heads and an optional

@@ -45,10 +45,10 @@ FAKE = 1 << 40   # 16-byte aligned, never dereferenced: validation fails first
 
 def call(**kw):
     a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), layout=0, B=1, H=2,
-             Sq=64, Skv=64, scale=0.088, mode=0, stream=0, splits=0, order=0, waves=0)
+             Sq=64, Skv=64, scale=0.088, mode=0, stream=0, splits=0, order=0, waves=0, grid=0)
     a.update(kw)
     return attn_fwd_bf16_raw(a["q"], a["k"], a["v"], a["o"], a["layout"], a["B"], a["H"], a["Sq"], a["Skv"],
-                             a["scale"], a["mode"], a["stream"], a["splits"], a["order"], a["waves"])
+                             a["scale"], a["mode"], a["stream"], a["splits"], a["order"], a["waves"], a["grid"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -58,7 +58,7 @@ def call(**kw):
     (dict(Skv=-5), -4), (dict(Sq=1 << 40), -4), (dict(scale=math.nan), -5), (dict(scale=math.inf), -5),
     (dict(q=FAKE + 8), -6), (dict(o=FAKE + (3 << 30) + 2), -6), (dict(o=FAKE), -7),
     (dict(o=FAKE + 64 * 2 * 128 * 2 - 16), -7), (dict(splits=65), -11), (dict(order=3), -11),
-    (dict(waves=3), -11), (dict(waves=16), -11), (dict(waves=-4), -11), (dict(waves=2), -11),
+    (dict(waves=3), -11), (dict(waves=16), -11), (dict(waves=-4), -11), (dict(waves=2), -11), (dict(grid=-1), -11),
 ])
 def test_argument_errors_before_device(kw, code):
     assert call(**kw) == code

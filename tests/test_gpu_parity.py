@@ -169,3 +169,25 @@ def test_xcd_and_naive_block_order_agree_bitwise():
     a = run_hip(q, k, v, "bshd", block_order=1)
     b = run_hip(q, k, v, "bshd", block_order=2)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("shape,kw", [
+    ((2, 3, 1100, 333), dict(grid=8, waves=8)),              # 30 items split by the planner, ragged tails
+    ((2, 3, 1100, 333), dict(grid=24, waves=8)),
+    ((2, 3, 1100, 333), dict(grid=16, waves=8, kv_splits=3, block_order=1)),
+    ((1, 75, 1024, 640), dict(grid=64, waves=8)),            # 256 whole items and a split ragged round
+    ((1, 40, 1500, 2100), dict(grid=8)),                     # 8 waves by the planner's choice
+    ((1, 75, 1024, 640), dict(grid=8, waves=4)),             # 4-wave groups: one per block regardless
+])
+def test_persistent_grid_agrees_bitwise(shape, kw):
+    """A grid of fewer 8-wave work-groups than the plan's blocks, each
+    walking every grid-th block and fetching the next one's Q and first K
+    tile under its current item's last iteration, gives the bits of one
+    block per work-group: whole and split blocks, ragged tails."""
+    B, H, Sq, Skv = shape
+    say(f"[case] persistent grid {shape} {kw}")
+    q, k, v = wl.random_qkv("bshd", B, H, Sq, Skv, 93)
+    base = {x: y for x, y in kw.items() if x != "grid"}
+    a = run_hip(q, k, v, "bshd", **base, grid=1 << 30)      # one block per work-group
+    b = run_hip(q, k, v, "bshd", **kw)
+    assert np.array_equal(a, b)

@@ -108,7 +108,7 @@ def test_plain_c_entry_point_matches_the_extended_one():
             assert rc == 0, rc
             rc = lib.attn_fwd_bf16_ex(ctypes.c_void_p(qd.data_ptr()), ctypes.c_void_p(kd.data_ptr()),
                                       ctypes.c_void_p(vd.data_ptr()), ctypes.c_void_p(ob.data_ptr()), layout, B, H,
-                                      Sq, Skv, ctypes.c_float(wl.DEFAULT_SCALE), m, ctypes.c_void_p(stream), 0, 0, 0)
+                                      Sq, Skv, ctypes.c_float(wl.DEFAULT_SCALE), m, ctypes.c_void_p(stream), 0, 0, 0, 0)
             assert rc == 0, rc
             torch.cuda.synchronize()
             assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), (B, H, Sq, Skv, m)
