@@ -457,9 +457,10 @@ extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const 
     p.causal_off = (int)(Skv - Sq);
     p.head_dim = (int)head_dim;
     void* ws = nullptr;
-    const int wrc = get_workspace(dev, stream, (size_t)n_q * sizeof(float), &ws);
+    const int wrc = get_workspace(dev, stream, 2 * (size_t)n_q * sizeof(float), &ws);
     if (wrc != ATTN_OK) return wrc;
     p.delta = (float*)ws;
+    p.lse2 = (float*)ws + n_q;
     if (attn_bwd::launch_bwd(p, (hipStream_t)stream) != 0) return ATTN_ERR_LAUNCH;
     return ATTN_OK;
 }

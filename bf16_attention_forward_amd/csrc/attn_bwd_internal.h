@@ -12,7 +12,8 @@ struct BwdParams {
     const uint16_t* o;    // forward output
     const uint16_t* dO;   // gradient of the output
     const float* lse;     // [B][H][Sq] forward log-sum-exp (natural log)
-    float* delta;         // [B][H][Sq] workspace: <dO_i, O_i>
+    float* delta;         // [B][H][Sq] workspace: -<dO_i, O_i> (negated: the dP products start from it)
+    float* lse2;          // [B][H][Sq] workspace: lse * log2(e)
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;

@@ -9,7 +9,9 @@
 //     dS = P o (dP - delta),   delta_i = <dO_i, O_i>,
 //     dQ = scale dS K,         dK = scale dS^T Q.
 // Three kernels:
-//  * attn_bwd_delta: delta_i, one thread per query row (fp32 from bf16).
+//  * attn_bwd_delta: delta_i, one thread per query row (fp32 from bf16),
+//    stored negated so that the dP products start from it, and the
+//    log-sum-exp in base 2.
 //  * attn_bwd_dq: one work-group of 8 waves owns 256 query rows (32 per wave,
 //    Q and dO fragments in registers as MFMA operand B) and streams 64-key
 //    K and V tiles through LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T (K and
@@ -203,7 +205,10 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
             acc = __builtin_fmaf(__uint_as_float(av[e] & 0xffff0000u), __uint_as_float(gv[e] & 0xffff0000u), acc);
         }
     }
-    p.delta[r] = acc;
+    // stored negated: the dP products start from it, so dP - delta comes out
+    // of the matrix core; and the log-sum-exp in base 2, as the exponents use it
+    p.delta[r] = -acc;
+    p.lse2[r] = p.lse[r] * LOG2E;
 }
 
 // ------------------------------------------------------------------- dQ
@@ -283,8 +288,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
             gf[qb][kk] = *(const bf16x8*)(gs + 32 * kk);
         }
         const int64_t ri = ((int64_t)b * p.H + h) * p.Sq + row;
-        lse2[qb] = p.lse[ri] * LOG2E;
-        dlt[qb] = p.delta[ri];
+        lse2[qb] = p.lse2[ri];
+        dlt[qb] = p.delta[ri];   // -delta
     }
     // Wait for these loads here, once: the register uses below make the
     // compiler place the waits before the loop instead of inside it, where
@@ -328,7 +333,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 #pragma unroll
                 for (int qb = 0; qb < 2; qb++) {
                     s[kb][qb] = mfma(kf, qf[qb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][qb]);
-                    dp[kb][qb] = mfma(vf, gf[qb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[kb][qb]);
+                    // from -delta: the product is dP - delta
+                    dp[kb][qb] = mfma(vf, gf[qb][kk], kk == 0 ? f32x4{dlt[qb], dlt[qb], dlt[qb], dlt[qb]} : dp[kb][qb]);
                 }
             }
     };
@@ -347,22 +353,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     // dS^T = P^T o (dP^T - delta), P^T = 2^(c s - L log2 e) of tile t; keys past
     // Skv (and, under the mask, past the row's diagonal) -> 0 by select
     auto elementwise = [&](int t) __attribute__((always_inline)) {
-        const int valid = p.Skv - t * TILE_ROWS - 4 * g;
+        auto ew = [&](auto maskc) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(maskc)::value;
+            const int valid = p.Skv - t * TILE_ROWS - 4 * g;
 #pragma unroll
-        for (int qb = 0; qb < 2; qb++) {
-            const int lim = CAUSAL ? min(valid, qrow0 + qb * 16 + j + p.causal_off + 1 - t * TILE_ROWS - 4 * g)
-                                   : valid;
-            float dsv[4][4];
+            for (int qb = 0; qb < 2; qb++) {
+                const int lim = CAUSAL ? min(valid, qrow0 + qb * 16 + j + p.causal_off + 1 - t * TILE_ROWS - 4 * g)
+                                       : valid;
+                float dsv[4][4];
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++)
+                for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.c, -lse2[qb]));
-                    dsv[kb][r] = (16 * kb + r < lim) ? pw * (dp[kb][qb][r] - dlt[qb]) : 0.f;
-                }
+                    for (int r = 0; r < 4; r++) {
+                        const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], p.c, -lse2[qb]));
+                        dsv[kb][r] = (!MASKED || 16 * kb + r < lim) ? pw * dp[kb][qb][r] : 0.f;
+                    }
 #pragma unroll
-            for (int kk = 0; kk < 2; kk++) dsf[qb][kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
-        }
+                for (int kk = 0; kk < 2; kk++) dsf[qb][kk] = pack_b(dsv[2 * kk], dsv[2 * kk + 1]);
+            }
+        };
+        // Keys past Skv, and under the mask keys past a row's diagonal, occur
+        // only in the ragged last tile and the tiles crossing this wave's
+        // diagonal (its first row's is the lowest): one uniform branch keeps
+        // the selects out of every other tile.
+        const bool edge = (t + 1) * TILE_ROWS > p.Skv ||
+                          (CAUSAL && (t + 1) * TILE_ROWS - 1 > qrow0 + p.causal_off);
+        if (edge) ew(std::true_type{});
+        else ew(std::false_type{});
     };
     // barrier of waves 0-3: after their elementwise step (the operands keep the
     // compiler from sinking that step below the barrier)
@@ -449,7 +466,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
 // waves of 16 keys.
 constexpr int DKV_NW = 4;
 constexpr int DKV_NSLOT = 4;                   // a power of two
-constexpr int LS_BYTES = 2 * TILE_ROWS * 4;   // L and delta of a tile's 64 queries
+constexpr int LS_BYTES = 2 * TILE_ROWS * 4;   // L (base 2) and -delta of a tile's 64 queries
 
 // dK and dV accumulate in the accumulation registers (AGPRs): the product
 // is written as inline assembly with its C/D operand bound to an AGPR, while
@@ -501,7 +518,7 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     constexpr int PD = HD == 128 ? 3 : 2;         // B-fragment prefetch distance, in chunks (at most 15 LDS reads in flight)
     static_assert(NKK <= NDB && PD <= NKK, "prefetch placement");
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[DKV_NSLOT * 2 * TILE_BYTES];   // per slot: Q, dO
-    __shared__ __attribute__((aligned(16))) uint8_t lsd[DKV_NSLOT * LS_BYTES];           // per slot: L, delta
+    __shared__ __attribute__((aligned(16))) uint8_t lsd[DKV_NSLOT * LS_BYTES];           // per slot: L, -delta
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, j = lane & 15;
@@ -544,6 +561,13 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     auto qslot = [&](int sl) { return (lds_u8*)tiles + sl * (2 * TILE_BYTES); };
     auto gslot = [&](int sl) { return (lds_u8*)tiles + sl * (2 * TILE_BYTES) + TILE_BYTES; };
     auto lslot = [&](int sl) { return (lds_u8*)lsd + sl * LS_BYTES; };
+    // L (base 2) and -delta of queries 16*mb + 4*g .. +3 of a tile's slot
+    auto read_l2 = [&](const lds_u8* lt, int mb) __attribute__((always_inline)) {
+        return *(const LDS_AS f32x4*)(lt + (16 * mb + 4 * g) * 4);
+    };
+    auto read_dl = [&](const lds_u8* lt, int mb) __attribute__((always_inline)) {
+        return *(const LDS_AS f32x4*)(lt + TILE_ROWS * 4 + (16 * mb + 4 * g) * 4);
+    };
     // the L and delta, Q, and dO tiles of tile r0 of query head hq into slot
     // sl, in three parts; each query head's tensors get their own buffer
     // ranges, so rows past Sq read as zero (the range check), never the next
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     // per step, L and delta first.
     auto issue_ld = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
         const int64_t rbh = ((int64_t)b * p.H + hq) * p.Sq;
-        dma4(buffer_rsrc(p.lse + rbh, (uint32_t)p.Sq * 4u), lslot(sl), lane * 4, r0 * 4);
+        dma4(buffer_rsrc(p.lse2 + rbh, (uint32_t)p.Sq * 4u), lslot(sl), lane * 4, r0 * 4);
         dma4(buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u), lslot(sl) + TILE_ROWS * 4, lane * 4, r0 * 4);
     };
     auto issue_q = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
@@ -618,13 +642,14 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     }
     lds_barrier_vm<NDMA + 2>();
 
-    // the straight fragments of query block 0 of the first tile
+    // the straight fragments, L and -delta of query block 0 of the first tile
     bf16x8 fa0[NKK][2];
 #pragma unroll
     for (int kk = 0; kk < NKK; kk++) {
         fa0[kk][0] = read_rows<HD>(qslot(0), a_row[kk], 0);
         fa0[kk][1] = read_rows<HD>(gslot(0), a_row[kk], 0);
     }
+    f32x4 l20 = read_l2(lslot(0), 0), dl0 = read_dl(lslot(0), 0);
 
     // one step on the tile in slot sl (first query row r0), issuing the
     // transfers of tile dr0 of head dhq into slot dsl among its products;
@@ -653,14 +678,15 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
             fb[ks][db][1] = read_cols<HD>(qt, a_col[db], ks);
         };
         auto read_ld = [&](int mb) __attribute__((always_inline)) {
-            l2[mb] = *(const LDS_AS f32x4*)(lt + (16 * mb + 4 * g) * 4);
-            dl[mb] = *(const LDS_AS f32x4*)(lt + TILE_ROWS * 4 + (16 * mb + 4 * g) * 4);
+            l2[mb] = read_l2(lt, mb);
+            dl[mb] = read_dl(lt, mb);
         };
         auto mfma_a = [&](int mb, int kk) __attribute__((always_inline)) {
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
                 s[kb][mb] = mfma(fa[mb][kk][0], kf[kb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][mb]);
-                dp[kb][mb] = mfma(fa[mb][kk][1], vf[kb][kk], kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : dp[kb][mb]);
+                // from -delta: the product is dP - delta
+                dp[kb][mb] = mfma(fa[mb][kk][1], vf[kb][kk], kk == 0 ? dl[mb] : dp[kb][mb]);
             }
         };
         // P and dS as operand B of half ks: k = queries 32 ks + 16 hf + 4 g + e
@@ -687,7 +713,7 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 const int r = 2 * h + i;
-                const float x = __builtin_fmaf(s[kb][mb][r], p.c, -l2[mb][r] * LOG2E);
+                const float x = __builtin_fmaf(s[kb][mb][r], p.c, -l2[mb][r]);
                 if (MASK) {
                     // query 16*mb + 4*g + r of the tile sees key kbase + 16*kb + j iff
                     // 16*mb + r >= kbase + 16*kb + j - (Skv - Sq) - r0 - 4*g
@@ -696,10 +722,10 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
                     pw[i] = in ? __builtin_amdgcn_exp2f(x) : 0.f;
                     // by select, like the weight: 0 * (dP - delta) would be NaN
                     // where a pair outside the mask meets a non-finite dP or delta
-                    ds[i] = in ? pw[i] * (dp[kb][mb][r] - dl[mb][r]) : 0.f;
+                    ds[i] = in ? pw[i] * dp[kb][mb][r] : 0.f;
                 } else {
                     pw[i] = __builtin_amdgcn_exp2f(x);
-                    ds[i] = pw[i] * (dp[kb][mb][r] - dl[mb][r]);
+                    ds[i] = pw[i] * dp[kb][mb][r];
                 }
             }
             pp[kb][mb][h] = __builtin_convertvector((f32x2{pw[0], pw[1]}), bf16x2);
@@ -711,10 +737,13 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
             __asm__ volatile("" : "+v"(pp[kb][mb][h]), "+v"(dsp[kb][mb][h]));
         };
 
-        // A0, with the reads of A1 and of L, delta
-        read_ld(0);
+        // A0 (its L and -delta came with the previous step: the dP products
+        // start from -delta), with the reads of A1 and of block 1's L, -delta
+        l2[0] = l20;
+        dl[0] = dl0;
 #pragma unroll
         for (int kk = 0; kk < NKK; kk++) {
+            if (kk == 0) read_ld(1);
             read_a(1, kk);
             mfma_a(0, kk);
             chunk_end<4, 0>(2 + (kk == 0 ? 2 : 0));
@@ -724,10 +753,10 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
         for (int mb = 1; mb < 4; mb++) {
 #pragma unroll
             for (int kk = 0; kk < NKK; kk++) {
-                if (kk == 0) read_ld(mb);
+                if (kk == 0 && mb < 3) read_ld(mb + 1);
                 if (kk == 0 && mb == 1) { issue_ld(dsl, dhq, dr0); issue_q(dsl, dhq, dr0); }
                 if (kk == 0 && mb == 2) issue_g(dsl, dhq, dr0);
-                int nr = kk == 0 ? 2 : 0;
+                int nr = (kk == 0 && mb < 3) ? 2 : 0;
                 if (mb < 3) { read_a(mb + 1, kk); nr += 2; }
                 else if (kk < PD) { read_b(0, kk); nr += 4; }
                 mfma_a(mb, kk);
@@ -759,12 +788,19 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
         // every wave has its transfers of the next step in LDS, and has
         // issued its last reads of the slot that step t+1's transfers reuse
         lds_barrier_vm<NDMA + 2>();
-        // B1, with the reads of B1 (the rest) and of the next tile's A0
+        // B1, with the reads of B1 (the rest) and of the next tile's A0 and its
+        // L, -delta
         const lds_u8* qn = qslot(nsl);
         const lds_u8* gn = gslot(nsl);
+        const lds_u8* ln = lslot(nsl);
+        static_assert(NDB - NKK - 1 >= 0 && NDB - NKK - 1 + PD < NDB, "the chunk before the A0 reads holds 6 reads");
 #pragma unroll
         for (int db = 0; db < NDB; db++) {
             if (db + PD < NDB) read_b(1, db + PD);
+            if (db == NDB - NKK - 1) {
+                l20 = read_l2(ln, 0);
+                dl0 = read_dl(ln, 0);
+            }
             // the NKK fragment pairs of the next A0, in the last NKK chunks
             if (db >= NDB - NKK) {
                 const int kk = db - (NDB - NKK);
@@ -772,7 +808,7 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
                 fa0[kk][1] = read_rows<HD>(gn, a_row[kk], 0);
             }
             mfma_b(1, db);
-            chunk_end<4, 0>((db + PD < NDB ? 4 : 0) + (db >= NDB - NKK ? 2 : 0));
+            chunk_end<4, 0>((db + PD < NDB ? 4 : 0) + (db >= NDB - NKK ? 2 : 0) + (db == NDB - NKK - 1 ? 2 : 0));
         }
     };
 
