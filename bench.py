@@ -198,6 +198,33 @@ def time_paged(steps, warmup):
     return statistics.median([a.elapsed_time(b) for a, b in evs])
 
 
+def time_varlen(steps, warmup):
+    """Median ms of attn_fwd_bf16_varlen on the packed-sequence workload."""
+    import torch
+    from bf16_attention_forward_amd import attn_fwd_bf16_varlen
+    from bf16_attention_forward_amd import workloads as wl
+
+    c = wl.VARLEN
+    pk = wl.make_packed(c["H"], c["H"], c["lens"], c["lens"], seed=c["seed"], q_factor=0.5, k_factor=0.5,
+                        v_factor=0.5)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = pk.q.to(dev), pk.k.to(dev), pk.v.to(dev)
+    cq, ck = pk.cu_q.to(dev), pk.cu_k.to(dev)
+    od = torch.empty_like(qd)
+    m = max(c["lens"])
+    run = lambda: attn_fwd_bf16_varlen(qd, kd, vd, cq, ck, od, max_seqlen_q=m, max_seqlen_k=m)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median([a.elapsed_time(b) for a, b in evs])
+
+
 def time_backward(w, steps, warmup):
     """Median ms of attn_bwd_bf16 on workload w (O and lse from the forward)."""
     import torch
@@ -270,6 +297,8 @@ def main():
                     help="time only the backward pass of the workload (one JSON line of its own)")
     ap.add_argument("--paged", action="store_true",
                     help="time only the paged key/value cache workload (one JSON line of its own)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time only the packed-sequence workload (one JSON line of its own)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -312,6 +341,17 @@ def main():
                           "config": {"workload": c["name"], "B": c["B"], "H": c["H"], "Sq": c["Sq"],
                                      "kv_lens": list(c["kv_lens"]), "page_size": c["page_size"],
                                      "head_dim": 128, "layout": "bshd", "round_mode": "rtne"}}), flush=True)
+        return
+    if args.varlen:
+        c = wl.VARLEN
+        em = time_varlen(steps=args.steps, warmup=args.warmup)
+        tf = wl.varlen_flops(c["H"], c["lens"], c["lens"]) / (em * 1e-3) / 1e12
+        print(json.dumps({"metric": "packed-sequence attention fwd TFLOPS (sum over sequences of 4*H*len^2*d)",
+                          "value": round(tf, 2), "unit": "TFLOP/s", "median_ms": round(em, 5),
+                          "steps": args.steps, "warmup": args.warmup,
+                          "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "config": {"workload": c["name"], "H": c["H"], "lens": list(c["lens"]),
+                                     "head_dim": 128, "layout": "thd", "round_mode": "rtne"}}), flush=True)
         return
     sclk_idle = read_sclk_mhz()
     order = {"planner": 0, "naive": 1, "xcd": 2}[args.block_order]
@@ -382,6 +422,12 @@ def main():
         extra[f"{c['name']}:rtne"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),
                                       "frac_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                       "note": "copy of the cached keys and values into the workspace included"}
+        # packed sequences of different lengths
+        c = wl.VARLEN
+        em = time_varlen(steps=20, warmup=5)
+        tf = wl.varlen_flops(c["H"], c["lens"], c["lens"]) / (em * 1e-3) / 1e12
+        extra[f"{c['name']}:rtne"] = {"median_ms": round(em, 4), "tflops": round(tf, 1),
+                                      "frac_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
 

@@ -7,8 +7,10 @@ seeded workload generators.  Importing it does not load the library; the
 first call does, and raises if it is not built.
 """
 from .binding import (AttnError, attn_bwd_bf16, attn_fwd_bf16, attn_fwd_bf16_gqa, attn_fwd_bf16_hd,  # noqa: F401
-                      attn_fwd_bf16_hd_noalloc, attn_fwd_bf16_paged, attn_fwd_bf16_raw, attn_status_string, attn_version,
+                      attn_fwd_bf16_hd_noalloc, attn_fwd_bf16_paged, attn_fwd_bf16_raw, attn_fwd_bf16_varlen,
+                      attn_status_string, attn_version,
                       load_library, LIB_PATH, EXPORTS, NOALLOC_SCRATCH_BYTES)
 
-__all__ = ["attn_fwd_bf16", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_fwd_bf16_hd_noalloc", "attn_fwd_bf16_paged", "attn_bwd_bf16", "attn_fwd_bf16_raw", "attn_status_string",
+__all__ = ["attn_fwd_bf16", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_fwd_bf16_hd_noalloc", "attn_fwd_bf16_paged",
+           "attn_fwd_bf16_varlen", "attn_bwd_bf16", "attn_fwd_bf16_raw", "attn_status_string",
            "attn_version", "load_library", "AttnError", "LIB_PATH", "EXPORTS"]

@@ -24,7 +24,7 @@ HEAD_DIM = 128
 
 # names of every entry point the header declares
 EXPORTS = ("attn_fwd_bf16", "attn_fwd_bf16_ex", "attn_fwd_bf16_gqa", "attn_fwd_bf16_hd", "attn_fwd_bf16_hd_noalloc",
-           "attn_fwd_bf16_paged",
+           "attn_fwd_bf16_paged", "attn_fwd_bf16_varlen",
            "attn_bwd_bf16", "attn_status_string", "attn_version")
 NOALLOC_SCRATCH_BYTES = 34078720   # ATTN_NOALLOC_SCRATCH_BYTES
 HEAD_DIMS = (128, 64)
@@ -65,6 +65,9 @@ def load_library(path: str | None = None):
     lib.attn_fwd_bf16_paged.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] + [ctypes.c_int64] * 9 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_bf16_paged.restype = ctypes.c_int
+    lib.attn_fwd_bf16_varlen.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 8 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_fwd_bf16_varlen.restype = ctypes.c_int
     lib.attn_bwd_bf16.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] + [ctypes.c_int64] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_bwd_bf16.restype = ctypes.c_int
@@ -286,6 +289,53 @@ def attn_fwd_bf16_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
                                      ATTN_LAYOUT[layout], B, Hq, Hkv, Sq, int(max_kv_len), page_size,
                                      int(block_table.shape[1]), num_pages, hd, sc, 1 if causal else 0,
                                      _mode(round_mode, round_weights), st.cuda_stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return (o, lse) if lse is not None else o
+
+
+def attn_fwd_bf16_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         cu_seqlens_k: torch.Tensor, o: torch.Tensor | None = None, *, max_seqlen_q: int,
+                         max_seqlen_k: int, scale: float | None = None, causal: bool = False,
+                         round_mode: str = "rtne", stream: torch.cuda.Stream | None = None,
+                         lse: torch.Tensor | None = None, return_lse: bool = False,
+                         round_weights: bool = False):
+    """attn_fwd_bf16_hd over packed sequences (attn_fwd_bf16_varlen): q, o
+    [total_q, Hq, head_dim] and k, v [total_k, Hkv, head_dim] bf16 hold the rows
+    of all sequences; cu_seqlens_q, cu_seqlens_k int32 [B + 1] are the prefix
+    sums of their row counts.  lse, if wanted, is [Hq, total_q].  Scale
+    defaults to 1/sqrt(head_dim)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D bfloat16 device tensor")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{name} must be a contiguous 1-D int32 device tensor")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.shape[0] < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1], B >= 1")
+    total_q, Hq, D = (int(x) for x in q.shape)
+    total_k, Hkv, Dk = (int(x) for x in k.shape)
+    if k.shape != v.shape or D != Dk or D not in HEAD_DIMS:
+        raise ValueError(f"k and v must be [total_k, Hkv, head_dim] alike, head_dim one of {HEAD_DIMS} as in q")
+    B = int(cu_seqlens_q.shape[0]) - 1
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous bfloat16 device tensor shaped like q")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 device tensor shaped [Hq, total_q]")
+    sc = float(1.0 / math.sqrt(D)) if scale is None else float(scale)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(),
+                                      cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
+                                      int(max_seqlen_k), D, sc, 1 if causal else 0,
+                                      _mode(round_mode, round_weights), st.cuda_stream)
     if rc != ATTN_OK:
         _raise(rc)
     return (o, lse) if lse is not None else o

@@ -139,6 +139,9 @@ struct RunOpts {
     int grid = 0;                  // at most this many work-groups (0: the planner's choice)
     bool noalloc = false;          // split partials in the fixed device array
     const int* kv_lens = nullptr;  // device [B]: keys of each batch entry (per-entry lengths run unsplit)
+    const int* cu_q = nullptr;     // device [B + 1]: packed sequences, prefix sums of the query rows
+    const int* cu_k = nullptr;     // and of the key rows (Sq, Skv: the longest sequence)
+    int64_t total_q = 0, total_k = 0;   // rows of the packed tensors
     bool kv_internal = false;      // k, v: the library's own BSHD copy (no alias or alignment check)
     bool check_only = false;       // validate the arguments, touch no device
     std::function<int(int)> pre_launch;   // runs after every check, right before the kernels are queued
@@ -151,7 +154,10 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     const int kv_splits = opt.kv_splits, block_order = opt.block_order, waves = opt.waves;
     const bool noalloc = opt.noalloc;
     const int* kv_lens = opt.kv_lens;
+    const bool packed = opt.cu_q != nullptr;             // packed sequences (rows of all entries in one tensor)
+    const bool per_entry = kv_lens || packed;            // per-entry key counts: unsplit, one block per work-group
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+    if (packed && (!opt.cu_k || layout != ATTN_LAYOUT_BSHD)) return ATTN_ERR_NULL;
     if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
     const int out_mode = round_mode & ~ATTN_ROUND_WEIGHTS;
     if (out_mode != ATTN_ROUND_RTNE && out_mode != ATTN_ROUND_RTNA && out_mode != ATTN_ROUND_RTZ)
@@ -164,7 +170,11 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     const int64_t lim31 = (int64_t)1 << 31;
     if (B >= lim31 || H >= lim31 || Sq >= lim31 || Skv >= lim31) return ATTN_ERR_SHAPE;
     if (B * H >= lim31) return ATTN_ERR_SHAPE;
-    const int64_t n_q = B * H * Sq, n_kv = B * Hkv * Skv;
+    if (packed && (opt.total_q < 1 || opt.total_k < 1 || opt.total_q >= lim31 || opt.total_k >= lim31))
+        return ATTN_ERR_SHAPE;
+    // elements of q (and o) and of k (and v): packed tensors hold total rows
+    const int64_t n_q = packed ? opt.total_q * H : B * H * Sq;
+    const int64_t n_kv = packed ? opt.total_k * Hkv : B * Hkv * Skv;
     if (n_q > ((int64_t)1 << 52) / kHeadDim || n_kv > ((int64_t)1 << 52) / kHeadDim) return ATTN_ERR_SHAPE;
     const bool kv_rows_bshd = opt.kv_internal || layout == ATTN_LAYOUT_BSHD;
     const int64_t kv_row = kv_rows_bshd ? Hkv * kHeadDim : kHeadDim;
@@ -195,9 +205,10 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     if (kv_splits < 0 || kv_splits > kMaxSplits || block_order < 0 || block_order > 2) return ATTN_ERR_OPTION;
     if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
     if (causal && (kv_splits > 1 || block_order == 2)) return ATTN_ERR_OPTION;
-    if (kv_lens && kv_splits > 1) return ATTN_ERR_OPTION;
-    if (opt.grid < 0 || (opt.grid > 0 && (causal || kv_lens))) return ATTN_ERR_OPTION;
+    if (per_entry && kv_splits > 1) return ATTN_ERR_OPTION;
+    if (opt.grid < 0 || (opt.grid > 0 && (causal || per_entry))) return ATTN_ERR_OPTION;
     if (kv_lens && ((uintptr_t)kv_lens & 3)) return ATTN_ERR_ALIGN;
+    if (packed && (((uintptr_t)opt.cu_q | (uintptr_t)opt.cu_k) & 3)) return ATTN_ERR_ALIGN;
     if (opt.check_only) return ATTN_OK;
 
     int dev = -1;
@@ -213,6 +224,10 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.o = (uint16_t*)o;
     p.lse = lse;
     p.kv_lens = kv_lens;
+    p.cu_q = opt.cu_q;
+    p.cu_k = opt.cu_k;
+    p.total_q = (int)opt.total_q;
+    p.total_k = (int)opt.total_k;
     if (layout == ATTN_LAYOUT_BSHD) {
         p.q_row = H * kHeadDim; p.q_head = kHeadDim; p.q_batch = Sq * H * kHeadDim;
     } else {
@@ -245,7 +260,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     const int n_kv_tiles = (int)((Skv + kKeyTile - 1) / kKeyTile);
     const int slots = info.n_cu * (8 / nw);   // resident work-groups: two waves per SIMD
     int n_full = p.n_items, splits = 1;
-    if (causal || kv_lens) {
+    if (causal || per_entry) {
         // Causal items differ in length (the diagonal), and so do the items
         // of batch entries with their own key counts: they run unsplit
         // (causal ones longest first, in naive block order: the kernel
@@ -284,7 +299,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     // work-groups, two per CU, whose item boundaries overlap the other's
     // work only when they run out of step.
     p.grid = p.n_blocks;
-    if (!causal && !kv_lens && nw == KERNEL_NW && head_dim == 128) {
+    if (!causal && !per_entry && nw == KERNEL_NW && head_dim == 128) {
         const int cap = std::max(8, (opt.grid > 0 ? opt.grid : slots) & ~7);
         if (cap < p.n_blocks) p.grid = cap;
     }
@@ -329,6 +344,21 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
                                  int layout, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                                  float scale, int causal, int round_mode, void* stream) {
     return run_attention(q, k, v, o, lse, layout, B, Hq, Hkv, Sq, Skv, 128, scale, causal, round_mode, stream, RunOpts());
+}
+
+extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int64_t B, int64_t Hq, int64_t Hkv, int64_t total_q, int64_t total_k,
+                                    int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t head_dim,
+                                    float scale, int causal, int round_mode, void* stream) {
+    if (!cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+    RunOpts opt;
+    opt.cu_q = cu_seqlens_q;
+    opt.cu_k = cu_seqlens_k;
+    opt.total_q = total_q;
+    opt.total_k = total_k;
+    return run_attention(q, k, v, o, lse, ATTN_LAYOUT_BSHD, B, Hq, Hkv, max_seqlen_q, max_seqlen_k, head_dim,
+                         scale, causal, round_mode, stream, opt);
 }
 
 extern "C" int attn_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,

@@ -49,6 +49,9 @@ struct AttnParams {
     uint16_t* o;
     float* lse;        // optional [B][H][Sq] natural-log log-sum-exp per query row (NULL: not written)
     const int* kv_lens;  // optional [B] keys of each batch entry, clamped to [0, Skv] (NULL: Skv each)
+    const int* cu_q;     // optional packed sequences: [B + 1] prefix sums of the query rows (Sq: the longest)
+    const int* cu_k;     // and of the key rows (Skv: the longest); q, o, k, v hold the rows of all entries
+    int total_q, total_k;  // rows of the packed tensors
     float* ws_o;       // split partial outputs [n_items - n_full][kv_splits][BM][128] (fp32)
     float* ws_ml;      // split partial (M, l) pairs [n_items - n_full][kv_splits][BM][2]
     int64_t q_row, q_head, q_batch;      // element strides of q and o

@@ -174,6 +174,33 @@ __device__ __forceinline__ int map_block(int bid, int n, int order) {
 // schedule on every XCD.  The entries are ranked in-wave when there are at
 // most 64 of them (ties by index); with more they run in index order.
 // Called with all 64 lanes of the wave active.
+// The query and key rows of batch entry b with per-entry counts: packed
+// sequences (cu_q, cu_k: prefix sums of the rows, clamped so a row never
+// falls outside the packed tensors or past the longest length the call
+// names), or a common query count and a key count per entry (kv_lens).
+template <class PT>
+__device__ __forceinline__ int entry_keys(PT& p, int b, int* first = nullptr) {
+    if (p.cu_k) {
+        const int s = min(max(p.cu_k[b], 0), p.total_k);
+        const int e = min(max(p.cu_k[b + 1], s), p.total_k);
+        if (first) *first = s;
+        return min(e - s, p.Skv);
+    }
+    if (first) *first = 0;
+    return min(max(p.kv_lens[b], 0), p.Skv);
+}
+template <class PT>
+__device__ __forceinline__ int entry_queries(PT& p, int b, int* first) {
+    if (p.cu_q) {
+        const int s = min(max(p.cu_q[b], 0), p.total_q);
+        const int e = min(max(p.cu_q[b + 1], s), p.total_q);
+        *first = s;
+        return min(e - s, p.Sq);
+    }
+    *first = 0;
+    return p.Sq;
+}
+
 template <class PT>
 __device__ __forceinline__ void kvlen_item(int pos, PT& p, int& qt, int& bh) {
     const int64_t M = (int64_t)p.H * p.n_qtiles;
@@ -192,7 +219,7 @@ __device__ __forceinline__ void kvlen_item(int pos, PT& p, int& qt, int& bh) {
     int b = r;
     if (p.B <= 64) {
         const int lane = threadIdx.x & 63;
-        const int len = lane < p.B ? min(max(p.kv_lens[lane], 0), p.Skv) : -1;
+        const int len = lane < p.B ? entry_keys(p, lane) : -1;
         int rank = 0;
         for (int u = 0; u < p.B; u++) {
             const int lu = __builtin_amdgcn_readlane(len, u);
@@ -259,6 +286,20 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     constexpr bool PERSIST = !CAUSAL && !KVL && NWT == 8 && HD == 128;
     struct Loc {
         int item, split, nsplit, qt, b, h, hk, coff, kv_begin, kv_end;
+        int sq;                          // query rows of the entry
+        int64_t qoff, koff, lse_off;     // elements to the entry's row 0 of head h (q, o), hk (k, v); lse index
+    };
+    // The element offsets of an item's rows (per-entry counts: from the
+    // locator; otherwise from b and h where they are used, as few values as
+    // possible live across the key loop)
+    auto q_off = [&](KParams& p, const Loc& L) __attribute__((always_inline)) -> int64_t {
+        return KVL ? L.qoff : (int64_t)L.b * p.q_batch + (int64_t)L.h * p.q_head;
+    };
+    auto k_off = [&](KParams& p, const Loc& L) __attribute__((always_inline)) -> int64_t {
+        return KVL ? L.koff : (int64_t)L.b * p.kv_batch + (int64_t)L.hk * p.kv_head;
+    };
+    auto lse_base = [&](KParams& p, const Loc& L) __attribute__((always_inline)) -> int64_t {
+        return KVL ? L.lse_off : ((int64_t)L.b * p.H + L.h) * p.Sq;
     };
     auto locate = [&](KParams& p, int vb) __attribute__((always_inline)) -> Loc {
         Loc L;
@@ -292,16 +333,30 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         L.h = bh % p.H;
         L.b = bh / p.H;
         L.hk = L.h / p.group;                      // key/value head of query head h
-        // keys of this batch entry (per-entry lengths: never split) and the
-        // causal offset that aligns its queries with the last of them
-        const int kvl = KVL ? min(max(p.kv_lens[L.b], 0), p.Skv) : p.Skv;
-        L.coff = KVL ? kvl - p.Sq : p.causal_off;
+        // keys and queries of this batch entry (per-entry lengths: never
+        // split) and the causal offset that aligns its queries with the last
+        // of its keys
+        int q0 = 0, k0 = 0;
+        const int kvl = KVL ? entry_keys(p, L.b, &k0) : p.Skv;
+        L.sq = KVL ? entry_queries(p, L.b, &q0) : p.Sq;
+        L.coff = KVL ? kvl - L.sq : p.causal_off;
+        L.qoff = L.koff = L.lse_off = 0;
+        if (KVL && p.cu_q) {
+            // packed sequences: rows of all entries in one tensor, lse [H][total rows]
+            L.qoff = (int64_t)q0 * p.q_row + (int64_t)L.h * p.q_head;
+            L.koff = (int64_t)k0 * p.kv_row + (int64_t)L.hk * p.kv_head;
+            L.lse_off = (int64_t)L.h * p.total_q + q0;
+        } else if (KVL) {
+            L.qoff = (int64_t)L.b * p.q_batch + (int64_t)L.h * p.q_head;
+            L.koff = (int64_t)L.b * p.kv_batch + (int64_t)L.hk * p.kv_head;
+            L.lse_off = ((int64_t)L.b * p.H + L.h) * p.Sq;
+        }
         // split s covers key tiles [s*T/ns, (s+1)*T/ns) of the T tiles: never empty for ns <= T
         L.kv_begin = (int)(((int64_t)L.split * p.n_kv_tiles) / L.nsplit) * BN;
         L.kv_end = min(kvl, (int)(((int64_t)(L.split + 1) * p.n_kv_tiles) / L.nsplit) * BN);
         if (CAUSAL) {
             // keys up to the diagonal of the tile's last row (never split)
-            const int last_row = min(p.Sq, (L.qt + 1) * BM) - 1;
+            const int last_row = min(L.sq, (L.qt + 1) * BM) - 1;
             L.kv_end = min(L.kv_end, last_row + L.coff + 1);
         }
         return L;
@@ -330,10 +385,10 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
         const int g = lane >> 4;       // lane group (0..3)
         const int j = lane & 15;       // lane within group
-        auto load_q = [&](KParams& p, const uint16_t* qb_base, int qrow0) __attribute__((always_inline)) {
+        auto load_q = [&](KParams& p, const uint16_t* qb_base, int qrow0, int sq) __attribute__((always_inline)) {
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) {
-                const int row = min(qrow0 + qb * 16 + j, p.Sq - 1);
+                const int row = min(qrow0 + qb * 16 + j, sq - 1);
                 const uint16_t* src = qb_base + (int64_t)row * p.q_row + 8 * g;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ks++) qf[qb][ks] = *(const bf16x8*)(src + 32 * ks);
@@ -342,27 +397,30 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         KParams& P = kernel_params<PERSIST>();
         const Loc L = locate(P, vb);
         const int kv_row_bytes = (int)(P.kv_row * 2);
-        const int item = L.item, split = L.split, nsplit = L.nsplit, qt = L.qt, b = L.b, h = L.h;
-        const int coff = L.coff, kv_begin = L.kv_begin, kv_end = L.kv_end;
+        const int item = L.item, split = L.split, nsplit = L.nsplit, qt = L.qt;
+        const int coff = L.coff, kv_begin = L.kv_begin, kv_end = L.kv_end, sq = L.sq;
         const int T = (kv_end - kv_begin + BN - 1) / BN;
 
-        const uint16_t* qbase = P.q + (int64_t)b * P.q_batch + (int64_t)h * P.q_head;
-        const char* kbase = (const char*)(P.k + (int64_t)b * P.kv_batch + (int64_t)L.hk * P.kv_head);
-        const char* vbase = (const char*)(P.v + (int64_t)b * P.kv_batch + (int64_t)L.hk * P.kv_head);
+        const uint16_t* qbase = P.q + q_off(P, L);
+        const char* kbase = (const char*)(P.k + k_off(P, L));
+        const char* vbase = (const char*)(P.v + k_off(P, L));
 
+        // an item past the last query row of its entry (packed sequences of
+        // different lengths): nothing to do
+        if (KVL && qt * BM >= sq) return;
         if ((CAUSAL || KVL) && kv_end <= kv_begin) {
             // No query row of the tile sees a key (a causal tile entirely above
             // the diagonal, or a batch entry with no keys): its rows are zeros
             // and their log-sum-exp is -inf.  Uniform across the work-group,
             // before any barrier or DMA.
-            uint16_t* obase = P.o + (int64_t)b * P.q_batch + (int64_t)h * P.q_head;
+            uint16_t* obase = P.o + q_off(P, L);
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) {
                 const int row = qt * BM + wave * 16 * NQB + qb * 16 + j;
-                if (row >= P.Sq) continue;
+                if (row >= sq) continue;
 #pragma unroll
                 for (int db = 0; db < NDB; db++) *(uint2*)(obase + (int64_t)row * P.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
-                if (P.lse && g == 0) P.lse[((int64_t)b * P.H + h) * P.Sq + row] = -__builtin_inff();
+                if (P.lse && g == 0) P.lse[lse_base(P, L) + row] = -__builtin_inff();
             }
             return;
         }
@@ -417,7 +475,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
 #pragma unroll
                 for (int r = 0; r < DMA_ROUNDS; r++) dma_k(r, kv_begin, sk0);
             }
-            load_q(P, qbase, qrow0);
+            load_q(P, qbase, qrow0, sq);
         }
         f32x4 o_acc[NDB][NQB];
 #pragma unroll
@@ -762,15 +820,15 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
             const int nv = vb + PN.grid;
             if (nv >= PN.n_blocks) return;
             const Loc N = locate(PN, nv);
-            const uint16_t* nq = PN.q + (int64_t)N.b * PN.q_batch + (int64_t)N.h * PN.q_head;
+            const uint16_t* nq = PN.q + q_off(PN, N);
             if (!late) {
-                const char* nk = (const char*)(PN.k + (int64_t)N.b * PN.kv_batch + (int64_t)N.hk * PN.kv_head);
+                const char* nk = (const char*)(PN.k + k_off(PN, N));
                 const i32x4 nrs = kv_rsrc(nk, N.kv_end, (int)(PN.kv_row * 2));
 #pragma unroll
                 for (int r = 0; r < DMA_ROUNDS; r++)
                     dma16(nrs, sk0 + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (N.kv_begin + RPR * r) * kv_row_bytes);
             }
-            load_q(PN, nq, N.qt * BM + wave * 16 * NQB);
+            load_q(PN, nq, N.qt * BM + wave * 16 * NQB, N.sq);
         };
         // the key loop, compiled once per wave group
         auto key_loop = [&](auto latec) __attribute__((always_inline)) {
@@ -807,17 +865,17 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
 #pragma unroll
                 for (int qb = 0; qb < NQB; qb++) {
                     const int row = qrow0 + qb * 16 + j;
-                    if (row >= P.Sq) continue;
+                    if (row >= sq) continue;
                     float v = (moff[qb] + __builtin_amdgcn_logf(l_row[qb])) * LN2;
                     if (CAUSAL && row + coff < 0) v = -__builtin_inff();
-                    P.lse[((int64_t)b * P.H + h) * P.Sq + row] = v;
+                    P.lse[lse_base(P, L) + row] = v;
                 }
             }
-            uint16_t* obase = P.o + (int64_t)b * P.q_batch + (int64_t)h * P.q_head;
+            uint16_t* obase = P.o + q_off(P, L);
 #pragma unroll
             for (int qb = 0; qb < NQB; qb++) {
                 const int row = qrow0 + qb * 16 + j;
-                if (row >= P.Sq) continue;
+                if (row >= sq) continue;
                 const float lr = l_row[qb];
                 const float inv = 1.0f / lr;
                 const bool no_key = CAUSAL && row + coff < 0;
@@ -926,7 +984,7 @@ int launch(const AttnParams& p, hipStream_t stream) {
     // per-entry key counts are a variant of their own: the kernels without
     // them carry none of their code
     auto go_nw = [&](auto hd, auto cpos, auto causal, auto nw) {
-        if (p.kv_lens) go_kv(hd, cpos, causal, std::true_type{}, nw);
+        if (p.kv_lens || p.cu_k) go_kv(hd, cpos, causal, std::true_type{}, nw);
         else go_kv(hd, cpos, causal, std::false_type{}, nw);
     };
     auto go = [&](auto hd, auto cpos, auto causal) {

@@ -214,6 +214,50 @@ def make_paged_kv(B: int, Hkv: int, kv_lens, page_size: int, seed: int, D: int =
 
 
 @dataclass
+class Packed:
+    """A batch of packed sequences (CPU tensors): q [total_q, H, D], k, v
+    [total_k, Hkv, D] bf16 hold the rows of all sequences; cu_q, cu_k int32
+    [B + 1] are the prefix sums of their row counts."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    cu_q: torch.Tensor
+    cu_k: torch.Tensor
+
+    def seq(self, b: int):
+        """Sequence b as BSHD tensors [1, len, heads, D] (q, k, v)."""
+        q0, q1 = int(self.cu_q[b]), int(self.cu_q[b + 1])
+        k0, k1 = int(self.cu_k[b]), int(self.cu_k[b + 1])
+        return self.q[q0:q1].unsqueeze(0), self.k[k0:k1].unsqueeze(0), self.v[k0:k1].unsqueeze(0)
+
+
+def make_packed(H: int, Hkv: int, lens_q, lens_k, seed: int, D: int = HEAD_DIM,
+                q_factor: float = 1.0, k_factor: float = 1.0, v_factor: float = 1.0) -> Packed:
+    """Seeded packed sequences of the given query and key row counts."""
+    lq, lk = [int(x) for x in lens_q], [int(x) for x in lens_k]
+    cu_q = torch.tensor([0] + list(np.cumsum(lq)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(lk)), dtype=torch.int32)
+    q = _draw((max(sum(lq), 1), H, D), 4 * seed + 0, q_factor)
+    k = _draw((max(sum(lk), 1), Hkv, D), 4 * seed + 1, k_factor)
+    v = _draw((max(sum(lk), 1), Hkv, D), 4 * seed + 2, v_factor)
+    return Packed(q, k, v, cu_q, cu_k)
+
+
+# Packed sequences: the video self-attention's 12 heads of 128 over eight
+# clips of different lengths (30 x 52 latent tokens per frame, 21 frames
+# down to 1 frame: 32760 down to 1560 tokens), self-attention within each
+# clip, all clips in one tensor.
+VARLEN = dict(name="varlen_self_attn_thd_h12_8clips", H=12,
+              lens=(32760, 24960, 18720, 12480, 9360, 6240, 3120, 1560), seed=1011,
+              note="packed sequences of different lengths")
+
+
+def varlen_flops(H: int, lens_q, lens_k, D: int = HEAD_DIM) -> int:
+    """Algorithmic FLOPs of packed non-causal attention: 4 * H * len_q * len_k * D per sequence."""
+    return sum(4 * H * int(a) * int(b) * D for a, b in zip(lens_q, lens_k))
+
+
+@dataclass
 class Injection:
     """Non-finite values planted into q and v (positions as (b, h, s, d))."""
     q_sites: list = field(default_factory=list)   # (b, h, i, d, value)

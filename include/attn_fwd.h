@@ -240,6 +240,46 @@ int attn_fwd_bf16_paged(const void* q, const void* k_cache, const void* v_cache,
                         int64_t page_size, int64_t pages_per_seq, int64_t num_pages, int64_t head_dim,
                         float scale, int causal, int round_mode, void* stream);
 
+/*
+ * attn_fwd_bf16_varlen -- attn_fwd_bf16_hd over a batch of packed sequences of
+ * different lengths: the variable-length batches the MoonMath article lists
+ * among its kernel's limitations (limitations paragraph), with the rows of all
+ * sequences in one tensor and no padding (the flexible layouts of the FlyDSL
+ * diffusion-attention article's section on what diffusion inference needs).
+ *
+ *   q, o        [total_q][Hq][head_dim] bf16, device, 16-byte aligned: the
+ *               query (and output) rows of sequence b are rows
+ *               cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   k, v        [total_k][Hkv][head_dim] bf16, device, 16-byte aligned: the
+ *               key/value rows of sequence b are rows cu_seqlens_k[b] ..
+ *               cu_seqlens_k[b+1]-1
+ *   lse         NULL, or fp32 [Hq][total_q], device, 4-byte aligned: the
+ *               natural-log log-sum-exp of each row's scaled scores (-inf
+ *               for a row that sees no key)
+ *   cu_seqlens_q, cu_seqlens_k  int32 [B+1], device, 4-byte aligned:
+ *               non-decreasing prefix sums of the sequences' row counts
+ *               (element 0 is 0, element B the total).  The kernel clamps
+ *               every entry into [0, total] and each length to
+ *               max_seqlen_q / max_seqlen_k, so no row outside the tensors
+ *               is ever read or written
+ *   B           sequences (>= 1); Hq, Hkv, head_dim as attn_fwd_bf16_hd
+ *   total_q, total_k   rows of the packed tensors (>= 1)
+ *   max_seqlen_q, max_seqlen_k  >= 1, at least every sequence's length
+ *   causal      0, or 1: query i of sequence b sees keys j <= i + (len_k(b)
+ *               - len_q(b)) (its queries are the last len_q(b) positions of
+ *               its keys); rows of a sequence with no keys are zeros
+ *
+ * Each sequence attends only to its own keys; the key range is never split.
+ * Ownership, asynchrony and error behaviour are those of attn_fwd_bf16_hd
+ * (no workspace is used); missing cu_seqlens give ATTN_ERR_NULL, sizes
+ * below 1 ATTN_ERR_SHAPE, misaligned cu_seqlens ATTN_ERR_ALIGN.
+ */
+int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t total_q, int64_t total_k,
+                         int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t head_dim,
+                         float scale, int causal, int round_mode, void* stream);
+
 /* Size in bytes of the fixed device array behind attn_fwd_bf16_hd_noalloc:
  * 256 partial query tiles x 256 rows x (128 + 2) fp32 values, the largest
  * split workspace the planner asks for on a 256-CU gfx950 device. */

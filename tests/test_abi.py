@@ -213,3 +213,34 @@ def test_paged_valid_arguments_reach_device_check():
     assert call_paged() == -8
     assert call_paged(causal=1, hd=64, layout=1) == -8
     assert call_paged(pps=5, max_kv=320) == -8                          # exactly covered
+
+
+def call_varlen(**kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), lse=None,
+             cq=FAKE + (4 << 30), ck=FAKE + (5 << 30), B=3, Hq=4, Hkv=2, tq=500, tk=700, mq=300, mk=400,
+             hd=128, scale=0.0883883, causal=0, mode=0, stream=0)
+    a.update(kw)
+    return load_library().attn_fwd_bf16_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                                               a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"], a["mk"],
+                                               a["hd"], a["scale"], a["causal"], a["mode"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=0), -1), (dict(ck=0), -1), (dict(q=0), -1), (dict(o=0), -1),
+    (dict(B=0), -4), (dict(tq=0), -4), (dict(tk=0), -4), (dict(mq=0), -4), (dict(mk=0), -4),
+    (dict(hd=96), -4), (dict(Hkv=3), -4), (dict(tq=1 << 31), -4), (dict(mk=1 << 31), -4),
+    (dict(cq=FAKE + (4 << 30) + 2), -6), (dict(ck=FAKE + (5 << 30) + 1), -6), (dict(q=FAKE + 8), -6),
+    (dict(o=FAKE + (1 << 30) + 64), -7),                                  # o inside k
+    (dict(lse=FAKE + (3 << 30) + 16), -7),                                # lse inside o
+    (dict(mode=5), -3), (dict(causal=2), -11), (dict(scale=float("nan")), -5),
+])
+def test_varlen_argument_errors_before_device(kw, code):
+    assert call_varlen(**kw) == code
+
+
+def test_varlen_valid_arguments_reach_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_varlen() == -8
+    assert call_varlen(causal=1, hd=64, lse=FAKE + (6 << 30)) == -8
