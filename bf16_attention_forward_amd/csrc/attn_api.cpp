@@ -142,6 +142,9 @@ struct RunOpts {
     const int* cu_q = nullptr;     // device [B + 1]: packed sequences, prefix sums of the query rows
     const int* cu_k = nullptr;     // and of the key rows (Sq, Skv: the longest sequence)
     int64_t total_q = 0, total_k = 0;   // rows of the packed tensors
+    const int* block_table = nullptr;   // device [B][pages_per_seq]: k, v are a paged cache read in place
+    int page_shift = 0, pages_per_seq = 0;
+    int64_t num_pages = 0;
     bool kv_internal = false;      // k, v: the library's own BSHD copy (no alias or alignment check)
     bool check_only = false;       // validate the arguments, touch no device
     std::function<int(int)> pre_launch;   // runs after every check, right before the kernels are queued
@@ -228,6 +231,10 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.cu_k = opt.cu_k;
     p.total_q = (int)opt.total_q;
     p.total_k = (int)opt.total_k;
+    p.block_table = opt.block_table;
+    p.page_shift = opt.page_shift;
+    p.pages_per_seq = opt.pages_per_seq;
+    p.num_pages = opt.num_pages;
     if (layout == ATTN_LAYOUT_BSHD) {
         p.q_row = H * kHeadDim; p.q_head = kHeadDim; p.q_batch = Sq * H * kHeadDim;
     } else {
@@ -238,6 +245,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     } else {
         p.kv_row = kHeadDim; p.kv_head = Skv * kHeadDim; p.kv_batch = Hkv * Skv * kHeadDim;
     }
+    if (opt.block_table) p.kv_batch = 0;   // a paged cache: an entry's rows come from its pages
     p.B = (int)B; p.H = (int)H; p.Sq = (int)Sq; p.Skv = (int)Skv;
     p.group = (int)(H / Hkv);
     p.causal = causal;
@@ -398,6 +406,20 @@ extern "C" int attn_fwd_bf16_paged(const void* q, const void* k_cache, const voi
     const int crc = run_attention(q, placeholder, placeholder, o, lse, layout, B, Hq, Hkv, Sq, max_kv_len, head_dim,
                                   scale, causal, round_mode, stream, opt);
     if (crc != ATTN_OK) return crc;
+    // Pages of a power-of-two number of rows, at least one key tile: the
+    // attention kernel reads the keys and values in place (a key tile never
+    // straddles two pages); other page sizes go through a contiguous copy.
+    if (page_size >= kKeyTile && (page_size & (page_size - 1)) == 0) {
+        int shift = 0;
+        while (((int64_t)1 << shift) < page_size) shift++;
+        opt.check_only = false;
+        opt.block_table = block_table;
+        opt.page_shift = shift;
+        opt.pages_per_seq = (int)pages_per_seq;
+        opt.num_pages = num_pages;
+        return run_attention(q, k_cache, v_cache, o, lse, layout, B, Hq, Hkv, Sq, max_kv_len, head_dim, scale,
+                             causal, round_mode, stream, opt);
+    }
     int dev = -1;
     DeviceInfo info;
     const int drc = probe_device(&dev, &info);

@@ -52,6 +52,11 @@ struct AttnParams {
     const int* cu_q;     // optional packed sequences: [B + 1] prefix sums of the query rows (Sq: the longest)
     const int* cu_k;     // and of the key rows (Skv: the longest); q, o, k, v hold the rows of all entries
     int total_q, total_k;  // rows of the packed tensors
+    // keys and values read in place from a paged cache (k, v: [pages][page_size][Hkv][D])
+    const int* block_table;  // optional [B][pages_per_seq]: page of each page_size rows of an entry
+    int page_shift;          // log2(page_size), page_size a power of two >= 64 (one key tile per page at most)
+    int pages_per_seq;
+    int64_t num_pages;
     float* ws_o;       // split partial outputs [n_items - n_full][kv_splits][BM][128] (fp32)
     float* ws_ml;      // split partial (M, l) pairs [n_items - n_full][kv_splits][BM][2]
     int64_t q_row, q_head, q_batch;      // element strides of q and o

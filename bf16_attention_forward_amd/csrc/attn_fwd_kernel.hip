@@ -364,7 +364,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // Buffer descriptor of a head's K or V rows [0, kv_end) (rows of
     // kv_row_bytes): reads at or beyond kv_end return zero.
     auto kv_rsrc = [&](const char* base, int kv_end, int kv_row_bytes) __attribute__((always_inline)) -> i32x4 {
-        const uint32_t nrec = (uint32_t)((int64_t)(kv_end - 1) * kv_row_bytes + ROW_BYTES);
+        const uint32_t nrec = kv_end > 0 ? (uint32_t)((int64_t)(kv_end - 1) * kv_row_bytes + ROW_BYTES) : 0u;
         const uint64_t a = (uint64_t)(uintptr_t)base;
         return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)nrec, 0x00020000};
     };
@@ -462,18 +462,43 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
             __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                              :: "s"(lds), "v"(voff), "s"(rsu), "s"(so) : "memory", "m0");
         };
-        // round r of the K (or V) tile that starts at key k0
-        auto dma_k = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
-            dma16(krs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 + RPR * r) * kv_row_bytes);
+        // Where a K or V tile comes from: a descriptor and the key of its first
+        // row.  Keys in place in a paged cache (per-entry counts with a block
+        // table): the tile's page -- a page holds whole tiles -- with rows up to
+        // the entry's last key in it, and no rows at all for a table entry
+        // outside the pool; otherwise the item's descriptor from row 0.
+        struct TileSrc {
+            i32x4 rs;
+            int first;
         };
-        auto dma_v = [&](int r, int k0, uint8_t* dst) __attribute__((always_inline)) {
-            dma16(vrs4, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 + RPR * r) * kv_row_bytes);
+        auto tile_src = [&](const char* head_base, const i32x4& item_rs, int k0) __attribute__((always_inline)) -> TileSrc {
+            if (!KVL || !P.block_table) return TileSrc{item_rs, 0};
+            const int i = k0 >> P.page_shift;
+            const int first = i << P.page_shift;
+            // the table through the constant address space: it does not change
+            // during the kernel, so the read is a scalar load (no vector memory
+            // wait at the head of the MFMA phase)
+            typedef const __attribute__((address_space(4))) int const_int;
+            const_int* bt = (const_int*)(uintptr_t)P.block_table;
+            const int pg = bt[(int64_t)L.b * P.pages_per_seq + i];
+            const bool ok = pg >= 0 && pg < P.num_pages;
+            const int end = min(kv_end, first + (1 << P.page_shift));
+            const char* pb = head_base + (ok ? ((int64_t)pg << P.page_shift) * kv_row_bytes : (int64_t)0);
+            return TileSrc{kv_rsrc(pb, ok ? end - first : 0, kv_row_bytes), first};
+        };
+        // round r of the K (or V) tile that starts at key k0, from src
+        auto dma_k = [&](int r, const TileSrc& src, int k0, uint8_t* dst) __attribute__((always_inline)) {
+            dma16(src.rs, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (k0 - src.first + RPR * r) * kv_row_bytes);
+        };
+        auto dma_v = [&](int r, const TileSrc& src, int k0, uint8_t* dst) __attribute__((always_inline)) {
+            dma16(src.rs, dst + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_v, (k0 - src.first + RPR * r) * kv_row_bytes);
         };
         const int qrow0 = qt * BM + wave * 16 * NQB;   // first query row of this wave
         if (!prefetched) {
             if (!late) {
+                const TileSrc src = tile_src(kbase, krs4, kv_begin);
 #pragma unroll
-                for (int r = 0; r < DMA_ROUNDS; r++) dma_k(r, kv_begin, sk0);
+                for (int r = 0; r < DMA_ROUNDS; r++) dma_k(r, src, kv_begin, sk0);
             }
             load_q(P, qbase, qrow0, sq);
         }
@@ -571,6 +596,16 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
             for (int i = 0; i < NKS; i++) __asm__ volatile("" : "+v"(k_addr[i]));
 #pragma unroll
             for (int i = 0; i < NDB; i++) __asm__ volatile("" : "+v"(v_addr[i]));
+            // the sources of this iteration's transfers (K_{t+1}, V_t), looked up
+            // before the first fragment read, so a page-table read waits for no
+            // LDS read
+            const int kk0 = kv_begin + min(t + 1, T - 1) * BN, vk0 = kv_begin + t * BN;
+            TileSrc ksrc{krs4, 0}, vsrc{vrs4, 0};
+            if (KVL && S0 == 0 && !LATE) {
+                ksrc = tile_src(kbase, krs4, kk0);
+                vsrc = tile_src(vbase, vrs4, vk0);
+                __asm__ volatile("" :: "s"(ksrc.rs), "s"(vsrc.rs));
+            }
             bf16x8 fr[PF];
 #pragma unroll
             for (int st = S0; st < S0 + PF && st < S1; st++) fr[(st - S0) % PF] = read_frag(st, kt, vt);
@@ -580,8 +615,8 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
                 if (S0 == 0 && (st - S0) % STRIDE == 0 && (st - S0) / STRIDE < NDMA && !LATE) {
                     const int k = (st - S0) / STRIDE;     // K and V rounds alternate
-                    if (k & 1) dma_v(k >> 1, kv_begin + t * BN, vc);
-                    else dma_k(k >> 1, kv_begin + min(t + 1, T - 1) * BN, kn);
+                    if (k & 1) dma_v(k >> 1, vsrc, vk0, vc);
+                    else dma_k(k >> 1, ksrc, kk0, kn);
                 }
                 use_frag(st, cur);
             }

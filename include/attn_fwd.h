@@ -223,12 +223,16 @@ int attn_fwd_bf16_hd(const void* q, const void* k, const void* v, void* o, float
  *   causal      0, or 1: query i of entry b sees keys j <= i + kv_lens[b] -
  *               Sq (its queries are the last Sq positions of its keys)
  *
- * The library first copies each entry's kv_lens[b] key and value rows into
- * a contiguous per-(device, stream) workspace of 2 * B * max_kv_len * Hkv *
- * head_dim bf16 values (HIP's stream-ordered allocator, as for the split
- * partials; ATTN_ERR_WORKSPACE while the stream is being captured), then
- * runs the attention kernel on it with the per-entry key counts; the key
- * range is never split.  Every other argument, ownership, asynchrony and
+ * With page_size a power of two of at least 64 (a 64-key tile never
+ * straddles two pages) the attention kernel reads the keys and values in
+ * place, looking up each tile's page in the table; nothing is allocated.
+ * Other page sizes go through a copy: the library first copies each entry's
+ * kv_lens[b] key and value rows into a contiguous per-(device, stream)
+ * workspace of 2 * B * max_kv_len * Hkv * head_dim bf16 values (HIP's
+ * stream-ordered allocator, as for the split partials; ATTN_ERR_WORKSPACE
+ * while the stream is being captured), then runs the attention kernel on it
+ * with the per-entry key counts.  Either way the key range is never split
+ * and the results are the same bits.  Every other argument, ownership, asynchrony and
  * error behaviour are those of attn_fwd_bf16_hd; page_size, pages_per_seq
  * or num_pages below 1, or a table too narrow for max_kv_len, give
  * ATTN_ERR_SHAPE; a misaligned cache, table or kv_lens ATTN_ERR_ALIGN; o or

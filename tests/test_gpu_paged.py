@@ -145,3 +145,32 @@ def test_many_entries_unsorted_lengths():
         q = wl.random_qkv("bshd", B, 2, 40, 1, 75 + B)[0]
         o = run_paged(q, pk, "bshd", "rtne", False, scale=wl.DEFAULT_SCALE)
         gate_entries(o, q, pk, "bshd", "rtne", False, 128, wl.DEFAULT_SCALE, f"B={B}")
+
+
+def test_in_place_and_copy_paths_agree_bitwise():
+    """Pages of 128 rows (read in place) and of 96 rows (copied first) holding
+    the same logical rows give the same bits, causal and not."""
+    B, H, Sq = 3, 4, 200
+    pk = wl.make_paged_kv(B, 2, (700, 129, 400), 128, seed=76)
+    q = wl.random_qkv("bshd", B, H, Sq, 1, 76)[0]
+    ps2 = 96
+    pages = [(int(pk.kv_lens[b]) + ps2 - 1) // ps2 for b in range(B)]
+    kc = torch.zeros((sum(pages) + 1, ps2, 2, 128), dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    table = torch.full((B, max(pages)), -1, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        kb, vb = dense_kv(pk, b)
+        n = kb.shape[1]
+        for i in range(pages[b]):
+            rows = slice(i * ps2, min(n, (i + 1) * ps2))
+            m = rows.stop - rows.start
+            kc[nxt, :m] = kb[0, rows]
+            vc[nxt, :m] = vb[0, rows]
+            table[b, i] = nxt
+            nxt += 1
+    pk2 = wl.PagedKV(kc, vc, table, pk.kv_lens, ps2, pk.max_kv_len)
+    for causal in (False, True):
+        a = run_paged(q, pk, "bshd", "rtne", causal, scale=wl.DEFAULT_SCALE)
+        b2 = run_paged(q, pk2, "bshd", "rtne", causal, scale=wl.DEFAULT_SCALE)
+        assert np.array_equal(a, b2), causal
