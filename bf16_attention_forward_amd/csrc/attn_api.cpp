@@ -305,9 +305,11 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     // per-entry-length items differ in cost and keep one block per
     // work-group, so the hardware balances them as they finish; so do 4-wave
     // work-groups, two per CU, whose item boundaries overlap the other's
-    // work only when they run out of step.
+    // work only when they run out of step.  The next item's Q tile moves
+    // through one buffer descriptor, so its extent must fit 31 bits.
     p.grid = p.n_blocks;
-    if (!causal && !per_entry && nw == KERNEL_NW && head_dim == 128) {
+    const bool qtile_fits = (bm - 1) * (int64_t)p.q_row * 2 + kHeadDim * 2 < lim31;
+    if (!causal && !per_entry && nw == KERNEL_NW && head_dim == 128 && qtile_fits) {
         const int cap = std::max(8, (opt.grid > 0 ? opt.grid : slots) & ~7);
         if (cap < p.n_blocks) p.grid = cap;
     }

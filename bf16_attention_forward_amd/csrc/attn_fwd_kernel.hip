@@ -284,6 +284,18 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // in step and their epilogues coincide, which measured slower.  At head
     // dimension 64 the item loop costs more registers than it saves time.)
     constexpr bool PERSIST = !CAUSAL && !KVL && NWT == 8 && HD == 128;
+    // A persistent work-group's next Q tile, staged by DMA during the current
+    // item's last iteration: per wave, its NQB x NKS fragments in operand
+    // order (fragment n of lane l at byte 1024 n + 16 l), so that no register
+    // holds it across the last iteration and the epilogue (held in registers,
+    // the compiler spilled it, and the spill store waited for the load from
+    // memory), and the next item reads each fragment with one conflict-free
+    // ds_read_b128.  Its smaller alignment places it after the four tile
+    // buffers, whose addresses then stay below 64 KiB and fold into the
+    // 16-bit offset field of every fragment read (below them, each read
+    // needed its own address add).
+    constexpr int QSTAGE_WAVE = NQB * NKS * 1024;
+    __shared__ __attribute__((aligned(16))) uint8_t sq_stage[PERSIST ? NW * QSTAGE_WAVE : 16];
     struct Loc {
         int item, split, nsplit, qt, b, h, hk, coff, kv_begin, kv_end;
         int sq;                          // query rows of the entry
@@ -501,6 +513,14 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 for (int r = 0; r < DMA_ROUNDS; r++) dma_k(r, src, kv_begin, sk0);
             }
             load_q(P, qbase, qrow0, sq);
+        } else if (PERSIST) {
+            // the fragments this wave staged during the previous item (its own
+            // transfers, complete since that item's epilogue wait)
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++)
+                    qf[qb][ks] = *(const LDS_AS bf16x8*)(LDS_AS const uint8_t*)(sq_stage + wave * QSTAGE_WAVE + (qb * NKS + ks) * 1024 + lane * 16);
         }
         f32x4 o_acc[NDB][NQB];
 #pragma unroll
@@ -846,10 +866,12 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 softmax(t, std::integral_constant<bool, decltype(s1c)::value == SS>{});
             if (!LATE && !LAST) sync();
         };
-        // The next block of a persistent work-group: its Q fragments (this item's
-        // are dead during the last iteration, which only runs the P.V product)
-        // and, from the issuing waves, its first K tile into sk0 (no K buffer is
-        // read in the last iteration).
+        // The next block of a persistent work-group: each wave's rows of its Q
+        // tile into the wave's stage and, from the issuing waves, its first K
+        // tile into sk0 (no K buffer is read in the last iteration).  Q rows
+        // past the entry's end read as zero (the descriptor ends at its last
+        // row; one-block-per-item runs repeat the last row instead, and
+        // neither kind can trigger the tile redo, so both give the same bits).
         auto prefetch_next = [&]() __attribute__((always_inline)) {
             KParams& PN = kernel_params<true>();
             const int nv = vb + PN.grid;
@@ -863,7 +885,15 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 for (int r = 0; r < DMA_ROUNDS; r++)
                     dma16(nrs, sk0 + ((r * 4 + (wave & 3)) * 64) * 16, dma_off_k, (N.kv_begin + RPR * r) * kv_row_bytes);
             }
-            load_q(PN, nq, N.qt * BM + wave * 16 * NQB, N.sq);
+            const int qrow_bytes = (int)(PN.q_row * 2);
+            const i32x4 qrs = kv_rsrc((const char*)(nq + (int64_t)N.qt * BM * PN.q_row), min(BM, N.sq - N.qt * BM), qrow_bytes);
+            const int qvoff = j * qrow_bytes + 16 * g;   // lane (g, j): row 16 qb + j, dims 32 ks + 8 g
+#pragma unroll
+            for (int qb = 0; qb < NQB; qb++)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++)
+                    dma16(qrs, sq_stage + wave * QSTAGE_WAVE + (qb * NKS + ks) * 1024, qvoff,
+                          (wave * 16 * NQB + 16 * qb) * qrow_bytes + 64 * ks);
         };
         // the key loop, compiled once per wave group
         auto key_loop = [&](auto latec) __attribute__((always_inline)) {

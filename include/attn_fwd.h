@@ -131,7 +131,8 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
  * GPU holds at once runs on a persistent grid of one work-group per CU,
  * each taking every grid-th block of the plan); n >= 1 = at most n 8-wave
  * work-groups (n rounded down to a multiple of 8, at least 8; 4-wave
- * work-groups always run one per block).  Other values return
+ * work-groups always run one per block, and so does every plan whose
+ * 256-row query tile spans 2 GiB or more of q).  Other values return
  * ATTN_ERR_OPTION.  The result does not depend on block_order, waves or
  * grid; it may differ in the last bits with kv_splits.
  */
