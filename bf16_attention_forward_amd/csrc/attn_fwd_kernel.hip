@@ -109,12 +109,29 @@ __device__ __forceinline__ float rowsum4(float x) {
     return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
-// fp32 -> bf16 bits in the requested mode; NaN -> 0x7FC0.
-__device__ __forceinline__ uint32_t to_bf16_bits(float f, int mode) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    uint32_t add = (mode == ROUND_RTNE) ? (0x7fffu + ((u >> 16) & 1u)) : (mode == ROUND_RTNA ? 0x8000u : 0u);
-    return (u + add) >> 16;
+// fp32 -> bf16 in the requested mode as integer arithmetic on the bit
+// pattern: add 0x7FFF plus the lowest kept bit (nearest-even), 0x8000 (ties
+// away) or 0 (toward zero), keep the high half.  A NaN first becomes the
+// canonical quiet NaN, whose sum keeps the high half 0x7FC0 in every mode;
+// an infinity stays one, and the nearest modes overflow to it.  The mode's
+// addend and the width of the lowest-bit field (1 or 0) are uniform, so a
+// value costs a select, a bit-field extract and one three-way add, with no
+// branch.
+struct Bf16Round {
+    uint32_t base, lsb_width;
+};
+__device__ __forceinline__ Bf16Round bf16_round(int mode) {
+    return Bf16Round{mode == ROUND_RTNE ? 0x7fffu : (mode == ROUND_RTNA ? 0x8000u : 0u), mode == ROUND_RTNE ? 1u : 0u};
+}
+// the rounded value in the high half of the result (the low half is discarded)
+__device__ __forceinline__ uint32_t bf16_round_hi(float f, Bf16Round m) {
+    // an integer select: a floating-point select may pass any NaN through
+    const uint32_t u = __builtin_isnan(f) ? 0x7fc00000u : __float_as_uint(f);
+    return u + m.base + __builtin_amdgcn_ubfe(u, 16, m.lsb_width);
+}
+// a and b rounded, packed as bf16 (a in the low half)
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b, Bf16Round m) {
+    return __builtin_amdgcn_perm(bf16_round_hi(b, m), bf16_round_hi(a, m), 0x07060302u);
 }
 
 // o / l with a reciprocal and one residual correction (q1 = q0 + (o - q0 l) r).
@@ -944,17 +961,16 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 const float lr = l_row[qb];
                 const float inv = 1.0f / lr;
                 const bool no_key = CAUSAL && row + coff < 0;
+                const Bf16Round rm = bf16_round(P.round_mode);
                 uint16_t* dst = obase + (int64_t)row * P.q_row + 4 * g;
 #pragma unroll
                 for (int db = 0; db < NDB; db++) {
                     f32x4 ov;
 #pragma unroll
                     for (int r = 0; r < 4; r++) ov[r] = no_key ? 0.f : div_corrected(o_acc[db][qb][r], lr, inv);
-                    const uint32_t b0 = to_bf16_bits(ov[0], P.round_mode), b1 = to_bf16_bits(ov[1], P.round_mode);
-                    const uint32_t b2 = to_bf16_bits(ov[2], P.round_mode), b3 = to_bf16_bits(ov[3], P.round_mode);
                     uint2 packed;
-                    packed.x = b0 | (b1 << 16);
-                    packed.y = b2 | (b3 << 16);
+                    packed.x = bf16_pack2(ov[0], ov[1], rm);
+                    packed.y = bf16_pack2(ov[2], ov[3], rm);
                     *(uint2*)(dst + 16 * db) = packed;
                 }
             }
@@ -1022,8 +1038,9 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(const AttnParams p) {
     for (int r = 0; r < 4; r++) ov[r] = div_corrected(acc[r], l, inv);
     uint16_t* dst = p.o + (int64_t)b * p.q_batch + (int64_t)h * p.q_head + (int64_t)row * p.q_row + 4 * d4;
     uint2 packed;
-    packed.x = to_bf16_bits(ov[0], p.round_mode) | (to_bf16_bits(ov[1], p.round_mode) << 16);
-    packed.y = to_bf16_bits(ov[2], p.round_mode) | (to_bf16_bits(ov[3], p.round_mode) << 16);
+    const Bf16Round rm = bf16_round(p.round_mode);
+    packed.x = bf16_pack2(ov[0], ov[1], rm);
+    packed.y = bf16_pack2(ov[2], ov[3], rm);
     *(uint2*)dst = packed;
 }
 
