@@ -275,11 +275,14 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     constexpr int NDB = HD / 16;                 // 16-dim blocks of O
     constexpr int SS = 4 * NKS;                  // fragment steps of S^T (4 key blocks x NKS)
     constexpr int ST = SS + 2 * NDB;             // all steps of a tile (+ NDB x 2 k-steps of O^T)
-    // Row sums of the weights: with HD = 64 the softmax VALU work outweighs
-    // the MFMAs, so the sums go to the matrix core (ones^T P^T, 2 MFMAs per
-    // query block and tile); with HD = 128 the MFMAs dominate and the VALU
-    // adds the weights.
-    constexpr bool MFMA_SUM = HD == 64;
+    // Row sums of the weights on the matrix core (ones^T P^T, 2 MFMAs per
+    // query block and tile) instead of VALU adds: the SIMD's VALU work, which
+    // overlaps the matrix work only in part, shrinks by a third of the
+    // softmax.  Always at HD = 64 (the softmax outweighs the MFMAs there); at
+    // HD = 128 in the variants without the causal mask or per-entry key
+    // counts, the ones whose registers take it (those two spill inside the
+    // key loop with it).
+    constexpr bool MFMA_SUM = HD == 64 || (!CAUSAL && !KVL);
     // Four distinct LDS objects (K and V, two buffers each): with the buffer
     // choice a compile-time constant the compiler can tell that a DMA into one
     // buffer does not alias reads of another and does not wait for it.
@@ -643,13 +646,17 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 vsrc = tile_src(vbase, vrs4, vk0);
                 __asm__ volatile("" :: "s"(ksrc.rs), "s"(vsrc.rs));
             }
-            bf16x8 fr[PF];
+            // a persistent work-group's last iteration (P.V only) reads two
+            // steps ahead: its accumulators and the epilogue's values leave
+            // fewer registers there
+            constexpr int PFL = PERSIST && S0 != 0 ? 2 : PF;
+            bf16x8 fr[PFL];
 #pragma unroll
-            for (int st = S0; st < S0 + PF && st < S1; st++) fr[(st - S0) % PF] = read_frag(st, kt, vt);
+            for (int st = S0; st < S0 + PFL && st < S1; st++) fr[(st - S0) % PFL] = read_frag(st, kt, vt);
 #pragma unroll
             for (int st = S0; st < S1; st++) {
-                const bf16x8 cur = fr[(st - S0) % PF];
-                if (st + PF < S1) fr[(st - S0) % PF] = read_frag(st + PF, kt, vt);
+                const bf16x8 cur = fr[(st - S0) % PFL];
+                if (st + PFL < S1) fr[(st - S0) % PFL] = read_frag(st + PFL, kt, vt);
                 if (S0 == 0 && (st - S0) % STRIDE == 0 && (st - S0) / STRIDE < NDMA && !LATE) {
                     const int k = (st - S0) / STRIDE;     // K and V rounds alternate
                     if (k & 1) dma_v(k >> 1, vsrc, vk0, vc);
@@ -657,16 +664,16 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 }
                 use_frag(st, cur);
             }
-            // keep the interleave: the reads of step st+PF, then the MFMAs of step st
+            // keep the interleave: the reads of step st+PFL, then the MFMAs of step st
 #pragma unroll
-            for (int st = S0; st < S0 + PF && st < S1; st++) {
+            for (int st = S0; st < S0 + PFL && st < S1; st++) {
                 if (st < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
 #pragma unroll
             for (int st = S0; st < S1; st++) {
-                if (st + PF < S1) {
-                    if (st + PF < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (st + PFL < S1) {
+                    if (st + PFL < SS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
                 if (MFMA_SUM && st >= SS && (st - SS) % NDB == NDB - 1) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);

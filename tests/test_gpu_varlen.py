@@ -65,14 +65,16 @@ def test_varlen_matches_oracle(case, mode):
 
 
 def test_single_sequence_equals_dense_bitwise():
-    """One sequence of the whole tensor gives the dense call's bits (the same
-    kernel on the same rows, keys unsplit)."""
-    from bf16_attention_forward_amd import attn_fwd_bf16
+    """One sequence of the whole tensor gives the dense call's bits under the
+    causal mask (the same kernel code on the same rows, keys unsplit; without
+    the mask the dense kernel at head dimension 128 sums the weights on the
+    matrix core and the per-sequence one with VALU adds)."""
+    from bf16_attention_forward_amd import attn_fwd_bf16_gqa
     S, Skv, H = 700, 900, 4
     pk = wl.make_packed(H, H, (S,), (Skv,), seed=81)
-    a = run_varlen(pk, scale=wl.DEFAULT_SCALE)
-    bd = attn_fwd_bf16(to_dev(pk.q[None]), to_dev(pk.k[None]), to_dev(pk.v[None]), layout="bshd",
-                       scale=wl.DEFAULT_SCALE, kv_splits=1)
+    a = run_varlen(pk, causal=True, scale=wl.DEFAULT_SCALE)
+    bd = attn_fwd_bf16_gqa(to_dev(pk.q[None]), to_dev(pk.k[None]), to_dev(pk.v[None]), layout="bshd",
+                           scale=wl.DEFAULT_SCALE, causal=True)
     torch.cuda.synchronize()
     assert np.array_equal(a, wl.bits(bd.cpu()[0]))
 
