@@ -477,8 +477,12 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         const i32x4 krs4 = kv_rsrc(kbase, kv_end, kv_row_bytes), vrs4 = kv_rsrc(vbase, kv_end, kv_row_bytes);
         auto dma16 = [&](const i32x4 rs, uint8_t* dst, int voff, int soff) __attribute__((always_inline)) {
             // the LDS address, the descriptor and the tile offset are
-            // wave-uniform; say so, so they stay in scalar registers
-            const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS uint8_t*)dst);
+            // wave-uniform; say so, so they stay in scalar registers.  The
+            // LDS address is the low half of the generic pointer (the shared
+            // aperture sits in the high half): a cast to the LDS address
+            // space would add a null test, two scalar instructions per
+            // transfer in the MFMA phase.
+            const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
             const int so = __builtin_amdgcn_readfirstlane(soff);
             const i32x4 rsu = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
                                __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
