@@ -216,8 +216,12 @@ __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
 // operand B).  The same software pipeline and out-of-phase wave groups as the
 // dK/dV kernel below: iteration t runs dQ^T += K_{t-1}^T dS^T_{t-1} (K_{t-1}
 // read transposed) and S^T_t = K_t Q^T, dP^T_t = V_t dO^T (tiles t read
-// straight), then the elementwise step of tile t; three K/V slots.
-constexpr int NSLOT = 3;
+// straight), then the elementwise step of tile t.  Four K/V slots: waves 0-3
+// issue the transfers of tile t+2 after their elementwise step of tile t,
+// where the SIMD's scalar and memory issue is idle (at the head of the
+// products they delayed the matrix work: 1.6-2.6% of the whole backward),
+// and their barrier leaves those transfers in flight.
+constexpr int NSLOT = 4;
 
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
@@ -264,13 +268,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     // tile 0: all 8 waves; later tiles: waves 0-3
     issue_tile_n<HD, NW>(ks, 0, kslot(0), wave, g, j);
     issue_tile_n<HD, NW>(vs, 0, vslot(0), wave, g, j);
-    auto issue_next = [&](int t) __attribute__((always_inline)) {
-        if (!late && t < T) {
-            const int sl = t % NSLOT;
-            issue_tile_n<HD, 4>(ks, t * TILE_ROWS, kslot(sl), wave, g, j);
-            issue_tile_n<HD, 4>(vs, t * TILE_ROWS, vslot(sl), wave, g, j);
-        }
+    // tile t (past the last tile: the last tile again) into slot t % NSLOT,
+    // from waves 0-3
+    auto issue_tile = [&](int t) __attribute__((always_inline)) {
+        const int tt = min(t, T - 1);
+        const int sl = t % NSLOT;
+        issue_tile_n<HD, 4>(ks, tt * TILE_ROWS, kslot(sl), wave, g, j);
+        issue_tile_n<HD, 4>(vs, tt * TILE_ROWS, vslot(sl), wave, g, j);
     };
+    constexpr int NDMA_Q = 2 * (TILE_ROWS / ((64 / (HD / 8)) * 4));   // transfers of one issue_tile per wave
 
     // Q and dO of query rows qrow0 + 16*qb + j (clamped; results of rows past
     // Sq are never stored), dims 32*kk + 8*g .. +7: operand B.
@@ -316,6 +322,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         const int row = 4 * g + (j >> 2);
         a_col[db] = row * ROW_BYTES + (((2 * db + ((j & 3) >> 1)) ^ swz<HD>(row)) << 4) + ((j & 1) << 3);
     }
+    if (!late) issue_tile(1);   // waves 0-3: tile 1 (the first barrier waits for it)
     lds_barrier();
 
     f32x4 s[4][2], dp[4][2];   // S^T, dP^T of tile t: lane (g, j) holds keys 16*kb + 4*g + r of query j
@@ -382,10 +389,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         else ew(std::false_type{});
     };
     // barrier of waves 0-3: after their elementwise step (the operands keep the
-    // compiler from sinking that step below the barrier)
+    // compiler from sinking that step below the barrier) and the transfers
+    // of the tile two ahead, which stay in flight (in-order completion: the
+    // tile one ahead, issued an iteration earlier, has landed)
     auto early_barrier = [&]() __attribute__((always_inline)) {
         __asm__ volatile("" :: "v"(dsf[0][0]), "v"(dsf[0][1]), "v"(dsf[1][0]), "v"(dsf[1][1]));
-        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(NDMA_Q) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto pin_addr = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -395,17 +406,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     };
 
     // iteration 0: products of tile 0 only
-    issue_next(1);
     pin_addr();
     __builtin_amdgcn_s_setprio(1);
     products_a(0);
     __builtin_amdgcn_s_setprio(0);
     if (late) lds_barrier();
     elementwise(0);
-    if (!late) early_barrier();
+    if (!late) { issue_tile(2); early_barrier(); }
     int cur = 1 % NSLOT, prev = 0;
     for (int t = 1; t < T; t++) {
-        issue_next(t + 1);
         pin_addr();
         __builtin_amdgcn_s_setprio(1);
         products_b(prev);   // first: dS^T of tile t-1 is then dead while S^T, dP^T accumulate
@@ -413,10 +422,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
         __builtin_amdgcn_s_setprio(0);
         if (late) lds_barrier();
         elementwise(t);
-        if (!late) early_barrier();
+        if (!late) { issue_tile(t + 2); early_barrier(); }
         prev = cur;
         cur = cur == NSLOT - 1 ? 0 : cur + 1;
     }
+    // the transfers still in flight (the last iteration's repeat of the last
+    // tile) land before the waves end
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // the last tile's dQ products (no LDS writes follow: no barrier)
     pin_addr();
     products_b(prev);
