@@ -586,18 +586,30 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     // head's rows.  Every wave issues the L and delta transfers (the same
     // bytes to the same LDS words), so all waves issue NDMA + 2 transfers
     // per step, L and delta first.
-    auto issue_ld = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
+    // The descriptors of query head hq's L, delta, Q and dO rows.  A step's
+    // transfers use the ones of the head two steps ahead, kept across steps
+    // and rebuilt only when that head changes (the 64-bit offsets cost about
+    // twenty scalar instructions, in a step whose one wave issues every
+    // instruction itself).
+    struct HeadSrc {
+        i32x4 lse, dlt;
+        TileSrc q, g;
+    };
+    auto head_src = [&](int hq) __attribute__((always_inline)) -> HeadSrc {
         const int64_t rbh = ((int64_t)b * p.H + hq) * p.Sq;
-        dma4(buffer_rsrc(p.lse2 + rbh, (uint32_t)p.Sq * 4u), lslot(sl), lane * 4, r0 * 4);
-        dma4(buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u), lslot(sl) + TILE_ROWS * 4, lane * 4, r0 * 4);
-    };
-    auto issue_q = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
         const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)hq * p.q_head;
-        issue_tile_n<HD, DKV_NW>(tile_src<HD>(p.q + qoff, p.q_row, p.Sq), r0, qslot(sl), wave, g, j);
+        return HeadSrc{buffer_rsrc(p.lse2 + rbh, (uint32_t)p.Sq * 4u), buffer_rsrc(p.delta + rbh, (uint32_t)p.Sq * 4u),
+                       tile_src<HD>(p.q + qoff, p.q_row, p.Sq), tile_src<HD>(p.dO + qoff, p.q_row, p.Sq)};
     };
-    auto issue_g = [&](int sl, int hq, int r0) __attribute__((always_inline)) {
-        const int64_t qoff = (int64_t)b * p.q_batch + (int64_t)hq * p.q_head;
-        issue_tile_n<HD, DKV_NW>(tile_src<HD>(p.dO + qoff, p.q_row, p.Sq), r0, gslot(sl), wave, g, j);
+    auto issue_ld = [&](int sl, const HeadSrc& h, int r0) __attribute__((always_inline)) {
+        dma4(h.lse, lslot(sl), lane * 4, r0 * 4);
+        dma4(h.dlt, lslot(sl) + TILE_ROWS * 4, lane * 4, r0 * 4);
+    };
+    auto issue_q = [&](int sl, const HeadSrc& h, int r0) __attribute__((always_inline)) {
+        issue_tile_n<HD, DKV_NW>(h.q, r0, qslot(sl), wave, g, j);
+    };
+    auto issue_g = [&](int sl, const HeadSrc& h, int r0) __attribute__((always_inline)) {
+        issue_tile_n<HD, DKV_NW>(h.g, r0, gslot(sl), wave, g, j);
     };
     // step u runs tile u % T of the group's query head u / T
     auto step_hq = [&](int u) { return hk * p.group + u / T; };
@@ -619,16 +631,19 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     // steps 0 and 1 (past the last step, the transfers of step t + 2 repeat
     // the last step's tiles into the free slot, so every step issues the
     // same transfers)
-    issue_ld(0, step_hq(0), step_r0(0));
-    issue_q(0, step_hq(0), step_r0(0));
-    issue_g(0, step_hq(0), step_r0(0));
     {
+        const HeadSrc h0 = head_src(step_hq(0));
+        issue_ld(0, h0, step_r0(0));
+        issue_q(0, h0, step_r0(0));
+        issue_g(0, h0, step_r0(0));
         const int u = min(1, TT - 1);
-        issue_ld(1, step_hq(u), step_r0(u));
-        issue_q(1, step_hq(u), step_r0(u));
-        issue_g(1, step_hq(u), step_r0(u));
+        const HeadSrc h1 = head_src(step_hq(u));
+        issue_ld(1, h1, step_r0(u));
+        issue_q(1, h1, step_r0(u));
+        issue_g(1, h1, step_r0(u));
     }
     int uh = min(2, TT - 1) / T, utq = min(2, TT - 1) % T;   // query head and tile of step min(t + 2, TT - 1)
+    HeadSrc hsrc = head_src(hk * p.group + uh);                // that head's descriptors
     // wait for the K and V loads here, once (not inside the loop, where the
     // wait would also hold for the transfers in flight)
 #pragma unroll
@@ -664,12 +679,13 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     f32x4 l20 = read_l2(lslot(0), 0), dl0 = read_dl(lslot(0), 0);
 
     // one step on the tile in slot sl (first query row r0), issuing the
-    // transfers of tile dr0 of head dhq into slot dsl among its products;
+    // transfers of tile dr0 of the head whose descriptors are dh into slot
+    // dsl among its products;
     // MASK: apply the causal mask by select.  Rows past Sq need no select: their Q, dO, L
     // and delta read as zero, so their weight is 2^0 = 1 and their dS is
     // 1 * (0 - 0) = 0, and both meet zero rows of dO and Q in the dV and dK
     // products.
-    auto run_step = [&](auto mask_c, int sl, int r0, int nsl, int dsl, int dhq, int dr0) __attribute__((always_inline)) {
+    auto run_step = [&](auto mask_c, int sl, int r0, int nsl, int dsl, const HeadSrc& dh, int dr0) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_c)::value;
         const lds_u8* qt = qslot(sl);
         const lds_u8* gt = gslot(sl);
@@ -766,8 +782,8 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
 #pragma unroll
             for (int kk = 0; kk < NKK; kk++) {
                 if (kk == 0 && mb < 3) read_ld(mb + 1);
-                if (kk == 0 && mb == 1) { issue_ld(dsl, dhq, dr0); issue_q(dsl, dhq, dr0); }
-                if (kk == 0 && mb == 2) issue_g(dsl, dhq, dr0);
+                if (kk == 0 && mb == 1) { issue_ld(dsl, dh, dr0); issue_q(dsl, dh, dr0); }
+                if (kk == 0 && mb == 2) issue_g(dsl, dh, dr0);
                 int nr = (kk == 0 && mb < 3) ? 2 : 0;
                 if (mb < 3) { read_a(mb + 1, kk); nr += 2; }
                 else if (kk < PD) { read_b(0, kk); nr += 4; }
@@ -829,10 +845,13 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
         const int r0 = q0 + tq * TILE_ROWS;             // first query row of the step's tile
         const int nsl = sl == DKV_NSLOT - 1 ? 0 : sl + 1;
         run_step(std::integral_constant<bool, CAUSAL>{}, sl, r0, nsl, (t + 2) & (DKV_NSLOT - 1),
-                 hk * p.group + uh, q0 + utq * TILE_ROWS);
+                 hsrc, q0 + utq * TILE_ROWS);
         if (t + 3 < TT) {
             utq = utq == T - 1 ? 0 : utq + 1;
-            uh += utq == 0;
+            if (utq == 0) {
+                uh++;
+                hsrc = head_src(hk * p.group + uh);
+            }
         }
         sl = nsl;
         tq = tq == T - 1 ? 0 : tq + 1;
