@@ -209,7 +209,7 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     if (causal != 0 && causal != 1) return ATTN_ERR_OPTION;
     if (causal && (kv_splits > 1 || block_order == 2)) return ATTN_ERR_OPTION;
     if (per_entry && kv_splits > 1) return ATTN_ERR_OPTION;
-    if (opt.grid < 0 || (opt.grid > 0 && (causal || per_entry))) return ATTN_ERR_OPTION;
+    if (opt.grid < 0 || (opt.grid > 0 && per_entry)) return ATTN_ERR_OPTION;
     if (kv_lens && ((uintptr_t)kv_lens & 3)) return ATTN_ERR_ALIGN;
     if (packed && (((uintptr_t)opt.cu_q | (uintptr_t)opt.cu_k) & 3)) return ATTN_ERR_ALIGN;
     if (opt.check_only) return ATTN_OK;
@@ -294,22 +294,23 @@ int run_attention(const void* q, const void* k, const void* v, void* o, float* l
     p.kv_splits = splits;
     p.n_kv_tiles = n_kv_tiles;
     p.n_blocks = n_full + (p.n_items - n_full) * splits;
-    // Without the causal mask or per-entry key counts every block of the
-    // plan costs the same (the split blocks of the last round alike), and an
-    // 8-wave plan at head dimension 128 with more blocks than resident
-    // work-groups runs on a persistent grid of one work-group per slot
-    // (the item loop does not pay at head dimension 64): each takes every grid-th
-    // block and fetches the next one's Q and first K tile under its current
-    // item's last iteration.  The grid is a multiple of 8, so each block
-    // keeps the XCD the XCD-aware order gave it.  Causal and
-    // per-entry-length items differ in cost and keep one block per
-    // work-group, so the hardware balances them as they finish; so do 4-wave
-    // work-groups, two per CU, whose item boundaries overlap the other's
-    // work only when they run out of step.  The next item's Q tile moves
-    // through one buffer descriptor, so its extent must fit 31 bits.
+    // An 8-wave plan at head dimension 128 without per-entry key counts and
+    // with more blocks than resident work-groups runs on a persistent grid
+    // of one work-group per slot (the item loop does not pay at head
+    // dimension 64): each runs one block per round and fetches the next
+    // one's Q and first K tile under its current item's last iteration.
+    // Without the causal mask every block costs the same and work-group w
+    // takes blocks w, w + G, w + 2G, ...; causal blocks, longest first, are
+    // walked back in every other round so that a long item pairs with a
+    // short one.  The grid is a multiple of 8, so each block keeps the XCD
+    // its order gave it.  Per-entry-length items keep one block per
+    // work-group, so the hardware balances them as they finish; so do
+    // 4-wave work-groups, two per CU, whose item boundaries overlap the
+    // other's work only when they run out of step.  The next item's Q tile
+    // moves through one buffer descriptor, so its extent must fit 31 bits.
     p.grid = p.n_blocks;
     const bool qtile_fits = (bm - 1) * (int64_t)p.q_row * 2 + kHeadDim * 2 < lim31;
-    if (!causal && !per_entry && nw == KERNEL_NW && head_dim == 128 && qtile_fits) {
+    if (!per_entry && nw == KERNEL_NW && head_dim == 128 && qtile_fits) {
         const int cap = std::max(8, (opt.grid > 0 ? opt.grid : slots) & ~7);
         if (cap < p.n_blocks) p.grid = cap;
     }

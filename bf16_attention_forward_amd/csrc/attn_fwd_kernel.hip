@@ -303,7 +303,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // item boundary with the other's matrix work; kept persistent, they run
     // in step and their epilogues coincide, which measured slower.  At head
     // dimension 64 the item loop costs more registers than it saves time.)
-    constexpr bool PERSIST = !CAUSAL && !KVL && NWT == 8 && HD == 128;
+    constexpr bool PERSIST = !KVL && NWT == 8 && HD == 128;
     // A persistent work-group's next Q tile, staged by DMA during the current
     // item's last iteration: per wave, its NQB x NKS fragments in operand
     // order (fragment n of lane l at byte 1024 n + 16 l), so that no register
@@ -405,7 +405,19 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
     // Rows past Sq are clamped (their results are never stored).
     bf16x8 qf[NQB][NKS];
 
+    // The plan's block that this work-group runs in round k: block k*G + w
+    // (w = the work-group, G = the grid).  Causal items run longest first, so
+    // odd rounds walk back (the groups of 8 in reverse order, each block's
+    // position within its group, and so its XCD, kept): a work-group that
+    // had one of the longest items in a round gets one of the shortest in the
+    // next, and the work-groups' totals stay close.
+    auto round_block = [&](KParams& p, int k) __attribute__((always_inline)) -> int {
+        const int w = blockIdx.x, G = p.grid;
+        const int off = (CAUSAL && (k & 1) && (G & 7) == 0) ? G - 8 - (w & ~7) + (w & 7) : w;
+        return k * G + off;
+    };
     int vb = blockIdx.x;
+    int round = 0;             // this work-group's item count so far
     bool prefetched = false;   // this item's Q and first K tile came with the previous item
     for (;;) {
         // The lane indices, from an opaque copy of the thread index: nothing
@@ -454,7 +466,13 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
                 for (int db = 0; db < NDB; db++) *(uint2*)(obase + (int64_t)row * P.q_row + 4 * g + 16 * db) = uint2{0u, 0u};
                 if (P.lse && g == 0) P.lse[lse_base(P, L) + row] = -__builtin_inff();
             }
-            return;
+            if (!PERSIST) return;
+            // a persistent work-group goes on with its next item (nothing was
+            // prefetched for it here)
+            vb = round_block(P, ++round);
+            if (vb >= P.n_blocks) return;
+            prefetched = false;
+            continue;
         }
 
         // The first four waves issue all K/V DMA: lane l of wave w in round r
@@ -902,7 +920,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
         // neither kind can trigger the tile redo, so both give the same bits).
         auto prefetch_next = [&]() __attribute__((always_inline)) {
             KParams& PN = kernel_params<true>();
-            const int nv = vb + PN.grid;
+            const int nv = round_block(PN, round + 1);
             if (nv >= PN.n_blocks) return;
             const Loc N = locate(PN, nv);
             const uint16_t* nq = PN.q + q_off(PN, N);
@@ -1003,7 +1021,7 @@ __global__ __launch_bounds__(NWT * 64, 8 / NWT) void attn_fwd_main(const AttnPar
             }
         }
         if (!PERSIST) break;
-        vb += P.grid;
+        vb = round_block(P, ++round);
         if (vb >= P.n_blocks) break;
         prefetched = true;
     }
