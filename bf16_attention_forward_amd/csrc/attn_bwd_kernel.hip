@@ -9,7 +9,7 @@
 //     dS = P o (dP - delta),   delta_i = <dO_i, O_i>,
 //     dQ = scale dS K,         dK = scale dS^T Q.
 // Three kernels:
-//  * attn_bwd_delta: delta_i, one thread per query row (fp32 from bf16),
+//  * attn_bwd_delta: delta_i, HD / 8 lanes per query row (fp32 from bf16),
 //    stored negated so that the dP products start from it, and the
 //    log-sum-exp in base 2.
 //  * attn_bwd_dq: one work-group of 8 waves owns 256 query rows (32 per wave,
@@ -184,31 +184,54 @@ __device__ __forceinline__ bf16x8 pack_b(const float* lo4, const float* hi4) {
 }
 
 // ---------------------------------------------------------------- delta
+// A row's 16-byte chunks go to consecutive lanes (HD / 8 lanes per row, so
+// each load of a wave reads whole rows, each one contiguous span), each lane
+// accumulates its 8 products and the row's lanes add theirs up by lane
+// exchange.  Each thread takes DELTA_PASSES rows, all loads issued before the
+// arithmetic, so enough bytes are in flight to stream O and dO at the memory
+// rate (one thread per row, each walking its own row, reached half of it).
+constexpr int DELTA_PASSES = 4;
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_delta(const BwdParams p) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (b*H + h)*Sq + i
-    if (r >= (int64_t)p.B * p.H * p.Sq) return;
-    const int i = (int)(r % p.Sq);
-    const int64_t bh = r / p.Sq;
-    const int h = (int)(bh % p.H), b = (int)(bh / p.H);
-    const int64_t off = (int64_t)b * p.q_batch + (int64_t)h * p.q_head + (int64_t)i * p.q_row;
-    const uint4* op = (const uint4*)(p.o + off);
-    const uint4* gp = (const uint4*)(p.dO + off);
-    float acc = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < HD / 8; c++) {
-        const uint4 a = op[c], g = gp[c];
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, gv[4] = {g.x, g.y, g.z, g.w};
+    constexpr int LPR = HD / 8;        // lanes per row
+    constexpr int RPP = 256 / LPR;     // rows per work-group and pass
+    const int64_t n = (int64_t)p.B * p.H * p.Sq;
+    const int c = threadIdx.x % LPR;
+    int64_t row[DELTA_PASSES];
+    uint4 a[DELTA_PASSES], g[DELTA_PASSES];
+#pragma unroll
+    for (int k = 0; k < DELTA_PASSES; k++) {
+        const int64_t r = ((int64_t)blockIdx.x * DELTA_PASSES + k) * RPP + threadIdx.x / LPR;   // (b*H + h)*Sq + i
+        row[k] = r;
+        a[k] = g[k] = uint4{0u, 0u, 0u, 0u};
+        if (r < n) {
+            const int i = (int)(r % p.Sq);
+            const int64_t bh = r / p.Sq;
+            const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+            const int64_t off = (int64_t)b * p.q_batch + (int64_t)h * p.q_head + (int64_t)i * p.q_row;
+            a[k] = ((const uint4*)(p.o + off))[c];
+            g[k] = ((const uint4*)(p.dO + off))[c];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < DELTA_PASSES; k++) {
+        const uint32_t av[4] = {a[k].x, a[k].y, a[k].z, a[k].w}, gv[4] = {g[k].x, g[k].y, g[k].z, g[k].w};
+        float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             acc = __builtin_fmaf(__uint_as_float(av[e] << 16), __uint_as_float(gv[e] << 16), acc);
             acc = __builtin_fmaf(__uint_as_float(av[e] & 0xffff0000u), __uint_as_float(gv[e] & 0xffff0000u), acc);
         }
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, LPR);
+        // stored negated: the dP products start from it, so dP - delta comes
+        // out of the matrix core; and the log-sum-exp in base 2, as the
+        // exponents use it
+        if (c == 0 && row[k] < n) {
+            p.delta[row[k]] = -acc;
+            p.lse2[row[k]] = p.lse[row[k]] * LOG2E;
+        }
     }
-    // stored negated: the dP products start from it, so dP - delta comes out
-    // of the matrix core; and the log-sum-exp in base 2, as the exponents use it
-    p.delta[r] = -acc;
-    p.lse2[r] = p.lse[r] * LOG2E;
 }
 
 // ------------------------------------------------------------------- dQ
@@ -892,7 +915,8 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
     auto go = [&](auto hd) -> int {
         constexpr int H_ = decltype(hd)::value;
         const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-        hipLaunchKernelGGL(attn_bwd_delta<H_>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
+        const int64_t per_group = DELTA_PASSES * 256 / (H_ / 8);
+        hipLaunchKernelGGL(attn_bwd_delta<H_>, dim3((unsigned)((rows + per_group - 1) / per_group)), dim3(256), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return -1;
         const dim3 gk((unsigned)((int64_t)p.B * p.Hkv * p.n_kblocks)), gq((unsigned)((int64_t)p.B * p.H * p.n_qblocks));
         if (p.causal) hipLaunchKernelGGL((attn_bwd_dkdv<H_, true>), gk, dim3(DKV_NW * 64), 0, stream, p);
