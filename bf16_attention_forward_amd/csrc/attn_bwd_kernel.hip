@@ -183,6 +183,22 @@ __device__ __forceinline__ bf16x8 pack_b(const float* lo4, const float* hi4) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ------------------------------------------------------------ block order
+// The hardware deals work-groups to the 8 XCDs round-robin (XCD = block id
+// mod 8), each XCD with its own L2.  A head's work-groups all stream the
+// same tiles (dQ: the head's K and V; dK/dV: its Q, dO, L and delta), so
+// without the mask block b runs work item order(b), XCD x holding the x-th
+// eighth of the items (head-major: a run of whole heads).  Under the mask
+// the items run longest first, rank-major (item = rank * BH + head), and
+// block b runs item b: when BH is a multiple of 8 each XCD already holds the
+// heads congruent to it mod 8 at every rank.
+__device__ __forceinline__ int bwd_item(int bid, int n, bool causal) {
+    if (causal) return bid;
+    const int x = bid & 7, s = bid >> 3;
+    const int per = n >> 3, rem = n & 7;
+    return x * per + (x < rem ? x : rem) + s;
+}
+
 // ---------------------------------------------------------------- delta
 // A row's 16-byte chunks go to consecutive lanes (HD / 8 lanes per row, so
 // each load of a wave reads whole rows, each one contiguous span), each lane
@@ -262,8 +278,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq(const BwdParams p) {
     // take the longest first (the last query tile of every head, then the
     // second last, ...) so the short ones fill the end of the launch
     const int BH = p.B * p.H;
-    const int qt = CAUSAL ? p.n_qblocks - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x % p.n_qblocks);
-    const int bh = CAUSAL ? (int)(blockIdx.x % BH) : (int)(blockIdx.x / p.n_qblocks);
+    const int it = bwd_item((int)blockIdx.x, (int)gridDim.x, CAUSAL);
+    const int qt = CAUSAL ? p.n_qblocks - 1 - it / BH : it % p.n_qblocks;
+    const int bh = CAUSAL ? it % BH : it / p.n_qblocks;
     const int h = bh % p.H, b = bh / p.H;
     const int qrow0 = qt * BMQ + wave * 32;
     // keys up to the diagonal of the work-group's last row under the mask
@@ -560,8 +577,9 @@ __global__ __launch_bounds__(DKV_NW * 64, 1) void attn_bwd_dkdv(const BwdParams 
     // under the mask a key block's query range shrinks with its index:
     // blocks take the longest (first key blocks of every head) first
     const int BH = p.B * p.Hkv;
-    const int kt_ = CAUSAL ? (int)(blockIdx.x / BH) : (int)(blockIdx.x % p.n_kblocks);
-    const int bh = CAUSAL ? (int)(blockIdx.x % BH) : (int)(blockIdx.x / p.n_kblocks);   // (b, key/value head)
+    const int it = bwd_item((int)blockIdx.x, (int)gridDim.x, CAUSAL);
+    const int kt_ = CAUSAL ? it / BH : it % p.n_kblocks;
+    const int bh = CAUSAL ? it % BH : it / p.n_kblocks;   // (b, key/value head)
     const int hk = bh % p.Hkv, b = bh / p.Hkv;
     const int kbase = kt_ * 128 + wave * 32;             // key block kb of this wave: keys kbase + 16 kb + j
     // query tiles [t0, t0 + T): under the mask the first query that sees the
