@@ -176,21 +176,23 @@ def test_causal_nonfinite_values_documented_pattern():
     assert_gate(st)
 
 
+@pytest.mark.parametrize("layout,mode", [("bshd", "rtne"), ("bhsd", "rtz")])
 @pytest.mark.parametrize("Sq,Skv", [(8192, 8192), (8192, 4096)])
-def test_causal_persistent_grid_equals_per_entry_calls_bitwise(Sq, Skv):
+def test_causal_persistent_grid_equals_per_entry_calls_bitwise(Sq, Skv, layout, mode):
     """Two batch entries of 6 query heads in 256-row tiles make 384 causal
     blocks, more than one 8-wave work-group per CU: they run on a persistent
     grid that walks the longest-first blocks back in every other round (with
     Sq > Skv the rows above the diagonal, placed last, take the no-key path
     inside the loop).  One entry alone is 192 blocks, one per work-group.
     Every row's arithmetic is the same either way, so the bits are too."""
-    layout, B, Hq, Hkv = "bshd", 2, 6, 2
-    say(f"[case] causal persistent {Sq}x{Skv}")
+    B, Hq, Hkv = 2, 6, 2
+    say(f"[case] causal persistent {Sq}x{Skv} {layout} {mode}")
     q, k, v = wl.random_qkv(layout, B, Hq, Sq, Skv, 64, Hkv=Hkv)
-    both = run_hip_gqa(q, k, v, layout, "rtne", causal=True)
+    both = run_hip_gqa(q, k, v, layout, mode, causal=True)
     for b in range(B):
         one = run_hip_gqa(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(), v[b:b + 1].contiguous(),
-                          layout, "rtne", causal=True)
+                          layout, mode, causal=True)
         assert np.array_equal(both[b:b + 1], one)
     if Sq > Skv:
-        assert np.all(both[:, :Sq - Skv] == 0)
+        rows = both[:, :Sq - Skv] if layout == "bshd" else both[:, :, :Sq - Skv]
+        assert np.all(rows == 0)
